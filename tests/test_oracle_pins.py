@@ -1,0 +1,330 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle itself.
+
+Each test names what it pins.  None of them calls the HIP library.
+"""
+
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute
+from oracle import relpos_oracle as orc
+from exact_attention_relative_amd.inputs import make_case
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+MASKS = {"none": (-1, -1), "causal": (-1, 0), "local": (2, 1)}
+
+
+def _case(mech, L=7, d=4, B=1, H=2, window=(-1, -1), seed=11, span=3, nb=8, md=12,
+          bidir=None, table_std=0.7, dtype="fp32"):
+    c = make_case(mech, B, H, L, d, dtype=dtype, window=window, seed=seed, rel_span=span,
+                  num_buckets=nb, max_distance=md, bidirectional=bidir, table_std=table_std)
+    p = orc.Params(**c["params"])
+    return c, p
+
+
+def _f64(c):
+    return (c["q"].astype(np.float64), c["k"].astype(np.float64), c["v"].astype(np.float64),
+            {n: t.astype(np.float64) for n, t in c["tables"].items()}, c["dout"].astype(np.float64))
+
+
+# ------------------------------------------------------------------------ T5 buckets
+
+def _golden_buckets():
+    rows = []
+    with open(os.path.join(GOLDEN, "t5_buckets.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            nb, md, bd, rel, exp = (int(x) for x in line.split())
+            rows.append((nb, md, bool(bd), rel, exp))
+    return rows
+
+
+@pytest.mark.parametrize("nb,md,bidir,rel,expected", _golden_buckets())
+def test_t5_bucket_closed_form(nb, md, bidir, rel, expected):
+    """Pin: hand-derived bucket thresholds, including exact power-of-two boundaries."""
+    assert orc.t5_bucket(rel, nb, md, bidir) == expected
+
+
+@pytest.mark.parametrize("nb,md,bidir", [(32, 128, True), (32, 1024, True), (32, 128, False),
+                                         (16, 64, True), (64, 512, False)])
+def test_t5_bucket_matches_float_log_form(nb, md, bidir):
+    """Pin: the integer-comparison floor equals the floating-point log form of the published
+    map on every offset |rel| < 8192 used by the workloads."""
+    for rel in range(-8191, 8192):
+        assert orc.t5_bucket(rel, nb, md, bidir) == brute._bucket_float(rel, nb, md, bidir), rel
+
+
+def test_t5_bucket_monotone_and_range():
+    """Pin: magnitude buckets never decrease with distance and stay inside the table."""
+    for bidir in (True, False):
+        prev = -1
+        for n in range(0, 9000):
+            b = orc.t5_bucket(-n, 32, 1024, bidir)
+            assert 0 <= b < 32
+            assert b >= prev
+            prev = b
+
+
+# ------------------------------------------------------------------------ index maps
+
+@pytest.mark.parametrize("mech", orc.MECHS)
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_index_maps_depend_only_on_offset(mech, mask):
+    """Pin: every table index is a function of i - j alone (idx[i][j] == idx[i+1][j+1])."""
+    L = 40
+    p = orc.Params(mech=mech, head_dim=8, window_left=MASKS[mask][0], window_right=MASKS[mask][1],
+                   num_buckets=16, max_distance=20, bidirectional=(mask == "none"), rel_span=5)
+    maps = orc.index_maps(np.arange(L), L, p)
+    for name, m in maps.items():
+        assert np.array_equal(m[1:, 1:], m[:-1, :-1]), name
+
+
+def test_index_map_clamps_closed_form():
+    """Pin: clamp rows written out at the ends of the span."""
+    L, k = 20, 4
+    p = orc.Params(mech="shaw", head_dim=8, rel_span=k)
+    row = orc.index_maps(np.arange(L), L, p)["row"]
+    assert row[10, 10] == k and row[10, 11] == k + 1 and row[10, 9] == k - 1
+    assert row[10, 14] == 2 * k and row[10, 19] == 2 * k and row[10, 6] == 0 and row[10, 0] == 0
+    p = orc.Params(mech="deberta", head_dim=8, rel_span=k)
+    m = orc.index_maps(np.arange(L), L, p)
+    # c2p row = clamp(i - j + k, 0, 2k-1); p2c row = clamp(j - i + k, 0, 2k-1)
+    assert m["c2p"][10, 10] == k and m["c2p"][10, 9] == k + 1 and m["c2p"][10, 11] == k - 1
+    assert m["c2p"][10, 0] == 2 * k - 1 and m["c2p"][10, 14] == 0
+    assert m["p2c"][10, 10] == k and m["p2c"][10, 11] == k + 1 and m["p2c"][10, 19] == 2 * k - 1
+    p = orc.Params(mech="txl", head_dim=8, window_right=0)
+    row = orc.index_maps(np.arange(L), L, p)["row"]
+    assert row[10, 3] == 7 and row[10, 10] == 0
+    p = orc.Params(mech="txl", head_dim=8)
+    row = orc.index_maps(np.arange(L), L, p)["row"]
+    assert row[10, 3] == 7 + L - 1 and row[3, 10] == -7 + L - 1
+
+
+# ------------------------------------------------------------------------ brute force
+
+@pytest.mark.parametrize("mech", orc.MECHS)
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_vectorised_matches_scalar_brute_force(mech, mask):
+    """Pin: pure-Python per-pair loops at L <= 8 agree with the vectorised oracle to 1e-12."""
+    c, p = _case(mech, L=8, d=4, B=1, H=2, window=MASKS[mask], span=3, nb=8, md=6,
+                 bidir=(mask != "causal"))
+    q, k, v, tab, _ = _f64(c)
+    O, LSE = orc.forward(p, q, k, v, tab)
+    tl = {n: t.tolist() for n, t in tab.items()}
+    for h in range(2):
+        Ob, Lb = brute.forward_head(p, q[0, h].tolist(), k[0, h].tolist(), v[0, h].tolist(), tl, h)
+        np.testing.assert_allclose(O[0, h], np.array(Ob), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(LSE[0, h], np.array(Lb), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------------------ library routine
+
+def _zero_tables(c):
+    return {n: np.zeros_like(t, dtype=np.float64) for n, t in c["tables"].items()}
+
+
+@pytest.mark.parametrize("mech", orc.MECHS)
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_zero_tables_reduce_to_sdpa(mech, mask):
+    """Pin: with every table zero the oracle is plain attention; forward and all three
+    input gradients match torch's scaled_dot_product_attention + autograd in float64."""
+    c, p = _case(mech, L=24, d=8, B=2, H=3, window=MASKS[mask], span=4, nb=8, md=16,
+                 bidir=(mask != "causal"))
+    q, k, v, _, do = _f64(c)
+    tab = _zero_tables(c)
+    O, LSE = orc.forward(p, q, k, v, tab)
+    dq, dk, dv, _ = orc.backward(p, q, k, v, tab, do)
+    L = q.shape[2]
+    mask_b = torch.from_numpy(orc.allowed_mask(np.arange(L), L, p))
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask_b,
+                                                           scale=p.s())
+    ref.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(O, ref.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_txl_position_free_is_attention_on_q_plus_u():
+    """Pin: T-XL with r = 0 is plain attention with queries q + u (library routine)."""
+    c, p = _case("txl", L=16, d=8, B=1, H=2, table_std=0.5)
+    q, k, v, tab, do = _f64(c)
+    tab["r"][:] = 0.0
+    O, _ = orc.forward(p, q, k, v, tab)
+    qu = q + tab["u"][None, :, None, :]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(qu), torch.from_numpy(k), torch.from_numpy(v), scale=p.s())
+    np.testing.assert_allclose(O, ref.numpy(), rtol=0, atol=1e-12)
+
+
+def test_t5_constant_bias_is_plain_attention():
+    """Pin: a T5 bias constant over buckets shifts every logit of a row equally."""
+    c, p = _case("t5", L=20, d=8, B=1, H=2, nb=8, md=10)
+    q, k, v, tab, _ = _f64(c)
+    tab["beta"][:] = 1.75
+    O, LSE = orc.forward(p, q, k, v, tab)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v), scale=p.s())
+    np.testing.assert_allclose(O, ref.numpy(), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_lse_closed_form(mask):
+    """Pin: with q = 0 and zero tables every allowed logit is 0, so LSE_i = ln(#allowed keys)."""
+    c, p = _case("shaw", L=12, d=4, window=MASKS[mask])
+    q, k, v, tab, _ = _f64(c)
+    q[:] = 0.0
+    _, LSE = orc.forward(p, q, k, v, _zero_tables(c))
+    L = 12
+    for i in range(L):
+        cnt = sum(1 for j in range(L)
+                  if (p.window_left < 0 or i - j <= p.window_left)
+                  and (p.window_right < 0 or j - i <= p.window_right))
+        assert abs(LSE[0, 0, i] - math.log(cnt)) < 1e-14
+
+
+# ------------------------------------------------------------------------ finite differences
+
+def _loss(p, q, k, v, tab, do):
+    O, _ = orc.forward(p, q, k, v, tab)
+    return float(np.sum(O * do))
+
+
+@pytest.mark.parametrize("mech", orc.MECHS)
+@pytest.mark.parametrize("mask", ["none", "causal"])
+def test_gradients_match_central_differences(mech, mask):
+    """Pin: every gradient element (q, k, v and every table) against central differences
+    of the forward pass in float64, h = 1e-6."""
+    c, p = _case(mech, L=6, d=3, B=1, H=2, window=MASKS[mask], span=2, nb=6, md=5,
+                 bidir=(mask != "causal"), table_std=0.6)
+    q, k, v, tab, do = _f64(c)
+    dq, dk, dv, g = orc.backward(p, q, k, v, tab, do)
+    h = 1e-6
+    targets = [("q", q, dq), ("k", k, dk), ("v", v, dv)]
+    targets += [(n, tab[n], g[n]) for n in tab]
+    for name, x, grad in targets:
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _loss(p, q, k, v, tab, do)
+            x[idx] = old - h
+            lm = _loss(p, q, k, v, tab, do)
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        scale = max(1.0, float(np.max(np.abs(fd))))
+        assert np.max(np.abs(fd - grad)) <= 1e-6 * scale, name
+
+
+# ------------------------------------------------------------------------ invariants
+
+@pytest.mark.parametrize("mech", orc.MECHS)
+def test_softmax_gradient_sums_vanish(mech):
+    """Pin: sum_j dS_ij = 0 exactly, hence sum_c dbeta[h,c] = 0, sum_c dw[c] = 0,
+    sum_c dKr[c] = 0 and sum_delta dr_h[delta] = 0."""
+    c, p = _case(mech, L=30, d=8, B=2, H=2, span=5, nb=10, md=20, table_std=0.5)
+    q, k, v, tab, do = _f64(c)
+    _, _, _, g = orc.backward(p, q, k, v, tab, do)
+    if mech == "t5":
+        assert np.max(np.abs(g["beta"].sum(axis=1))) < 1e-12
+    if mech == "shaw":
+        assert np.max(np.abs(g["w"].sum(axis=0))) < 1e-12
+    if mech == "deberta":
+        assert np.max(np.abs(g["kr"].sum(axis=0))) < 1e-12
+        assert np.max(np.abs(g["qr"].sum(axis=0))) > 1e-6   # column sums of dS do not vanish
+    if mech == "txl":
+        assert np.max(np.abs(g["r"].sum(axis=1))) < 1e-12
+
+
+def test_shaw_causal_future_rows_have_zero_gradient():
+    """Pin: under a causal mask no pair has j > i, so dw rows k+1..2k are exactly 0."""
+    c, p = _case("shaw", L=16, d=4, window=(-1, 0), span=4)
+    q, k, v, tab, do = _f64(c)
+    _, _, _, g = orc.backward(p, q, k, v, tab, do)
+    assert np.all(g["w"][5:] == 0.0)
+    assert np.max(np.abs(g["w"][:5])) > 0
+
+
+@pytest.mark.parametrize("mech", ["t5", "shaw", "txl"])
+def test_key_shift_invariance(mech):
+    """Pin: adding a constant vector to every key shifts each row's logits by one constant
+    (the relative terms do not involve k for these mechanisms), so O is unchanged."""
+    c, p = _case(mech, L=20, d=6, B=1, H=2, table_std=0.5, nb=8, md=10)
+    q, k, v, tab, _ = _f64(c)
+    O1, _ = orc.forward(p, q, k, v, tab)
+    O2, _ = orc.forward(p, q, k + np.linspace(-1, 2, 6), v, tab)
+    np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-12)
+
+
+def test_deberta_is_not_key_shift_invariant():
+    c, p = _case("deberta", L=20, d=6, table_std=0.5)
+    q, k, v, tab, _ = _f64(c)
+    O1, _ = orc.forward(p, q, k, v, tab)
+    O2, _ = orc.forward(p, q, k + np.linspace(-1, 2, 6), v, tab)
+    assert np.max(np.abs(O1 - O2)) > 1e-6
+
+
+# ------------------------------------------------------------------------ cross-mechanism
+
+def test_shaw_equals_txl_with_reversed_table():
+    """Pin: Shaw with k >= L-1 equals bidirectional T-XL with u = v = 0 and
+    r[delta + L - 1] = w[k - delta]; gradients map the same way."""
+    L, d, kk = 9, 4, 10
+    c, p = _case("shaw", L=L, d=d, B=1, H=2, span=kk, table_std=0.8)
+    q, k, v, tab, do = _f64(c)
+    w = tab["w"]
+    pt = orc.Params(mech="txl", head_dim=d)
+    deltas = np.arange(-(L - 1), L)
+    r = np.stack([w[kk - deltas]] * 2)                    # [H, 2L-1, d]
+    tx = {"r": r, "u": np.zeros((2, d)), "v": np.zeros((2, d))}
+    O1, L1 = orc.forward(p, q, k, v, tab)
+    O2, L2 = orc.forward(pt, q, k, v, tx)
+    np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(L1, L2, rtol=0, atol=1e-12)
+    g1 = orc.backward(p, q, k, v, tab, do)
+    g2 = orc.backward(pt, q, k, v, tx, do)
+    for a, b in zip(g1[:3], g2[:3]):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+    dr = g2[3]["r"].sum(axis=0)                            # r shared via stacking
+    np.testing.assert_allclose(g1[3]["w"][kk - deltas], dr, rtol=0, atol=1e-12)
+
+
+def test_deberta_c2p_equals_shaw_and_p2c_is_its_transpose():
+    """Pin: DeBERTa with Qr = 0 equals Shaw under the same scale with w[k_s - delta] =
+    Kr[delta + k_d]; and swapping (q, Kr) with (k, Qr) transposes the score matrix."""
+    L, d, kd, ks = 9, 4, 10, 9
+    c, p = _case("deberta", L=L, d=d, B=1, H=1, span=kd, table_std=0.8)
+    q, k, v, tab, _ = _f64(c)
+    s = p.s()
+    tab0 = {"kr": tab["kr"].copy(), "qr": np.zeros_like(tab["qr"])}
+    w = np.zeros((2 * ks + 1, d))
+    for delta in range(-(L - 1), L):
+        w[ks - delta] = tab0["kr"][delta + kd]
+    ps = orc.Params(mech="shaw", head_dim=d, rel_span=ks, scale=s)
+    O1, _ = orc.forward(p, q, k, v, tab0)
+    O2, _ = orc.forward(ps, q, k, v, {"w": w})
+    np.testing.assert_allclose(O1, O2, rtol=0, atol=1e-12)
+    rows = np.arange(L)
+    S = orc.scores_rows(p, q[0, 0], k[0, 0], tab, 0, rows)
+    St = orc.scores_rows(p, k[0, 0], q[0, 0], {"kr": tab["qr"], "qr": tab["kr"]}, 0, rows)
+    np.testing.assert_allclose(S, St.T, rtol=0, atol=1e-12)
+
+
+def test_bias_is_toeplitz_for_constant_rows():
+    """Pin: with every query row equal (Shaw, T-XL) or every key row equal (DeBERTa p2c)
+    the additive term depends on i - j only."""
+    for mech in ("shaw", "txl", "deberta"):
+        c, p = _case(mech, L=14, d=4, B=1, H=1, span=4, table_std=0.8)
+        q, k, v, tab, _ = _f64(c)
+        q[:] = q[:, :, :1, :]
+        k[:] = k[:, :, :1, :]
+        Bm = orc.bias_rows(p, q[0, 0], k[0, 0], tab, 0, np.arange(14))
+        np.testing.assert_allclose(Bm[1:, 1:], Bm[:-1, :-1], rtol=0, atol=1e-14)

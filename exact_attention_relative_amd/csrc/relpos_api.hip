@@ -1,0 +1,301 @@
+// C ABI: descriptor validation, workspace layout, T5 bucket thresholds and kernel dispatch.
+#include <math.h>
+#include <string.h>
+
+#include <vector>
+
+#include "../../include/relpos_attn.h"
+#include "relpos_kernels.h"
+
+using namespace relpos;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ------------------------------------------------------------------ exact T5 thresholds
+// Non-negative big integers, little-endian 32-bit limbs.
+struct Big {
+  std::vector<uint32_t> d{1u};
+  void mul(uint32_t m) {
+    uint64_t carry = 0;
+    for (auto& x : d) {
+      uint64_t v = (uint64_t)x * m + carry;
+      x = (uint32_t)v;
+      carry = v >> 32;
+    }
+    if (carry) d.push_back((uint32_t)carry);
+  }
+};
+int cmp(const Big& a, const Big& b) {
+  size_t na = a.d.size(), nb = b.d.size();
+  while (na > 1 && a.d[na - 1] == 0) --na;
+  while (nb > 1 && b.d[nb - 1] == 0) --nb;
+  if (na != nb) return na < nb ? -1 : 1;
+  for (size_t i = na; i-- > 0;)
+    if (a.d[i] != b.d[i]) return a.d[i] < b.d[i] ? -1 : 1;
+  return 0;
+}
+Big bigpow_prod(uint32_t x, int ex, uint32_t y, int ey) {
+  Big r;
+  for (int i = 0; i < ex; ++i) r.mul(x);
+  for (int i = 0; i < ey; ++i) r.mul(y);
+  return r;
+}
+// floor(ln(n / me) / ln(md / me) * E) >= t  <=>  n^E me^t >= md^t me^E
+bool reaches(uint32_t n, int t, uint32_t me, uint32_t md, int E) {
+  return cmp(bigpow_prod(n, E, me, t), bigpow_prod(md, t, me, E)) >= 0;
+}
+
+bool build_t5_map(const relpos_desc* d, T5Map* m) {
+  memset(m, 0, sizeof(*m));
+  const int nb = d->num_buckets;
+  m->bidirectional = d->bidirectional ? 1 : 0;
+  const int half = m->bidirectional ? nb / 2 : nb;
+  m->half = half;
+  m->max_exact = half / 2;
+  const int E = half - m->max_exact;
+  m->nthr = E - 1;
+  if (m->nthr > kMaxThresholds) return false;
+  const uint32_t me = (uint32_t)m->max_exact, md = (uint32_t)d->max_distance;
+  for (int t = 1; t <= E - 1; ++t) {
+    // smallest n in [me, md] with floor(...) >= t (n = md always reaches t <= E)
+    uint32_t lo = me, hi = md;
+    while (lo < hi) {
+      uint32_t mid = lo + (hi - lo) / 2;
+      if (reaches(mid, t, me, md, E)) hi = mid; else lo = mid + 1;
+    }
+    m->thr[t - 1] = (int)lo;
+  }
+  return true;
+}
+
+// ------------------------------------------------------------------ validation
+struct Plan {
+  bool fp32;
+  int B, H, L;
+  int nrel, txl_off;
+  float scale;
+  T5Map t5;
+  // workspace offsets (bytes)
+  size_t off_bucket, off_lut, off_rowc, off_keyc, off_uk, off_vr, off_dsum;
+  size_t off_part_q, off_part_k, off_part_qv, off_part_kv;
+  int64_t part_q_stride, part_k_stride;
+  size_t fwd_bytes, bwd_bytes;
+};
+
+int make_plan(const relpos_desc* d, Plan* p) {
+  if (!d) return RELPOS_E_INVALID;
+  if (d->mech < RELPOS_T5 || d->mech > RELPOS_DEBERTA) return RELPOS_E_INVALID;
+  if (d->dtype != RELPOS_BF16 && d->dtype != RELPOS_FP32) return RELPOS_E_INVALID;
+  if (d->batch < 0 || d->heads < 1 || d->seqlen < 0 || d->head_dim < 1) return RELPOS_E_INVALID;
+  if (d->window_left < -1 || d->window_right < -1) return RELPOS_E_INVALID;
+  if (!(isfinite(d->scale)) || d->scale < 0.f) return RELPOS_E_INVALID;
+  if (d->head_dim != kHeadDim) return RELPOS_E_UNSUPPORTED;
+  if (d->seqlen > (1 << 28) || d->heads > (1 << 20) || d->batch > (1 << 20)) return RELPOS_E_UNSUPPORTED;
+  const int64_t nqb = (d->seqlen + 127) / 128;
+  if (d->batch * d->heads * nqb > 0x7FFFFFFFLL) return RELPOS_E_UNSUPPORTED;
+  memset(p, 0, sizeof(*p));
+  p->fp32 = d->dtype == RELPOS_FP32;
+  p->B = (int)d->batch;
+  p->H = (int)d->heads;
+  p->L = (int)d->seqlen;
+  const int L = p->L;
+  switch (d->mech) {
+    case RELPOS_T5: {
+      if (d->num_buckets < 2 || d->num_buckets > 256) return RELPOS_E_INVALID;
+      if (d->bidirectional && (d->num_buckets % 2 != 0 || d->num_buckets < 4)) return RELPOS_E_INVALID;
+      const int half = d->bidirectional ? d->num_buckets / 2 : d->num_buckets;
+      if (half / 2 < 1 || d->max_distance <= half / 2) return RELPOS_E_INVALID;
+      if (!build_t5_map(d, &p->t5)) return RELPOS_E_UNSUPPORTED;
+      break;
+    }
+    case RELPOS_SHAW:
+    case RELPOS_DEBERTA:
+      if (d->rel_span < 1 || d->rel_span > (1 << 26)) return RELPOS_E_INVALID;
+      break;
+    case RELPOS_TXL:
+      break;
+  }
+  p->nrel = (d->window_right == 0) ? L : 2 * L - 1;
+  p->txl_off = (d->window_right == 0) ? 0 : L - 1;
+  if (d->scale > 0.f) p->scale = d->scale;
+  else p->scale = (float)(1.0 / sqrt((d->mech == RELPOS_DEBERTA ? 3.0 : 1.0) * (double)d->head_dim));
+
+  // ---- workspace layout ----
+  const size_t rows = (size_t)p->B * p->H * L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
+  if (d->mech == RELPOS_T5) {
+    p->off_bucket = take(sizeof(int32_t) * (size_t)(L > 0 ? 2 * L - 1 : 1));
+    p->off_lut = take(sizeof(float) * (size_t)p->H * (L > 0 ? 2 * L - 1 : 1));
+  }
+  if (d->mech == RELPOS_SHAW || d->mech == RELPOS_DEBERTA) p->off_rowc = take(sizeof(float) * rows * 2);
+  if (d->mech == RELPOS_DEBERTA) p->off_keyc = take(sizeof(float) * rows * 2);
+  if (d->mech == RELPOS_TXL) {
+    p->off_uk = take(sizeof(float) * rows);
+    p->off_vr = take(sizeof(float) * (size_t)p->H * p->nrel);
+  }
+  p->fwd_bytes = off;
+  p->off_dsum = take(sizeof(float) * rows);
+  p->bwd_bytes = off;
+  return RELPOS_OK;
+}
+
+bool ws_ok(const void* ws, size_t have, size_t need) {
+  if (need == 0) return true;
+  return ws != nullptr && have >= need && ((uintptr_t)ws % kAlign) == 0;
+}
+
+// Fills the per-call tables every pass needs (index maps, LUTs, row dots).
+hipError_t run_prep(const relpos_desc* d, const Plan& p, const void* q, const void* k,
+                    const void* rel_a, const void* rel_b, const float* bias_a, const float* bias_b,
+                    char* ws, hipStream_t st) {
+  const int L = p.L;
+  const int64_t rows = (int64_t)p.B * p.H * L;
+  hipError_t e = hipSuccess;
+  if (d->mech == RELPOS_T5) {
+    e = launch_index_map(MECH_T5, L, 0, 0, 0, p.t5, (int32_t*)(ws + p.off_bucket), nullptr, st);
+    if (e != hipSuccess) return e;
+    e = launch_t5_lut(bias_a, p.H, L, d->num_buckets, 1.0f / p.scale, p.t5, (float*)(ws + p.off_lut), st);
+  } else if (d->mech == RELPOS_SHAW) {
+    RowDotArgs r{q, rows, L, p.H, rel_a, 0, 0, 2 * d->rel_span, 2, (float*)(ws + p.off_rowc)};
+    e = launch_rowdot(r, p.fp32, p.fp32, st);
+  } else if (d->mech == RELPOS_DEBERTA) {
+    RowDotArgs r{q, rows, L, p.H, rel_a, 0, 0, 2 * d->rel_span - 1, 2, (float*)(ws + p.off_rowc)};
+    e = launch_rowdot(r, p.fp32, p.fp32, st);
+    if (e != hipSuccess) return e;
+    RowDotArgs r2{k, rows, L, p.H, rel_b, 0, 0, 2 * d->rel_span - 1, 2, (float*)(ws + p.off_keyc)};
+    e = launch_rowdot(r2, p.fp32, p.fp32, st);
+  } else if (d->mech == RELPOS_TXL) {
+    RowDotArgs r{k, rows, L, p.H, bias_a, kHeadDim, 0, 0, 1, (float*)(ws + p.off_uk)};
+    e = launch_rowdot(r, p.fp32, true, st);
+    if (e != hipSuccess) return e;
+    RowDotArgs r2{rel_a, (int64_t)p.H * p.nrel, p.nrel, p.H, bias_b, kHeadDim, 0, 0, 1,
+                  (float*)(ws + p.off_vr)};
+    e = launch_rowdot(r2, p.fp32, true, st);
+  }
+  return e;
+}
+
+AttnShape make_shape(const relpos_desc* d, const Plan& p) {
+  AttnShape s;
+  s.B = p.B;
+  s.H = p.H;
+  s.L = p.L;
+  s.wl = d->window_left;
+  s.wr = d->window_right;
+  s.mech = d->mech;
+  s.span = d->rel_span;
+  s.nrel = p.nrel;
+  s.txl_off = p.txl_off;
+  s.scale = p.scale;
+  return s;
+}
+
+// Table pointers each mechanism requires / forbids.
+int check_tables(const relpos_desc* d, const void* rel_a, const void* rel_b, const void* bias_a,
+                 const void* bias_b) {
+  bool need_ra = false, need_rb = false, need_ba = false, need_bb = false;
+  switch (d->mech) {
+    case RELPOS_T5: need_ba = true; break;
+    case RELPOS_SHAW: need_ra = true; break;
+    case RELPOS_TXL: need_ra = need_ba = need_bb = true; break;
+    case RELPOS_DEBERTA: need_ra = need_rb = true; break;
+  }
+  if ((rel_a != nullptr) != need_ra || (rel_b != nullptr) != need_rb) return RELPOS_E_INVALID;
+  if ((bias_a != nullptr) != need_ba || (bias_b != nullptr) != need_bb) return RELPOS_E_INVALID;
+  for (const void* ptr : {rel_a, rel_b, bias_a, bias_b})
+    if (ptr && !aligned16(ptr)) return RELPOS_E_INVALID;
+  return RELPOS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int relpos_version(void) { return 100; }
+
+const char* relpos_status_string(int status) {
+  switch (status) {
+    case RELPOS_OK: return "ok";
+    case RELPOS_E_INVALID: return "invalid argument";
+    case RELPOS_E_UNSUPPORTED: return "unsupported configuration";
+    case RELPOS_E_WORKSPACE: return "workspace missing, misaligned or too small";
+    case RELPOS_E_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int relpos_attn_workspace_size(const relpos_desc* desc, int pass, size_t* bytes) {
+  if (!bytes || (pass != 0 && pass != 1)) return RELPOS_E_INVALID;
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != RELPOS_OK) return st;
+  *bytes = pass == 0 ? p.fwd_bytes : p.bwd_bytes;
+  return RELPOS_OK;
+}
+
+int relpos_index_map(const relpos_desc* desc, int32_t* out_a, int32_t* out_b, void* stream) {
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != RELPOS_OK) return st;
+  if (p.L == 0) return RELPOS_OK;
+  if (!out_a || !aligned16(out_a)) return RELPOS_E_INVALID;
+  if ((desc->mech == RELPOS_DEBERTA) != (out_b != nullptr)) return RELPOS_E_INVALID;
+  if (out_b && !aligned16(out_b)) return RELPOS_E_INVALID;
+  hipError_t e = launch_index_map(desc->mech, p.L, desc->rel_span, p.nrel, p.txl_off, p.t5, out_a,
+                                  out_b, (hipStream_t)stream);
+  return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
+}
+
+int relpos_attn_fwd(const relpos_desc* desc, const void* q, const void* k, const void* v,
+                    const void* rel_a, const void* rel_b, const float* bias_a, const float* bias_b,
+                    void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != RELPOS_OK) return st;
+  st = check_tables(desc, rel_a, rel_b, bias_a, bias_b);
+  if (st != RELPOS_OK) return st;
+  if (p.B == 0 || p.L == 0) return RELPOS_OK;
+  for (const void* ptr : {q, k, v, (const void*)o, (const void*)lse})
+    if (!ptr || !aligned16(ptr)) return RELPOS_E_INVALID;
+  if (!ws_ok(workspace, workspace_bytes, p.fwd_bytes)) return RELPOS_E_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  hipError_t e = run_prep(desc, p, q, k, rel_a, rel_b, bias_a, bias_b, ws, s);
+  if (e != hipSuccess) return RELPOS_E_LAUNCH;
+  FwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.sh = make_shape(desc, p);
+  a.q = q; a.k = k; a.v = v;
+  a.rel_a = rel_a; a.rel_b = rel_b;
+  a.o = o; a.lse = lse;
+  if (desc->mech == RELPOS_T5) {
+    a.lut = (const float*)(ws + p.off_lut);
+    a.bucket = (const int*)(ws + p.off_bucket);
+  }
+  if (desc->mech == RELPOS_SHAW || desc->mech == RELPOS_DEBERTA) a.rowc = (const float*)(ws + p.off_rowc);
+  if (desc->mech == RELPOS_DEBERTA) a.keyc = (const float*)(ws + p.off_keyc);
+  if (desc->mech == RELPOS_TXL) {
+    a.uk = (const float*)(ws + p.off_uk);
+    a.vr = (const float*)(ws + p.off_vr);
+  }
+  e = launch_fwd(a, p.fp32, s);
+  return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
+}
+
+int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const void* v,
+                    const void* o, const float* lse, const void* dout, const void* rel_a,
+                    const void* rel_b, const float* bias_a, const float* bias_b, void* dq, void* dk,
+                    void* dv, float* drel_a, float* drel_b, float* dbias_a, float* dbias_b,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  (void)desc; (void)q; (void)k; (void)v; (void)o; (void)lse; (void)dout; (void)rel_a; (void)rel_b;
+  (void)bias_a; (void)bias_b; (void)dq; (void)dk; (void)dv; (void)drel_a; (void)drel_b;
+  (void)dbias_a; (void)dbias_b; (void)workspace; (void)workspace_bytes; (void)stream;
+  return RELPOS_E_UNSUPPORTED;
+}
+
+}  // extern "C"

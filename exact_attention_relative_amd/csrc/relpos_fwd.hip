@@ -1,0 +1,297 @@
+// Forward kernel: exact softmax attention with additive relative-position terms, one
+// workgroup per (batch, head, 128-query block), keys streamed in 64-row tiles with an
+// online softmax.  The relative term is folded into the score tile and never stored (abstract
+// of "Fast and Exact Relative-Position Attention via Structure-Aware Kernels"; zicq.com
+// explainer, section on how structure-aware tiling stays exact: B is added inside the online
+// softmax accumulation instead of being built as a full matrix first).
+//
+// Scores are kept in "y units": y = q.k + (relative term) / s, the natural logit being s*y.
+// exp(s*y - s*m) = exp2(y * c - m * c) with c = s * log2(e).
+#include "relpos_tile.h"
+
+namespace relpos {
+
+template <typename T, int MECH>
+__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+  constexpr int NP = Elem<T>::NP;
+  constexpr bool REL = (MECH != MECH_T5);
+  __shared__ __attribute__((aligned(16))) uint16_t ks[NP * BOTH * TSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[NP * BOTH * TSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t win[REL ? NP * WIN * TSTR : 8];
+  __shared__ __attribute__((aligned(16))) float gsb[REL ? NWAVE * WROWS * GSTR : 4];
+  __shared__ __attribute__((aligned(16))) float vec_s[WIN];     // T5 LUT slice / T-XL v.r
+  __shared__ __attribute__((aligned(16))) float kvec_s[2 * BOTH]; // T-XL u.k / DeBERTa k.Qr ends
+
+  const AttnShape sh = a.sh;
+  const int L = sh.L;
+  const int nqb = (L + BLANE - 1) / BLANE;
+  const int bid = blockIdx.x;
+  int qb = bid % nqb;
+  const int bh = bid / nqb;
+  if (sh.wr == 0) qb = nqb - 1 - qb;   // causal: longest rows first
+  const int h = bh % sh.H;
+  const int i0 = qb * BLANE;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int l32 = lane & 31, kh = lane >> 5;
+  const int qw0 = i0 + WROWS * w;
+  const int my_i = qw0 + l32;
+
+  const int64_t bh_off = (int64_t)bh * L * kHeadDim;
+  const T* qg = (const T*)a.q + bh_off;
+  const T* kg = (const T*)a.k + bh_off;
+  const T* vg = (const T*)a.v + bh_off;
+  const float s = sh.scale;
+  const float c = s * kLog2e;
+  const int span = sh.span;
+
+  // Lane-side operand: this lane's query row.
+  Op<NP> qop[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    if (my_i < L) {
+      qop[cc] = op_from_global<T>(qg + (int64_t)my_i * kHeadDim + 16 * cc + 8 * kh);
+    } else {
+      float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      qop[cc] = op_from_f32<NP>(z);
+    }
+  }
+  // Clipped-end constants of this query row (Shaw: q.w[0], q.w[2k]; DeBERTa: q.Kr[0], q.Kr[2k-1]).
+  float rc_lo = 0.f, rc_hi = 0.f;
+  if constexpr (MECH == MECH_SHAW || MECH == MECH_DEBERTA) {
+    if (my_i < L) {
+      rc_lo = a.rowc[((int64_t)bh * L + my_i) * 2 + 0];
+      rc_hi = a.rowc[((int64_t)bh * L + my_i) * 2 + 1];
+    }
+  }
+
+  float m_run = kNegInf, l_run = 0.f;
+  f32x16 oacc[2] = {f32x16{}, f32x16{}};
+
+  // Key range of this workgroup under the mask.
+  int j_lo = 0, j_hi = L - 1;
+  if (sh.wl >= 0) j_lo = max(0, i0 - sh.wl);
+  if (sh.wr >= 0) j_hi = min(L - 1, i0 + BLANE - 1 + sh.wr);
+  const int jt0 = (j_lo / BOTH) * BOTH;
+
+  float* gs = gsb + (REL ? w * WROWS * GSTR : 0);
+
+  for (int j0 = jt0; j0 <= j_hi; j0 += BOTH) {
+    // ---- tile classification (offset-aware scheduling) ----
+    // wave tile offsets delta = i - j in [dlo, dhi]
+    const int dlo = qw0 - (j0 + BOTH - 1), dhi = qw0 + WROWS - 1 - j0;
+    const int wg_dlo = i0 - (j0 + BOTH - 1), wg_dhi = i0 + BLANE - 1 - j0;
+    const int dlo_c = clampi(dlo, 1 - L, L - 1), dhi_c = clampi(dhi, 1 - L, L - 1);
+    bool wave_none = (j0 >= L) || (qw0 >= L);
+    if (sh.wl >= 0 && dlo > sh.wl) wave_none = true;
+    if (sh.wr >= 0 && -dhi > sh.wr) wave_none = true;
+    bool wave_full = (j0 + BOTH <= L) && (sh.wl < 0 || dhi <= sh.wl) && (sh.wr < 0 || -dlo <= sh.wr);
+    // relative-term class: 0 general, 1 clipped low (delta small), 2 clipped high
+    int cls = 0;
+    bool wg_general = true;
+    if constexpr (MECH == MECH_SHAW) {
+      // row = clamp(j - i, -k, k) + k: clipped when j - i >= k (hi row) or <= -k (row 0)
+      if (-dhi >= span) cls = 2; else if (-dlo <= -span) cls = 1;
+      wg_general = !((-wg_dhi >= span) || (-wg_dlo <= -span));
+    } else if constexpr (MECH == MECH_DEBERTA) {
+      if (dlo >= span) cls = 2; else if (dhi <= -span) cls = 1;
+      wg_general = !((wg_dlo >= span) || (wg_dhi <= -span));
+    } else if constexpr (MECH == MECH_T5) {
+      // one bucket for the whole wave tile: the offsets lie on one side of 0 (where the
+      // bucket map is monotone) and both ends share a bucket
+      if ((dlo_c >= 0 || dhi_c < 0) && a.bucket[dlo_c + L - 1] == a.bucket[dhi_c + L - 1])
+        cls = 1;
+    }
+
+    __syncthreads();  // previous tile's LDS reads are done
+    stage64<T, NP>(ks, kg, j0, L);
+    stage64<T, NP>(vs, vg, j0, L);
+    if constexpr (MECH == MECH_T5) {
+      for (int x = tid; x < WIN; x += 256) {
+        const int d = wg_dlo + x;   // window row x <-> delta = i0 - j0 - 63 + x
+        vec_s[x] = (d > -L && d < L) ? a.lut[(int64_t)h * (2 * L - 1) + d + L - 1] : 0.f;
+      }
+    } else if (wg_general) {
+      const int toff = sh.txl_off, nrel = sh.nrel;
+      const T* tab = (const T*)a.rel_a;
+      if constexpr (MECH == MECH_TXL) tab += (int64_t)h * nrel * kHeadDim;
+      stage_window<T, NP>(win, tab, [&](int x) {
+        return row_side_row(MECH, wg_dlo + x, span, nrel, toff);
+      });
+      if constexpr (MECH == MECH_TXL) {
+        for (int x = tid; x < WIN; x += 256) {
+          const int r = row_side_row(MECH, wg_dlo + x, span, nrel, toff);
+          vec_s[x] = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+        }
+      }
+    }
+    if constexpr (MECH == MECH_TXL) {
+      if (tid < BOTH) kvec_s[tid] = (j0 + tid < L) ? a.uk[(int64_t)bh * L + j0 + tid] : 0.f;
+    }
+    if constexpr (MECH == MECH_DEBERTA) {
+      if (tid < 2 * BOTH) {
+        const int jj = j0 + (tid >> 1);
+        kvec_s[tid] = (jj < L) ? a.keyc[((int64_t)bh * L + jj) * 2 + (tid & 1)] : 0.f;
+      }
+    }
+    __syncthreads();
+
+    f32x16 sc[2];
+    Op<NP> kop[2][4];
+    if (!wave_none) {
+      other_dot_lane<NP>(sc, ks, qop, kop);
+    }
+    float rowconst = 0.f;
+    // ---- relative terms (row side) ----
+    if constexpr (MECH == MECH_T5) {
+      if (!wave_none) {
+        if (cls == 1) {
+          rowconst = vec_s[dlo_c - wg_dlo];
+        } else {
+          add_offset_vec(sc, vec_s, WROWS * w);
+        }
+      }
+    } else if constexpr (MECH == MECH_SHAW) {
+      if (!wave_none) {
+        if (cls == 2) rowconst = rc_hi;
+        else if (cls == 1) rowconst = rc_lo;
+        else {
+          rowside_products<NP, false>(gs, win, WROWS * w, qop, nullptr);
+          wave_lds_sync();
+          rowside_gather(sc, gs);
+        }
+      }
+    } else if constexpr (MECH == MECH_TXL) {
+      if (!wave_none) {
+        rowside_products<NP, true>(gs, win, WROWS * w, qop, vec_s);
+        wave_lds_sync();
+        rowside_gather(sc, gs);
+        add_other_vec(sc, kvec_s, 1);
+      }
+    } else if constexpr (MECH == MECH_DEBERTA) {
+      if (!wave_none) {
+        if (cls == 2) { rowconst = rc_hi; add_other_vec(sc, kvec_s + 0, 2); }
+        else if (cls == 1) { rowconst = rc_lo; add_other_vec(sc, kvec_s + 1, 2); }
+        else {
+          rowside_products<NP, false>(gs, win, WROWS * w, qop, nullptr);
+          wave_lds_sync();
+          rowside_gather(sc, gs);
+        }
+      }
+      if (wg_general) {
+        // column side (p2c): restage the window with Qr rows
+        __syncthreads();
+        stage_window<T, NP>(win, (const T*)a.rel_b, [&](int x) {
+          // column window row x <-> rho = j - i = (j0 - i0 - 127) + x
+          return p2c_row(-((j0 - i0 - (BLANE - 1)) + x), span);
+        });
+        __syncthreads();
+        if (!wave_none && cls == 0) {
+#pragma unroll
+          for (int ob = 0; ob < 2; ++ob) {
+            wave_lds_sync();
+            colside_products<NP, false>(gs, win, (BLANE - WROWS) - WROWS * w, ob, kop, nullptr);
+            wave_lds_sync();
+            colside_gather(sc, gs, ob);
+          }
+        }
+      }
+    }
+    if (wave_none) continue;
+
+    // ---- mask ----
+    if (!wave_full) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
+          if (!(j < L && pair_allowed(my_i, j, sh.wl, sh.wr))) sc[b][r] = kNegInf;
+        }
+    }
+
+    // ---- online softmax ----
+    float mx = kNegInf;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][r]);
+    mx = fmaxf(mx, xhalf(mx));
+    mx += rowconst;
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    const float alpha = fast_exp2((m_run - m_use) * c);
+    const float bias = (rowconst - m_use) * c;
+    float psum = 0.f;
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(fmaf(sc[b][r], c, bias));
+        sc[b][r] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < 2; ++db) oacc[db] *= alpha;
+
+    // ---- O^T += V^T P^T ----
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      Op<NP> pop = op_from_acc<NP>(sc, cc);
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        Op<NP> vop = op_rows_tr<NP>(vs, BOTH * TSTR, TSTR, 16 * cc, 32 * db);
+        mma<NP>(oacc[db], vop, pop);
+      }
+    }
+  }
+
+  // ---- epilogue ----
+  const float l_tot = l_run + xhalf(l_run);
+  const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
+  if (my_i < L) {
+    T* og = (T*)a.o + bh_off + (int64_t)my_i * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * kh;
+        float o0 = oacc[db][4 * g] * inv, o1 = oacc[db][4 * g + 1] * inv;
+        float o2 = oacc[db][4 * g + 2] * inv, o3 = oacc[db][4 * g + 3] * inv;
+        if constexpr (NP == 1) {
+          u32x2 pk = {pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+          *(u32x2*)(og + d) = pk;
+        } else {
+          f32x4 v4 = {o0, o1, o2, o3};
+          *(f32x4*)(og + d) = v4;
+        }
+      }
+    if (kh == 0) {
+      a.lse[(int64_t)bh * L + my_i] = (l_tot > 0.f) ? (s * m_run + logf(l_tot)) : kNegInf;
+    }
+  }
+}
+
+template <typename T>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  const int nqb = (a.sh.L + BLANE - 1) / BLANE;
+  const dim3 grid((unsigned)(nqb * a.sh.B * a.sh.H));
+  switch (a.sh.mech) {
+    case MECH_T5: hipLaunchKernelGGL((fwd_kernel<T, MECH_T5>), grid, dim3(256), 0, stream, a); break;
+    case MECH_SHAW: hipLaunchKernelGGL((fwd_kernel<T, MECH_SHAW>), grid, dim3(256), 0, stream, a); break;
+    case MECH_TXL: hipLaunchKernelGGL((fwd_kernel<T, MECH_TXL>), grid, dim3(256), 0, stream, a); break;
+    case MECH_DEBERTA: hipLaunchKernelGGL((fwd_kernel<T, MECH_DEBERTA>), grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, bool fp32, hipStream_t stream) {
+  return fp32 ? launch_fwd_t<float>(a, stream) : launch_fwd_t<uint16_t>(a, stream);
+}
+
+}  // namespace relpos

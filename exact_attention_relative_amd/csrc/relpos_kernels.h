@@ -1,0 +1,111 @@
+// Kernel argument blocks and launcher declarations shared by the host dispatcher and the
+// kernel translation units.  Plain structs, passed to kernels by value.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace relpos {
+
+enum { MECH_T5 = 0, MECH_SHAW = 1, MECH_TXL = 2, MECH_DEBERTA = 3 };
+
+constexpr int kHeadDim = 64;
+constexpr int kMaxThresholds = 64;
+
+// T5 bucket map: magnitude n >= max_exact lands in max_exact + #{e : n >= thr[e]}.
+struct T5Map {
+  int bidirectional;
+  int half;        // buckets per direction (upper half offset when bidirectional)
+  int max_exact;
+  int nthr;        // log buckets - 1
+  int thr[kMaxThresholds];
+};
+
+// Everything the attention kernels need to know about one call.
+struct AttnShape {
+  int B, H, L;
+  int wl, wr;       // window; -1 = unbounded
+  int mech;
+  int span;         // Shaw / DeBERTa k
+  int nrel;         // T-XL table rows
+  int txl_off;      // T-XL row = delta + txl_off
+  float scale;      // s
+};
+
+struct FwdArgs {
+  AttnShape sh;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* rel_a;   // Shaw w, T-XL r, DeBERTa Kr
+  const void* rel_b;   // DeBERTa Qr
+  void* o;
+  float* lse;
+  const float* lut;    // T5: beta[bucket(delta)] / s per head, [H, 2L - 1]
+  const float* uk;     // T-XL: u_h . k_j, [B, H, L]
+  const float* vr;     // T-XL: v_h . r_h[row], [H, nrel]
+  const float* rowc;   // Shaw / DeBERTa: per-query clipped-end products, [B, H, L, 2]
+  const float* keyc;   // DeBERTa: per-key clipped-end p2c products, [B, H, L, 2]
+  const int* bucket;   // T5: bucket of every offset, [2L - 1]
+};
+
+struct BwdArgs {
+  AttnShape sh;
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;
+  const float* dsum;   // D_i = dO_i . O_i, [B, H, L]
+  const void* rel_a;
+  const void* rel_b;
+  const float* lut;
+  const float* uk;
+  const float* vr;
+  const float* rowc;
+  const float* keyc;
+  const int* bucket;
+  const float* bias_a; // T-XL u
+  const float* bias_b; // T-XL v
+  void* dq;
+  void* dk;
+  void* dv;
+  float* part_q;       // query-side partials (dQ pass)
+  float* part_k;       // key-side partials (dK/dV pass)
+  float* part_qv;      // query-side per-owner small vectors (T-XL dv, clipped sums)
+  float* part_kv;      // key-side per-owner small vectors (T-XL du)
+  int64_t part_q_stride;  // floats per owner
+  int64_t part_k_stride;
+};
+
+// ----------------------------------------------------------------------------- launchers
+// Each returns a hipError_t from hipGetLastError() after enqueueing on `stream`.
+hipError_t launch_fwd(const FwdArgs& a, bool fp32, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, bool fp32, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, bool fp32, hipStream_t stream);
+
+// out[n * ne + e] = x_n . y_e(h(n)) for rows x_n of length 64.  Row n belongs to head
+// (n / rows_per_head) % H; y_e(h) = y + h * y_head_stride + y_row[e] * 64.
+struct RowDotArgs {
+  const void* x;
+  int64_t nrows;
+  int64_t rows_per_head;
+  int H;
+  const void* y;
+  int64_t y_head_stride;
+  int y_row0, y_row1;
+  int ne;
+  float* out;
+};
+hipError_t launch_rowdot(const RowDotArgs& a, bool x_fp32, bool y_fp32, hipStream_t stream);
+
+hipError_t launch_t5_lut(const float* beta, int H, int L, int nb, float inv_scale, const T5Map& m,
+                         float* lut, hipStream_t stream);
+hipError_t launch_index_map(int mech, int L, int span, int nrel, int txl_off, const T5Map& m,
+                            int32_t* out_a, int32_t* out_b, hipStream_t stream);
+// D_n = dO_n . O_n over rows of length 64
+hipError_t launch_dsum(const void* o, const void* dout, int64_t nrows, bool fp32, float* dsum,
+                       hipStream_t stream);
+
+}  // namespace relpos

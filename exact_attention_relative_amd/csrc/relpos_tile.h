@@ -1,0 +1,226 @@
+// Wave-level tile engine shared by the forward, dQ and dK/dV kernels.
+//
+// A workgroup owns 128 "lane-side" rows (4 waves x 32; queries in the forward and dQ
+// kernels, keys in the dK/dV kernel) and streams 64-row "other-side" tiles through LDS.
+// Every 32x32x16 MFMA accumulator then has one lane-side row per lane (lane % 32) and
+// other-side rows in its registers: register r of block b holds other-side row
+// 32 b + 8 (r / 4) + 4 (lane / 32) + r % 4.
+//
+// Offset-aware tiling (abstract, item 1; zicq.com explainer, section on offset-aware
+// tiling): a 32 x 64 wave tile touches only 95 offsets, so the table rows of those offsets
+// are staged once per workgroup tile in LDS (a 192-row window shared by the 4 waves) and
+// the relation products are computed once per offset (abstract, item 2; explainer, section
+// on reusing query/key relation products) on MFMA as a [96 offsets x 32 rows] block.  The
+// products are skew-gathered back into the score layout through a wave-private LDS buffer.
+#pragma once
+
+#include "relpos_device.h"
+
+namespace relpos {
+
+constexpr int NWAVE = 4;
+constexpr int WROWS = 32;            // lane-side rows per wave
+constexpr int BLANE = NWAVE * WROWS; // lane-side rows per workgroup
+constexpr int BOTH = 64;             // other-side rows per step
+constexpr int TSTR = 72;             // LDS row stride (elements) of 64-wide bf16 tiles
+constexpr int WIN = 192;             // window rows (BLANE + BOTH - 1 = 191, padded)
+constexpr int GSTR = 100;            // skew buffer row stride (floats)
+
+// ---------------------------------------------------------------------------------------
+// Staging (all 256 threads).  Tiles hold NP bf16 planes of [rows][TSTR].
+// ---------------------------------------------------------------------------------------
+// 64 consecutive rows of a [*, 64] tensor; rows >= nvalid are zero.
+template <typename T, int NP>
+__device__ __forceinline__ void stage64(uint16_t* tile, const T* base, int row0, int nvalid) {
+  const int t = threadIdx.x;
+  const int r = t >> 2;
+  const int c = (t & 3) * 16;
+  const int plane = BOTH * TSTR;
+  if (row0 + r < nvalid) {
+    const T* g = base + (int64_t)(row0 + r) * kHeadDim + c;
+    lds_store8<T>(tile, plane, r * TSTR + c, g);
+    lds_store8<T>(tile, plane, r * TSTR + c + 8, g + 8);
+  } else {
+    lds_zero8<NP>(tile, plane, r * TSTR + c);
+    lds_zero8<NP>(tile, plane, r * TSTR + c + 8);
+  }
+}
+
+// WIN window rows; window row x reads table row rowfn(x) (< 0 = zero row).
+template <typename T, int NP, typename F>
+__device__ __forceinline__ void stage_window(uint16_t* win, const T* table, F rowfn) {
+  const int t = threadIdx.x;
+  const int c = (t & 3) * 16;
+  const int plane = WIN * TSTR;
+#pragma unroll
+  for (int x0 = 0; x0 < WIN; x0 += 64) {
+    const int x = x0 + (t >> 2);
+    const int row = rowfn(x);
+    if (row >= 0) {
+      const T* g = table + (int64_t)row * kHeadDim + c;
+      lds_store8<T>(win, plane, x * TSTR + c, g);
+      lds_store8<T>(win, plane, x * TSTR + c + 8, g + 8);
+    } else {
+      lds_zero8<NP>(win, plane, x * TSTR + c);
+      lds_zero8<NP>(win, plane, x * TSTR + c + 8);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Wave products.  `lane` operands: Op<NP> x[4] for the wave's 32 lane-side rows (lane % 32
+// = row, k = d chunk c: 16 c + 8 (lane / 32) .. + 7).
+// ---------------------------------------------------------------------------------------
+// acc[b] = Y[32 b + m] . X[n]  (C[m = other row][n = lane row]); Y is a 64-row LDS tile.
+template <int NP>
+__device__ __forceinline__ void other_dot_lane(f32x16 acc[2], const uint16_t* ytile,
+                                               const Op<NP> xop[4], Op<NP> yop[2][4]) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    acc[b] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      yop[b][c] = op_from_lds<NP>(ytile, BOTH * TSTR, (32 * b + l32) * TSTR + 16 * c + 8 * kh);
+      mma<NP>(acc[b], yop[b][c], xop[c]);
+    }
+  }
+}
+
+// Row-side relation products for one wave: g[bb] = Win[w0 + 32 bb + m] . X[n], then (opt.)
+// g += vec[w0 + t] per window row t.  Written to the wave's skew buffer gs[n][t].
+template <int NP, bool ADDVEC>
+__device__ __forceinline__ void rowside_products(float* gs, const uint16_t* win, int w0,
+                                                 const Op<NP> xop[4], const float* vec) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int bb = 0; bb < 3; ++bb) {
+    f32x16 g = {};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      Op<NP> a = op_from_lds<NP>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
+      mma<NP>(g, a, xop[c]);
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int t = 32 * bb + 8 * q4 + 4 * kh;
+      f32x4 v = {g[4 * q4], g[4 * q4 + 1], g[4 * q4 + 2], g[4 * q4 + 3]};
+      if constexpr (ADDVEC) {
+        f32x4 add = *(const f32x4*)(vec + w0 + t);
+        v += add;
+      }
+      *(f32x4*)(gs + l32 * GSTR + t) = v;
+    }
+  }
+}
+
+// Gather: s[b][r] += gs[n][n - y + 63] with y the other-side row of register (b, r).
+__device__ __forceinline__ void rowside_gather(f32x16 s[2], const float* gs) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
+      s[b][r] += gs[l32 * GSTR + l32 - y + 63];
+    }
+}
+
+// Column-side relation products for other-side block ob (32 rows): h[bb'] = Win[w0 + 32 bb + m]
+// . Y[32 ob + n] for bb in {ob, ob + 1}; written to gs[n][t'] (n = other row within block).
+template <int NP, bool ADDVEC>
+__device__ __forceinline__ void colside_products(float* gs, const uint16_t* win, int w0, int ob,
+                                                 const Op<NP> yop[2][4], const float* vec) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int bb = ob + i;
+    f32x16 g = {};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      Op<NP> a = op_from_lds<NP>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
+      mma<NP>(g, a, yop[ob][c]);
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int t = 32 * bb + 8 * q4 + 4 * kh;
+      f32x4 v = {g[4 * q4], g[4 * q4 + 1], g[4 * q4 + 2], g[4 * q4 + 3]};
+      if constexpr (ADDVEC) {
+        f32x4 add = *(const f32x4*)(vec + w0 + t);
+        v += add;
+      }
+      *(f32x4*)(gs + l32 * GSTR + t) = v;
+    }
+  }
+}
+
+// Gather for column side block ob: s[ob][r] += gs[y - 32 ob][y - n + 31].
+__device__ __forceinline__ void colside_gather(f32x16 s[2], const float* gs, int ob) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int yy = 8 * (r >> 2) + 4 * kh + (r & 3);   // other row within block
+    const int y = 32 * ob + yy;
+    s[ob][r] += gs[yy * GSTR + y - l32 + 31];
+  }
+}
+
+// Element-wise addition of an LDS vector indexed by the lane-side window t = n - y + 63 + w0.
+__device__ __forceinline__ void add_offset_vec(f32x16 s[2], const float* vec, int w0) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
+      s[b][r] += vec[w0 + l32 - y + 63];
+    }
+}
+
+// s[b][r] += vec[y * stride] (a per-other-row term, broadcast over lanes).
+__device__ __forceinline__ void add_other_vec(f32x16 s[2], const float* vec, int stride) {
+  const int lane = __lane_id();
+  const int kh = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
+      s[b][r] += vec[y * stride];
+    }
+}
+
+// Operand whose k index runs down 16 consecutive rows of an LDS tile (row-major, TSTR):
+// 32x32x16 A/B layout with m/n = column col0 + (lane % 32) and k = rows row0 + (8 i + 4 kh
+// + j) as the P / dS register permutation expects (slot j < 4: row0 + 4 kh + j, slot
+// 4 + j: row0 + 8 + 4 kh + j).
+template <int NP>
+__device__ __forceinline__ Op<NP> op_rows_tr(const uint16_t* tile, int plane, int stride,
+                                             int row0, int col0) {
+  const int lane = __lane_id();
+  const int g = lane >> 4, i = lane & 15;
+  const int kh = g >> 1;
+  const int col = col0 + 16 * (g & 1) + 4 * (i & 3);
+  const int r = row0 + 4 * kh + (i >> 2);
+  return op_tr_from_lds<NP>(tile, plane, r * stride + col, (r + 8) * stride + col);
+}
+
+// Operand from an fp32 register block in accumulator layout: 16 consecutive other-side
+// rows 16 c .. 16 c + 15 of s[c / 2].
+template <int NP>
+__device__ __forceinline__ Op<NP> op_from_acc(const f32x16 s[2], int c) {
+  float x[8];
+  const f32x16& v = s[c >> 1];
+  const int base = 8 * (c & 1);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = v[base + i];
+  return op_from_f32<NP>(x);
+}
+
+}  // namespace relpos

@@ -1,0 +1,124 @@
+/*
+ * relpos_attn.h -- C ABI of the MI355X (gfx950) exact relative-position attention library.
+ *
+ * Operation.  For every batch b and head h, with query i and key j (0 <= i, j < L),
+ *
+ *     S_ij = s * q_i . k_j + B_ij          (pairs outside the mask are -inf)
+ *     O    = softmax_j(S) V,   LSE_i = ln sum_j exp(S_ij)
+ *
+ * the score of "Fast and Exact Relative-Position Attention via Structure-Aware Kernels"
+ * (zicq.com explainer, section on why relative-position attention is hard to make fast),
+ * computed exactly and without ever forming the L x L term B (abstract: exact attention with
+ * additive relative-position terms folded into FlashAttention-style tiling).  The four B terms
+ * are the mechanisms the authors list in their comment on the Hugging Face paper page:
+ *
+ *   RELPOS_T5       B_ij = beta[h][bucket(j - i)]                        (bias_a = beta)
+ *   RELPOS_SHAW     B_ij = s q_i . w[clamp(j - i, -k, k) + k]           (rel_a = w)
+ *   RELPOS_TXL      S_ij = s ((q_i + u_h) . k_j + (q_i + v_h) . r_h[row(i - j)])
+ *                   (rel_a = r, bias_a = u, bias_b = v)
+ *   RELPOS_DEBERTA  S_ij = s (q_i . k_j + q_i . Kr[clamp(i - j + k, 0, 2k - 1)]
+ *                                       + k_j . Qr[clamp(j - i + k, 0, 2k - 1)])
+ *                   (rel_a = Kr, rel_b = Qr)
+ *
+ * T5 buckets follow the published T5 log-bucket map with an exact floor (bidirectional maps put
+ * keys after the query in the upper half).  T-XL tables hold offsets 0..L-1 (row = i - j) when
+ * the mask is causal (window_right == 0) and -(L-1)..L-1 (row = i - j + L - 1) otherwise.
+ * Default scale s: 1/sqrt(d), and 1/sqrt(3d) for DeBERTa.
+ *
+ * Mask: pair (i, j) is allowed iff (window_left < 0 || i - j <= window_left) and
+ * (window_right < 0 || j - i <= window_right).  (-1,-1) none, (-1,0) causal, (w,w) local.
+ *
+ * Layouts (row-major, last index fastest, no padding):
+ *   q, k, v, o, dout, dq, dk, dv : [batch, heads, seqlen, head_dim], element type `dtype`
+ *   lse                          : [batch, heads, seqlen] float (natural log)
+ *   T5 beta  [heads, num_buckets] float        Shaw w     [2k+1, head_dim] dtype (shared)
+ *   T-XL r   [heads, Nrel, head_dim] dtype     T-XL u, v  [heads, head_dim] float
+ *   DeBERTa Kr, Qr [2k, head_dim] dtype (shared across heads)
+ * Every table gradient is float with the table's shape and is OVERWRITTEN (not accumulated).
+ * Unused table / gradient slots must be NULL.
+ *
+ * Ownership: the caller owns every buffer, including the workspace (size it with
+ * relpos_attn_workspace_size).  The library never allocates device memory.  All device
+ * pointers must be 16-byte aligned, the workspace 256-byte aligned.  Work is enqueued on
+ * `stream` (a hipStream_t; NULL = the default stream) and the call returns without
+ * synchronising.  Results are bitwise deterministic: no atomics are used anywhere.
+ *
+ * Errors: every entry point returns RELPOS_OK (0) or a negative status; on error nothing has
+ * been launched.  RELPOS_E_LAUNCH reports a failed kernel launch (work already enqueued by the
+ * same call may have run).  relpos_status_string() names a status.
+ */
+#ifndef RELPOS_ATTN_H
+#define RELPOS_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { RELPOS_T5 = 0, RELPOS_SHAW = 1, RELPOS_TXL = 2, RELPOS_DEBERTA = 3 } relpos_mech;
+typedef enum { RELPOS_BF16 = 0, RELPOS_FP32 = 1 } relpos_dtype;
+
+enum {
+  RELPOS_OK = 0,
+  RELPOS_E_INVALID = -1,     /* bad enum, shape, NULL / misaligned pointer, span inconsistent */
+  RELPOS_E_UNSUPPORTED = -2, /* valid request outside what the kernels implement (head_dim != 64) */
+  RELPOS_E_WORKSPACE = -3,   /* workspace NULL or smaller than relpos_attn_workspace_size() */
+  RELPOS_E_LAUNCH = -4       /* a kernel launch failed */
+};
+
+typedef struct relpos_desc {
+  int32_t mech;           /* relpos_mech */
+  int32_t dtype;          /* relpos_dtype of q, k, v, o, dout, dq, dk, dv and rel_a / rel_b */
+  int64_t batch;          /* >= 0 (0 = nothing to do) */
+  int64_t heads;          /* >= 1 */
+  int64_t seqlen;         /* L >= 0, queries and keys alike */
+  int64_t head_dim;       /* d; the kernels implement d = 64 */
+  int32_t window_left;    /* -1 = unbounded */
+  int32_t window_right;   /* -1 = unbounded; 0 = causal */
+  int32_t rel_span;       /* Shaw / DeBERTa k >= 1; ignored for T5 and T-XL */
+  int32_t num_buckets;    /* T5: even when bidirectional, >= 2 per direction */
+  int32_t max_distance;   /* T5: > num_buckets / 4 (bidirectional) or num_buckets / 2 */
+  int32_t bidirectional;  /* T5: 1 = separate buckets for keys after the query */
+  float scale;            /* 0 = default */
+} relpos_desc;
+
+/* Bytes of workspace the forward (pass 0) or backward (pass 1) call needs. */
+int relpos_attn_workspace_size(const relpos_desc* desc, int pass, size_t* bytes);
+
+/* Forward: writes O and LSE. */
+int relpos_attn_fwd(const relpos_desc* desc, const void* q, const void* k, const void* v,
+                    const void* rel_a, const void* rel_b, const float* bias_a,
+                    const float* bias_b, void* o, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Backward from (q, k, v, o, lse, dout): writes dq, dk, dv and the table gradients
+ * (T5: dbias_a = dbeta; Shaw: drel_a = dw; T-XL: drel_a = dr, dbias_a = du, dbias_b = dv;
+ * DeBERTa: drel_a = dKr, drel_b = dQr).  Table gradients are reduced over every (batch, head)
+ * that reads the table, in a fixed order, without atomics (offset-sharded partials followed
+ * by a second aggregation pass). */
+int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const void* v,
+                    const void* o, const float* lse, const void* dout, const void* rel_a,
+                    const void* rel_b, const float* bias_a, const float* bias_b, void* dq,
+                    void* dk, void* dv, float* drel_a, float* drel_b, float* dbias_a,
+                    float* dbias_b, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Index maps the kernels use, computed on the device: for every offset delta = i - j in
+ * [-(L-1), L-1], out_a[delta + L - 1] is the table row of that offset (T5 bucket, Shaw row,
+ * T-XL row or -1 when the table has no such row, DeBERTa c2p row) and, for DeBERTa only,
+ * out_b[delta + L - 1] is the p2c row (out_b must be NULL otherwise).  Both int32 device
+ * buffers of 2L - 1 entries. */
+int relpos_index_map(const relpos_desc* desc, int32_t* out_a, int32_t* out_b, void* stream);
+
+/* Static string naming a status code. */
+const char* relpos_status_string(int status);
+
+/* Library ABI version (major * 100 + minor). */
+int relpos_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RELPOS_ATTN_H */

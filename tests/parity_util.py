@@ -1,0 +1,55 @@
+"""Shared helpers for the GPU parity tests: seeded cases, oracle runs and error metrics."""
+
+from __future__ import annotations
+
+import numpy as np
+
+from exact_attention_relative_amd.inputs import make_case
+from oracle import relpos_oracle as orc
+
+# Tolerances stated for this path: bf16 inputs with fp32 accumulation -> O max-abs <= 1e-2 and
+# relative L2 <= 2e-2 for every gradient; fp32 mode -> 1e-4 for both.
+TOL = {"bf16": {"o": 1e-2, "grad": 2e-2, "lse": 2e-3},
+       "fp32": {"o": 1e-4, "grad": 1e-4, "lse": 1e-4}}
+
+MASKS = {"none": (-1, -1), "causal": (-1, 0), "local": (70, 45)}
+
+
+def case(mech, B=2, H=3, L=200, dtype="bf16", mask="none", seed=7, span=None, table_std=None,
+         nb=32, md=None, bidir=None):
+    window = MASKS[mask] if isinstance(mask, str) else mask
+    if span is None:
+        span = {"shaw": 48, "deberta": 40}.get(mech, 0)
+    if md is None:
+        md = max(16, L // 2)
+    c = make_case(mech, B, H, L, 64, dtype=dtype, window=window, seed=seed, rel_span=span,
+                  num_buckets=nb, max_distance=md, bidirectional=bidir, table_std=table_std)
+    return c
+
+
+def params(c) -> orc.Params:
+    return orc.Params(**c["params"])
+
+
+def tables64(c):
+    return {n: t.astype(np.float64) for n, t in c["tables"].items()}
+
+
+def oracle_forward(c):
+    return orc.forward(params(c), c["q"], c["k"], c["v"], tables64(c))
+
+
+def oracle_backward(c):
+    return orc.backward(params(c), c["q"], c["k"], c["v"], tables64(c), c["dout"])
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    den = np.linalg.norm(b.ravel())
+    num = np.linalg.norm((a - b).ravel())
+    return num / den if den > 0 else num
+
+
+def to_np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)

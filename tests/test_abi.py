@@ -1,0 +1,120 @@
+"""Host-side checks of the C ABI: exports, descriptor validation and workspace sizing.
+None of these launches a kernel, so they run without a GPU."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_attention_relative_amd as ear
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "relpos_attn.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(relpos_\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ear.load_library()
+    names = _declared()
+    assert set(names) == set(ear.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    assert ear.relpos_status_string(0) == "ok"
+    for st in (-1, -2, -3, -4):
+        assert ear.relpos_status_string(st) != "unknown status"
+    assert ear.relpos_status_string(-99) == "unknown status"
+    assert ear.relpos_version() >= 100
+
+
+def _ws(desc, pass_=0):
+    out = ctypes.c_size_t(0)
+    st = ear.load_library().relpos_attn_workspace_size(ctypes.byref(desc), pass_, ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("kw,expected", [
+    (dict(mech=7), ear.RELPOS_E_INVALID),
+    (dict(dtype=5), ear.RELPOS_E_INVALID),
+    (dict(batch=-1), ear.RELPOS_E_INVALID),
+    (dict(heads=0), ear.RELPOS_E_INVALID),
+    (dict(seqlen=-3), ear.RELPOS_E_INVALID),
+    (dict(head_dim=0), ear.RELPOS_E_INVALID),
+    (dict(head_dim=128), ear.RELPOS_E_UNSUPPORTED),
+    (dict(window=(-2, 0)), ear.RELPOS_E_INVALID),
+    (dict(rel_span=0), ear.RELPOS_E_INVALID),
+    (dict(scale=-1.0), ear.RELPOS_E_INVALID),
+    (dict(scale=float("nan")), ear.RELPOS_E_INVALID),
+])
+def test_invalid_descriptors(kw, expected):
+    base = dict(mech="shaw", batch=2, heads=4, seqlen=100, head_dim=64, rel_span=8)
+    base.update(kw)
+    raw_dtype = base.pop("dtype", None)
+    mech = base.pop("mech")
+    desc = ear.make_desc(mech, base.pop("batch"), base.pop("heads"), base.pop("seqlen"),
+                         base.pop("head_dim"), **base)
+    if raw_dtype is not None:
+        desc.dtype = raw_dtype
+    assert _ws(desc)[0] == expected
+
+
+@pytest.mark.parametrize("nb,md,bidir,ok", [(32, 128, True, True), (31, 128, True, False),
+                                            (2, 128, True, False), (32, 8, True, False),
+                                            (32, 9, True, True), (8, 5, False, True),
+                                            (8, 4, False, False), (512, 4096, True, False)])
+def test_t5_descriptor_rules(nb, md, bidir, ok):
+    desc = ear.make_desc("t5", 1, 1, 64, num_buckets=nb, max_distance=md, bidirectional=bidir)
+    st, _ = _ws(desc)
+    assert (st == 0) == ok, st
+
+
+def test_workspace_sizes_scale_with_shape():
+    small = ear.make_desc("txl", 1, 2, 100)
+    big = ear.make_desc("txl", 2, 2, 400)
+    st1, n1 = _ws(small)
+    st2, n2 = _ws(big)
+    assert st1 == st2 == 0 and 0 < n1 < n2
+    for mech in ("t5", "shaw", "txl", "deberta"):
+        d = ear.make_desc(mech, 2, 3, 300, rel_span=5)
+        s0, f = _ws(d, 0)
+        s1, b = _ws(d, 1)
+        assert s0 == s1 == 0 and b >= f > 0
+    assert _ws(ear.make_desc("shaw", 1, 1, 10, rel_span=2), 2)[0] == ear.RELPOS_E_INVALID
+
+
+def test_fwd_rejects_bad_pointers_without_launching():
+    lib = ear.load_library()
+    desc = ear.make_desc("shaw", 1, 1, 64, rel_span=4)
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 255) & ~255
+    # missing q
+    st = lib.relpos_attn_fwd(ctypes.byref(desc), None, base, base, base, None, None, None, base,
+                             base, base, 1 << 12, None)
+    assert st == ear.RELPOS_E_INVALID
+    # misaligned k
+    st = lib.relpos_attn_fwd(ctypes.byref(desc), base, base + 2, base, base, None, None, None,
+                             base, base, base, 1 << 12, None)
+    assert st == ear.RELPOS_E_INVALID
+    # table slot that Shaw does not use
+    st = lib.relpos_attn_fwd(ctypes.byref(desc), base, base, base, base, base, None, None, base,
+                             base, base, 1 << 12, None)
+    assert st == ear.RELPOS_E_INVALID
+    # workspace too small / misaligned
+    st = lib.relpos_attn_fwd(ctypes.byref(desc), base, base, base, base, None, None, None, base,
+                             base, base, 16, None)
+    assert st == ear.RELPOS_E_WORKSPACE
+    st = lib.relpos_attn_fwd(ctypes.byref(desc), base, base, base, base, None, None, None, base,
+                             base, base + 16, 1 << 12, None)
+    assert st == ear.RELPOS_E_WORKSPACE
+
+
+def test_missing_library_is_an_error(tmp_path):
+    with pytest.raises(RuntimeError):
+        ear.load_library(str(tmp_path / "nope.so"))

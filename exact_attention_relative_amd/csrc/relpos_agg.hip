@@ -1,0 +1,171 @@
+// Second pass of offset-based gradient sharding (zicq.com explainer, section on offset-based
+// gradient sharding: aggregate locally first, then merge): every table-gradient element sums
+// the per-workgroup partials in ascending owner order, and reductions over offsets use a fixed
+// tree, so the result is bitwise reproducible.  Outputs are overwritten.
+#include "relpos_device.h"
+
+namespace relpos {
+
+// out[r * 64 + d] = scale * sum_{o < nown} part[o * stride + r * 64 + d]
+__global__ void agg_rows_kernel(const float* __restrict__ part, int64_t stride, int nown,
+                                int64_t nelem, float scale, float* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= nelem) return;
+  float acc = 0.f;
+  for (int o = 0; o < nown; ++o) acc += part[(int64_t)o * stride + e];
+  out[e] = acc * scale;
+}
+
+// Owner (workgroup) of batch b, head h, block position p, and the first lane offset of its
+// compact partial: the dQ pass visits blocks in reverse order under a causal mask.
+__device__ __forceinline__ void owner_of(int b, int h, int p, int H, int nb, bool rev, int L,
+                                         int64_t& own, int& lam_base) {
+  const int blk = rev ? nb - 1 - p : p;
+  own = ((int64_t)b * H + h) * nb + p;
+  lam_base = blk * 128 - L - 64;
+}
+
+// diag[h][delta + L - 1] = sum over (b, block) of the per-offset dS sums
+__global__ void agg_diag_kernel(const float* __restrict__ pdiag, int B, int H, int L, int nb,
+                                int rev, int nrt, float* __restrict__ diag) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int n = 2 * L - 1;
+  if (idx >= (int64_t)H * n) return;
+  const int h = (int)(idx / n);
+  const int delta = (int)(idx % n) - (L - 1);
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int p = 0; p < nb; ++p) {
+      int64_t own;
+      int base;
+      owner_of(b, h, p, H, nb, rev != 0, L, own, base);
+      const int x = delta - base;
+      if (x >= 0 && x < nrt) acc += pdiag[own * nrt + x];
+    }
+  diag[idx] = acc;
+}
+
+// T-XL dr[h][row][d] = s (sum_{b, block} part[own][(delta - base) * 64 + d] + v_h[d] diag_h[delta])
+__global__ void agg_txl_dr_kernel(const float* __restrict__ prow, const float* __restrict__ diag,
+                                  const float* __restrict__ v, int B, int H, int L, int nb, int rev,
+                                  int nrt, int nrel, int off, float s, float* __restrict__ dr) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)H * nrel * kHeadDim) return;
+  const int d = (int)(idx % kHeadDim);
+  const int row = (int)((idx / kHeadDim) % nrel);
+  const int h = (int)(idx / ((int64_t)kHeadDim * nrel));
+  const int delta = row - off;
+  float acc = 0.f;
+  if (delta > -L && delta < L) {
+    for (int b = 0; b < B; ++b)
+      for (int p = 0; p < nb; ++p) {
+        int64_t own;
+        int base;
+        owner_of(b, h, p, H, nb, rev != 0, L, own, base);
+        const int x = delta - base;
+        if (x >= 0 && x < nrt) acc += prow[(own * nrt + x) * kHeadDim + d];
+      }
+    acc = fmaf(v[(int64_t)h * kHeadDim + d], diag[(int64_t)h * (2 * L - 1) + delta + L - 1], acc);
+  }
+  dr[idx] = acc * s;
+}
+
+// Fixed-order block reduction helper (256 threads).
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+  sh[threadIdx.x] = v;
+  __syncthreads();
+  for (int st = 128; st > 0; st >>= 1) {
+    if ((int)threadIdx.x < st) sh[threadIdx.x] += sh[threadIdx.x + st];
+    __syncthreads();
+  }
+  float r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+// T5 dbeta[h][c] = sum over offsets with bucket c of diag_h[delta]
+__global__ void agg_t5_kernel(const float* __restrict__ diag, const int* __restrict__ bucket, int L,
+                              int nbk, float* __restrict__ dbeta) {
+  __shared__ float sh[256];
+  const int h = blockIdx.x / nbk, cb = blockIdx.x % nbk;
+  const int n = 2 * L - 1;
+  float acc = 0.f;
+  for (int x = threadIdx.x; x < n; x += 256)
+    if (bucket[x] == cb) acc += diag[(int64_t)h * n + x];
+  const float tot = block_sum(acc, sh);
+  if (threadIdx.x == 0) dbeta[blockIdx.x] = tot;
+}
+
+// T-XL dv[h][d] = s sum_delta diag_h[delta] r_h[row(delta)][d]
+template <typename T>
+__global__ void agg_txl_dv_kernel(const float* __restrict__ diag, const T* __restrict__ r, int L,
+                                  int nrel, int off, float s, float* __restrict__ dv) {
+  __shared__ float sh[256];
+  const int h = blockIdx.x / kHeadDim, d = blockIdx.x % kHeadDim;
+  const int n = 2 * L - 1;
+  float acc = 0.f;
+  for (int x = threadIdx.x; x < n; x += 256) {
+    const int delta = x - (L - 1);
+    const int row = delta + off;
+    if (row >= 0 && row < nrel)
+      acc = fmaf(diag[(int64_t)h * n + x], Elem<T>::to_f(r[((int64_t)h * nrel + row) * kHeadDim + d]), acc);
+  }
+  const float tot = block_sum(acc, sh);
+  if (threadIdx.x == 0) dv[blockIdx.x] = tot * s;
+}
+
+// T-XL du[h][d] = s sum_{b, block} part_kv[own][d]
+__global__ void agg_txl_du_kernel(const float* __restrict__ pkv, int B, int H, int nb, float s,
+                                  float* __restrict__ du) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= H * kHeadDim) return;
+  const int h = idx / kHeadDim, d = idx % kHeadDim;
+  float acc = 0.f;
+  for (int b = 0; b < B; ++b)
+    for (int p = 0; p < nb; ++p) acc += pkv[(((int64_t)b * H + h) * nb + p) * kHeadDim + d];
+  du[idx] = acc * s;
+}
+
+static inline int nblk(int64_t n, int t) { return (int)((n + t - 1) / t); }
+
+hipError_t launch_agg_rows(const float* part, int64_t stride, int nown, int64_t nelem, float scale,
+                           float* out, hipStream_t st) {
+  if (nelem == 0) return hipSuccess;
+  hipLaunchKernelGGL(agg_rows_kernel, dim3(nblk(nelem, 256)), dim3(256), 0, st, part, stride, nown,
+                     nelem, scale, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool rev, int nrt,
+                           float* diag, hipStream_t st) {
+  const int64_t n = (int64_t)H * (2 * L - 1);
+  hipLaunchKernelGGL(agg_diag_kernel, dim3(nblk(n, 256)), dim3(256), 0, st, pdiag, B, H, L, nb,
+                     rev ? 1 : 0, nrt, diag);
+  return hipGetLastError();
+}
+
+hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int nbk, float* dbeta,
+                         hipStream_t st) {
+  hipLaunchKernelGGL(agg_t5_kernel, dim3(H * nbk), dim3(256), 0, st, diag, bucket, L, nbk, dbeta);
+  return hipGetLastError();
+}
+
+hipError_t launch_agg_txl(const float* prow, const float* pkv, const float* diag, const void* r,
+                          const float* v, int B, int H, int L, int nb, bool rev, int nrt, int nrel,
+                          int off, float s, bool fp32, float* dr, float* du, float* dv,
+                          hipStream_t st) {
+  const int64_t n = (int64_t)H * nrel * kHeadDim;
+  hipLaunchKernelGGL(agg_txl_dr_kernel, dim3(nblk(n, 256)), dim3(256), 0, st, prow, diag, v, B, H,
+                     L, nb, rev ? 1 : 0, nrt, nrel, off, s, dr);
+  if (fp32)
+    hipLaunchKernelGGL((agg_txl_dv_kernel<float>), dim3(H * kHeadDim), dim3(256), 0, st, diag,
+                       (const float*)r, L, nrel, off, s, dv);
+  else
+    hipLaunchKernelGGL((agg_txl_dv_kernel<uint16_t>), dim3(H * kHeadDim), dim3(256), 0, st, diag,
+                       (const uint16_t*)r, L, nrel, off, s, dv);
+  hipLaunchKernelGGL(agg_txl_du_kernel, dim3(nblk(H * kHeadDim, 256)), dim3(256), 0, st, pkv, B, H,
+                     nb, s, du);
+  return hipGetLastError();
+}
+
+}  // namespace relpos

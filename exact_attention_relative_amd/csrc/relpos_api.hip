@@ -81,8 +81,9 @@ struct Plan {
   T5Map t5;
   // workspace offsets (bytes)
   size_t off_bucket, off_lut, off_rowc, off_keyc, off_uk, off_vr, off_dsum;
-  size_t off_part_q, off_part_k, off_part_qv, off_part_kv;
+  size_t off_part_q, off_part_k, off_part_qv, off_part_kv, off_diag;
   int64_t part_q_stride, part_k_stride;
+  int nb, nrt, owners;
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -139,7 +140,24 @@ int make_plan(const relpos_desc* d, Plan* p) {
     p->off_vr = take(sizeof(float) * (size_t)p->H * p->nrel);
   }
   p->fwd_bytes = off;
+  // backward: D, per-workgroup partials (one owner per 128-row block of each (batch, head)),
+  // and the per-head diagonal sums of the aggregation pass
   p->off_dsum = take(sizeof(float) * rows);
+  p->nb = (L + 127) / 128;
+  p->nrt = L + 256;
+  p->owners = p->B * p->H * p->nb;
+  const size_t own = (size_t)p->owners;
+  const int k = d->rel_span;
+  if (d->mech == RELPOS_SHAW) p->part_q_stride = (int64_t)(2 * k + 1) * kHeadDim;
+  if (d->mech == RELPOS_DEBERTA) p->part_q_stride = p->part_k_stride = (int64_t)(2 * k) * kHeadDim;
+  if (d->mech == RELPOS_TXL) p->part_q_stride = (int64_t)p->nrt * kHeadDim;
+  if (p->part_q_stride) p->off_part_q = take(sizeof(float) * own * p->part_q_stride);
+  if (p->part_k_stride) p->off_part_k = take(sizeof(float) * own * p->part_k_stride);
+  if (d->mech == RELPOS_T5 || d->mech == RELPOS_TXL) {
+    p->off_part_qv = take(sizeof(float) * own * p->nrt);
+    p->off_diag = take(sizeof(float) * (size_t)p->H * (L > 0 ? 2 * L - 1 : 1));
+  }
+  if (d->mech == RELPOS_TXL) p->off_part_kv = take(sizeof(float) * own * kHeadDim);
   p->bwd_bytes = off;
   return RELPOS_OK;
 }
@@ -161,7 +179,8 @@ hipError_t run_prep(const relpos_desc* d, const Plan& p, const void* q, const vo
     if (e != hipSuccess) return e;
     e = launch_t5_lut(bias_a, p.H, L, d->num_buckets, 1.0f / p.scale, p.t5, (float*)(ws + p.off_lut), st);
   } else if (d->mech == RELPOS_SHAW) {
-    RowDotArgs r{q, rows, L, p.H, rel_a, 0, 0, 2 * d->rel_span, 2, (float*)(ws + p.off_rowc)};
+    // end A (j - i >= k) reads w[2k], end B (j - i <= -k) reads w[0]
+    RowDotArgs r{q, rows, L, p.H, rel_a, 0, 2 * d->rel_span, 0, 2, (float*)(ws + p.off_rowc)};
     e = launch_rowdot(r, p.fp32, p.fp32, st);
   } else if (d->mech == RELPOS_DEBERTA) {
     RowDotArgs r{q, rows, L, p.H, rel_a, 0, 0, 2 * d->rel_span - 1, 2, (float*)(ws + p.off_rowc)};
@@ -292,10 +311,101 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
                     const void* rel_b, const float* bias_a, const float* bias_b, void* dq, void* dk,
                     void* dv, float* drel_a, float* drel_b, float* dbias_a, float* dbias_b,
                     void* workspace, size_t workspace_bytes, void* stream) {
-  (void)desc; (void)q; (void)k; (void)v; (void)o; (void)lse; (void)dout; (void)rel_a; (void)rel_b;
-  (void)bias_a; (void)bias_b; (void)dq; (void)dk; (void)dv; (void)drel_a; (void)drel_b;
-  (void)dbias_a; (void)dbias_b; (void)workspace; (void)workspace_bytes; (void)stream;
-  return RELPOS_E_UNSUPPORTED;
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != RELPOS_OK) return st;
+  st = check_tables(desc, rel_a, rel_b, bias_a, bias_b);
+  if (st != RELPOS_OK) return st;
+  // every table has its gradient slot, and no other slot is set
+  if ((drel_a != nullptr) != (rel_a != nullptr) || (drel_b != nullptr) != (rel_b != nullptr) ||
+      (dbias_a != nullptr) != (bias_a != nullptr) || (dbias_b != nullptr) != (bias_b != nullptr))
+    return RELPOS_E_INVALID;
+  for (const void* ptr : {(const void*)drel_a, (const void*)drel_b, (const void*)dbias_a, (const void*)dbias_b})
+    if (ptr && !aligned16(ptr)) return RELPOS_E_INVALID;
+  if (p.fp32) return RELPOS_E_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.L == 0) return RELPOS_OK;
+  if (p.B == 0) {
+    // no pairs: every table gradient is zero
+    size_t n_a = 0, n_b = 0, n_ba = 0, n_bb = 0;
+    const size_t H = (size_t)p.H, L = (size_t)p.L, k2 = 2 * (size_t)desc->rel_span;
+    switch (desc->mech) {
+      case RELPOS_T5: n_ba = H * desc->num_buckets; break;
+      case RELPOS_SHAW: n_a = (k2 + 1) * kHeadDim; break;
+      case RELPOS_TXL: n_a = H * p.nrel * kHeadDim; n_ba = n_bb = H * kHeadDim; break;
+      case RELPOS_DEBERTA: n_a = n_b = k2 * kHeadDim; break;
+    }
+    (void)L;
+    hipError_t e = hipSuccess;
+    if (n_a) e = launch_agg_rows(nullptr, 0, 0, (int64_t)n_a, 0.f, drel_a, s);
+    if (e == hipSuccess && n_b) e = launch_agg_rows(nullptr, 0, 0, (int64_t)n_b, 0.f, drel_b, s);
+    if (e == hipSuccess && n_ba) e = launch_agg_rows(nullptr, 0, 0, (int64_t)n_ba, 0.f, dbias_a, s);
+    if (e == hipSuccess && n_bb) e = launch_agg_rows(nullptr, 0, 0, (int64_t)n_bb, 0.f, dbias_b, s);
+    return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
+  }
+  for (const void* ptr : {q, k, v, o, (const void*)lse, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!ptr || !aligned16(ptr)) return RELPOS_E_INVALID;
+  if (!ws_ok(workspace, workspace_bytes, p.bwd_bytes)) return RELPOS_E_WORKSPACE;
+  char* ws = (char*)workspace;
+  hipError_t e = run_prep(desc, p, q, k, rel_a, rel_b, bias_a, bias_b, ws, s);
+  if (e != hipSuccess) return RELPOS_E_LAUNCH;
+  const int64_t rows = (int64_t)p.B * p.H * p.L;
+  e = launch_dsum(o, dout, rows, p.fp32, (float*)(ws + p.off_dsum), s);
+  if (e != hipSuccess) return RELPOS_E_LAUNCH;
+
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.sh = make_shape(desc, p);
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.lse = lse;
+  a.dsum = (const float*)(ws + p.off_dsum);
+  a.rel_a = rel_a; a.rel_b = rel_b;
+  a.bias_a = bias_a; a.bias_b = bias_b;
+  if (desc->mech == RELPOS_T5) {
+    a.lut = (const float*)(ws + p.off_lut);
+    a.bucket = (const int*)(ws + p.off_bucket);
+  }
+  if (desc->mech == RELPOS_SHAW || desc->mech == RELPOS_DEBERTA) a.rowc = (const float*)(ws + p.off_rowc);
+  if (desc->mech == RELPOS_DEBERTA) a.keyc = (const float*)(ws + p.off_keyc);
+  if (desc->mech == RELPOS_TXL) {
+    a.uk = (const float*)(ws + p.off_uk);
+    a.vr = (const float*)(ws + p.off_vr);
+  }
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  if (p.part_q_stride) a.part_q = (float*)(ws + p.off_part_q);
+  if (p.part_k_stride) a.part_k = (float*)(ws + p.off_part_k);
+  if (p.off_part_qv) a.part_qv = (float*)(ws + p.off_part_qv);
+  if (p.off_part_kv) a.part_kv = (float*)(ws + p.off_part_kv);
+  a.part_q_stride = p.part_q_stride;
+  a.part_k_stride = p.part_k_stride;
+
+  e = launch_bwd_dq(a, p.fp32, s);
+  if (e != hipSuccess) return RELPOS_E_LAUNCH;
+  e = launch_bwd_dkdv(a, p.fp32, s);
+  if (e != hipSuccess) return RELPOS_E_LAUNCH;
+
+  const bool rev = desc->window_right == 0;
+  float* diag = p.off_diag ? (float*)(ws + p.off_diag) : nullptr;
+  switch (desc->mech) {
+    case RELPOS_T5:
+      e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, p.nrt, diag, s);
+      if (e == hipSuccess) e = launch_agg_t5(diag, a.bucket, p.H, p.L, desc->num_buckets, dbias_a, s);
+      break;
+    case RELPOS_SHAW:
+      e = launch_agg_rows(a.part_q, p.part_q_stride, p.owners, p.part_q_stride, p.scale, drel_a, s);
+      break;
+    case RELPOS_DEBERTA:
+      e = launch_agg_rows(a.part_q, p.part_q_stride, p.owners, p.part_q_stride, p.scale, drel_a, s);
+      if (e == hipSuccess)
+        e = launch_agg_rows(a.part_k, p.part_k_stride, p.owners, p.part_k_stride, p.scale, drel_b, s);
+      break;
+    case RELPOS_TXL:
+      e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, p.nrt, diag, s);
+      if (e == hipSuccess)
+        e = launch_agg_txl(a.part_q, a.part_kv, diag, rel_a, bias_b, p.B, p.H, p.L, p.nb, rev, p.nrt,
+                           p.nrel, p.txl_off, p.scale, p.fp32, drel_a, dbias_a, dbias_b, s);
+      break;
+  }
+  return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
 }
 
 }  // extern "C"

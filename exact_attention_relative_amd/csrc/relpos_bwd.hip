@@ -1,0 +1,793 @@
+// Backward kernels.  One template, instantiated twice per mechanism:
+//   DIR 0: lane side = queries (128 per workgroup), keys streamed: dQ and the query-side table
+//          gradients (Shaw w, T-XL r and its diagonal sums, DeBERTa Kr, T5 diagonal sums).
+//   DIR 1: lane side = keys, queries streamed: dK, dV and the key-side table gradient
+//          (DeBERTa Qr), plus the T-XL u gradient.
+// Both recompute S and P = exp(S - LSE) per tile exactly as the forward does and form
+// dS = P (dP - D) in fp32.  Relation products are reused in both directions (abstract,
+// item 2).  Table gradients follow offset-based gradient sharding (abstract, item 3; zicq.com
+// explainer, section on offset-based gradient sharding): each workgroup accumulates, per
+// offset, the sum over its own rows in registers and writes every offset of its partial
+// exactly once; a second pass (relpos_agg.hip) merges the partials in a fixed order.  No
+// atomics anywhere, so results are bitwise reproducible.
+//
+// Per step, dS is scattered into a workgroup buffer E[t][x] indexed by window offset t and
+// lane-side row x (the band t = x - y + 63 of the 64 streamed rows y).  Then
+//   dX_rel += Win^T E^T                     (per wave, its 96-offset window)
+//   dTable_window[t] += sum_x E[t][x] X[x]  (workgroup GEMM, 3 tiles per wave)
+// The window slides by 64 offsets per step, so a wave's three 32-offset accumulators shift by
+// two positions each step and the one that leaves the window is final: it is written out.
+#include "relpos_tile.h"
+
+namespace relpos {
+
+constexpr int ESTR16 = 136;   // bf16 E row stride (elements)
+constexpr int GS2 = 68;       // half-window skew buffer stride (floats)
+
+template <int MECH, int DIR>
+struct BV {
+  static constexpr bool ROW = DIR == 0 ? MECH != MECH_T5 : MECH == MECH_DEBERTA;
+  static constexpr bool COL = DIR == 0 ? MECH == MECH_DEBERTA : MECH != MECH_T5;
+  static constexpr bool TXL = MECH == MECH_TXL;
+  static constexpr bool CLIP = MECH == MECH_SHAW || MECH == MECH_DEBERTA;
+  static constexpr bool DIAG = DIR == 0 && (MECH == MECH_T5 || MECH == MECH_TXL);
+  static constexpr bool EBUF = ROW;
+  static constexpr bool WINB = ROW || COL;
+  static constexpr bool GSB = ROW || COL || DIAG;
+
+  // row-side table row of lane offset lam = a - b
+  __device__ static int row_of(int lam, int span, int nrel, int off) {
+    if (DIR == 0) return row_side_row(MECH, lam, span, nrel, off);
+    return clampi(lam + span, 0, 2 * span - 1);   // DeBERTa p2c: lam = j - i
+  }
+  // column-side table row of other offset mu = b - a
+  __device__ static int col_of(int mu, int span, int nrel, int off) {
+    if (DIR == 0) return clampi(mu + span, 0, 2 * span - 1);   // DeBERTa p2c: mu = j - i
+    return row_side_row(MECH, mu, span, nrel, off);             // mu = i - j
+  }
+  // offsets <= TA share end row A, >= TB share end row B (Shaw / DeBERTa only)
+  __device__ static int TA(int span) { return -span; }
+  __device__ static int TB(int span) { return MECH == MECH_SHAW ? span : span - 1; }
+  __device__ static int rowA(int span) { return MECH == MECH_SHAW ? 2 * span : 0; }
+  __device__ static int rowB(int span) { return MECH == MECH_SHAW ? 0 : 2 * span - 1; }
+};
+
+// ----------------------------------------------------------------------------- skew helpers
+// Half-window skew: the 96-offset product block is written 64 columns at a time.
+__device__ __forceinline__ void put_block(float* gs, const f32x16& g, int bb, int tbase) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int t = 32 * bb + 8 * q4 + 4 * kh - tbase;
+    f32x4 v = {g[4 * q4], g[4 * q4 + 1], g[4 * q4 + 2], g[4 * q4 + 3]};
+    *(f32x4*)(gs + l32 * GS2 + t) = v;
+  }
+}
+
+// Row side, all three 32-offset blocks of products in registers (optionally + vec[w0 + t]).
+template <bool ADDVEC>
+__device__ __forceinline__ void row_products(f32x16 g[3], const uint16_t* win, int w0,
+                                             const Op<1> xop[4], const float* vec) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int bb = 0; bb < 3; ++bb) {
+    g[bb] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      Op<1> aop = op_from_lds<1>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
+      mma<1>(g[bb], aop, xop[c]);
+    }
+    if constexpr (ADDVEC) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 add = *(const f32x4*)(vec + w0 + 32 * bb + 8 * q4 + 4 * kh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g[bb][4 * q4 + i] += add[i];
+      }
+    }
+  }
+}
+
+// s[b][r] += G[n][n - y + 63]: block b = 0 needs offsets 32..94, block 1 needs 0..62.
+__device__ __forceinline__ void row_skew_add(f32x16 s[2], const f32x16 g[3], float* gs) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+  wave_lds_sync();
+  put_block(gs, g[1], 1, 32);
+  put_block(gs, g[2], 2, 32);
+  wave_lds_sync();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int y = 8 * (r >> 2) + 4 * kh + (r & 3);
+    s[0][r] += gs[l32 * GS2 + l32 - y + 63 - 32];
+  }
+  wave_lds_sync();
+  put_block(gs, g[0], 0, 0);
+  put_block(gs, g[1], 1, 0);
+  wave_lds_sync();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int y = 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+    s[1][r] += gs[l32 * GS2 + l32 - y + 63];
+  }
+}
+
+// Column side for other block ob: products Win[w0 + t'] . Y[32 ob + n] for t' in
+// [32 ob, 32 ob + 64), then s[ob][r] += H[y - 32 ob][y - n + 31].
+template <bool ADDVEC>
+__device__ __forceinline__ void col_skew_add(f32x16 s[2], const uint16_t* win, int w0, int ob,
+                                             const Op<1> yop[2][4], const float* vec, float* gs) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+  f32x16 h[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int bb = ob + i;
+    h[i] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      Op<1> aop = op_from_lds<1>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
+      mma<1>(h[i], aop, yop[ob][c]);
+    }
+    if constexpr (ADDVEC) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 add = *(const f32x4*)(vec + w0 + 32 * bb + 8 * q4 + 4 * kh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[i][4 * q4 + j] += add[j];
+      }
+    }
+  }
+  wave_lds_sync();
+  put_block(gs, h[0], ob, 32 * ob);
+  put_block(gs, h[1], ob + 1, 32 * ob);
+  wave_lds_sync();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int yy = 8 * (r >> 2) + 4 * kh + (r & 3);
+    const int y = 32 * ob + yy;
+    s[ob][r] += gs[yy * GS2 + y - l32 + 31 - 32 * ob];
+  }
+}
+
+// A operand with the k order of op_rows_tr / op_from_acc (slot j < 4: k = 4 kh + j,
+// slot 4 + j: k = 8 + 4 kh + j) read from 16 consecutive bf16 of a row at element e.
+__device__ __forceinline__ Op<1> op_from_lds_perm(const uint16_t* base, int e) {
+  const int kh = __lane_id() >> 5;
+  u32x2 lo = *(const u32x2*)(base + e + 4 * kh);
+  u32x2 hi = *(const u32x2*)(base + e + 8 + 4 * kh);
+  u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  Op<1> o;
+  o.p[0] = u4_to_bf8(v);
+  return o;
+}
+
+// ----------------------------------------------------------------------------- kernel
+template <int MECH, int DIR>
+__global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
+  using V = BV<MECH, DIR>;
+  typedef uint16_t T;
+  constexpr int NP = 1;
+  __shared__ __attribute__((aligned(16))) uint16_t ys[BOTH * TSTR];     // K (dir 0) / Q (dir 1)
+  __shared__ __attribute__((aligned(16))) uint16_t y2s[BOTH * TSTR];    // V (dir 0) / dO (dir 1)
+  __shared__ __attribute__((aligned(16))) uint16_t win[V::WINB ? WIN * TSTR : 8];
+  __shared__ __attribute__((aligned(16))) float gsb[V::GSB ? NWAVE * WROWS * GS2 : 4];
+  __shared__ __attribute__((aligned(16))) uint16_t ebuf[V::EBUF ? WIN * ESTR16 : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[V::ROW ? BLANE * TSTR : 8];   // lane rows X
+  __shared__ __attribute__((aligned(16))) float vec_s[WIN];        // T5 LUT / T-XL v.r window
+  __shared__ __attribute__((aligned(16))) float ovec_s[2 * BOTH];  // per-other-row constants
+  __shared__ __attribute__((aligned(16))) float lsd_s[2 * BOTH];   // dir 1: LSE*log2e, D per query
+  __shared__ __attribute__((aligned(16))) float ring[V::DIAG ? 256 : 4];
+  __shared__ __attribute__((aligned(16))) float wsum[V::DIAG ? NWAVE * 96 : 4];
+  __shared__ __attribute__((aligned(16))) float endc[V::CLIP && V::ROW ? 2 * BLANE : 4];
+
+  const AttnShape sh = a.sh;
+  const int L = sh.L;
+  const int nb = (L + BLANE - 1) / BLANE;
+  const int bid = blockIdx.x;
+  int blk = bid % nb;
+  const int bh = bid / nb;
+  if (sh.wr == 0) blk = (DIR == 0) ? nb - 1 - blk : blk;   // causal: longest first
+  const int h = bh % sh.H;
+  const int A0 = blk * BLANE;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, kh = lane >> 5;
+  const int aw0 = A0 + WROWS * w;
+  const int my_a = aw0 + l32;
+  const int span = sh.span, nrel = sh.nrel, toff = sh.txl_off;
+  const float s = sh.scale, c = s * kLog2e;
+  const int64_t bh_off = (int64_t)bh * L * kHeadDim;
+  const int64_t owner = (int64_t)bid;   // partial slot of this workgroup
+
+  const T* xg = (const T*)(DIR == 0 ? a.q : a.k) + bh_off;
+  const T* x2g = (const T*)(DIR == 0 ? a.dout : a.v) + bh_off;
+  const T* yg = (const T*)(DIR == 0 ? a.k : a.q) + bh_off;
+  const T* y2g = (const T*)(DIR == 0 ? a.v : a.dout) + bh_off;
+  const T* trow = (const T*)(DIR == 0 ? a.rel_a : a.rel_b);   // row-side table
+  const T* tcol = (const T*)(DIR == 0 ? a.rel_b : a.rel_a);   // column-side table
+  if constexpr (MECH == MECH_TXL) {
+    if (DIR == 0) trow += (int64_t)h * nrel * kHeadDim;
+    else tcol += (int64_t)h * nrel * kHeadDim;
+  }
+  const float* rc_g = DIR == 0 ? a.rowc : a.keyc;   // lane rows . row table ends (A, B)
+  const float* oc_g = DIR == 0 ? a.keyc : a.rowc;   // other rows . column table ends (A, B)
+
+  // ---- lane-side registers ----
+  Op<NP> xop[4], x2op[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    if (my_a < L) {
+      xop[cc] = op_from_global<T>(xg + (int64_t)my_a * kHeadDim + 16 * cc + 8 * kh);
+      x2op[cc] = op_from_global<T>(x2g + (int64_t)my_a * kHeadDim + 16 * cc + 8 * kh);
+    } else {
+      float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      xop[cc] = op_from_f32<NP>(z);
+      x2op[cc] = xop[cc];
+    }
+  }
+  float lse2 = __builtin_inff(), dsum_l = 0.f;   // dir 0: per lane
+  if (DIR == 0 && my_a < L) {
+    lse2 = a.lse[(int64_t)bh * L + my_a] * kLog2e;
+    dsum_l = a.dsum[(int64_t)bh * L + my_a];
+    if (!(lse2 > kNegInf)) lse2 = __builtin_inff();   // empty row: P = 0
+  }
+  float rcA = 0.f, rcB = 0.f;
+  if constexpr (V::CLIP && V::ROW) {
+    if (my_a < L) {
+      rcA = rc_g[((int64_t)bh * L + my_a) * 2 + 0];
+      rcB = rc_g[((int64_t)bh * L + my_a) * 2 + 1];
+    }
+  }
+  float ukl = 0.f;   // dir 1 T-XL: u . k of this lane's key
+  if constexpr (MECH == MECH_TXL && DIR == 1) {
+    if (my_a < L) ukl = a.uk[(int64_t)bh * L + my_a];
+  }
+
+  // ---- sweep range over the other side ----
+  int b_lo = 0, b_hi = L - 1;
+  if (DIR == 0) {
+    if (sh.wl >= 0) b_lo = max(0, A0 - sh.wl);
+    if (sh.wr >= 0) b_hi = min(L - 1, A0 + BLANE - 1 + sh.wr);
+  } else {
+    if (sh.wr >= 0) b_lo = max(0, A0 - sh.wr);
+    if (sh.wl >= 0) b_hi = min(L - 1, A0 + BLANE - 1 + sh.wl);
+  }
+  const int bt0 = (b_lo / BOTH) * BOTH;
+  const int nsteps = (b_hi >= b_lo) ? (b_hi - bt0) / BOTH + 1 : 0;
+  const int bt_last = bt0 + (nsteps - 1) * BOTH;
+
+  // ---- partial layouts ----
+  // lane offsets lam of this workgroup lie in [lam_base, lam_base + nrt)
+  const int lam_base = A0 - L - 64;
+  const int nrt = L + 256;
+  float* prow = nullptr;     // row-side table partial
+  int prow_rows = 0;
+  if constexpr (V::ROW) {
+    if constexpr (MECH == MECH_TXL) prow_rows = nrt;
+    else prow_rows = (MECH == MECH_SHAW) ? 2 * span + 1 : 2 * span;
+    prow = (DIR == 0 ? a.part_q : a.part_k) + owner * (DIR == 0 ? a.part_q_stride : a.part_k_stride);
+  }
+  float* pdiag = nullptr;
+  if constexpr (V::DIAG) pdiag = a.part_qv + owner * (int64_t)nrt;
+
+  // lane offsets the sweep writes: every window row of every step, [A0 - b0 - 63, A0 - b0 + 128],
+  // for the table partial; the diagonal sums stop one short (the last window row has no pairs)
+  const int cov_lo = A0 - bt_last - 63, cov_hi = A0 - bt0 + 128, cov_hi_diag = cov_hi - 1;
+
+  // ---- zero what the sweep will not write ----
+  if constexpr (V::ROW) {
+    for (int64_t e = tid; e < (int64_t)prow_rows * kHeadDim; e += 256) {
+      const int row = (int)(e / kHeadDim);
+      bool covered;
+      if constexpr (MECH == MECH_TXL) {
+        const int lam = lam_base + row;
+        covered = nsteps > 0 && lam >= cov_lo && lam <= cov_hi;
+      } else {
+        // end rows are written by the end-row pass; interior rows iff their offset is covered
+        int lam;
+        if constexpr (MECH == MECH_SHAW) lam = span - row;   // dir 0 only: row = clamp(-lam) + k
+        else lam = row - span;                               // row = clamp(lam + k)
+        const bool end = row == V::rowA(span) || row == V::rowB(span);
+        covered = end || (nsteps > 0 && lam >= cov_lo && lam <= cov_hi);
+      }
+      if (!covered) prow[e] = 0.f;
+    }
+  }
+  if constexpr (V::DIAG) {
+    for (int e = tid; e < nrt; e += 256) {
+      const int lam = lam_base + e;
+      if (!(nsteps > 0 && lam >= cov_lo && lam <= cov_hi_diag)) pdiag[e] = 0.f;
+    }
+    for (int e = tid; e < 256; e += 256) ring[e] = 0.f;
+  }
+  if constexpr (V::EBUF) {
+    const int n16 = (WIN * ESTR16) / 8;
+    u32x4 z = {0u, 0u, 0u, 0u};
+    for (int e = tid; e < n16; e += 256) *(u32x4*)(ebuf + 8 * e) = z;
+  }
+  if constexpr (V::ROW) {
+    stage64<T, NP>(xs, xg, A0, L);
+    stage64<T, NP>(xs + BOTH * TSTR, xg, A0 + BOTH, L);
+  }
+
+  // ---- accumulators ----
+  f32x16 gacc[2] = {f32x16{}, f32x16{}};    // dX (content + relation), dir 1: dK
+  f32x16 vacc[2] = {f32x16{}, f32x16{}};    // dir 1: dV
+  f32x16 racc[3] = {f32x16{}, f32x16{}, f32x16{}};   // row-side table window accumulators
+  float cA = 0.f, cB = 0.f;                  // clipped-end sums of dS (lane row)
+  float colsum = 0.f;                        // dir 1 T-XL: sum_i dS_ij
+  const int gdb = w & 1, gp = w >> 1;        // GEMM tiles of this wave: d-block, t-block parity
+
+  float* gs = gsb + (V::GSB ? w * WROWS * GS2 : 0);
+  uint16_t* e16 = ebuf;
+
+  for (int step = 0; step < nsteps; ++step) {
+    const int b0 = bt0 + step * BOTH;
+    const int cwin = A0 - b0;             // workgroup window row t <-> lam = cwin - 63 + t
+    const int lamlo = aw0 - b0 - 63, lamhi = aw0 + 31 - b0;
+    // delta = i - j range of the wave tile
+    const int dlo = DIR == 0 ? lamlo : -lamhi, dhi = DIR == 0 ? lamhi : -lamlo;
+    bool wave_none = (b0 >= L) || (aw0 >= L);
+    if (sh.wl >= 0 && dlo > sh.wl) wave_none = true;
+    if (sh.wr >= 0 && -dhi > sh.wr) wave_none = true;
+    const bool wave_full = (b0 + BOTH <= L) && (aw0 + WROWS <= L) &&
+                           (sh.wl < 0 || dhi <= sh.wl) && (sh.wr < 0 || -dlo <= sh.wr);
+    // ---- tile classes ----
+    int rcls = 0, ccls = 0;   // 0 general, 1 = all end A, 2 = all end B
+    bool wg_general = true;
+    if constexpr (V::CLIP) {
+      const int ta = V::TA(span), tb = V::TB(span);
+      const int wlo = cwin - 63, whi = cwin + 127;   // workgroup lam range
+      bool wg_row = true, wg_col = true;
+      if constexpr (V::ROW) {
+        if (lamhi <= ta) rcls = 1; else if (lamlo >= tb) rcls = 2;
+        wg_row = !(whi <= ta || wlo >= tb);
+      }
+      if constexpr (V::COL) {
+        if (-lamlo <= ta) ccls = 1; else if (-lamhi >= tb) ccls = 2;
+        wg_col = !(-wlo <= ta || -whi >= tb);
+      }
+      wg_general = (V::ROW && wg_row) || (V::COL && wg_col);
+    }
+    int t5cls = 0;
+    if constexpr (MECH == MECH_T5) {
+      const int lo = clampi(dlo, 1 - L, L - 1), hi = clampi(dhi, 1 - L, L - 1);
+      if ((lo >= 0 || hi < 0) && a.bucket[lo + L - 1] == a.bucket[hi + L - 1]) t5cls = 1;
+      // the workgroup needs the E buffer when any of its waves is not single-bucket
+      const int wlo = DIR == 0 ? cwin - 63 : -(cwin + 127), whi = DIR == 0 ? cwin + 127 : -(cwin - 63);
+      const int l2 = clampi(wlo, 1 - L, L - 1), h2 = clampi(whi, 1 - L, L - 1);
+      wg_general = !((l2 >= 0 || h2 < 0) && a.bucket[l2 + L - 1] == a.bucket[h2 + L - 1]);
+    }
+
+    // ---- stage ----
+    __syncthreads();
+    stage64<T, NP>(ys, yg, b0, L);
+    stage64<T, NP>(y2s, y2g, b0, L);
+    if constexpr (MECH == MECH_T5) {
+      for (int x = tid; x < WIN; x += 256) {
+        const int lam = cwin - 63 + x;
+        const int d = DIR == 0 ? lam : -lam;
+        vec_s[x] = (d > -L && d < L) ? a.lut[(int64_t)h * (2 * L - 1) + d + L - 1] : 0.f;
+      }
+    }
+    if constexpr (MECH == MECH_TXL && DIR == 0) {
+      if (tid < BOTH) ovec_s[tid] = (b0 + tid < L) ? a.uk[(int64_t)bh * L + b0 + tid] : 0.f;
+    }
+    if constexpr (V::CLIP && V::COL) {
+      if (tid < 2 * BOTH) {
+        const int yy = b0 + (tid >> 1);
+        ovec_s[tid] = (yy < L) ? oc_g[((int64_t)bh * L + yy) * 2 + (tid & 1)] : 0.f;
+      }
+    }
+    if constexpr (DIR == 1) {
+      if (tid < BOTH) {
+        const int yy = b0 + tid;
+        float l2 = __builtin_inff(), dd = 0.f;
+        if (yy < L) {
+          l2 = a.lse[(int64_t)bh * L + yy] * kLog2e;
+          if (!(l2 > kNegInf)) l2 = __builtin_inff();
+          dd = a.dsum[(int64_t)bh * L + yy];
+        }
+        lsd_s[tid] = l2;
+        lsd_s[BOTH + tid] = dd;
+      }
+    }
+    // column side first (its window is replaced by the row-side window afterwards)
+    if constexpr (V::COL) {
+      if (wg_general) {
+        stage_window<T, NP>(win, tcol, [&](int x) {
+          // column window row x <-> mu = b - a = (b0 - A0 - 127) + x
+          return V::col_of((b0 - A0 - (BLANE - 1)) + x, span, nrel, toff);
+        });
+        if constexpr (MECH == MECH_TXL) {
+          for (int x = tid; x < WIN; x += 256) {
+            const int r = V::col_of((b0 - A0 - (BLANE - 1)) + x, span, nrel, toff);
+            vec_s[x] = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+          }
+        }
+      }
+    }
+    __syncthreads();
+
+    f32x16 sc[2];
+    Op<NP> yop[2][4];
+    if (!wave_none) other_dot_lane<NP>(sc, ys, xop, yop);
+    float lconst = 0.f;   // per-lane additive term (y units)
+    if constexpr (V::COL) {
+      if (!wave_none) {
+        if (V::CLIP && ccls != 0) {
+          add_other_vec(sc, ovec_s + (ccls == 1 ? 0 : 1), 2);
+        } else if (wg_general) {
+          col_skew_add<MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 0, yop, vec_s, gs);
+          col_skew_add<MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 1, yop, vec_s, gs);
+        }
+      }
+    }
+    if constexpr (V::ROW) {
+      if (wg_general) {
+        __syncthreads();   // column-side window reads done
+        stage_window<T, NP>(win, trow, [&](int x) {
+          return V::row_of(cwin - 63 + x, span, nrel, toff);
+        });
+        if constexpr (MECH == MECH_TXL) {
+          for (int x = tid; x < WIN; x += 256) {
+            const int r = V::row_of(cwin - 63 + x, span, nrel, toff);
+            vec_s[x] = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+          }
+        }
+        __syncthreads();
+      }
+      if (!wave_none) {
+        if (V::CLIP && rcls != 0) {
+          lconst = (rcls == 1) ? rcA : rcB;
+        } else {
+          f32x16 g[3];
+          row_products<MECH == MECH_TXL>(g, win, WROWS * w, xop, vec_s);
+          row_skew_add(sc, g, gs);
+        }
+      }
+    }
+    if constexpr (MECH == MECH_T5) {
+      if (!wave_none) {
+        if (t5cls == 1) {
+          const int lo = clampi(DIR == 0 ? lamlo : -lamhi, 1 - L, L - 1);
+          const int lamx = DIR == 0 ? lo : -lo;
+          lconst = vec_s[lamx - (cwin - 63)];
+        } else {
+          add_offset_vec(sc, vec_s, WROWS * w);
+        }
+      }
+    }
+    if constexpr (MECH == MECH_TXL) {
+      if (!wave_none) {
+        if (DIR == 0) add_other_vec(sc, ovec_s, 1);
+        else lconst = ukl;
+      }
+    }
+
+    f32x16 ds[2];
+    if (!wave_none) {
+      // ---- P ----
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
+          float bias;
+          if (DIR == 0) bias = lconst * c - lse2;
+          else bias = lconst * c - lsd_s[y];
+          float p = fast_exp2(fmaf(sc[b][r], c, bias));
+          if (!wave_full) {
+            const int ii = DIR == 0 ? my_a : b0 + y;
+            const int jj = DIR == 0 ? b0 + y : my_a;
+            if (!(ii < L && jj < L && pair_allowed(ii, jj, sh.wl, sh.wr))) p = 0.f;
+          }
+          sc[b][r] = p;
+        }
+      // ---- dP, dS ----
+      Op<NP> y2op[2][4];
+      f32x16 dp[2];
+      other_dot_lane<NP>(dp, y2s, x2op, y2op);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
+          const float dd = DIR == 0 ? dsum_l : lsd_s[BOTH + y];
+          ds[b][r] = sc[b][r] * (dp[b][r] - dd);
+        }
+      // ---- content gradients ----
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        Op<NP> dsop = op_from_acc<NP>(ds, cc);
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          Op<NP> yt = op_rows_tr<NP>(ys, BOTH * TSTR, TSTR, 16 * cc, 32 * db);
+          mma<NP>(gacc[db], yt, dsop);
+        }
+      }
+      if constexpr (DIR == 1) {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+          Op<NP> pop = op_from_acc<NP>(sc, cc);
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+            Op<NP> yt = op_rows_tr<NP>(y2s, BOTH * TSTR, TSTR, 16 * cc, 32 * db);
+            mma<NP>(vacc[db], yt, pop);
+          }
+        }
+      }
+      if constexpr (MECH == MECH_TXL && DIR == 1) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) colsum += ds[b][r];
+      }
+    }
+
+    // ---- offset-sharded row-side gradients ----
+    if constexpr (V::EBUF) {
+      const bool use_e = wg_general;
+      if (use_e) {
+        __syncthreads();   // skew buffers and previous E reads are done
+        // scatter the band; clipped elements go to the end-row sums instead
+        const int xcol = WROWS * w + l32;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
+            const int t = xcol - y + 63;
+            float v = wave_none ? 0.f : ds[b][r];
+            if constexpr (V::CLIP) {
+              const int lam = cwin - 63 + t;
+              if (lam <= V::TA(span)) { cA += v; v = 0.f; }
+              else if (lam >= V::TB(span)) { cB += v; v = 0.f; }
+            }
+            e16[t * ESTR16 + xcol] = f2bf_bits(v);
+          }
+        __syncthreads();
+      } else if (!wave_none) {
+        // the whole wave tile reads one end row
+        float tot = 0.f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tot += ds[b][r];
+        if constexpr (V::CLIP) {
+          if (rcls == 1) cA += tot; else cB += tot;
+        }
+      }
+
+      if constexpr (V::ROW) {
+        // slide the window accumulators by two blocks; the block leaving the window is final
+        if (step > 0) {
+          const int pc = cwin + BOTH;   // previous step's window base (lam = pc - 63 + t)
+          const int a2 = gp + 4;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int t = 32 * a2 + 8 * (r >> 2) + 4 * kh + (r & 3);
+            const int lam = pc - 63 + t;
+            const int d = 32 * gdb + l32;
+            if constexpr (MECH == MECH_TXL) {
+              prow[(int64_t)(lam - lam_base) * kHeadDim + d] = racc[2][r];
+            } else {
+              if (lam > V::TA(span) && lam < V::TB(span)) {
+                const int row = V::row_of(lam, span, nrel, toff);
+                prow[(int64_t)row * kHeadDim + d] = racc[2][r];
+              }
+            }
+          }
+          racc[2] = racc[1];
+          racc[1] = racc[0];
+          racc[0] = f32x16{};
+        }
+        if (wg_general) {
+          // dX_rel += Win^T E^T over this wave's 96 offsets
+#pragma unroll
+          for (int cc = 0; cc < 6; ++cc) {
+            Op<NP> eop = op_rows_tr<NP>(e16, WIN * ESTR16, ESTR16, WROWS * w + 16 * cc, WROWS * w);
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+              Op<NP> wt = op_rows_tr<NP>(win, WIN * TSTR, TSTR, WROWS * w + 16 * cc, 32 * db);
+              mma<NP>(gacc[db], wt, eop);
+            }
+          }
+          // workgroup GEMM: racc[i] (t-block gp + 2 i, d-block gdb) += E[t][x] X[x][d]
+#pragma unroll
+          for (int i = 0; i < 3; ++i) {
+            const int ab = gp + 2 * i;
+            const int c_lo = max(0, 2 * ab - 4), c_hi = min(7, 2 * ab + 1);
+            for (int cq = c_lo; cq <= c_hi; ++cq) {
+              Op<NP> eop = op_from_lds_perm(e16, (32 * ab + l32) * ESTR16 + 16 * cq);
+              Op<NP> xop2 = op_rows_tr<NP>(xs, BLANE * TSTR, TSTR, 16 * cq, 32 * gdb);
+              mma<NP>(racc[i], eop, xop2);
+            }
+          }
+        }
+      }
+
+    }
+
+    // ---- per-offset fp32 sums of dS (T5 bias gradient; T-XL v term and v gradient) ----
+    if constexpr (V::DIAG) {
+      float* wv = wsum + 96 * w;
+      const bool single = (MECH == MECH_T5) && t5cls == 1;
+      if (!wave_none && !single) {
+        // dS[n][y] into the wave buffer, then sums along the diagonals t = n - y + 63
+        wave_lds_sync();
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            f32x4 v4 = {ds[b][4 * g4], ds[b][4 * g4 + 1], ds[b][4 * g4 + 2], ds[b][4 * g4 + 3]};
+            *(f32x4*)(gs + l32 * GS2 + 32 * b + 8 * g4 + 4 * kh) = v4;
+          }
+        wave_lds_sync();
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int t = lane + 64 * half;
+          if (t < 96) {
+            const int n0 = max(0, t - 63), n1 = min(WROWS - 1, t);
+            float sum = 0.f;
+            for (int n = n0; n <= n1; ++n) sum += gs[n * GS2 + n + 63 - t];
+            wv[t] = sum;
+          }
+        }
+      } else {
+        // single bucket: the wave total goes to one offset of the tile (window row 63)
+        float tot = 0.f;
+        if (!wave_none) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tot += ds[b][r];
+          tot += xhalf(tot);
+          for (int m = 1; m < 32; m <<= 1) tot += __shfl_xor(tot, m);
+        }
+        wv[lane] = (lane == 63) ? tot : 0.f;
+        if (lane < 32) wv[64 + lane] = 0.f;
+      }
+      __syncthreads();
+      if (tid < WIN - 1) {
+        float sum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NWAVE; ++ww) {
+          const int t = tid - 32 * ww;
+          if (t >= 0 && t < 96) sum += wsum[96 * ww + t];
+        }
+        const int lam = cwin - 63 + tid;
+        float val = ring[lam & 255] + sum;
+        // offsets above the next window are final
+        if (step == nsteps - 1 || tid >= 127) {
+          pdiag[lam - lam_base] = val;
+          val = 0.f;
+        }
+        ring[lam & 255] = val;
+      }
+    }
+  }
+
+  // ---- final flush of the window accumulators ----
+  if constexpr (V::ROW) {
+    if (nsteps > 0) {
+      const int pc = A0 - bt_last;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int ab = gp + 2 * i;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * ab + 8 * (r >> 2) + 4 * kh + (r & 3);
+          const int lam = pc - 63 + t;
+          const int d = 32 * gdb + l32;
+          if constexpr (MECH == MECH_TXL) {
+            prow[(int64_t)(lam - lam_base) * kHeadDim + d] = racc[i][r];
+          } else {
+            if (lam > V::TA(span) && lam < V::TB(span)) {
+              const int row = V::row_of(lam, span, nrel, toff);
+              prow[(int64_t)row * kHeadDim + d] = racc[i][r];
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // ---- end rows (clipped offsets): table gradient and lane gradient ----
+  if constexpr (V::CLIP && V::ROW) {
+    // cA / cB hold this lane's sum over its half of the other rows
+    cA += xhalf(cA);
+    cB += xhalf(cB);
+    if (kh == 0) {
+      endc[WROWS * w + l32] = (my_a < L) ? cA : 0.f;
+      endc[BLANE + WROWS * w + l32] = (my_a < L) ? cB : 0.f;
+    }
+    __syncthreads();
+    if (tid < 2 * kHeadDim) {
+      const int e = tid / kHeadDim, d = tid % kHeadDim;
+      float acc = 0.f;
+      for (int x = 0; x < BLANE; ++x) acc = fmaf(endc[e * BLANE + x], bf_bits2f(xs[x * TSTR + d]), acc);
+      const int row = e == 0 ? V::rowA(span) : V::rowB(span);
+      prow[(int64_t)row * kHeadDim + d] = acc;
+    }
+    // dX += cA T[rowA] + cB T[rowB]
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * db + 8 * (r >> 2) + 4 * kh + (r & 3);
+        const float ta = bf_bits2f(trow[(int64_t)V::rowA(span) * kHeadDim + d]);
+        const float tb = bf_bits2f(trow[(int64_t)V::rowB(span) * kHeadDim + d]);
+        gacc[db][r] = fmaf(cA, ta, fmaf(cB, tb, gacc[db][r]));
+      }
+  }
+
+  // ---- T-XL key side: dK += u * colsum; du partial = sum_j colsum_j k_j ----
+  if constexpr (MECH == MECH_TXL && DIR == 1) {
+    colsum += xhalf(colsum);
+    const float* u = a.bias_a + (int64_t)h * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * db + 8 * (r >> 2) + 4 * kh + (r & 3);
+        gacc[db][r] = fmaf(colsum, u[d], gacc[db][r]);
+      }
+    __shared__ float csum[BLANE];
+    if (kh == 0) csum[WROWS * w + l32] = (my_a < L) ? colsum : 0.f;
+    __syncthreads();
+    if (tid < kHeadDim) {
+      float acc = 0.f;
+      for (int x = 0; x < BLANE && A0 + x < L; ++x)
+        acc = fmaf(csum[x], bf_bits2f(xg[(int64_t)(A0 + x) * kHeadDim + tid]), acc);
+      a.part_kv[owner * kHeadDim + tid] = acc;
+    }
+  }
+
+  // ---- store dX (dQ or dK) and dV ----
+  if (my_a < L) {
+    T* gx = (T*)(DIR == 0 ? a.dq : a.dk) + bh_off + (int64_t)my_a * kHeadDim;
+    T* gv = (T*)a.dv + bh_off + (int64_t)my_a * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * kh;
+        u32x2 pk = {pack_bf16x2(gacc[db][4 * g] * s, gacc[db][4 * g + 1] * s),
+                    pack_bf16x2(gacc[db][4 * g + 2] * s, gacc[db][4 * g + 3] * s)};
+        *(u32x2*)(gx + d) = pk;
+        if constexpr (DIR == 1) {
+          u32x2 pv = {pack_bf16x2(vacc[db][4 * g], vacc[db][4 * g + 1]),
+                      pack_bf16x2(vacc[db][4 * g + 2], vacc[db][4 * g + 3])};
+          *(u32x2*)(gv + d) = pv;
+        }
+      }
+  }
+}
+
+template <int DIR>
+static hipError_t launch_bwd_dir(const BwdArgs& a, hipStream_t stream) {
+  const int nb = (a.sh.L + BLANE - 1) / BLANE;
+  const dim3 grid((unsigned)(nb * a.sh.B * a.sh.H));
+  switch (a.sh.mech) {
+    case MECH_T5: hipLaunchKernelGGL((bwd_kernel<MECH_T5, DIR>), grid, dim3(256), 0, stream, a); break;
+    case MECH_SHAW: hipLaunchKernelGGL((bwd_kernel<MECH_SHAW, DIR>), grid, dim3(256), 0, stream, a); break;
+    case MECH_TXL: hipLaunchKernelGGL((bwd_kernel<MECH_TXL, DIR>), grid, dim3(256), 0, stream, a); break;
+    case MECH_DEBERTA: hipLaunchKernelGGL((bwd_kernel<MECH_DEBERTA, DIR>), grid, dim3(256), 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, bool fp32, hipStream_t stream) {
+  if (fp32) return hipErrorInvalidValue;
+  return launch_bwd_dir<0>(a, stream);
+}
+hipError_t launch_bwd_dkdv(const BwdArgs& a, bool fp32, hipStream_t stream) {
+  if (fp32) return hipErrorInvalidValue;
+  return launch_bwd_dir<1>(a, stream);
+}
+
+}  // namespace relpos

@@ -58,12 +58,14 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       qop[cc] = op_from_f32<NP>(z);
     }
   }
-  // Clipped-end constants of this query row (Shaw: q.w[0], q.w[2k]; DeBERTa: q.Kr[0], q.Kr[2k-1]).
-  float rc_lo = 0.f, rc_hi = 0.f;
+  // Clipped-end constants of this query row: the products with the table row shared by all
+  // offsets delta <= -k (end A) and by all large offsets (end B).  Shaw: A = w[2k], B = w[0];
+  // DeBERTa: A = Kr[0], B = Kr[2k-1].
+  float rcA = 0.f, rcB = 0.f;
   if constexpr (MECH == MECH_SHAW || MECH == MECH_DEBERTA) {
     if (my_i < L) {
-      rc_lo = a.rowc[((int64_t)bh * L + my_i) * 2 + 0];
-      rc_hi = a.rowc[((int64_t)bh * L + my_i) * 2 + 1];
+      rcA = a.rowc[((int64_t)bh * L + my_i) * 2 + 0];
+      rcB = a.rowc[((int64_t)bh * L + my_i) * 2 + 1];
     }
   }
 
@@ -155,8 +157,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       }
     } else if constexpr (MECH == MECH_SHAW) {
       if (!wave_none) {
-        if (cls == 2) rowconst = rc_hi;
-        else if (cls == 1) rowconst = rc_lo;
+        if (cls == 2) rowconst = rcA;        // j - i >= k: row 2k
+        else if (cls == 1) rowconst = rcB;   // j - i <= -k: row 0
         else {
           rowside_products<NP, false>(gs, win, WROWS * w, qop, nullptr);
           wave_lds_sync();
@@ -172,8 +174,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       }
     } else if constexpr (MECH == MECH_DEBERTA) {
       if (!wave_none) {
-        if (cls == 2) { rowconst = rc_hi; add_other_vec(sc, kvec_s + 0, 2); }
-        else if (cls == 1) { rowconst = rc_lo; add_other_vec(sc, kvec_s + 1, 2); }
+        if (cls == 2) { rowconst = rcB; add_other_vec(sc, kvec_s + 0, 2); }        // delta >= k
+        else if (cls == 1) { rowconst = rcA; add_other_vec(sc, kvec_s + 1, 2); }   // delta <= -k
         else {
           rowside_products<NP, false>(gs, win, WROWS * w, qop, nullptr);
           wave_lds_sync();

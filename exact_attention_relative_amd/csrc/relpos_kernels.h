@@ -104,6 +104,18 @@ hipError_t launch_t5_lut(const float* beta, int H, int L, int nb, float inv_scal
                          float* lut, hipStream_t stream);
 hipError_t launch_index_map(int mech, int L, int span, int nrel, int txl_off, const T5Map& m,
                             int32_t* out_a, int32_t* out_b, hipStream_t stream);
+// second-pass aggregation of the backward's offset-sharded partials
+hipError_t launch_agg_rows(const float* part, int64_t stride, int nown, int64_t nelem, float scale,
+                           float* out, hipStream_t st);
+hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool rev, int nrt,
+                           float* diag, hipStream_t st);
+hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int nbk, float* dbeta,
+                         hipStream_t st);
+hipError_t launch_agg_txl(const float* prow, const float* pkv, const float* diag, const void* r,
+                          const float* v, int B, int H, int L, int nb, bool rev, int nrt, int nrel,
+                          int off, float s, bool fp32, float* dr, float* du, float* dv,
+                          hipStream_t st);
+
 // D_n = dO_n . O_n over rows of length 64
 hipError_t launch_dsum(const void* o, const void* dout, int64_t nrows, bool fp32, float* dsum,
                        hipStream_t stream);

@@ -1,0 +1,282 @@
+"""Benchmark of the exact relative-position attention hot path on one MI355X.
+
+A step is one forward + backward pass of all four mechanisms (T5, Shaw, DeBERTa, T-XL) over the
+long-context workload B=4, H=8, L=8192, d=64, bidirectional, bf16 inputs with fp32 accumulation
+(T5 32 buckets / max_distance 1024, Shaw k=256, DeBERTa k=512, T-XL full span).  The value is
+the whole step's algorithmic TFLOP/s: F_fwd = 4 N d + F_rel and F_bwd = 10 N d + 3 F_rel per
+mechanism, N = attended pairs, F_rel = 2 d x distinct (row, table-row) relation products (0 for
+T5, N for T-XL).  Inputs are resident in HBM before the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+MECH_ORDER = ("t5", "shaw", "deberta", "txl")
+CFG_NAME = {"t5": "long_t5_L8192", "shaw": "long_shaw_L8192", "deberta": "long_deberta_L8192",
+            "txl": "long_txl_L8192"}
+
+
+# ------------------------------------------------------------------ algorithmic flop counts
+def _allowed_count_per_row(L, wl, wr):
+    i = np.arange(L)
+    lo = np.zeros(L, dtype=np.int64) if wl < 0 else np.maximum(0, i - wl)
+    hi = np.full(L, L - 1, dtype=np.int64) if wr < 0 else np.minimum(L - 1, i + wr)
+    return lo, hi
+
+
+def _distinct_clamped(lo_off, hi_off, lo_clip, hi_clip):
+    """Number of distinct values of clamp(x, lo_clip, hi_clip) for integer x in [lo_off, hi_off]."""
+    a = np.clip(lo_off, lo_clip, hi_clip)
+    b = np.clip(hi_off, lo_clip, hi_clip)
+    return np.where(hi_off >= lo_off, b - a + 1, 0)
+
+
+def flop_counts(mech, B, H, L, d, wl, wr, span):
+    """(N, F_rel) for one call: attended pairs and relation-product flops."""
+    lo, hi = _allowed_count_per_row(L, wl, wr)
+    per_row = np.maximum(hi - lo + 1, 0)
+    n_pairs = int(per_row.sum()) * B * H
+    i = np.arange(L)
+    if mech == "t5":
+        rel = 0
+    elif mech == "txl":
+        rel = n_pairs
+    elif mech == "shaw":
+        # row i reads clamp(j - i, -k, k) for j in [lo, hi]
+        rel = int(_distinct_clamped(lo - i, hi - i, -span, span).sum()) * B * H
+    elif mech == "deberta":
+        # c2p: clamp(i - j + k) per query row; p2c: clamp(j - i + k) per key column
+        c2p = _distinct_clamped(i - hi, i - lo, -span, span - 1).sum()
+        jlo, jhi = _allowed_count_per_row(L, wr, wl)   # queries attending key j
+        p2c = _distinct_clamped(i - jhi, i - jlo, -span, span - 1).sum()
+        rel = int(c2p + p2c) * B * H
+    else:
+        raise ValueError(mech)
+    return n_pairs, 2 * d * rel
+
+
+def pass_flops(mech, B, H, L, d, wl, wr, span):
+    n, frel = flop_counts(mech, B, H, L, d, wl, wr, span)
+    return {"fwd": 4 * n * d + frel, "bwd": 10 * n * d + 3 * frel,
+            # split of the backward between its two kernels (accounting convention)
+            "bwd_dq": 2 * n * d + 2 * frel, "bwd_dkdv": 8 * n * d + frel, "pairs": n}
+
+
+# ------------------------------------------------------------------ GPU side
+def build_mech(mech, torch):
+    from exact_attention_relative_amd import runner
+    from exact_attention_relative_amd.inputs import make_config
+    case = make_config(CFG_NAME[mech])
+    desc = runner.desc_for(case)
+    dev = runner.to_device(case)
+    ws_f, nf = runner.workspace(desc, 0)
+    ws_b, nb = runner.workspace(desc, 1)
+    o = torch.empty_like(dev["q"])
+    lse = torch.empty(dev["q"].shape[:-1], dtype=torch.float32, device="cuda")
+    grads = runner.alloc_grads(desc, dev)
+    cfg = case["config"]
+    B, H, L, d = case["shape"]
+    fl = pass_flops(mech, B, H, L, d, cfg["window"][0], cfg["window"][1], cfg.get("rel_span", 0))
+    return dict(mech=mech, case=case, desc=desc, dev=dev, ws_f=ws_f, ws_b=ws_b, o=o, lse=lse,
+                grads=grads, flops=fl)
+
+
+def run_fwd(m):
+    from exact_attention_relative_amd import relpos_attn_fwd
+    from exact_attention_relative_amd.runner import slots
+    d = m["dev"]
+    relpos_attn_fwd(m["desc"], d["q"], d["k"], d["v"], *slots(d), m["o"], m["lse"], m["ws_f"],
+                    m["ws_f"].numel())
+
+
+def run_bwd(m):
+    from exact_attention_relative_amd import runner
+    runner.backward(m["desc"], m["dev"], m["o"], m["lse"], ws=m["ws_b"], grads=m["grads"])
+
+
+def step(mechs, hook=None):
+    """One pass of the hot path.  hook = (mech, kernel_id, start, stop) records one kernel."""
+    from exact_attention_relative_amd import relpos_profile_events, RELPOS_PROF_OFF
+    for m in mechs:
+        on = hook is not None and hook[0] == m["mech"]
+        if on:
+            relpos_profile_events(hook[2], hook[3], hook[1])
+        run_fwd(m)
+        run_bwd(m)
+        if on:
+            relpos_profile_events(None, None, RELPOS_PROF_OFF)
+
+
+def time_kernel(torch, mechs, mech, kid, reps=3):
+    evs = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    for a, b in evs:
+        step([m for m in mechs if m["mech"] == mech], hook=(mech, kid, a, b))
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+
+def cpu_baseline(budget_heads=1):
+    """The fp64 oracle, as it stands, on one (batch, head) slice of each mechanism's workload
+    (forward + backward), timed on the host cores; scaled to TFLOP/s by the slice's flops."""
+    from exact_attention_relative_amd.inputs import make_config
+    from oracle import relpos_oracle as orc
+    cores = len(os.sched_getaffinity(0))
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    tot_s, tot_f = 0.0, 0.0
+    for mech in MECH_ORDER:
+        case = make_config(CFG_NAME[mech])
+        p = orc.Params(**case["params"])
+        tab = {n: t.astype(np.float64) for n, t in case["tables"].items()}
+        cfg = case["config"]
+        B, H, L, d = case["shape"]
+        fl = pass_flops(mech, 1, budget_heads, L, d, cfg["window"][0], cfg["window"][1],
+                        cfg.get("rel_span", 0))
+        t0 = time.time()
+        for h in range(budget_heads):
+            orc.forward_rows(p, case["q"], case["k"], case["v"], tab, 0, h)
+            orc.backward_head(p, case["q"], case["k"], case["v"], tab, case["dout"], 0, h)
+        tot_s += time.time() - t0
+        tot_f += fl["fwd"] + fl["bwd"]
+        del case, tab
+    return {"value": tot_f / tot_s / 1e12, "unit": "TFLOP/s", "cores": min(cores, threads),
+            "kind": "oracle",
+            "sample": f"forward + backward of {budget_heads} (batch, head) slice(s) of each of the "
+                      f"four mechanisms at L=8192 (fp64 NumPy oracle), {tot_s:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the workload shards over (batch, head) with no exchange except a table-gradient "
+              "all-reduce, which is not implemented)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from exact_attention_relative_amd import (RELPOS_PROF_BWD_DKDV, RELPOS_PROF_BWD_DQ,
+                                              RELPOS_PROF_FWD)
+    torch.cuda.init()
+    mechs = []
+    per_mech = {}
+    for mech in MECH_ORDER:
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        m = build_mech(mech, torch)
+        torch.cuda.synchronize()
+        torch.cuda.reset_peak_memory_stats()
+        run_fwd(m)
+        torch.cuda.synchronize()
+        peak_fwd = torch.cuda.max_memory_allocated() - base
+        run_bwd(m)
+        torch.cuda.synchronize()
+        peak_all = torch.cuda.max_memory_allocated() - base
+        mechs.append(m)
+        per_mech[mech] = {"peak_mem_fwd_GiB": peak_fwd / 2**30, "peak_mem_fwd_bwd_GiB": peak_all / 2**30,
+                          "naive_fp32_bias_GiB": 4 * m["case"]["shape"][0] * m["case"]["shape"][1] * m["case"]["shape"][2] ** 2 / 2**30}
+        print(f"[bench] built {mech}", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        step(mechs)
+    torch.cuda.synchronize()
+
+    # per-pass times of each mechanism (separate from the timed region)
+    kid = {"fwd": RELPOS_PROF_FWD, "bwd_dq": RELPOS_PROF_BWD_DQ, "bwd_dkdv": RELPOS_PROF_BWD_DKDV}
+    kernel_ms = {}
+    for m in mechs:
+        mech = m["mech"]
+        for name, k in kid.items():
+            kernel_ms[(mech, name)] = time_kernel(torch, mechs, mech, k)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record(); run_fwd(m); ev[1].record(); run_bwd(m); ev[2].record()
+        torch.cuda.synchronize()
+        tf, tb = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+        fl = m["flops"]
+        per_mech[mech].update({
+            "fwd_ms": tf, "bwd_ms": tb,
+            "fwd_TFLOPs": fl["fwd"] / tf / 1e9, "bwd_TFLOPs": fl["bwd"] / tb / 1e9,
+            "fwd_bwd_TFLOPs": (fl["fwd"] + fl["bwd"]) / (tf + tb) / 1e9,
+            "fwd_bwd_frac_bf16_peak": (fl["fwd"] + fl["bwd"]) / (tf + tb) / 1e9 / PEAK_BF16_TFLOPS,
+            "kernel_ms": {n: kernel_ms[(mech, n)] for n in kid}})
+    dom = max(kernel_ms, key=kernel_ms.get)
+    dom_mech, dom_kernel = dom
+    dm = next(m for m in mechs if m["mech"] == dom_mech)
+
+    # ---- timed region ----
+    evs = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(); b.record()
+        evs.append((a, b))
+    t_start, t_stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for s in range(args.steps):
+        step(mechs, hook=(dom_mech, kid[dom_kernel], evs[s][0], evs[s][1]))
+    t_stop.record()
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_stop) / args.steps
+    dom_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    step_flops = sum(m["flops"]["fwd"] + m["flops"]["bwd"] for m in mechs)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+    dom_flops = dm["flops"][dom_kernel]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "kernel": f"{dom_kernel} pass kernel, {dom_mech}", "avg_ms": dom_ms,
+                "flops_per_launch": dom_flops}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        for m in mechs:
+            del m["dev"]
+        mechs.clear()
+        torch.cuda.empty_cache()
+        cpu = cpu_baseline()
+
+    out = {
+        "metric": "fwd+bwd TFLOP/s and % bf16 MFMA peak at L=8192 per mechanism; peak memory",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "frac_bf16_peak": value / PEAK_BF16_TFLOPS,
+        "config": {"workload": "long-context relative-position attention: B=4 H=8 L=8192 d=64, "
+                               "bidirectional; T5 32 buckets max_distance 1024, Shaw k=256, "
+                               "DeBERTa k=512, T-XL full span; fwd+bwd of all four per step",
+                   "global_batch": 4, "seq_len": 8192, "heads": 8, "head_dim": 64},
+        "per_mechanism": per_mech,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -24,7 +24,8 @@ RELPOS_E_WORKSPACE = -3
 RELPOS_E_LAUNCH = -4
 
 EXPORTED = ("relpos_attn_workspace_size", "relpos_attn_fwd", "relpos_attn_bwd",
-            "relpos_index_map", "relpos_status_string", "relpos_version")
+            "relpos_index_map", "relpos_profile_events", "relpos_status_string", "relpos_version")
+RELPOS_PROF_OFF, RELPOS_PROF_FWD, RELPOS_PROF_BWD_DQ, RELPOS_PROF_BWD_DKDV = 0, 1, 2, 3
 
 
 class relpos_desc(ctypes.Structure):
@@ -66,6 +67,8 @@ def load_library(path: str | None = None):
     lib.relpos_attn_bwd.restype = i32
     lib.relpos_index_map.argtypes = [dp, vp, vp, vp]
     lib.relpos_index_map.restype = i32
+    lib.relpos_profile_events.argtypes = [vp, vp, i32]
+    lib.relpos_profile_events.restype = i32
     lib.relpos_status_string.argtypes = [i32]
     lib.relpos_status_string.restype = ctypes.c_char_p
     lib.relpos_version.argtypes = []
@@ -151,4 +154,15 @@ def relpos_index_map(desc, out_a, out_b=None, stream=None, check=True) -> int:
     st = load_library().relpos_index_map(ctypes.byref(desc), _ptr(out_a), _ptr(out_b), _stream(stream))
     if check:
         _check(st, "relpos_index_map")
+    return st
+
+
+def relpos_profile_events(start_event, stop_event, kernel: int) -> int:
+    """start_event / stop_event: torch.cuda.Event(enable_timing=True) (or raw hipEvent_t ints)."""
+    def raw(e):
+        if e is None or isinstance(e, int):
+            return e
+        return e.cuda_event
+    st = load_library().relpos_profile_events(raw(start_event), raw(stop_event), int(kernel))
+    _check(st, "relpos_profile_events")
     return st

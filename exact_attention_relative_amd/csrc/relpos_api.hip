@@ -231,9 +231,39 @@ int check_tables(const relpos_desc* d, const void* rel_a, const void* rel_b, con
   return RELPOS_OK;
 }
 
+// profiling hook (see relpos_profile_events)
+hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+int g_prof_kernel = RELPOS_PROF_OFF;
+
+template <typename F>
+hipError_t timed(int which, hipStream_t st, F launch) {
+  const bool on = g_prof_kernel == which;
+  if (on) {
+    hipError_t e = hipEventRecord(g_prof_start, st);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = launch();
+  if (on && e == hipSuccess) e = hipEventRecord(g_prof_stop, st);
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
+
+int relpos_profile_events(void* start_event, void* stop_event, int kernel) {
+  if (kernel == RELPOS_PROF_OFF) {
+    g_prof_kernel = RELPOS_PROF_OFF;
+    g_prof_start = g_prof_stop = nullptr;
+    return RELPOS_OK;
+  }
+  if (kernel < RELPOS_PROF_FWD || kernel > RELPOS_PROF_BWD_DKDV || !start_event || !stop_event)
+    return RELPOS_E_INVALID;
+  g_prof_start = (hipEvent_t)start_event;
+  g_prof_stop = (hipEvent_t)stop_event;
+  g_prof_kernel = kernel;
+  return RELPOS_OK;
+}
 
 int relpos_version(void) { return 100; }
 
@@ -302,7 +332,7 @@ int relpos_attn_fwd(const relpos_desc* desc, const void* q, const void* k, const
     a.uk = (const float*)(ws + p.off_uk);
     a.vr = (const float*)(ws + p.off_vr);
   }
-  e = launch_fwd(a, p.fp32, s);
+  e = timed(RELPOS_PROF_FWD, s, [&] { return launch_fwd(a, p.fp32, s); });
   return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
 }
 
@@ -378,9 +408,9 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
   a.part_q_stride = p.part_q_stride;
   a.part_k_stride = p.part_k_stride;
 
-  e = launch_bwd_dq(a, p.fp32, s);
+  e = timed(RELPOS_PROF_BWD_DQ, s, [&] { return launch_bwd_dq(a, p.fp32, s); });
   if (e != hipSuccess) return RELPOS_E_LAUNCH;
-  e = launch_bwd_dkdv(a, p.fp32, s);
+  e = timed(RELPOS_PROF_BWD_DKDV, s, [&] { return launch_bwd_dkdv(a, p.fp32, s); });
   if (e != hipSuccess) return RELPOS_E_LAUNCH;
 
   const bool rev = desc->window_right == 0;

@@ -48,7 +48,7 @@ def to_device(case: dict, device="cuda") -> dict:
     return dev
 
 
-def _slots(dev):
+def slots(dev):
     return tuple(dev.get(s) for s in ("rel_a", "rel_b", "bias_a", "bias_b"))
 
 
@@ -65,7 +65,7 @@ def forward(desc, dev, ws=None):
         ws, n = workspace(desc, 0, q.device)
     else:
         n = ws.numel()
-    relpos_attn_fwd(desc, q, dev["k"], dev["v"], *_slots(dev), o, lse, ws, n)
+    relpos_attn_fwd(desc, q, dev["k"], dev["v"], *slots(dev), o, lse, ws, n)
     return o, lse
 
 
@@ -85,7 +85,7 @@ def backward(desc, dev, o, lse, ws=None, grads=None):
         ws, n = workspace(desc, 1, dev["q"].device)
     else:
         n = ws.numel()
-    relpos_attn_bwd(desc, dev["q"], dev["k"], dev["v"], o, lse, dev["dout"], *_slots(dev),
+    relpos_attn_bwd(desc, dev["q"], dev["k"], dev["v"], o, lse, dev["dout"], *slots(dev),
                     grads["dq"], grads["dk"], grads["dv"], grads.get("drel_a"), grads.get("drel_b"),
                     grads.get("dbias_a"), grads.get("dbias_b"), ws, n)
     return grads

@@ -111,6 +111,15 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
  * buffers of 2L - 1 entries. */
 int relpos_index_map(const relpos_desc* desc, int32_t* out_a, int32_t* out_b, void* stream);
 
+/* Profiling hook for benchmarks.  When `kernel` is RELPOS_PROF_FWD, RELPOS_PROF_BWD_DQ or
+ * RELPOS_PROF_BWD_DKDV, later calls record `start_event` on their stream just before enqueueing
+ * that kernel and `stop_event` just after it (both hipEvent_t created by the caller).
+ * RELPOS_PROF_OFF (0) clears the hook.  Process-wide setting, not thread-safe; intended for
+ * single-threaded benchmark drivers only.  Returns RELPOS_E_INVALID for an unknown kernel id or
+ * NULL events. */
+enum { RELPOS_PROF_OFF = 0, RELPOS_PROF_FWD = 1, RELPOS_PROF_BWD_DQ = 2, RELPOS_PROF_BWD_DKDV = 3 };
+int relpos_profile_events(void* start_event, void* stop_event, int kernel);
+
 /* Static string naming a status code. */
 const char* relpos_status_string(int status);
 

@@ -6,13 +6,25 @@
 
 namespace relpos {
 
+// Sum of n strided partials with 8 loads in flight: lane j of 8 accumulates owners j, j + 8,
+// ...; the eight sums are then added in a fixed tree.  Deterministic for a given n.
+__device__ __forceinline__ float strided_sum(const float* __restrict__ p, int64_t stride, int n) {
+  float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  int o = 0;
+  for (; o + 8 <= n; o += 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] += p[(int64_t)(o + j) * stride];
+  }
+  for (int j = 0; o + j < n; ++j) a[j] += p[(int64_t)(o + j) * stride];
+  return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
+}
+
 // out[r * 64 + d] = scale * sum_{o < nown} part[o * stride + r * 64 + d]
 __global__ void agg_rows_kernel(const float* __restrict__ part, int64_t stride, int nown,
                                 int64_t nelem, float scale, float* __restrict__ out) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= nelem) return;
-  float acc = 0.f;
-  for (int o = 0; o < nown; ++o) acc += part[(int64_t)o * stride + e];
+  const float acc = nown > 0 ? strided_sum(part + e, stride, nown) : 0.f;
   out[e] = acc * scale;
 }
 
@@ -57,14 +69,22 @@ __global__ void agg_txl_dr_kernel(const float* __restrict__ prow, const float* _
   const int delta = row - off;
   float acc = 0.f;
   if (delta > -L && delta < L) {
+    float a8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int b = 0; b < B; ++b)
-      for (int p = 0; p < nb; ++p) {
-        int64_t own;
-        int base;
-        owner_of(b, h, p, H, nb, rev != 0, L, own, base);
-        const int x = delta - base;
-        if (x >= 0 && x < nrt) acc += prow[(own * nrt + x) * kHeadDim + d];
+      for (int p0 = 0; p0 < nb; p0 += 8) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int p = p0 + j;
+          if (p < nb) {
+            int64_t own;
+            int base;
+            owner_of(b, h, p, H, nb, rev != 0, L, own, base);
+            const int x = delta - base;
+            if (x >= 0 && x < nrt) a8[j] += prow[(own * nrt + x) * kHeadDim + d];
+          }
+        }
       }
+    acc = ((a8[0] + a8[1]) + (a8[2] + a8[3])) + ((a8[4] + a8[5]) + (a8[6] + a8[7]));
     acc = fmaf(v[(int64_t)h * kHeadDim + d], diag[(int64_t)h * (2 * L - 1) + delta + L - 1], acc);
   }
   dr[idx] = acc * s;

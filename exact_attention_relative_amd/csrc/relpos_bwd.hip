@@ -22,7 +22,6 @@
 namespace relpos {
 
 constexpr int ESTR16 = 136;   // bf16 E row stride (elements)
-constexpr int GS2 = 68;       // half-window skew buffer stride (floats)
 
 template <int MECH, int DIR>
 struct BV {
@@ -52,106 +51,6 @@ struct BV {
   __device__ static int rowB(int span) { return MECH == MECH_SHAW ? 0 : 2 * span - 1; }
 };
 
-// ----------------------------------------------------------------------------- skew helpers
-// Half-window skew: the 96-offset product block is written 64 columns at a time.
-__device__ __forceinline__ void put_block(float* gs, const f32x16& g, int bb, int tbase) {
-  const int lane = __lane_id();
-  const int l32 = lane & 31, kh = lane >> 5;
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    const int t = 32 * bb + 8 * q4 + 4 * kh - tbase;
-    f32x4 v = {g[4 * q4], g[4 * q4 + 1], g[4 * q4 + 2], g[4 * q4 + 3]};
-    *(f32x4*)(gs + l32 * GS2 + t) = v;
-  }
-}
-
-// Row side, all three 32-offset blocks of products in registers (optionally + vec[w0 + t]).
-template <bool ADDVEC>
-__device__ __forceinline__ void row_products(f32x16 g[3], const uint16_t* win, int w0,
-                                             const Op<1> xop[4], const float* vec) {
-  const int lane = __lane_id();
-  const int l32 = lane & 31, kh = lane >> 5;
-#pragma unroll
-  for (int bb = 0; bb < 3; ++bb) {
-    g[bb] = f32x16{};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      Op<1> aop = op_from_lds<1>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
-      mma<1>(g[bb], aop, xop[c]);
-    }
-    if constexpr (ADDVEC) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 add = *(const f32x4*)(vec + w0 + 32 * bb + 8 * q4 + 4 * kh);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) g[bb][4 * q4 + i] += add[i];
-      }
-    }
-  }
-}
-
-// s[b][r] += G[n][n - y + 63]: block b = 0 needs offsets 32..94, block 1 needs 0..62.
-__device__ __forceinline__ void row_skew_add(f32x16 s[2], const f32x16 g[3], float* gs) {
-  const int lane = __lane_id();
-  const int l32 = lane & 31, kh = lane >> 5;
-  wave_lds_sync();
-  put_block(gs, g[1], 1, 32);
-  put_block(gs, g[2], 2, 32);
-  wave_lds_sync();
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int y = 8 * (r >> 2) + 4 * kh + (r & 3);
-    s[0][r] += gs[l32 * GS2 + l32 - y + 63 - 32];
-  }
-  wave_lds_sync();
-  put_block(gs, g[0], 0, 0);
-  put_block(gs, g[1], 1, 0);
-  wave_lds_sync();
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int y = 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-    s[1][r] += gs[l32 * GS2 + l32 - y + 63];
-  }
-}
-
-// Column side for other block ob: products Win[w0 + t'] . Y[32 ob + n] for t' in
-// [32 ob, 32 ob + 64), then s[ob][r] += H[y - 32 ob][y - n + 31].
-template <bool ADDVEC>
-__device__ __forceinline__ void col_skew_add(f32x16 s[2], const uint16_t* win, int w0, int ob,
-                                             const Op<1> yop[2][4], const float* vec, float* gs) {
-  const int lane = __lane_id();
-  const int l32 = lane & 31, kh = lane >> 5;
-  f32x16 h[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int bb = ob + i;
-    h[i] = f32x16{};
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      Op<1> aop = op_from_lds<1>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
-      mma<1>(h[i], aop, yop[ob][c]);
-    }
-    if constexpr (ADDVEC) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 add = *(const f32x4*)(vec + w0 + 32 * bb + 8 * q4 + 4 * kh);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) h[i][4 * q4 + j] += add[j];
-      }
-    }
-  }
-  wave_lds_sync();
-  put_block(gs, h[0], ob, 32 * ob);
-  put_block(gs, h[1], ob + 1, 32 * ob);
-  wave_lds_sync();
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int yy = 8 * (r >> 2) + 4 * kh + (r & 3);
-    const int y = 32 * ob + yy;
-    s[ob][r] += gs[yy * GS2 + y - l32 + 31 - 32 * ob];
-  }
-}
-
 // A operand with the k order of op_rows_tr / op_from_acc (slot j < 4: k = 4 kh + j,
 // slot 4 + j: k = 8 + 4 kh + j) read from 16 consecutive bf16 of a row at element e.
 __device__ __forceinline__ Op<1> op_from_lds_perm(const uint16_t* base, int e) {
@@ -166,7 +65,7 @@ __device__ __forceinline__ Op<1> op_from_lds_perm(const uint16_t* base, int e) {
 
 // ----------------------------------------------------------------------------- kernel
 template <int MECH, int DIR>
-__global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
+__device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   using V = BV<MECH, DIR>;
   typedef uint16_t T;
   constexpr int NP = 1;
@@ -176,8 +75,9 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float gsb[V::GSB ? NWAVE * WROWS * GS2 : 4];
   __shared__ __attribute__((aligned(16))) uint16_t ebuf[V::EBUF ? WIN * ESTR16 : 8];
   __shared__ __attribute__((aligned(16))) uint16_t xs[V::ROW ? BLANE * TSTR : 8];   // lane rows X
-  __shared__ __attribute__((aligned(16))) float vec_s[WIN];        // T5 LUT / T-XL v.r window
-  __shared__ __attribute__((aligned(16))) float ovec_s[2 * BOTH];  // per-other-row constants
+  __shared__ __attribute__((aligned(16))) float vec_s[(MECH == MECH_T5 || MECH == MECH_TXL) ? WIN : 4];  // T5 LUT / T-XL v.r
+  constexpr bool OVEC = (MECH == MECH_TXL && DIR == 0) || (V::CLIP && V::COL);
+  __shared__ __attribute__((aligned(16))) float ovec_s[OVEC ? 2 * BOTH : 4];  // per-other-row constants
   __shared__ __attribute__((aligned(16))) float lsd_s[2 * BOTH];   // dir 1: LSE*log2e, D per query
   __shared__ __attribute__((aligned(16))) float ring[V::DIAG ? 256 : 4];
   __shared__ __attribute__((aligned(16))) float wsum[V::DIAG ? NWAVE * 96 : 4];
@@ -420,8 +320,8 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
         if (V::CLIP && ccls != 0) {
           add_other_vec(sc, ovec_s + (ccls == 1 ? 0 : 1), 2);
         } else if (wg_general) {
-          col_skew_add<MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 0, yop, vec_s, gs);
-          col_skew_add<MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 1, yop, vec_s, gs);
+          col_skew_add<NP, MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 0, yop, vec_s, gs);
+          col_skew_add<NP, MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 1, yop, vec_s, gs);
         }
       }
     }
@@ -444,7 +344,7 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
           lconst = (rcls == 1) ? rcA : rcB;
         } else {
           f32x16 g[3];
-          row_products<MECH == MECH_TXL>(g, win, WROWS * w, xop, vec_s);
+          row_products<NP, MECH == MECH_TXL>(g, win, WROWS * w, xop, vec_s);
           row_skew_add(sc, g, gs);
         }
       }
@@ -735,7 +635,8 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
         const int d = 32 * db + 8 * (r >> 2) + 4 * kh + (r & 3);
         gacc[db][r] = fmaf(colsum, u[d], gacc[db][r]);
       }
-    __shared__ float csum[BLANE];
+    float* csum = lsd_s;   // the per-query vectors are dead after the sweep
+    __syncthreads();
     if (kh == 0) csum[WROWS * w + l32] = (my_a < L) ? colsum : 0.f;
     __syncthreads();
     if (tid < kHeadDim) {
@@ -767,15 +668,35 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
   }
 }
 
+// Variants whose LDS footprint leaves room for two workgroups per CU are compiled for two
+// waves per SIMD (at most 256 registers per lane); the others for one.
+template <int MECH, int DIR>
+__global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
+  bwd_body<MECH, DIR>(a);
+}
+template <int MECH, int DIR>
+__global__ __launch_bounds__(256, 1) void bwd_kernel_1wg(BwdArgs a) {
+  bwd_body<MECH, DIR>(a);
+}
+template <int MECH, int DIR>
+constexpr bool two_wg() {
+  return MECH == MECH_T5 || (MECH == MECH_SHAW && DIR == 1);
+}
+template <int MECH, int DIR>
+static void launch_one(const BwdArgs& a, dim3 grid, hipStream_t stream) {
+  if constexpr (two_wg<MECH, DIR>()) hipLaunchKernelGGL((bwd_kernel<MECH, DIR>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((bwd_kernel_1wg<MECH, DIR>), grid, dim3(256), 0, stream, a);
+}
+
 template <int DIR>
 static hipError_t launch_bwd_dir(const BwdArgs& a, hipStream_t stream) {
   const int nb = (a.sh.L + BLANE - 1) / BLANE;
   const dim3 grid((unsigned)(nb * a.sh.B * a.sh.H));
   switch (a.sh.mech) {
-    case MECH_T5: hipLaunchKernelGGL((bwd_kernel<MECH_T5, DIR>), grid, dim3(256), 0, stream, a); break;
-    case MECH_SHAW: hipLaunchKernelGGL((bwd_kernel<MECH_SHAW, DIR>), grid, dim3(256), 0, stream, a); break;
-    case MECH_TXL: hipLaunchKernelGGL((bwd_kernel<MECH_TXL, DIR>), grid, dim3(256), 0, stream, a); break;
-    case MECH_DEBERTA: hipLaunchKernelGGL((bwd_kernel<MECH_DEBERTA, DIR>), grid, dim3(256), 0, stream, a); break;
+    case MECH_T5: launch_one<MECH_T5, DIR>(a, grid, stream); break;
+    case MECH_SHAW: launch_one<MECH_SHAW, DIR>(a, grid, stream); break;
+    case MECH_TXL: launch_one<MECH_TXL, DIR>(a, grid, stream); break;
+    case MECH_DEBERTA: launch_one<MECH_DEBERTA, DIR>(a, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -26,18 +26,19 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
 // ---------------------------------------------------------------------------------------
-// bf16 conversions (round to nearest even, as the hardware converter does)
+// bf16 conversions: the CDNA4 packed converter (v_cvt_pk_bf16_f32, round to nearest even)
 // ---------------------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 __device__ __forceinline__ uint16_t f2bf_bits(float x) {
-  uint32_t u = __builtin_bit_cast(uint32_t, x);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return (uint16_t)(pack_bf16x2(x, 0.f) & 0xFFFFu);
 }
 __device__ __forceinline__ float bf_bits2f(uint16_t b) {
   return __builtin_bit_cast(float, (uint32_t)b << 16);
-}
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bf_bits(lo) | ((uint32_t)f2bf_bits(hi) << 16);
 }
 // Split x into hi + lo with both parts bf16 (the three-product fp32 emulation).
 __device__ __forceinline__ void split_bf16(float x, uint16_t& hi, uint16_t& lo) {

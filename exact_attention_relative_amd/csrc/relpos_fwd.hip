@@ -12,15 +12,17 @@
 namespace relpos {
 
 template <typename T, int MECH>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+__device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   constexpr int NP = Elem<T>::NP;
   constexpr bool REL = (MECH != MECH_T5);
+  constexpr bool VEC = (MECH == MECH_T5 || MECH == MECH_TXL);
+  constexpr int KVEC = (MECH == MECH_DEBERTA) ? 2 * BOTH : (MECH == MECH_TXL ? BOTH : 1);
   __shared__ __attribute__((aligned(16))) uint16_t ks[NP * BOTH * TSTR];
   __shared__ __attribute__((aligned(16))) uint16_t vs[NP * BOTH * TSTR];
   __shared__ __attribute__((aligned(16))) uint16_t win[REL ? NP * WIN * TSTR : 8];
-  __shared__ __attribute__((aligned(16))) float gsb[REL ? NWAVE * WROWS * GSTR : 4];
-  __shared__ __attribute__((aligned(16))) float vec_s[WIN];     // T5 LUT slice / T-XL v.r
-  __shared__ __attribute__((aligned(16))) float kvec_s[2 * BOTH]; // T-XL u.k / DeBERTa k.Qr ends
+  __shared__ __attribute__((aligned(16))) float gsb[REL ? NWAVE * WROWS * GS2 : 4];
+  __shared__ __attribute__((aligned(16))) float vec_s[VEC ? WIN : 4];   // T5 LUT slice / T-XL v.r
+  __shared__ __attribute__((aligned(16))) float kvec_s[KVEC];           // T-XL u.k / DeBERTa k.Qr ends
 
   const AttnShape sh = a.sh;
   const int L = sh.L;
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   if (sh.wr >= 0) j_hi = min(L - 1, i0 + BLANE - 1 + sh.wr);
   const int jt0 = (j_lo / BOTH) * BOTH;
 
-  float* gs = gsb + (REL ? w * WROWS * GSTR : 0);
+  float* gs = gsb + (REL ? w * WROWS * GS2 : 0);
 
   for (int j0 = jt0; j0 <= j_hi; j0 += BOTH) {
     // ---- tile classification (offset-aware scheduling) ----
@@ -160,16 +162,16 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
         if (cls == 2) rowconst = rcA;        // j - i >= k: row 2k
         else if (cls == 1) rowconst = rcB;   // j - i <= -k: row 0
         else {
-          rowside_products<NP, false>(gs, win, WROWS * w, qop, nullptr);
-          wave_lds_sync();
-          rowside_gather(sc, gs);
+          f32x16 g[3];
+          row_products<NP, false>(g, win, WROWS * w, qop, nullptr);
+          row_skew_add(sc, g, gs);
         }
       }
     } else if constexpr (MECH == MECH_TXL) {
       if (!wave_none) {
-        rowside_products<NP, true>(gs, win, WROWS * w, qop, vec_s);
-        wave_lds_sync();
-        rowside_gather(sc, gs);
+        f32x16 g[3];
+        row_products<NP, true>(g, win, WROWS * w, qop, vec_s);
+        row_skew_add(sc, g, gs);
         add_other_vec(sc, kvec_s, 1);
       }
     } else if constexpr (MECH == MECH_DEBERTA) {
@@ -177,9 +179,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
         if (cls == 2) { rowconst = rcB; add_other_vec(sc, kvec_s + 0, 2); }        // delta >= k
         else if (cls == 1) { rowconst = rcA; add_other_vec(sc, kvec_s + 1, 2); }   // delta <= -k
         else {
-          rowside_products<NP, false>(gs, win, WROWS * w, qop, nullptr);
-          wave_lds_sync();
-          rowside_gather(sc, gs);
+          f32x16 g[3];
+          row_products<NP, false>(g, win, WROWS * w, qop, nullptr);
+          row_skew_add(sc, g, gs);
         }
       }
       if (wg_general) {
@@ -192,12 +194,8 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
         __syncthreads();
         if (!wave_none && cls == 0) {
 #pragma unroll
-          for (int ob = 0; ob < 2; ++ob) {
-            wave_lds_sync();
-            colside_products<NP, false>(gs, win, (BLANE - WROWS) - WROWS * w, ob, kop, nullptr);
-            wave_lds_sync();
-            colside_gather(sc, gs, ob);
-          }
+          for (int ob = 0; ob < 2; ++ob)
+            col_skew_add<NP, false>(sc, win, (BLANE - WROWS) - WROWS * w, ob, kop, nullptr, gs);
         }
       }
     }
@@ -215,16 +213,26 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     }
 
     // ---- online softmax ----
+    // The rescale of O and l is skipped when no row of the wave raised its running max (the
+    // factor would be exactly 1), which is the common case after the first tiles.  The
+    // running max stays exact, so the largest weight of every row is exactly 1.
     float mx = kNegInf;
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[b][r]);
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[b][r], sc[b][r + 1]));
     mx = fmaxf(mx, xhalf(mx));
     mx += rowconst;
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run - m_use) * c);
+    const bool raise = mx > m_run;
+    if (__any(raise)) {
+      const float m_new = raise ? mx : m_run;
+      const float alpha = raise ? fast_exp2((m_run - m_new) * c) : 1.f;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
     const float bias = (rowconst - m_use) * c;
     float psum = 0.f;
 #pragma unroll
@@ -235,10 +243,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
         sc[b][r] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < 2; ++db) oacc[db] *= alpha;
+    l_run += psum;
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
@@ -278,15 +283,32 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   }
 }
 
+// Two workgroups (8 waves) per CU when the LDS footprint allows it (bf16); the launch bound
+// caps registers at 256 per lane so the register file does not become the limit instead.
+template <typename T, int MECH>
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+  fwd_body<T, MECH>(a);
+}
+template <typename T, int MECH>
+__global__ __launch_bounds__(256, 1) void fwd_kernel_1wg(FwdArgs a) {
+  fwd_body<T, MECH>(a);
+}
+
+template <typename T, int MECH>
+static void launch_one(const FwdArgs& a, dim3 grid, hipStream_t stream) {
+  if constexpr (Elem<T>::NP == 1) hipLaunchKernelGGL((fwd_kernel<T, MECH>), grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL((fwd_kernel_1wg<T, MECH>), grid, dim3(256), 0, stream, a);
+}
+
 template <typename T>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   const int nqb = (a.sh.L + BLANE - 1) / BLANE;
   const dim3 grid((unsigned)(nqb * a.sh.B * a.sh.H));
   switch (a.sh.mech) {
-    case MECH_T5: hipLaunchKernelGGL((fwd_kernel<T, MECH_T5>), grid, dim3(256), 0, stream, a); break;
-    case MECH_SHAW: hipLaunchKernelGGL((fwd_kernel<T, MECH_SHAW>), grid, dim3(256), 0, stream, a); break;
-    case MECH_TXL: hipLaunchKernelGGL((fwd_kernel<T, MECH_TXL>), grid, dim3(256), 0, stream, a); break;
-    case MECH_DEBERTA: hipLaunchKernelGGL((fwd_kernel<T, MECH_DEBERTA>), grid, dim3(256), 0, stream, a); break;
+    case MECH_T5: launch_one<T, MECH_T5>(a, grid, stream); break;
+    case MECH_SHAW: launch_one<T, MECH_SHAW>(a, grid, stream); break;
+    case MECH_TXL: launch_one<T, MECH_TXL>(a, grid, stream); break;
+    case MECH_DEBERTA: launch_one<T, MECH_DEBERTA>(a, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -24,7 +24,7 @@ constexpr int BLANE = NWAVE * WROWS; // lane-side rows per workgroup
 constexpr int BOTH = 64;             // other-side rows per step
 constexpr int TSTR = 72;             // LDS row stride (elements) of 64-wide bf16 tiles
 constexpr int WIN = 192;             // window rows (BLANE + BOTH - 1 = 191, padded)
-constexpr int GSTR = 100;            // skew buffer row stride (floats)
+constexpr int GS2 = 68;              // skew buffer row stride (floats): 64 offsets + pad
 
 // ---------------------------------------------------------------------------------------
 // Staging (all 256 threads).  Tiles hold NP bf16 planes of [rows][TSTR].
@@ -88,85 +88,105 @@ __device__ __forceinline__ void other_dot_lane(f32x16 acc[2], const uint16_t* yt
   }
 }
 
-// Row-side relation products for one wave: g[bb] = Win[w0 + 32 bb + m] . X[n], then (opt.)
-// g += vec[w0 + t] per window row t.  Written to the wave's skew buffer gs[n][t].
+// ---------------------------------------------------------------------------------------
+// Skew through a wave-private LDS buffer of 32 rows x 64 offsets: the 96-offset product
+// block of a wave is written 64 columns at a time and read back along the diagonals.
+// ---------------------------------------------------------------------------------------
+__device__ __forceinline__ void put_block(float* gs, const f32x16& g, int bb, int tbase) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int t = 32 * bb + 8 * q4 + 4 * kh - tbase;
+    f32x4 v = {g[4 * q4], g[4 * q4 + 1], g[4 * q4 + 2], g[4 * q4 + 3]};
+    *(f32x4*)(gs + l32 * GS2 + t) = v;
+  }
+}
+
+// Row side, all three 32-offset blocks of products in registers (optionally + vec[w0 + t]).
 template <int NP, bool ADDVEC>
-__device__ __forceinline__ void rowside_products(float* gs, const uint16_t* win, int w0,
-                                                 const Op<NP> xop[4], const float* vec) {
+__device__ __forceinline__ void row_products(f32x16 g[3], const uint16_t* win, int w0,
+                                             const Op<NP> xop[4], const float* vec) {
   const int lane = __lane_id();
   const int l32 = lane & 31, kh = lane >> 5;
 #pragma unroll
   for (int bb = 0; bb < 3; ++bb) {
-    f32x16 g = {};
+    g[bb] = f32x16{};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      Op<NP> a = op_from_lds<NP>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
-      mma<NP>(g, a, xop[c]);
+      Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
+      mma<NP>(g[bb], aop, xop[c]);
     }
+    if constexpr (ADDVEC) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int t = 32 * bb + 8 * q4 + 4 * kh;
-      f32x4 v = {g[4 * q4], g[4 * q4 + 1], g[4 * q4 + 2], g[4 * q4 + 3]};
-      if constexpr (ADDVEC) {
-        f32x4 add = *(const f32x4*)(vec + w0 + t);
-        v += add;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 add = *(const f32x4*)(vec + w0 + 32 * bb + 8 * q4 + 4 * kh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g[bb][4 * q4 + i] += add[i];
       }
-      *(f32x4*)(gs + l32 * GSTR + t) = v;
     }
   }
 }
 
-// Gather: s[b][r] += gs[n][n - y + 63] with y the other-side row of register (b, r).
-__device__ __forceinline__ void rowside_gather(f32x16 s[2], const float* gs) {
+// s[b][r] += G[n][n - y + 63]: block b = 0 needs offsets 32..94, block 1 needs 0..62.
+__device__ __forceinline__ void row_skew_add(f32x16 s[2], const f32x16 g[3], float* gs) {
   const int lane = __lane_id();
   const int l32 = lane & 31, kh = lane >> 5;
+  wave_lds_sync();
+  put_block(gs, g[1], 1, 32);
+  put_block(gs, g[2], 2, 32);
+  wave_lds_sync();
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int r = 0; r < 16; ++r) {
+    const int y = 8 * (r >> 2) + 4 * kh + (r & 3);
+    s[0][r] += gs[l32 * GS2 + l32 - y + 63 - 32];
+  }
+  wave_lds_sync();
+  put_block(gs, g[0], 0, 0);
+  put_block(gs, g[1], 1, 0);
+  wave_lds_sync();
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
-      s[b][r] += gs[l32 * GSTR + l32 - y + 63];
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int y = 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
+    s[1][r] += gs[l32 * GS2 + l32 - y + 63];
+  }
 }
 
-// Column-side relation products for other-side block ob (32 rows): h[bb'] = Win[w0 + 32 bb + m]
-// . Y[32 ob + n] for bb in {ob, ob + 1}; written to gs[n][t'] (n = other row within block).
+// Column side for other block ob: products Win[w0 + t'] . Y[32 ob + n] for t' in
+// [32 ob, 32 ob + 64), then s[ob][r] += H[y - 32 ob][y - n + 31].
 template <int NP, bool ADDVEC>
-__device__ __forceinline__ void colside_products(float* gs, const uint16_t* win, int w0, int ob,
-                                                 const Op<NP> yop[2][4], const float* vec) {
+__device__ __forceinline__ void col_skew_add(f32x16 s[2], const uint16_t* win, int w0, int ob,
+                                             const Op<NP> yop[2][4], const float* vec, float* gs) {
   const int lane = __lane_id();
   const int l32 = lane & 31, kh = lane >> 5;
+  f32x16 h[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int bb = ob + i;
-    f32x16 g = {};
+    h[i] = f32x16{};
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      Op<NP> a = op_from_lds<NP>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
-      mma<NP>(g, a, yop[ob][c]);
+      Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
+      mma<NP>(h[i], aop, yop[ob][c]);
     }
+    if constexpr (ADDVEC) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int t = 32 * bb + 8 * q4 + 4 * kh;
-      f32x4 v = {g[4 * q4], g[4 * q4 + 1], g[4 * q4 + 2], g[4 * q4 + 3]};
-      if constexpr (ADDVEC) {
-        f32x4 add = *(const f32x4*)(vec + w0 + t);
-        v += add;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        f32x4 add = *(const f32x4*)(vec + w0 + 32 * bb + 8 * q4 + 4 * kh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[i][4 * q4 + j] += add[j];
       }
-      *(f32x4*)(gs + l32 * GSTR + t) = v;
     }
   }
-}
-
-// Gather for column side block ob: s[ob][r] += gs[y - 32 ob][y - n + 31].
-__device__ __forceinline__ void colside_gather(f32x16 s[2], const float* gs, int ob) {
-  const int lane = __lane_id();
-  const int l32 = lane & 31, kh = lane >> 5;
+  wave_lds_sync();
+  put_block(gs, h[0], ob, 32 * ob);
+  put_block(gs, h[1], ob + 1, 32 * ob);
+  wave_lds_sync();
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int yy = 8 * (r >> 2) + 4 * kh + (r & 3);   // other row within block
+    const int yy = 8 * (r >> 2) + 4 * kh + (r & 3);
     const int y = 32 * ob + yy;
-    s[ob][r] += gs[yy * GSTR + y - l32 + 31];
+    s[ob][r] += gs[yy * GS2 + y - l32 + 31 - 32 * ob];
   }
 }
 

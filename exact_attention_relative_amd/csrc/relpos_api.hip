@@ -81,7 +81,7 @@ struct Plan {
   T5Map t5;
   // workspace offsets (bytes)
   size_t off_bucket, off_lut, off_rowc, off_keyc, off_uk, off_vr, off_dsum;
-  size_t off_part_q, off_part_k, off_part_qv, off_part_kv, off_diag;
+  size_t off_part_q, off_part_k, off_part_qv, off_part_kv, off_diag, off_xpart, off_vpart, off_cab;
   int64_t part_q_stride, part_k_stride;
   int nb, nrt, owners;
   size_t fwd_bytes, bwd_bytes;
@@ -158,6 +158,12 @@ int make_plan(const relpos_desc* d, Plan* p) {
     p->off_diag = take(sizeof(float) * (size_t)p->H * (L > 0 ? 2 * L - 1 : 1));
   }
   if (d->mech == RELPOS_TXL) p->off_part_kv = take(sizeof(float) * own * kHeadDim);
+  if (d->mech == RELPOS_SHAW || d->mech == RELPOS_DEBERTA) {
+    // split passes: clipped-step partials handed from the light kernel to the general one
+    p->off_xpart = take(sizeof(float) * rows * kHeadDim);
+    p->off_cab = take(sizeof(float) * rows * 2);
+  }
+  if (d->mech == RELPOS_DEBERTA) p->off_vpart = take(sizeof(float) * rows * kHeadDim);
   p->bwd_bytes = off;
   return RELPOS_OK;
 }
@@ -407,6 +413,9 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
   if (p.off_part_kv) a.part_kv = (float*)(ws + p.off_part_kv);
   a.part_q_stride = p.part_q_stride;
   a.part_k_stride = p.part_k_stride;
+  if (p.off_xpart) a.xpart = (float*)(ws + p.off_xpart);
+  if (p.off_vpart) a.vpart = (float*)(ws + p.off_vpart);
+  if (p.off_cab) a.cab = (float*)(ws + p.off_cab);
 
   e = timed(RELPOS_PROF_BWD_DQ, s, [&] { return launch_bwd_dq(a, p.fp32, s); });
   if (e != hipSuccess) return RELPOS_E_LAUNCH;

@@ -23,10 +23,18 @@ namespace relpos {
 
 constexpr int ESTR16 = 136;   // bf16 E row stride (elements)
 
-template <int MECH, int DIR>
+// PART 0: the whole sweep.  PART 1 (light): only the steps whose workgroup tile is clipped
+// (every offset beyond the span), without any relation-product machinery, writing fp32 partial
+// dX / dV and the end-row sums.  PART 2: only the contiguous range of general steps, merging
+// the light pass's partials into the final outputs.
+template <int MECH, int DIR, int PART>
 struct BV {
-  static constexpr bool ROW = DIR == 0 ? MECH != MECH_T5 : MECH == MECH_DEBERTA;
-  static constexpr bool COL = DIR == 0 ? MECH == MECH_DEBERTA : MECH != MECH_T5;
+  static constexpr bool HAS_ROW = DIR == 0 ? MECH != MECH_T5 : MECH == MECH_DEBERTA;
+  static constexpr bool HAS_COL = DIR == 0 ? MECH == MECH_DEBERTA : MECH != MECH_T5;
+  static constexpr bool LIGHT = PART == 1;
+  static constexpr bool FAT = PART == 2;
+  static constexpr bool ROW = HAS_ROW && !LIGHT;
+  static constexpr bool COL = HAS_COL && !LIGHT;
   static constexpr bool TXL = MECH == MECH_TXL;
   static constexpr bool CLIP = MECH == MECH_SHAW || MECH == MECH_DEBERTA;
   static constexpr bool DIAG = DIR == 0 && (MECH == MECH_T5 || MECH == MECH_TXL);
@@ -64,9 +72,9 @@ __device__ __forceinline__ Op<1> op_from_lds_perm(const uint16_t* base, int e) {
 }
 
 // ----------------------------------------------------------------------------- kernel
-template <int MECH, int DIR>
+template <int MECH, int DIR, int PART>
 __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
-  using V = BV<MECH, DIR>;
+  using V = BV<MECH, DIR, PART>;
   typedef uint16_t T;
   constexpr int NP = 1;
   __shared__ __attribute__((aligned(16))) uint16_t ys[BOTH * TSTR];     // K (dir 0) / Q (dir 1)
@@ -76,7 +84,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   __shared__ __attribute__((aligned(16))) uint16_t ebuf[V::EBUF ? WIN * ESTR16 : 8];
   __shared__ __attribute__((aligned(16))) uint16_t xs[V::ROW ? BLANE * TSTR : 8];   // lane rows X
   __shared__ __attribute__((aligned(16))) float vec_s[(MECH == MECH_T5 || MECH == MECH_TXL) ? WIN : 4];  // T5 LUT / T-XL v.r
-  constexpr bool OVEC = (MECH == MECH_TXL && DIR == 0) || (V::CLIP && V::COL);
+  constexpr bool OVEC = (MECH == MECH_TXL && DIR == 0) || (V::CLIP && V::HAS_COL);
   __shared__ __attribute__((aligned(16))) float ovec_s[OVEC ? 2 * BOTH : 4];  // per-other-row constants
   __shared__ __attribute__((aligned(16))) float lsd_s[2 * BOTH];   // dir 1: LSE*log2e, D per query
   __shared__ __attribute__((aligned(16))) float ring[V::DIAG ? 256 : 4];
@@ -134,7 +142,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if (!(lse2 > kNegInf)) lse2 = __builtin_inff();   // empty row: P = 0
   }
   float rcA = 0.f, rcB = 0.f;
-  if constexpr (V::CLIP && V::ROW) {
+  if constexpr (V::CLIP && V::HAS_ROW) {
     if (my_a < L) {
       rcA = rc_g[((int64_t)bh * L + my_a) * 2 + 0];
       rcB = rc_g[((int64_t)bh * L + my_a) * 2 + 1];
@@ -154,8 +162,27 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if (sh.wr >= 0) b_lo = max(0, A0 - sh.wr);
     if (sh.wl >= 0) b_hi = min(L - 1, A0 + BLANE - 1 + sh.wl);
   }
-  const int bt0 = (b_lo / BOTH) * BOTH;
-  const int nsteps = (b_hi >= b_lo) ? (b_hi - bt0) / BOTH + 1 : 0;
+  const int bt_all = (b_lo / BOTH) * BOTH;
+  const int nsteps_all = (b_hi >= b_lo) ? (b_hi - bt_all) / BOTH + 1 : 0;
+  // workgroup tile of step base b0 needs relation products (some offset not clipped)
+  auto wg_gen = [&](int b0) {
+    if constexpr (V::CLIP) {
+      const int ta = V::TA(span), tb = V::TB(span);
+      const int wlo = A0 - b0 - 63, whi = A0 - b0 + 127;
+      const bool gr = V::HAS_ROW && !(whi <= ta || wlo >= tb);
+      const bool gc = V::HAS_COL && !(-wlo <= ta || -whi >= tb);
+      return gr || gc;
+    }
+    return true;
+  };
+  // the general steps form one contiguous range (the window slides monotonically)
+  int g_first = nsteps_all, g_last = -1;
+  if constexpr (PART != 0) {
+    for (int s2 = 0; s2 < nsteps_all; ++s2)
+      if (wg_gen(bt_all + s2 * BOTH)) { g_first = min(g_first, s2); g_last = s2; }
+  }
+  const int bt0 = V::FAT ? bt_all + g_first * BOTH : bt_all;
+  const int nsteps = V::FAT ? (g_last >= g_first ? g_last - g_first + 1 : 0) : nsteps_all;
   const int bt_last = bt0 + (nsteps - 1) * BOTH;
 
   // ---- partial layouts ----
@@ -225,6 +252,9 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 
   for (int step = 0; step < nsteps; ++step) {
     const int b0 = bt0 + step * BOTH;
+    if constexpr (V::LIGHT) {
+      if (step >= g_first && step <= g_last) continue;   // left to the general pass
+    }
     const int cwin = A0 - b0;             // workgroup window row t <-> lam = cwin - 63 + t
     const int lamlo = aw0 - b0 - 63, lamhi = aw0 + 31 - b0;
     // delta = i - j range of the wave tile
@@ -239,17 +269,13 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     bool wg_general = true;
     if constexpr (V::CLIP) {
       const int ta = V::TA(span), tb = V::TB(span);
-      const int wlo = cwin - 63, whi = cwin + 127;   // workgroup lam range
-      bool wg_row = true, wg_col = true;
-      if constexpr (V::ROW) {
+      if constexpr (V::HAS_ROW) {
         if (lamhi <= ta) rcls = 1; else if (lamlo >= tb) rcls = 2;
-        wg_row = !(whi <= ta || wlo >= tb);
       }
-      if constexpr (V::COL) {
+      if constexpr (V::HAS_COL) {
         if (-lamlo <= ta) ccls = 1; else if (-lamhi >= tb) ccls = 2;
-        wg_col = !(-wlo <= ta || -whi >= tb);
       }
-      wg_general = (V::ROW && wg_row) || (V::COL && wg_col);
+      wg_general = wg_gen(b0);
     }
     int t5cls = 0;
     if constexpr (MECH == MECH_T5) {
@@ -275,7 +301,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if constexpr (MECH == MECH_TXL && DIR == 0) {
       if (tid < BOTH) ovec_s[tid] = (b0 + tid < L) ? a.uk[(int64_t)bh * L + b0 + tid] : 0.f;
     }
-    if constexpr (V::CLIP && V::COL) {
+    if constexpr (V::CLIP && V::HAS_COL) {
       if (tid < 2 * BOTH) {
         const int yy = b0 + (tid >> 1);
         ovec_s[tid] = (yy < L) ? oc_g[((int64_t)bh * L + yy) * 2 + (tid & 1)] : 0.f;
@@ -315,11 +341,11 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     Op<NP> yop[2][4];
     if (!wave_none) other_dot_lane<NP>(sc, ys, xop, yop);
     float lconst = 0.f;   // per-lane additive term (y units)
-    if constexpr (V::COL) {
+    if constexpr (V::HAS_COL) {
       if (!wave_none) {
         if (V::CLIP && ccls != 0) {
           add_other_vec(sc, ovec_s + (ccls == 1 ? 0 : 1), 2);
-        } else if (wg_general) {
+        } else if (V::COL && wg_general) {
           col_skew_add<NP, MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 0, yop, vec_s, gs);
           col_skew_add<NP, MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 1, yop, vec_s, gs);
         }
@@ -339,10 +365,12 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         }
         __syncthreads();
       }
+    }
+    if constexpr (V::HAS_ROW) {
       if (!wave_none) {
         if (V::CLIP && rcls != 0) {
           lconst = (rcls == 1) ? rcA : rcB;
-        } else {
+        } else if constexpr (V::ROW) {
           f32x16 g[3];
           row_products<NP, MECH == MECH_TXL>(g, win, WROWS * w, xop, vec_s);
           row_skew_add(sc, g, gs);
@@ -428,6 +456,17 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     }
 
     // ---- offset-sharded row-side gradients ----
+    if constexpr (V::CLIP && V::HAS_ROW) {
+      if (!(V::EBUF && wg_general) && !wave_none) {
+        // the whole wave tile reads one end row
+        float tot = 0.f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tot += ds[b][r];
+        if (rcls == 1) cA += tot; else cB += tot;
+      }
+    }
     if constexpr (V::EBUF) {
       const bool use_e = wg_general;
       if (use_e) {
@@ -449,16 +488,6 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             e16[t * ESTR16 + xcol] = f2bf_bits(v);
           }
         __syncthreads();
-      } else if (!wave_none) {
-        // the whole wave tile reads one end row
-        float tot = 0.f;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) tot += ds[b][r];
-        if constexpr (V::CLIP) {
-          if (rcls == 1) cA += tot; else cB += tot;
-        }
       }
 
       if constexpr (V::ROW) {
@@ -595,11 +624,64 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     }
   }
 
+  // ---- light pass: hand the partial sums to the general pass ----
+  if constexpr (V::LIGHT) {
+    if constexpr (V::HAS_ROW) {
+      cA += xhalf(cA);
+      cB += xhalf(cB);
+    }
+    if (my_a < L) {
+      const int64_t rowoff = ((int64_t)bh * L + my_a) * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * kh;
+          f32x4 v4 = {gacc[db][4 * g], gacc[db][4 * g + 1], gacc[db][4 * g + 2], gacc[db][4 * g + 3]};
+          *(f32x4*)(a.xpart + rowoff + d) = v4;
+          if constexpr (DIR == 1) {
+            f32x4 w4 = {vacc[db][4 * g], vacc[db][4 * g + 1], vacc[db][4 * g + 2], vacc[db][4 * g + 3]};
+            *(f32x4*)(a.vpart + rowoff + d) = w4;
+          }
+        }
+      if (V::HAS_ROW && kh == 0) {
+        a.cab[((int64_t)bh * L + my_a) * 2 + 0] = cA;
+        a.cab[((int64_t)bh * L + my_a) * 2 + 1] = cB;
+      }
+    }
+    return;
+  }
+  if constexpr (V::FAT) {
+    if (my_a < L) {
+      const int64_t rowoff = ((int64_t)bh * L + my_a) * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * kh;
+          f32x4 v4 = *(const f32x4*)(a.xpart + rowoff + d);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gacc[db][4 * g + i] += v4[i];
+          if constexpr (DIR == 1) {
+            f32x4 w4 = *(const f32x4*)(a.vpart + rowoff + d);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vacc[db][4 * g + i] += w4[i];
+          }
+        }
+    }
+  }
+
   // ---- end rows (clipped offsets): table gradient and lane gradient ----
   if constexpr (V::CLIP && V::ROW) {
     // cA / cB hold this lane's sum over its half of the other rows
     cA += xhalf(cA);
     cB += xhalf(cB);
+    if constexpr (V::FAT) {
+      if (my_a < L) {
+        cA += a.cab[((int64_t)bh * L + my_a) * 2 + 0];
+        cB += a.cab[((int64_t)bh * L + my_a) * 2 + 1];
+      }
+    }
     if (kh == 0) {
       endc[WROWS * w + l32] = (my_a < L) ? cA : 0.f;
       endc[BLANE + WROWS * w + l32] = (my_a < L) ? cB : 0.f;
@@ -670,22 +752,38 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 
 // Variants whose LDS footprint leaves room for two workgroups per CU are compiled for two
 // waves per SIMD (at most 256 registers per lane); the others for one.
-template <int MECH, int DIR>
+template <int MECH, int DIR, int PART>
 __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
-  bwd_body<MECH, DIR>(a);
+  bwd_body<MECH, DIR, PART>(a);
 }
-template <int MECH, int DIR>
+template <int MECH, int DIR, int PART>
 __global__ __launch_bounds__(256, 1) void bwd_kernel_1wg(BwdArgs a) {
-  bwd_body<MECH, DIR>(a);
+  bwd_body<MECH, DIR, PART>(a);
 }
+// Passes that carry relation-gradient machinery for clipped mechanisms run in two parts.
 template <int MECH, int DIR>
+constexpr bool split_pass() {
+  return (MECH == MECH_SHAW && DIR == 0) || MECH == MECH_DEBERTA;
+}
+template <int MECH, int DIR, int PART>
 constexpr bool two_wg() {
-  return MECH == MECH_T5 || (MECH == MECH_SHAW && DIR == 1);
+  return MECH == MECH_T5 || (MECH == MECH_SHAW && DIR == 1) || PART == 1;
+}
+template <int MECH, int DIR, int PART>
+static void launch_part(const BwdArgs& a, dim3 grid, hipStream_t stream) {
+  if constexpr (two_wg<MECH, DIR, PART>())
+    hipLaunchKernelGGL((bwd_kernel<MECH, DIR, PART>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_kernel_1wg<MECH, DIR, PART>), grid, dim3(256), 0, stream, a);
 }
 template <int MECH, int DIR>
 static void launch_one(const BwdArgs& a, dim3 grid, hipStream_t stream) {
-  if constexpr (two_wg<MECH, DIR>()) hipLaunchKernelGGL((bwd_kernel<MECH, DIR>), grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((bwd_kernel_1wg<MECH, DIR>), grid, dim3(256), 0, stream, a);
+  if constexpr (split_pass<MECH, DIR>()) {
+    launch_part<MECH, DIR, 1>(a, grid, stream);
+    launch_part<MECH, DIR, 2>(a, grid, stream);
+  } else {
+    launch_part<MECH, DIR, 0>(a, grid, stream);
+  }
 }
 
 template <int DIR>

@@ -77,6 +77,9 @@ struct BwdArgs {
   float* part_kv;      // key-side per-owner small vectors (T-XL du)
   int64_t part_q_stride;  // floats per owner
   int64_t part_k_stride;
+  float* xpart;        // split passes: fp32 dX from the clipped steps, [B, H, L, 64]
+  float* vpart;        // split key-side pass: fp32 dV from the clipped steps
+  float* cab;          // split passes: end-row sums of dS per lane row, [B, H, L, 2]
 };
 
 // ----------------------------------------------------------------------------- launchers

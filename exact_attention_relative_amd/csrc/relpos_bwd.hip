@@ -83,7 +83,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   __shared__ __attribute__((aligned(16))) float gsb[V::GSB ? NWAVE * WROWS * GS2 : 4];
   __shared__ __attribute__((aligned(16))) uint16_t ebuf[V::EBUF ? WIN * ESTR16 : 8];
   __shared__ __attribute__((aligned(16))) uint16_t xs[V::ROW ? BLANE * TSTR : 8];   // lane rows X
-  __shared__ __attribute__((aligned(16))) float vec_s[(MECH == MECH_T5 || MECH == MECH_TXL) ? WIN : 4];  // T5 LUT / T-XL v.r
+  __shared__ __attribute__((aligned(16))) float vec_s[MECH == MECH_T5 ? WIN : 4];  // T5 LUT slice
   constexpr bool OVEC = (MECH == MECH_TXL && DIR == 0) || (V::CLIP && V::HAS_COL);
   __shared__ __attribute__((aligned(16))) float ovec_s[OVEC ? 2 * BOTH : 4];  // per-other-row constants
   __shared__ __attribute__((aligned(16))) float lsd_s[2 * BOTH];   // dir 1: LSE*log2e, D per query
@@ -250,6 +250,17 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   float* gs = gsb + (V::GSB ? w * WROWS * GS2 : 0);
   uint16_t* e16 = ebuf;
 
+  // the next step's streamed tiles are read into registers while the current step computes
+  auto step_base = [&](int st) { return bt0 + st * BOTH; };
+  auto step_skipped = [&](int st) { return V::LIGHT && st >= g_first && st <= g_last; };
+  int next = 0;
+  while (next < nsteps && step_skipped(next)) ++next;
+  TilePrefetch<T> py, py2;
+  if (next < nsteps) {
+    py.load(yg, step_base(next), L);
+    py2.load(y2g, step_base(next), L);
+  }
+
   for (int step = 0; step < nsteps; ++step) {
     const int b0 = bt0 + step * BOTH;
     if constexpr (V::LIGHT) {
@@ -289,8 +300,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 
     // ---- stage ----
     __syncthreads();
-    stage64<T, NP>(ys, yg, b0, L);
-    stage64<T, NP>(y2s, y2g, b0, L);
+    py.store(ys);
+    py2.store(y2s);
     if constexpr (MECH == MECH_T5) {
       for (int x = tid; x < WIN; x += 256) {
         const int lam = cwin - 63 + x;
@@ -320,6 +331,20 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         lsd_s[BOTH + tid] = dd;
       }
     }
+    // row side staged now when there is no column side
+    if constexpr (V::ROW && !V::COL) {
+      if (wg_general) {
+        stage_window<T, NP>(win, trow, [&](int x) {
+          return V::row_of(cwin - 63 + x, span, nrel, toff);
+        });
+        if constexpr (MECH == MECH_TXL) {
+          for (int x = tid; x < WIN; x += 256) {
+            const int r = V::row_of(cwin - 63 + x, span, nrel, toff);
+            *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+          }
+        }
+      }
+    }
     // column side first (its window is replaced by the row-side window afterwards)
     if constexpr (V::COL) {
       if (wg_general) {
@@ -330,10 +355,17 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         if constexpr (MECH == MECH_TXL) {
           for (int x = tid; x < WIN; x += 256) {
             const int r = V::col_of((b0 - A0 - (BLANE - 1)) + x, span, nrel, toff);
-            vec_s[x] = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+            *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
           }
         }
       }
+    }
+    // issue the next step's tile reads (after this step's staging reads have been consumed)
+    next = step + 1;
+    while (next < nsteps && step_skipped(next)) ++next;
+    if (next < nsteps) {
+      py.load(yg, step_base(next), L);
+      py2.load(y2g, step_base(next), L);
     }
     __syncthreads();
 
@@ -346,23 +378,17 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         if (V::CLIP && ccls != 0) {
           add_other_vec(sc, ovec_s + (ccls == 1 ? 0 : 1), 2);
         } else if (V::COL && wg_general) {
-          col_skew_add<NP, MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 0, yop, vec_s, gs);
-          col_skew_add<NP, MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 1, yop, vec_s, gs);
+          col_skew_add<NP, MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 0, ys, gs);
+          col_skew_add<NP, MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 1, ys, gs);
         }
       }
     }
-    if constexpr (V::ROW) {
+    if constexpr (V::ROW && V::COL) {
       if (wg_general) {
         __syncthreads();   // column-side window reads done
         stage_window<T, NP>(win, trow, [&](int x) {
           return V::row_of(cwin - 63 + x, span, nrel, toff);
         });
-        if constexpr (MECH == MECH_TXL) {
-          for (int x = tid; x < WIN; x += 256) {
-            const int r = V::row_of(cwin - 63 + x, span, nrel, toff);
-            vec_s[x] = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
-          }
-        }
         __syncthreads();
       }
     }
@@ -372,7 +398,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           lconst = (rcls == 1) ? rcA : rcB;
         } else if constexpr (V::ROW) {
           f32x16 g[3];
-          row_products<NP, MECH == MECH_TXL>(g, win, WROWS * w, xop, vec_s);
+          row_products<NP, MECH == MECH_TXL>(g, win, WROWS * w, xop);
           row_skew_add(sc, g, gs);
         }
       }
@@ -559,6 +585,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         for (int half = 0; half < 2; ++half) {
           const int t = lane + 64 * half;
           if (t < 96) {
+            // diagonal t runs through rows n with 0 <= n + 63 - t < 64
             const int n0 = max(0, t - 63), n1 = min(WROWS - 1, t);
             float sum = 0.f;
             for (int n = n0; n <= n1; ++n) sum += gs[n * GS2 + n + 63 - t];
@@ -767,7 +794,7 @@ constexpr bool split_pass() {
 }
 template <int MECH, int DIR, int PART>
 constexpr bool two_wg() {
-  return MECH == MECH_T5 || (MECH == MECH_SHAW && DIR == 1) || PART == 1;
+  return MECH == MECH_T5 || (DIR == 1 && (MECH == MECH_SHAW || MECH == MECH_TXL)) || PART == 1;
 }
 template <int MECH, int DIR, int PART>
 static void launch_part(const BwdArgs& a, dim3 grid, hipStream_t stream) {

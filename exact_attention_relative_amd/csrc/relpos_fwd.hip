@@ -15,13 +15,13 @@ template <typename T, int MECH>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   constexpr int NP = Elem<T>::NP;
   constexpr bool REL = (MECH != MECH_T5);
-  constexpr bool VEC = (MECH == MECH_T5 || MECH == MECH_TXL);
+  constexpr bool VEC = (MECH == MECH_T5);
   constexpr int KVEC = (MECH == MECH_DEBERTA) ? 2 * BOTH : (MECH == MECH_TXL ? BOTH : 1);
   __shared__ __attribute__((aligned(16))) uint16_t ks[NP * BOTH * TSTR];
   __shared__ __attribute__((aligned(16))) uint16_t vs[NP * BOTH * TSTR];
   __shared__ __attribute__((aligned(16))) uint16_t win[REL ? NP * WIN * TSTR : 8];
   __shared__ __attribute__((aligned(16))) float gsb[REL ? NWAVE * WROWS * GS2 : 4];
-  __shared__ __attribute__((aligned(16))) float vec_s[VEC ? WIN : 4];   // T5 LUT slice / T-XL v.r
+  __shared__ __attribute__((aligned(16))) float vec_s[VEC ? WIN : 4];   // T5 LUT slice
   __shared__ __attribute__((aligned(16))) float kvec_s[KVEC];           // T-XL u.k / DeBERTa k.Qr ends
 
   const AttnShape sh = a.sh;
@@ -82,6 +82,13 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 
   float* gs = gsb + (REL ? w * WROWS * GS2 : 0);
 
+  // K and V of the next tile are read into registers while the current tile computes
+  TilePrefetch<T> pk, pv;
+  if (jt0 <= j_hi) {
+    pk.load(kg, jt0, L);
+    pv.load(vg, jt0, L);
+  }
+
   for (int j0 = jt0; j0 <= j_hi; j0 += BOTH) {
     // ---- tile classification (offset-aware scheduling) ----
     // wave tile offsets delta = i - j in [dlo, dhi]
@@ -110,8 +117,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     }
 
     __syncthreads();  // previous tile's LDS reads are done
-    stage64<T, NP>(ks, kg, j0, L);
-    stage64<T, NP>(vs, vg, j0, L);
+    pk.store(ks);
+    pv.store(vs);
     if constexpr (MECH == MECH_T5) {
       for (int x = tid; x < WIN; x += 256) {
         const int d = wg_dlo + x;   // window row x <-> delta = i0 - j0 - 63 + x
@@ -127,7 +134,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
       if constexpr (MECH == MECH_TXL) {
         for (int x = tid; x < WIN; x += 256) {
           const int r = row_side_row(MECH, wg_dlo + x, span, nrel, toff);
-          vec_s[x] = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+          *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
         }
       }
     }
@@ -139,6 +146,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
         const int jj = j0 + (tid >> 1);
         kvec_s[tid] = (jj < L) ? a.keyc[((int64_t)bh * L + jj) * 2 + (tid & 1)] : 0.f;
       }
+    }
+    if (j0 + BOTH <= j_hi) {
+      pk.load(kg, j0 + BOTH, L);
+      pv.load(vg, j0 + BOTH, L);
     }
     __syncthreads();
 
@@ -163,14 +174,14 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
         else if (cls == 1) rowconst = rcB;   // j - i <= -k: row 0
         else {
           f32x16 g[3];
-          row_products<NP, false>(g, win, WROWS * w, qop, nullptr);
+          row_products<NP, false>(g, win, WROWS * w, qop);
           row_skew_add(sc, g, gs);
         }
       }
     } else if constexpr (MECH == MECH_TXL) {
       if (!wave_none) {
         f32x16 g[3];
-        row_products<NP, true>(g, win, WROWS * w, qop, vec_s);
+        row_products<NP, true>(g, win, WROWS * w, qop);
         row_skew_add(sc, g, gs);
         add_other_vec(sc, kvec_s, 1);
       }
@@ -180,7 +191,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
         else if (cls == 1) { rowconst = rcA; add_other_vec(sc, kvec_s + 1, 2); }   // delta <= -k
         else {
           f32x16 g[3];
-          row_products<NP, false>(g, win, WROWS * w, qop, nullptr);
+          row_products<NP, false>(g, win, WROWS * w, qop);
           row_skew_add(sc, g, gs);
         }
       }
@@ -195,7 +206,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
         if (!wave_none && cls == 0) {
 #pragma unroll
           for (int ob = 0; ob < 2; ++ob)
-            col_skew_add<NP, false>(sc, win, (BLANE - WROWS) - WROWS * w, ob, kop, nullptr, gs);
+            col_skew_add<NP, false>(sc, win, (BLANE - WROWS) - WROWS * w, ob, ks, gs);
         }
       }
     }

@@ -26,6 +26,15 @@ constexpr int TSTR = 72;             // LDS row stride (elements) of 64-wide bf1
 constexpr int WIN = 192;             // window rows (BLANE + BOTH - 1 = 191, padded)
 constexpr int GS2 = 68;              // skew buffer row stride (floats): 64 offsets + pad
 
+// A per-window-row fp32 value (T-XL v.r) kept in the 16-byte padding of the window's rows:
+// window rows 4 q .. 4 q + 3 store theirs in the padding of row q.
+__device__ __forceinline__ float* win_vec(uint16_t* win, int x) {
+  return (float*)(win + (x >> 2) * TSTR + kHeadDim) + (x & 3);
+}
+__device__ __forceinline__ f32x4 win_vec4(const uint16_t* win, int x) {   // x % 4 == 0
+  return *(const f32x4*)(win + (x >> 2) * TSTR + kHeadDim);
+}
+
 // ---------------------------------------------------------------------------------------
 // Staging (all 256 threads).  Tiles hold NP bf16 planes of [rows][TSTR].
 // ---------------------------------------------------------------------------------------
@@ -45,6 +54,56 @@ __device__ __forceinline__ void stage64(uint16_t* tile, const T* base, int row0,
     lds_zero8<NP>(tile, plane, r * TSTR + c + 8);
   }
 }
+
+// Register prefetch of a 64-row tile: this thread's 16 elements (row t / 4, columns
+// 16 (t % 4) ..).  load() issues the global reads early; store() writes them to LDS later.
+template <typename T>
+struct TilePrefetch {
+  static constexpr int NCH = sizeof(T) == 2 ? 2 : 4;   // 16-byte chunks per thread
+  u32x4 v[NCH];
+  __device__ __forceinline__ void load(const T* base, int row0, int nvalid) {
+    const int t = threadIdx.x;
+    const int r = t >> 2, c = (t & 3) * 16;
+    if (row0 + r < nvalid) {
+      const u32x4* g = (const u32x4*)(base + (int64_t)(row0 + r) * kHeadDim + c);
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) v[i] = g[i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* tile) const {
+    const int t = threadIdx.x;
+    const int e = (t >> 2) * TSTR + (t & 3) * 16;
+    if constexpr (NCH == 2) {
+      *(u32x4*)(tile + e) = v[0];
+      *(u32x4*)(tile + e + 8) = v[1];
+    } else {
+      // fp32: split into (hi, lo) bf16 planes
+      const int plane = BOTH * TSTR;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 h, l;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // elements are copied out by value first: a bit cast of a vector-element lvalue
+          // reads the vector's first element whatever the index
+          const u32x4 ch = v[2 * half + i / 2];
+          const uint32_t u0 = ch[2 * (i % 2)], u1 = ch[2 * (i % 2) + 1];
+          const float x0 = __uint_as_float(u0), x1 = __uint_as_float(u1);
+          uint16_t h0, l0, h1, l1;
+          split_bf16(x0, h0, l0);
+          split_bf16(x1, h1, l1);
+          h[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          l[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        *(u32x4*)(tile + e + 8 * half) = h;
+        *(u32x4*)(tile + plane + e + 8 * half) = l;
+      }
+    }
+  }
+};
 
 // WIN window rows; window row x reads table row rowfn(x) (< 0 = zero row).
 template <typename T, int NP, typename F>
@@ -103,10 +162,11 @@ __device__ __forceinline__ void put_block(float* gs, const f32x16& g, int bb, in
   }
 }
 
-// Row side, all three 32-offset blocks of products in registers (optionally + vec[w0 + t]).
+// Row side, all three 32-offset blocks of products in registers (optionally + the per-row
+// value kept in the window's padding, win_vec).
 template <int NP, bool ADDVEC>
 __device__ __forceinline__ void row_products(f32x16 g[3], const uint16_t* win, int w0,
-                                             const Op<NP> xop[4], const float* vec) {
+                                             const Op<NP> xop[4]) {
   const int lane = __lane_id();
   const int l32 = lane & 31, kh = lane >> 5;
 #pragma unroll
@@ -120,7 +180,7 @@ __device__ __forceinline__ void row_products(f32x16 g[3], const uint16_t* win, i
     if constexpr (ADDVEC) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 add = *(const f32x4*)(vec + w0 + 32 * bb + 8 * q4 + 4 * kh);
+        f32x4 add = win_vec4(win, w0 + 32 * bb + 8 * q4 + 4 * kh);
 #pragma unroll
         for (int i = 0; i < 4; ++i) g[bb][4 * q4 + i] += add[i];
       }
@@ -154,9 +214,10 @@ __device__ __forceinline__ void row_skew_add(f32x16 s[2], const f32x16 g[3], flo
 
 // Column side for other block ob: products Win[w0 + t'] . Y[32 ob + n] for t' in
 // [32 ob, 32 ob + 64), then s[ob][r] += H[y - 32 ob][y - n + 31].
+// The other-side operands are re-read from the streamed tile (fewer live registers).
 template <int NP, bool ADDVEC>
 __device__ __forceinline__ void col_skew_add(f32x16 s[2], const uint16_t* win, int w0, int ob,
-                                             const Op<NP> yop[2][4], const float* vec, float* gs) {
+                                             const uint16_t* ytile, float* gs) {
   const int lane = __lane_id();
   const int l32 = lane & 31, kh = lane >> 5;
   f32x16 h[2];
@@ -167,12 +228,13 @@ __device__ __forceinline__ void col_skew_add(f32x16 s[2], const uint16_t* win, i
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
-      mma<NP>(h[i], aop, yop[ob][c]);
+      Op<NP> yop = op_from_lds<NP>(ytile, BOTH * TSTR, (32 * ob + l32) * TSTR + 16 * c + 8 * kh);
+      mma<NP>(h[i], aop, yop);
     }
     if constexpr (ADDVEC) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 add = *(const f32x4*)(vec + w0 + 32 * bb + 8 * q4 + 4 * kh);
+        f32x4 add = win_vec4(win, w0 + 32 * bb + 8 * q4 + 4 * kh);
 #pragma unroll
         for (int j = 0; j < 4; ++j) h[i][4 * q4 + j] += add[j];
       }

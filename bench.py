@@ -8,13 +8,24 @@ mechanism, N = attended pairs, F_rel = 2 d x distinct (row, table-row) relation 
 T5, N for T-XL).  Inputs are resident in HBM before the timed region.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Profiling helpers (rocprofv3 runs and their committed summaries under profiles/):
+    python bench.py --only txl --copy-calibration-mib 1024 ...   (run under rocprofv3 --pmc)
+    python bench.py --summarize-pmc FETCH.csv WRITE.csv --copy-mib 1024 --out profiles/X.md --cmd "..."
+    python bench.py --summarize-stats kernel_stats.csv --out profiles/X.md --cmd "..."
+The roofline's `traffic` is read from profiles/hbm_traffic_*.md, and only while the kernel
+sources hash to the value recorded there (else null: the counters predate the kernel).
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -27,6 +38,9 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
 MECH_ORDER = ("t5", "shaw", "deberta", "txl")
+MECH_ID = {"t5": 0, "shaw": 1, "txl": 2, "deberta": 3}   # relpos_mech values
+CSRC = os.path.join(ROOT, "exact_attention_relative_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
 CFG_NAME = {"t5": "long_t5_L8192", "shaw": "long_shaw_L8192", "deberta": "long_deberta_L8192",
             "txl": "long_txl_L8192"}
 
@@ -75,6 +89,118 @@ def pass_flops(mech, B, H, L, d, wl, wr, span):
     return {"fwd": 4 * n * d + frel, "bwd": 10 * n * d + 3 * frel,
             # split of the backward between its two kernels (accounting convention)
             "bwd_dq": 2 * n * d + 2 * frel, "bwd_dkdv": 8 * n * d + frel, "pairs": n}
+
+
+# ------------------------------------------------------------------ profile summaries
+def kernel_source_sha():
+    """Hash of every kernel source file: counters taken on other sources are stale."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+_KNAME = re.compile(r"(fwd|bwd)_kernel(?:_1wg)?<([^>]*)>")
+
+
+def pass_of_kernel(name):
+    """(mechanism, pass) of a library kernel name, or None for helpers (prep, aggregation)."""
+    m = _KNAME.search(name)
+    if not m:
+        return None
+    args = [a.strip() for a in m.group(2).split(",")]
+    inv = {v: k for k, v in MECH_ID.items()}
+    if m.group(1) == "fwd":
+        return inv[int(args[-1])], "fwd"
+    return inv[int(args[0])], ("bwd_dq" if int(args[1]) == 0 else "bwd_dkdv")
+
+
+def _pmc_rows(path):
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_pmc(fetch_csv, write_csv, copy_mib, out, cmd):
+    """HBM bytes per pass launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each divided
+    by the factor the same counter reads for a plain copy of copy_mib MiB."""
+    known_kib = copy_mib * 1024.0
+    res = {}
+    for ctr, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = [r for r in _pmc_rows(path) if r["Counter_Name"] == ctr]
+        copies = [float(r["Counter_Value"]) for r in rows if "copy" in r["Kernel_Name"].lower()]
+        factor = max(copies) / known_kib
+        per = {}
+        for r in rows:
+            key = pass_of_kernel(r["Kernel_Name"])
+            if key is None:
+                continue
+            name = r["Kernel_Name"].replace("relpos::", "")
+            per.setdefault(key, {}).setdefault(name, []).append(float(r["Counter_Value"]))
+        res[ctr] = (factor, per)
+    f_fetch, per_fetch = res["FETCH_SIZE"]
+    f_write, per_write = res["WRITE_SIZE"]
+    sha = kernel_source_sha()
+    lines = ["# HBM traffic per launch from rocprofv3 counters (long-context workload, L=8192)", "",
+             "Commands (run from the repository root on one MI355X; one counter per run):", "",
+             "```", cmd, "```", "",
+             f"Copy calibration: a plain {copy_mib} MiB device copy reads FETCH_SIZE = "
+             f"{f_fetch:.4f} x its bytes and WRITE_SIZE = {f_write:.4f} x its bytes; the kernel "
+             "counters below are divided by these factors.", "",
+             "| pass | kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | "
+             "calibrated MB/dispatch |", "|---|---|---:|---:|---:|---:|"]
+    records = []
+    for key in sorted(per_fetch):
+        total = 0.0
+        for name, vals in sorted(per_fetch[key].items()):
+            fv = float(np.mean(vals))
+            wv = float(np.mean(per_write.get(key, {}).get(name, [0.0])))
+            b = (fv / f_fetch + wv / f_write) * 1024.0
+            total += b
+            lines.append(f"| {key[0]} {key[1]} | `{name[:70]}` | {len(vals)} | {fv:.1f} | {wv:.1f} | "
+                         f"{b / 1e6:.1f} |")
+        records.append({"mech": key[0], "pass": key[1], "source_sha": sha,
+                        "bytes_per_launch": total})
+    lines += ["", f"Kernel sources hash: `{sha}`.", ""]
+    for r in records:
+        lines.append("traffic-record: " + json.dumps(r))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_stats(stats_csv, out, cmd, title):
+    rows = _pmc_rows(stats_csv)
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "",
+             "```", cmd, "```", "",
+             "| kernel | pass | calls | avg (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---|---:|---:|---:|---:|---:|"]
+    for r in rows:
+        name = r["Name"].replace("relpos::", "").replace("|", "/")
+        key = pass_of_kernel(r["Name"])
+        tag = f"{key[0]} {key[1]}" if key else "helper"
+        if len(name) > 80:
+            name = name[:80] + "..."
+        lines.append(f"| `{name}` | {tag} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['Percentage']):.2f}% |")
+    lines += ["", f"Kernel sources hash: `{kernel_source_sha()}`."]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def recorded_traffic(mech, pass_name):
+    """Calibrated HBM bytes per launch of (mech, pass), if counters exist for these sources."""
+    sha = kernel_source_sha()
+    for path in sorted(glob.glob(os.path.join(PROFILES, "hbm_traffic_*.md"))):
+        with open(path) as f:
+            for line in f:
+                if line.startswith("traffic-record: "):
+                    r = json.loads(line[len("traffic-record: "):])
+                    if r["mech"] == mech and r["pass"] == pass_name and r["source_sha"] == sha:
+                        return r["bytes_per_launch"], os.path.relpath(path, ROOT)
+    return None, None
 
 
 # ------------------------------------------------------------------ GPU side
@@ -171,7 +297,23 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated mechanisms (profiling runs; the value then covers only them)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one plain device copy of this size first (counter calibration)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV")
+    ap.add_argument("--copy-mib", type=int, default=1024)
+    ap.add_argument("--out")
+    ap.add_argument("--cmd", default="")
+    ap.add_argument("--title", default="rocprofv3 kernel statistics")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.copy_mib, args.out, args.cmd)
+        return
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats, args.out, args.cmd, args.title)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(the workload shards over (batch, head) with no exchange except a table-gradient "
@@ -182,9 +324,19 @@ def main():
     from exact_attention_relative_amd import (RELPOS_PROF_BWD_DKDV, RELPOS_PROF_BWD_DQ,
                                               RELPOS_PROF_FWD)
     torch.cuda.init()
+    if args.copy_calibration_mib > 0:
+        n = args.copy_calibration_mib * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+    order = MECH_ORDER if args.only is None else tuple(x for x in args.only.split(",") if x)
     mechs = []
     per_mech = {}
-    for mech in MECH_ORDER:
+    for mech in order:
         torch.cuda.synchronize()
         base = torch.cuda.memory_allocated()
         torch.cuda.reset_peak_memory_stats()
@@ -248,10 +400,12 @@ def main():
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     dom_flops = dm["flops"][dom_kernel]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    traffic, traffic_src = recorded_traffic(dom_mech, dom_kernel)
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "kernel": f"{dom_kernel} pass kernel, {dom_mech}", "avg_ms": dom_ms,
-                "flops_per_launch": dom_flops}
+                "flops_per_launch": dom_flops, "traffic_source": traffic_src,
+                "kernel_source_sha": kernel_source_sha()}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -270,7 +424,8 @@ def main():
         "config": {"workload": "long-context relative-position attention: B=4 H=8 L=8192 d=64, "
                                "bidirectional; T5 32 buckets max_distance 1024, Shaw k=256, "
                                "DeBERTa k=512, T-XL full span; fwd+bwd of all four per step",
-                   "global_batch": 4, "seq_len": 8192, "heads": 8, "head_dim": 64},
+                   "global_batch": 4, "seq_len": 8192, "heads": 8, "head_dim": 64,
+                   "mechanisms": [m for m in order]},
         "per_mechanism": per_mech,
         "roofline": roofline,
         "cpu_baseline": cpu,

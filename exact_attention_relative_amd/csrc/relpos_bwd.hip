@@ -94,7 +94,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const AttnShape sh = a.sh;
   const int L = sh.L;
   const int nb = (L + BLANE - 1) / BLANE;
-  const int bid = blockIdx.x;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
   int blk = bid % nb;
   const int bh = bid / nb;
   if (sh.wr == 0) blk = (DIR == 0) ? nb - 1 - blk : blk;   // causal: longest first

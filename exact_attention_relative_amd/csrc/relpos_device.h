@@ -236,6 +236,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // ---------------------------------------------------------------------------------------
 // Index maps (bit-exact; offsets delta = i - j)
 // ---------------------------------------------------------------------------------------
+// Workgroups are dispatched round-robin over the chip's 8 XCDs (hardware id % 8), each with
+// its own L2.  Renumbering so that every XCD runs one contiguous range of logical workgroups
+// puts the blocks of one (batch, head) on the same L2, where they share K / V and table rows.
+constexpr int kNumXcd = 8;
+__device__ __forceinline__ int xcd_remap(int hw_id, int nwg) {
+  const int xcd = hw_id % kNumXcd, slot = hw_id / kNumXcd;
+  const int per = nwg / kNumXcd, rem = nwg % kNumXcd;
+  return xcd < rem ? xcd * (per + 1) + slot : rem * (per + 1) + (xcd - rem) * per + slot;
+}
+
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // T5 bucket of offset delta = i - j, from the integer thresholds the host computed.

@@ -27,7 +27,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   const AttnShape sh = a.sh;
   const int L = sh.L;
   const int nqb = (L + BLANE - 1) / BLANE;
-  const int bid = blockIdx.x;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
   int qb = bid % nqb;
   const int bh = bid / nqb;
   if (sh.wr == 0) qb = nqb - 1 - qb;   // causal: longest rows first

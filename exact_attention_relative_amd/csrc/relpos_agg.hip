@@ -57,9 +57,11 @@ __global__ void agg_diag_kernel(const float* __restrict__ pdiag, int B, int H, i
   diag[idx] = acc;
 }
 
-// T-XL dr[h][row][d] = s (sum_{b, block} part[own][(delta - base) * 64 + d] + v_h[d] diag_h[delta])
+// T-XL dr[h][row][d] = s (sum_{b, key block} part[own][(delta - base) * 64 + d] + v_h[d] diag_h[delta]);
+// the partials come from the dK/dV pass: owner (b, h, p) holds offset delta at row
+// delta + 128 p + 192.
 __global__ void agg_txl_dr_kernel(const float* __restrict__ prow, const float* __restrict__ diag,
-                                  const float* __restrict__ v, int B, int H, int L, int nb, int rev,
+                                  const float* __restrict__ v, int B, int H, int L, int nb,
                                   int nrt, int nrel, int off, float s, float* __restrict__ dr) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)H * nrel * kHeadDim) return;
@@ -76,10 +78,8 @@ __global__ void agg_txl_dr_kernel(const float* __restrict__ prow, const float* _
         for (int j = 0; j < 8; ++j) {
           const int p = p0 + j;
           if (p < nb) {
-            int64_t own;
-            int base;
-            owner_of(b, h, p, H, nb, rev != 0, L, own, base);
-            const int x = delta - base;
+            const int64_t own = ((int64_t)b * H + h) * nb + p;
+            const int x = delta + 128 * p + 192;
             if (x >= 0 && x < nrt) a8[j] += prow[(own * nrt + x) * kHeadDim + d];
           }
         }
@@ -171,12 +171,12 @@ hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int
 }
 
 hipError_t launch_agg_txl(const float* prow, const float* pkv, const float* diag, const void* r,
-                          const float* v, int B, int H, int L, int nb, bool rev, int nrt, int nrel,
+                          const float* v, int B, int H, int L, int nb, int nrt, int nrel,
                           int off, float s, bool fp32, float* dr, float* du, float* dv,
                           hipStream_t st) {
   const int64_t n = (int64_t)H * nrel * kHeadDim;
   hipLaunchKernelGGL(agg_txl_dr_kernel, dim3(nblk(n, 256)), dim3(256), 0, st, prow, diag, v, B, H,
-                     L, nb, rev ? 1 : 0, nrt, nrel, off, s, dr);
+                     L, nb, nrt, nrel, off, s, dr);
   if (fp32)
     hipLaunchKernelGGL((agg_txl_dv_kernel<float>), dim3(H * kHeadDim), dim3(256), 0, st, diag,
                        (const float*)r, L, nrel, off, s, dv);

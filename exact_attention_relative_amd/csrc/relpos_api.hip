@@ -440,7 +440,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
     case RELPOS_TXL:
       e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, p.nrt, diag, s);
       if (e == hipSuccess)
-        e = launch_agg_txl(a.part_q, a.part_kv, diag, rel_a, bias_b, p.B, p.H, p.L, p.nb, rev, p.nrt,
+        e = launch_agg_txl(a.part_q, a.part_kv, diag, rel_a, bias_b, p.B, p.H, p.L, p.nb, p.nrt,
                            p.nrel, p.txl_off, p.scale, p.fp32, drel_a, dbias_a, dbias_b, s);
       break;
   }

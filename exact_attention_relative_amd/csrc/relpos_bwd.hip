@@ -11,17 +11,24 @@
 // exactly once; a second pass (relpos_agg.hip) merges the partials in a fixed order.  No
 // atomics anywhere, so results are bitwise reproducible.
 //
-// Per step, dS is scattered into a workgroup buffer E[t][x] indexed by window offset t and
-// lane-side row x (the band t = x - y + 63 of the 64 streamed rows y).  Then
+// Shaw / DeBERTa: per step, dS is scattered into a workgroup buffer E[t][x] indexed by window
+// offset t and lane-side row x (the band t = x - y + 63 of the 64 streamed rows y).  Then
 //   dX_rel += Win^T E^T                     (per wave, its 96-offset window)
 //   dTable_window[t] += sum_x E[t][x] X[x]  (workgroup GEMM, 3 tiles per wave)
 // The window slides by 64 offsets per step, so a wave's three 32-offset accumulators shift by
 // two positions each step and the one that leaves the window is final: it is written out.
+// T-XL (full span, every tile general) splits the same work over the two passes so that each
+// fits two workgroups per CU: the dQ pass reads dX_rel's skewed operand straight from the
+// wave's fp32 dS buffer, and the dK/dV pass runs the table GEMM over its streamed query tile,
+//   dr_window[t] += sum_y E2[t][y] Q[y],   E2[t][y] = dS[y][x], t = y - x + 127,
+// with E2 in the space of the column-side skew buffer.
 #include "relpos_tile.h"
 
 namespace relpos {
 
 constexpr int ESTR16 = 136;   // bf16 E row stride (elements)
+constexpr int ESTRT = 200;    // bf16 E2T row stride (elements): 192 window offsets + pad
+static_assert(BOTH * ESTRT * 2 <= NWAVE * WROWS * GS2 * 4, "E2T fits the column-skew buffer");
 
 // PART 0: the whole sweep.  PART 1 (light): only the steps whose workgroup tile is clipped
 // (every offset beyond the span), without any relation-product machinery, writing fp32 partial
@@ -38,7 +45,9 @@ struct BV {
   static constexpr bool TXL = MECH == MECH_TXL;
   static constexpr bool CLIP = MECH == MECH_SHAW || MECH == MECH_DEBERTA;
   static constexpr bool DIAG = DIR == 0 && (MECH == MECH_T5 || MECH == MECH_TXL);
-  static constexpr bool EBUF = ROW;
+  static constexpr bool EBUF = ROW && !TXL;          // shared E buffer + lane-side table GEMM
+  static constexpr bool GSREL = TXL && DIR == 0;      // dX_rel from the wave's fp32 dS buffer
+  static constexpr bool TG1 = TXL && DIR == 1;        // table GEMM over the streamed rows
   static constexpr bool WINB = ROW || COL;
   static constexpr bool GSB = ROW || COL || DIAG;
 
@@ -71,6 +80,23 @@ __device__ __forceinline__ Op<1> op_from_lds_perm(const uint16_t* base, int e) {
   return o;
 }
 
+// Zero the slots of an op_from_lds_perm operand (row t, columns ybase + perm k) outside the
+// band y <= t <= y + 127.
+__device__ __forceinline__ void band_mask(Op<1>& o, int t, int ybase) {
+  const int kh = __lane_id() >> 5;
+  u32x4 v = __builtin_bit_cast(u32x4, o.p[0]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s0 = 2 * i, s1 = 2 * i + 1;
+    const int y0 = ybase + (s0 < 4 ? 4 * kh + s0 : 8 + 4 * kh + s0 - 4);
+    const int y1 = ybase + (s1 < 4 ? 4 * kh + s1 : 8 + 4 * kh + s1 - 4);
+    const uint32_t m = ((unsigned)(t - y0) <= 127u ? 0x0000FFFFu : 0u) |
+                       ((unsigned)(t - y1) <= 127u ? 0xFFFF0000u : 0u);
+    v[i] &= m;
+  }
+  o.p[0] = u4_to_bf8(v);
+}
+
 // ----------------------------------------------------------------------------- kernel
 template <int MECH, int DIR, int PART>
 __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
@@ -80,16 +106,17 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   __shared__ __attribute__((aligned(16))) uint16_t ys[BOTH * TSTR];     // K (dir 0) / Q (dir 1)
   __shared__ __attribute__((aligned(16))) uint16_t y2s[BOTH * TSTR];    // V (dir 0) / dO (dir 1)
   __shared__ __attribute__((aligned(16))) uint16_t win[V::WINB ? WIN * TSTR : 8];
-  __shared__ __attribute__((aligned(16))) float gsb[V::GSB ? NWAVE * WROWS * GS2 : 4];
+  // the skewed reads of the dX_rel operand reach up to 32 floats beyond a wave's buffer
+  constexpr int GSG = V::GSREL ? 32 : 0;
+  __shared__ __attribute__((aligned(16))) float gsb_raw[V::GSB ? NWAVE * WROWS * GS2 + 2 * GSG : 4];
   __shared__ __attribute__((aligned(16))) uint16_t ebuf[V::EBUF ? WIN * ESTR16 : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[V::ROW ? BLANE * TSTR : 8];   // lane rows X
+  __shared__ __attribute__((aligned(16))) uint16_t xs[V::EBUF ? BLANE * TSTR : 8];   // lane rows X
   __shared__ __attribute__((aligned(16))) float vec_s[MECH == MECH_T5 ? WIN : 4];  // T5 LUT slice
-  constexpr bool OVEC = (MECH == MECH_TXL && DIR == 0) || (V::CLIP && V::HAS_COL);
-  __shared__ __attribute__((aligned(16))) float ovec_s[OVEC ? 2 * BOTH : 4];  // per-other-row constants
-  __shared__ __attribute__((aligned(16))) float lsd_s[2 * BOTH];   // dir 1: LSE*log2e, D per query
-  __shared__ __attribute__((aligned(16))) float ring[V::DIAG ? 256 : 4];
-  __shared__ __attribute__((aligned(16))) float wsum[V::DIAG ? NWAVE * 96 : 4];
+  constexpr int NOVEC = (MECH == MECH_TXL && DIR == 0) ? BOTH : (V::CLIP && V::HAS_COL ? 2 * BOTH : 4);
+  __shared__ __attribute__((aligned(16))) float ovec_s[NOVEC];   // per-other-row constants
+  __shared__ __attribute__((aligned(16))) float lsd_s[DIR == 1 ? 2 * BOTH : 4];   // LSE*log2e, D per query
   __shared__ __attribute__((aligned(16))) float endc[V::CLIP && V::ROW ? 2 * BLANE : 4];
+  float* const gsb = gsb_raw + GSG;
 
   const AttnShape sh = a.sh;
   const int L = sh.L;
@@ -191,11 +218,14 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int nrt = L + 256;
   float* prow = nullptr;     // row-side table partial
   int prow_rows = 0;
-  if constexpr (V::ROW) {
-    if constexpr (MECH == MECH_TXL) prow_rows = nrt;
-    else prow_rows = (MECH == MECH_SHAW) ? 2 * span + 1 : 2 * span;
+  if constexpr (V::EBUF) {
+    prow_rows = (MECH == MECH_SHAW) ? 2 * span + 1 : 2 * span;
     prow = (DIR == 0 ? a.part_q : a.part_k) + owner * (DIR == 0 ? a.part_q_stride : a.part_k_stride);
   }
+  // T-XL r partial of the key-side pass: row b0 + 65 + t holds window row t of step base b0
+  // (offset delta = b0 - A0 - 127 + t), i.e. row delta + A0 + 192
+  float* ptg = nullptr;
+  if constexpr (V::TG1) ptg = a.part_q + owner * a.part_q_stride;
   float* pdiag = nullptr;
   if constexpr (V::DIAG) pdiag = a.part_qv + owner * (int64_t)nrt;
 
@@ -204,22 +234,23 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int cov_lo = A0 - bt_last - 63, cov_hi = A0 - bt0 + 128, cov_hi_diag = cov_hi - 1;
 
   // ---- zero what the sweep will not write ----
-  if constexpr (V::ROW) {
+  if constexpr (V::EBUF) {
     for (int64_t e = tid; e < (int64_t)prow_rows * kHeadDim; e += 256) {
       const int row = (int)(e / kHeadDim);
-      bool covered;
-      if constexpr (MECH == MECH_TXL) {
-        const int lam = lam_base + row;
-        covered = nsteps > 0 && lam >= cov_lo && lam <= cov_hi;
-      } else {
-        // end rows are written by the end-row pass; interior rows iff their offset is covered
-        int lam;
-        if constexpr (MECH == MECH_SHAW) lam = span - row;   // dir 0 only: row = clamp(-lam) + k
-        else lam = row - span;                               // row = clamp(lam + k)
-        const bool end = row == V::rowA(span) || row == V::rowB(span);
-        covered = end || (nsteps > 0 && lam >= cov_lo && lam <= cov_hi);
-      }
+      // end rows are written by the end-row pass; interior rows iff their offset is covered
+      int lam;
+      if constexpr (MECH == MECH_SHAW) lam = span - row;   // dir 0 only: row = clamp(-lam) + k
+      else lam = row - span;                               // row = clamp(lam + k)
+      const bool end = row == V::rowA(span) || row == V::rowB(span);
+      const bool covered = end || (nsteps > 0 && lam >= cov_lo && lam <= cov_hi);
       if (!covered) prow[e] = 0.f;
+    }
+  }
+  if constexpr (V::TG1) {
+    // rows written by the sweep: [bt0 + 65, bt_last + 256]
+    for (int64_t e = tid; e < (int64_t)nrt * kHeadDim; e += 256) {
+      const int row = (int)(e / kHeadDim);
+      if (!(nsteps > 0 && row >= bt0 + 65 && row <= bt_last + 256)) ptg[e] = 0.f;
     }
   }
   if constexpr (V::DIAG) {
@@ -227,14 +258,13 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       const int lam = lam_base + e;
       if (!(nsteps > 0 && lam >= cov_lo && lam <= cov_hi_diag)) pdiag[e] = 0.f;
     }
-    for (int e = tid; e < 256; e += 256) ring[e] = 0.f;
   }
   if constexpr (V::EBUF) {
     const int n16 = (WIN * ESTR16) / 8;
     u32x4 z = {0u, 0u, 0u, 0u};
     for (int e = tid; e < n16; e += 256) *(u32x4*)(ebuf + 8 * e) = z;
   }
-  if constexpr (V::ROW) {
+  if constexpr (V::EBUF) {
     stage64<T, NP>(xs, xg, A0, L);
     stage64<T, NP>(xs + BOTH * TSTR, xg, A0 + BOTH, L);
   }
@@ -245,6 +275,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   f32x16 racc[3] = {f32x16{}, f32x16{}, f32x16{}};   // row-side table window accumulators
   float cA = 0.f, cB = 0.f;                  // clipped-end sums of dS (lane row)
   float colsum = 0.f;                        // dir 1 T-XL: sum_i dS_ij
+  float dcarry = 0.f;                        // diagonal sum of offsets lam = tid (mod 256)
   const int gdb = w & 1, gp = w >> 1;        // GEMM tiles of this wave: d-block, t-block parity
 
   float* gs = gsb + (V::GSB ? w * WROWS * GS2 : 0);
@@ -256,7 +287,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   int next = 0;
   while (next < nsteps && step_skipped(next)) ++next;
   TilePrefetch<T> py, py2;
-  if (next < nsteps) {
+  if (!V::TG1 && next < nsteps) {
     py.load(yg, step_base(next), L);
     py2.load(y2g, step_base(next), L);
   }
@@ -300,8 +331,13 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 
     // ---- stage ----
     __syncthreads();
-    py.store(ys);
-    py2.store(y2s);
+    if constexpr (V::TG1) {   // registers are the limit here: stage directly
+      stage64<T, NP>(ys, yg, b0, L);
+      stage64<T, NP>(y2s, y2g, b0, L);
+    } else {
+      py.store(ys);
+      py2.store(y2s);
+    }
     if constexpr (MECH == MECH_T5) {
       for (int x = tid; x < WIN; x += 256) {
         const int lam = cwin - 63 + x;
@@ -363,7 +399,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     // issue the next step's tile reads (after this step's staging reads have been consumed)
     next = step + 1;
     while (next < nsteps && step_skipped(next)) ++next;
-    if (next < nsteps) {
+    if (!V::TG1 && next < nsteps) {
       py.load(yg, step_base(next), L);
       py2.load(y2g, step_base(next), L);
     }
@@ -422,6 +458,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     }
 
     f32x16 ds[2];
+    Op<NP> dso[4];   // dS as bf16 MFMA operands (16 other-side rows each)
     if (!wave_none) {
       // ---- P ----
 #pragma unroll
@@ -452,33 +489,34 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           const float dd = DIR == 0 ? dsum_l : lsd_s[BOTH + y];
           ds[b][r] = sc[b][r] * (dp[b][r] - dd);
         }
-      // ---- content gradients ----
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        Op<NP> dsop = op_from_acc<NP>(ds, cc);
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          Op<NP> yt = op_rows_tr<NP>(ys, BOTH * TSTR, TSTR, 16 * cc, 32 * db);
-          mma<NP>(gacc[db], yt, dsop);
-        }
-      }
-      if constexpr (DIR == 1) {
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {
-          Op<NP> pop = op_from_acc<NP>(sc, cc);
-#pragma unroll
-          for (int db = 0; db < 2; ++db) {
-            Op<NP> yt = op_rows_tr<NP>(y2s, BOTH * TSTR, TSTR, 16 * cc, 32 * db);
-            mma<NP>(vacc[db], yt, pop);
-          }
-        }
-      }
       if constexpr (MECH == MECH_TXL && DIR == 1) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) colsum += ds[b][r];
       }
+      // ---- content gradients (P and dS packed to bf16 once; the fp32 copies can die) ----
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) dso[cc] = op_from_acc<NP>(ds, cc);
+      if constexpr (DIR == 1) {
+        Op<NP> po[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) po[cc] = op_from_acc<NP>(sc, cc);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+            Op<NP> yt = op_rows_tr<NP>(y2s, BOTH * TSTR, TSTR, 16 * cc, 32 * db);
+            mma<NP>(vacc[db], yt, po[cc]);
+          }
+      }
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          Op<NP> yt = op_rows_tr<NP>(ys, BOTH * TSTR, TSTR, 16 * cc, 32 * db);
+          mma<NP>(gacc[db], yt, dso[cc]);
+        }
     }
 
     // ---- offset-sharded row-side gradients ----
@@ -526,13 +564,9 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             const int t = 32 * a2 + 8 * (r >> 2) + 4 * kh + (r & 3);
             const int lam = pc - 63 + t;
             const int d = 32 * gdb + l32;
-            if constexpr (MECH == MECH_TXL) {
-              prow[(int64_t)(lam - lam_base) * kHeadDim + d] = racc[2][r];
-            } else {
-              if (lam > V::TA(span) && lam < V::TB(span)) {
-                const int row = V::row_of(lam, span, nrel, toff);
-                prow[(int64_t)row * kHeadDim + d] = racc[2][r];
-              }
+            if (lam > V::TA(span) && lam < V::TB(span)) {
+              const int row = V::row_of(lam, span, nrel, toff);
+              prow[(int64_t)row * kHeadDim + d] = racc[2][r];
             }
           }
           racc[2] = racc[1];
@@ -566,9 +600,58 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 
     }
 
+    // ---- T-XL key side: dr window GEMM over the streamed query rows ----
+    if constexpr (V::TG1) {
+      // E2T[y][t] = dS[y][x] with t = y - x + 127, in the column-skew buffer's space: for one
+      // register, the 32 lanes of a half-wave write 32 consecutive t
+      uint16_t* e2t = (uint16_t*)gsb;
+      __syncthreads();   // every wave's column-skew reads are done
+      uint16_t* eb = e2t + (127 - (WROWS * w + l32) + 4 * kh) + 4 * kh * ESTRT;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        // operand slot i of dso[cc] is register 8 (cc % 2) + i of block cc / 2
+        const u32x4 wv = __builtin_bit_cast(u32x4, dso[cc].p[0]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * (cc & 1) + i;
+          const int yc = 32 * (cc >> 1) + 8 * (r >> 2) + (r & 3);   // y - 4 kh
+          const uint32_t word = wv[i >> 1];
+          const uint16_t bits = (uint16_t)((i & 1) ? (word >> 16) : (word & 0xFFFFu));
+          eb[yc * (ESTRT + 1)] = wave_none ? (uint16_t)0 : bits;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int ab = gp + 2 * i;
+        const int tlo = 32 * ab, thi = tlo + 31;
+#pragma unroll
+        for (int cq = 0; cq < 4; ++cq) {
+          const int ylo = 16 * cq, yhi = ylo + 15;
+          if (thi < ylo || tlo > yhi + 127) continue;   // no pair of this block and chunk
+          Op<NP> eop = op_rows_tr<NP>(e2t, 0, ESTRT, ylo, tlo);
+          if (!(tlo >= yhi && thi <= ylo + 127)) band_mask(eop, tlo + l32, ylo);
+          Op<NP> qop2 = op_rows_tr<NP>(ys, BOTH * TSTR, TSTR, ylo, 32 * gdb);
+          mma<NP>(racc[i], eop, qop2);
+        }
+      }
+      // block gp leaves the window with this step (the next window starts 64 offsets higher)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * gp + 8 * (r >> 2) + 4 * kh + (r & 3);
+        ptg[(int64_t)(b0 + 65 + t) * kHeadDim + 32 * gdb + l32] = racc[0][r];
+      }
+      racc[0] = racc[1];
+      racc[1] = racc[2];
+      racc[2] = f32x16{};
+    }
+
     // ---- per-offset fp32 sums of dS (T5 bias gradient; T-XL v term and v gradient) ----
     if constexpr (V::DIAG) {
-      float* wv = wsum + 96 * w;
+      // a wave's 96 sums live in the padding columns of its dS buffer (4 per row)
+      auto wsum_at = [&](int ww, int t) {
+        return gsb + ww * WROWS * GS2 + (t >> 2) * GS2 + kHeadDim + (t & 3);
+      };
       const bool single = (MECH == MECH_T5) && t5cls == 1;
       if (!wave_none && !single) {
         // dS[n][y] into the wave buffer, then sums along the diagonals t = n - y + 63
@@ -581,6 +664,31 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             *(f32x4*)(gs + l32 * GS2 + 32 * b + 8 * g4 + 4 * kh) = v4;
           }
         wave_lds_sync();
+        if constexpr (V::GSREL) {
+          // dX_rel^T[d][x] += sum_t Win[32 w + t][d] E[x][t] with E[x][t] = dS[x][x + 63 - t]
+          // for t in [x, x + 63] (else 0), read along the skewed diagonal of the buffer
+          const float* grow = gs + l32 * GS2 + l32 + 63 - 4 * kh;
+#pragma unroll
+          for (int cc = 0; cc < 6; ++cc) {
+            float e8[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int t0 = 16 * cc + 4 * kh + j, t1 = t0 + 8;
+              float v0 = grow[-(16 * cc + j)], v1 = grow[-(16 * cc + 8 + j)];
+              if (cc < 2) { v0 = t0 >= l32 ? v0 : 0.f; v1 = t1 >= l32 ? v1 : 0.f; }
+              if (cc > 3) { v0 = t0 <= l32 + 63 ? v0 : 0.f; v1 = t1 <= l32 + 63 ? v1 : 0.f; }
+              e8[j] = v0;
+              e8[4 + j] = v1;
+            }
+            Op<NP> eop = op_from_f32<NP>(e8);
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+              Op<NP> wt = op_rows_tr<NP>(win, WIN * TSTR, TSTR, WROWS * w + 16 * cc, 32 * db);
+              mma<NP>(gacc[db], wt, eop);
+            }
+          }
+        }
+        float sums[2] = {0.f, 0.f};
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
           const int t = lane + 64 * half;
@@ -589,9 +697,12 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             const int n0 = max(0, t - 63), n1 = min(WROWS - 1, t);
             float sum = 0.f;
             for (int n = n0; n <= n1; ++n) sum += gs[n * GS2 + n + 63 - t];
-            wv[t] = sum;
+            sums[half] = sum;
           }
         }
+        wave_lds_sync();   // this wave's reads of its buffer precede the writes to its padding
+        *wsum_at(w, lane) = sums[0];
+        if (lane < 32) *wsum_at(w, 64 + lane) = sums[1];
       } else {
         // single bucket: the wave total goes to one offset of the tile (window row 63)
         float tot = 0.f;
@@ -603,31 +714,34 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           tot += xhalf(tot);
           for (int m = 1; m < 32; m <<= 1) tot += __shfl_xor(tot, m);
         }
-        wv[lane] = (lane == 63) ? tot : 0.f;
-        if (lane < 32) wv[64 + lane] = 0.f;
+        wave_lds_sync();
+        *wsum_at(w, lane) = (lane == 63) ? tot : 0.f;
+        if (lane < 32) *wsum_at(w, 64 + lane) = 0.f;
       }
       __syncthreads();
-      if (tid < WIN - 1) {
+      // thread tid carries the offsets lam = tid (mod 256): at most one window row per step
+      const int t = (tid - (cwin - 63)) & 255;
+      if (t < WIN - 1) {
         float sum = 0.f;
 #pragma unroll
         for (int ww = 0; ww < NWAVE; ++ww) {
-          const int t = tid - 32 * ww;
-          if (t >= 0 && t < 96) sum += wsum[96 * ww + t];
+          const int tt = t - 32 * ww;
+          if (tt >= 0 && tt < 96) sum += *wsum_at(ww, tt);
         }
-        const int lam = cwin - 63 + tid;
-        float val = ring[lam & 255] + sum;
+        const int lam = cwin - 63 + t;
+        float val = dcarry + sum;
         // offsets above the next window are final
-        if (step == nsteps - 1 || tid >= 127) {
+        if (step == nsteps - 1 || t >= 127) {
           pdiag[lam - lam_base] = val;
           val = 0.f;
         }
-        ring[lam & 255] = val;
+        dcarry = val;
       }
     }
   }
 
   // ---- final flush of the window accumulators ----
-  if constexpr (V::ROW) {
+  if constexpr (V::EBUF) {
     if (nsteps > 0) {
       const int pc = A0 - bt_last;
 #pragma unroll
@@ -638,14 +752,24 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           const int t = 32 * ab + 8 * (r >> 2) + 4 * kh + (r & 3);
           const int lam = pc - 63 + t;
           const int d = 32 * gdb + l32;
-          if constexpr (MECH == MECH_TXL) {
-            prow[(int64_t)(lam - lam_base) * kHeadDim + d] = racc[i][r];
-          } else {
-            if (lam > V::TA(span) && lam < V::TB(span)) {
-              const int row = V::row_of(lam, span, nrel, toff);
-              prow[(int64_t)row * kHeadDim + d] = racc[i][r];
-            }
+          if (lam > V::TA(span) && lam < V::TB(span)) {
+            const int row = V::row_of(lam, span, nrel, toff);
+            prow[(int64_t)row * kHeadDim + d] = racc[i][r];
           }
+        }
+      }
+    }
+  }
+  if constexpr (V::TG1) {
+    // blocks gp + 2 and gp + 4 of the last window (shifted into racc[0], racc[1])
+    if (nsteps > 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ab = gp + 2 + 2 * i;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * ab + 8 * (r >> 2) + 4 * kh + (r & 3);
+          ptg[(int64_t)(bt_last + 65 + t) * kHeadDim + 32 * gdb + l32] = racc[i][r];
         }
       }
     }
@@ -794,7 +918,7 @@ constexpr bool split_pass() {
 }
 template <int MECH, int DIR, int PART>
 constexpr bool two_wg() {
-  return MECH == MECH_T5 || (DIR == 1 && (MECH == MECH_SHAW || MECH == MECH_TXL)) || PART == 1;
+  return MECH == MECH_T5 || MECH == MECH_TXL || (DIR == 1 && MECH == MECH_SHAW) || PART == 1;
 }
 template <int MECH, int DIR, int PART>
 static void launch_part(const BwdArgs& a, dim3 grid, hipStream_t stream) {

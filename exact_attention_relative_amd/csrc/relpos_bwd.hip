@@ -128,7 +128,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int h = bh % sh.H;
   const int A0 = blk * BLANE;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, l32 = lane & 31, kh = lane >> 5;
+  const int w = wave_index(), lane = tid & 63, l32 = lane & 31, kh = lane >> 5;
   const int aw0 = A0 + WROWS * w;
   const int my_a = aw0 + l32;
   const int span = sh.span, nrel = sh.nrel, toff = sh.txl_off;

@@ -236,6 +236,30 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // ---------------------------------------------------------------------------------------
 // Index maps (bit-exact; offsets delta = i - j)
 // ---------------------------------------------------------------------------------------
+// Index of the calling wave in its workgroup, as a wave-uniform (scalar) value: every
+// per-wave decision derived from it is then taken on the scalar unit.
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
+// max(a, b, c) as one v_maximum3_f32 (NaN-propagating; no canonicalisation of the inputs)
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
+// Sum of the 8 bf16 values of an operand register group, accumulated in fp32 on the dot unit.
+__device__ __forceinline__ float sum_bf16x8(const bf16x8& v, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t word = u[i];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, word), one, acc, false);
+  }
+  return acc;
+}
+
 // Workgroups are dispatched round-robin over the chip's 8 XCDs (hardware id % 8), each with
 // its own L2.  Renumbering so that every XCD runs one contiguous range of logical workgroups
 // puts the blocks of one (batch, head) on the same L2, where they share K / V and table rows.

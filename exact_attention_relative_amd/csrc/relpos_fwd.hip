@@ -35,7 +35,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   const int i0 = qb * BLANE;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = wave_index();
   const int lane = tid & 63;
   const int l32 = lane & 31, kh = lane >> 5;
   const int qw0 = i0 + WROWS * w;
@@ -231,8 +231,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[b][r], sc[b][r + 1]));
-    mx = fmaxf(mx, xhalf(mx));
+      for (int r = 0; r < 16; r += 2) mx = max3f(mx, sc[b][r], sc[b][r + 1]);
+    mx = max3f(mx, xhalf(mx), kNegInf);
     mx += rowconst;
     const bool raise = mx > m_run;
     if (__any(raise)) {
@@ -252,18 +252,25 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
       for (int r = 0; r < 16; ++r) {
         const float p = fast_exp2(fmaf(sc[b][r], c, bias));
         sc[b][r] = p;
-        psum += p;
+        if constexpr (NP == 2) psum += p;
       }
+    Op<NP> pop[4];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) pop[cc] = op_from_acc<NP>(sc, cc);
+    // bf16: the denominator sums exactly the rounded weights that multiply V
+    if constexpr (NP == 1) {
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) psum = sum_bf16x8(pop[cc].p[0], psum);
+    }
     l_run += psum;
 
     // ---- O^T += V^T P^T ----
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) {
-      Op<NP> pop = op_from_acc<NP>(sc, cc);
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         Op<NP> vop = op_rows_tr<NP>(vs, BOTH * TSTR, TSTR, 16 * cc, 32 * db);
-        mma<NP>(oacc[db], vop, pop);
+        mma<NP>(oacc[db], vop, pop[cc]);
       }
     }
   }

@@ -63,7 +63,8 @@ typedef enum { RELPOS_BF16 = 0, RELPOS_FP32 = 1 } relpos_dtype;
 enum {
   RELPOS_OK = 0,
   RELPOS_E_INVALID = -1,     /* bad enum, shape, NULL / misaligned pointer, span inconsistent */
-  RELPOS_E_UNSUPPORTED = -2, /* valid request outside what the kernels implement (head_dim != 64) */
+  RELPOS_E_UNSUPPORTED = -2, /* valid request outside what the kernels implement: head_dim != 64,
+                                 or a backward in fp32 (the fp32 forward is implemented) */
   RELPOS_E_WORKSPACE = -3,   /* workspace NULL or smaller than relpos_attn_workspace_size() */
   RELPOS_E_LAUNCH = -4       /* a kernel launch failed */
 };
@@ -97,7 +98,8 @@ int relpos_attn_fwd(const relpos_desc* desc, const void* q, const void* k, const
  * (T5: dbias_a = dbeta; Shaw: drel_a = dw; T-XL: drel_a = dr, dbias_a = du, dbias_b = dv;
  * DeBERTa: drel_a = dKr, drel_b = dQr).  Table gradients are reduced over every (batch, head)
  * that reads the table, in a fixed order, without atomics (offset-sharded partials followed
- * by a second aggregation pass). */
+ * by a second aggregation pass).  bf16 only: dtype RELPOS_FP32 returns RELPOS_E_UNSUPPORTED
+ * before any launch. */
 int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const void* v,
                     const void* o, const float* lse, const void* dout, const void* rel_a,
                     const void* rel_b, const float* bias_a, const float* bias_b, void* dq,

@@ -460,34 +460,43 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     f32x16 ds[2];
     Op<NP> dso[4];   // dS as bf16 MFMA operands (16 other-side rows each)
     if (!wave_none) {
-      // ---- P ----
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
-          float bias;
-          if (DIR == 0) bias = lconst * c - lse2;
-          else bias = lconst * c - lsd_s[y];
-          float p = fast_exp2(fmaf(sc[b][r], c, bias));
-          if (!wave_full) {
-            const int ii = DIR == 0 ? my_a : b0 + y;
-            const int jj = DIR == 0 ? b0 + y : my_a;
-            if (!(ii < L && jj < L && pair_allowed(ii, jj, sh.wl, sh.wr))) p = 0.f;
-          }
-          sc[b][r] = p;
-        }
-      // ---- dP, dS ----
+      // query-side pass: dP first, its MFMAs run while the exponentials below are computed
       Op<NP> y2op[2][4];
       f32x16 dp[2];
-      other_dot_lane<NP>(dp, y2s, x2op, y2op);
+      if constexpr (DIR == 0) other_dot_lane<NP>(dp, y2s, x2op, y2op);
+      // ---- P ----  (key-side pass: LSE of the streamed queries, 4 rows per read)
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
-          const float dd = DIR == 0 ? dsum_l : lsd_s[BOTH + y];
-          ds[b][r] = sc[b][r] * (dp[b][r] - dd);
+        for (int g = 0; g < 4; ++g) {
+          f32x4 l4 = {lse2, lse2, lse2, lse2};
+          if constexpr (DIR == 1) l4 = *(const f32x4*)(lsd_s + 32 * b + 8 * g + 4 * kh);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sc[b][4 * g + i] = fast_exp2(fmaf(sc[b][4 * g + i], c, lconst * c - l4[i]));
+        }
+      if (!wave_full) {
+        const int wlx = sh.wl < 0 ? L : sh.wl, wrx = sh.wr < 0 ? L : sh.wr;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
+            const int ii = DIR == 0 ? my_a : b0 + y;
+            const int jj = DIR == 0 ? b0 + y : my_a;
+            sc[b][r] = pair_ok(ii, jj, L, wlx, wrx) ? sc[b][r] : 0.f;
+          }
+      }
+      if constexpr (DIR == 1) other_dot_lane<NP>(dp, y2s, x2op, y2op);
+      // ---- dS ----
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 d4 = {dsum_l, dsum_l, dsum_l, dsum_l};
+          if constexpr (DIR == 1) d4 = *(const f32x4*)(lsd_s + BOTH + 32 * b + 8 * g + 4 * kh);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ds[b][4 * g + i] = sc[b][4 * g + i] * (dp[b][4 * g + i] - d4[i]);
         }
       if constexpr (MECH == MECH_TXL && DIR == 1) {
 #pragma unroll

@@ -302,5 +302,10 @@ __device__ __forceinline__ int p2c_row(int delta, int span) { return clampi(-del
 __device__ __forceinline__ bool pair_allowed(int i, int j, int wl, int wr) {
   return (wl < 0 || i - j <= wl) && (wr < 0 || j - i <= wr);
 }
+// The same test without branches, for per-element use: wlx / wrx are the window bounds with
+// "unbounded" (< 0) replaced by L, and rows / columns at or beyond L are excluded.
+__device__ __forceinline__ bool pair_ok(int i, int j, int L, int wlx, int wrx) {
+  return (i < L) & (j < L) & (i - j <= wlx) & (j - i <= wrx);
+}
 
 }  // namespace relpos

@@ -214,12 +214,13 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
 
     // ---- mask ----
     if (!wave_full) {
+      const int wlx = sh.wl < 0 ? L : sh.wl, wrx = sh.wr < 0 ? L : sh.wr;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int j = j0 + 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
-          if (!(j < L && pair_allowed(my_i, j, sh.wl, sh.wr))) sc[b][r] = kNegInf;
+          sc[b][r] = pair_ok(my_i, j, L, wlx, wrx) ? sc[b][r] : kNegInf;
         }
     }
 
@@ -311,11 +312,21 @@ template <typename T, int MECH>
 __global__ __launch_bounds__(256, 1) void fwd_kernel_1wg(FwdArgs a) {
   fwd_body<T, MECH>(a);
 }
+// T5 keeps only K, V and a LUT slice in LDS (19 KB): three workgroups per CU when the
+// registers fit 168 per lane.
+template <typename T, int MECH>
+__global__ __launch_bounds__(256, 3) void fwd_kernel_3wg(FwdArgs a) {
+  fwd_body<T, MECH>(a);
+}
 
 template <typename T, int MECH>
 static void launch_one(const FwdArgs& a, dim3 grid, hipStream_t stream) {
-  if constexpr (Elem<T>::NP == 1) hipLaunchKernelGGL((fwd_kernel<T, MECH>), grid, dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL((fwd_kernel_1wg<T, MECH>), grid, dim3(256), 0, stream, a);
+  if constexpr (Elem<T>::NP == 1 && MECH == MECH_T5)
+    hipLaunchKernelGGL((fwd_kernel_3wg<T, MECH>), grid, dim3(256), 0, stream, a);
+  else if constexpr (Elem<T>::NP == 1)
+    hipLaunchKernelGGL((fwd_kernel<T, MECH>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel_1wg<T, MECH>), grid, dim3(256), 0, stream, a);
 }
 
 template <typename T>

@@ -407,7 +407,11 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 
     f32x16 sc[2];
     Op<NP> yop[2][4];
-    if (!wave_none) other_dot_lane<NP>(sc, ys, xop, yop);
+    if (!wave_none) {
+      // T-XL query side: the scores start from u.k of each streamed key
+      if constexpr (MECH == MECH_TXL && DIR == 0) other_dot_lane<NP, true>(sc, ys, xop, yop, ovec_s);
+      else other_dot_lane<NP>(sc, ys, xop, yop);
+    }
     float lconst = 0.f;   // per-lane additive term (y units)
     if constexpr (V::HAS_COL) {
       if (!wave_none) {
@@ -452,8 +456,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     }
     if constexpr (MECH == MECH_TXL) {
       if (!wave_none) {
-        if (DIR == 0) add_other_vec(sc, ovec_s, 1);
-        else lconst = ukl;
+        if (DIR == 1) lconst = ukl;
       }
     }
 

@@ -156,7 +156,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     f32x16 sc[2];
     Op<NP> kop[2][4];
     if (!wave_none) {
-      other_dot_lane<NP>(sc, ks, qop, kop);
+      // T-XL: the scores start from u.k of each key
+      if constexpr (MECH == MECH_TXL) other_dot_lane<NP, true>(sc, ks, qop, kop, kvec_s);
+      else other_dot_lane<NP>(sc, ks, qop, kop);
     }
     float rowconst = 0.f;
     // ---- relative terms (row side) ----
@@ -183,7 +185,6 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
         f32x16 g[3];
         row_products<NP, true>(g, win, WROWS * w, qop);
         row_skew_add(sc, g, gs);
-        add_other_vec(sc, kvec_s, 1);
       }
     } else if constexpr (MECH == MECH_DEBERTA) {
       if (!wave_none) {

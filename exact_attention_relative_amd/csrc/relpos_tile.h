@@ -131,14 +131,25 @@ __device__ __forceinline__ void stage_window(uint16_t* win, const T* table, F ro
 // = row, k = d chunk c: 16 c + 8 (lane / 32) .. + 7).
 // ---------------------------------------------------------------------------------------
 // acc[b] = Y[32 b + m] . X[n]  (C[m = other row][n = lane row]); Y is a 64-row LDS tile.
-template <int NP>
+// With INIT the accumulator starts from vec[other row] (a per-other-row additive term) and
+// the MFMA adds the products to it.
+template <int NP, bool INIT = false>
 __device__ __forceinline__ void other_dot_lane(f32x16 acc[2], const uint16_t* ytile,
-                                               const Op<NP> xop[4], Op<NP> yop[2][4]) {
+                                               const Op<NP> xop[4], Op<NP> yop[2][4],
+                                               const float* vec = nullptr) {
   const int lane = __lane_id();
   const int l32 = lane & 31, kh = lane >> 5;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     acc[b] = f32x16{};
+    if constexpr (INIT) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v4 = *(const f32x4*)(vec + 32 * b + 8 * q4 + 4 * kh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[b][4 * q4 + i] = v4[i];
+      }
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       yop[b][c] = op_from_lds<NP>(ytile, BOTH * TSTR, (32 * b + l32) * TSTR + 16 * c + 8 * kh);
@@ -172,18 +183,18 @@ __device__ __forceinline__ void row_products(f32x16 g[3], const uint16_t* win, i
 #pragma unroll
   for (int bb = 0; bb < 3; ++bb) {
     g[bb] = f32x16{};
+    if constexpr (ADDVEC) {   // the MFMA accumulates on top of the per-row value
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v4 = win_vec4(win, w0 + 32 * bb + 8 * q4 + 4 * kh);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) g[bb][4 * q4 + i] = v4[i];
+      }
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
       mma<NP>(g[bb], aop, xop[c]);
-    }
-    if constexpr (ADDVEC) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 add = win_vec4(win, w0 + 32 * bb + 8 * q4 + 4 * kh);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) g[bb][4 * q4 + i] += add[i];
-      }
     }
   }
 }
@@ -225,19 +236,19 @@ __device__ __forceinline__ void col_skew_add(f32x16 s[2], const uint16_t* win, i
   for (int i = 0; i < 2; ++i) {
     const int bb = ob + i;
     h[i] = f32x16{};
+    if constexpr (ADDVEC) {   // the MFMA accumulates on top of the per-row value
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 v4 = win_vec4(win, w0 + 32 * bb + 8 * q4 + 4 * kh);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[i][4 * q4 + j] = v4[j];
+      }
+    }
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
       Op<NP> yop = op_from_lds<NP>(ytile, BOTH * TSTR, (32 * ob + l32) * TSTR + 16 * c + 8 * kh);
       mma<NP>(h[i], aop, yop);
-    }
-    if constexpr (ADDVEC) {
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        f32x4 add = win_vec4(win, w0 + 32 * bb + 8 * q4 + 4 * kh);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) h[i][4 * q4 + j] += add[j];
-      }
     }
   }
   wave_lds_sync();

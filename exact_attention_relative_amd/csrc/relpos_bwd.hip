@@ -648,10 +648,10 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         }
       }
       // block gp leaves the window with this step (the next window starts 64 offsets higher)
+      {
+        float* fb = ptg + (int64_t)(b0 + 65 + 32 * gp + 4 * kh) * kHeadDim + 32 * gdb + l32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * gp + 8 * (r >> 2) + 4 * kh + (r & 3);
-        ptg[(int64_t)(b0 + 65 + t) * kHeadDim + 32 * gdb + l32] = racc[0][r];
+        for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = racc[0][r];
       }
       racc[0] = racc[1];
       racc[1] = racc[2];
@@ -777,12 +777,10 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if (nsteps > 0) {
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const int ab = gp + 2 + 2 * i;
+        float* fb = ptg + (int64_t)(bt_last + 65 + 32 * (gp + 2 + 2 * i) + 4 * kh) * kHeadDim +
+                    32 * gdb + l32;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * ab + 8 * (r >> 2) + 4 * kh + (r & 3);
-          ptg[(int64_t)(bt_last + 65 + t) * kHeadDim + 32 * gdb + l32] = racc[i][r];
-        }
+        for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = racc[i][r];
       }
     }
   }

@@ -57,37 +57,49 @@ __global__ void agg_diag_kernel(const float* __restrict__ pdiag, int B, int H, i
   diag[idx] = acc;
 }
 
-// T-XL dr[h][row][d] = s (sum_{b, key block} part[own][(delta - base) * 64 + d] + v_h[d] diag_h[delta]);
-// the partials come from the dK/dV pass: owner (b, h, p) holds offset delta at row
-// delta + 128 p + 192.
-__global__ void agg_txl_dr_kernel(const float* __restrict__ prow, const float* __restrict__ diag,
-                                  const float* __restrict__ v, int B, int H, int L, int nb,
-                                  int nrt, int nrel, int off, float s, float* __restrict__ dr) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= (int64_t)H * nrel * kHeadDim) return;
-  const int d = (int)(idx % kHeadDim);
-  const int row = (int)((idx / kHeadDim) % nrel);
-  const int h = (int)(idx / ((int64_t)kHeadDim * nrel));
-  const int delta = row - off;
-  float acc = 0.f;
-  if (delta > -L && delta < L) {
-    float a8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int b = 0; b < B; ++b)
-      for (int p0 = 0; p0 < nb; p0 += 8) {
+// T-XL dr[h][row][d] = s (sum_{b, key block} part[own][delta + 128 p + 192][d] + v_h[d] diag_h[delta]).
+// The partials come from the dK/dV pass: owner (b, h, p) holds offset delta at row
+// delta + 128 p + 192.  One workgroup per (head, 64 consecutive offsets): for every owner the
+// 64 rows it holds for those offsets are one contiguous 16 KB block, read whole and added in
+// a fixed owner order.
+__global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict__ prow,
+                                                         const float* __restrict__ diag,
+                                                         const float* __restrict__ v, int B, int H,
+                                                         int L, int nb, int nrt, int nrel, int off,
+                                                         float s, float* __restrict__ dr) {
+  const int nch = (nrel + 63) / 64;
+  const int h = blockIdx.x / nch, row0 = 64 * (blockIdx.x % nch);
+  const int t = threadIdx.x;
+  const int delta0 = row0 - off;
+  f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
+  for (int b = 0; b < B; ++b)
+    for (int p = 0; p < nb; ++p) {
+      const int x0 = delta0 + 128 * p + 192;
+      if (x0 + 63 < 0 || x0 >= nrt) continue;   // no row of this owner in the block
+      const float* base = prow + (((int64_t)b * H + h) * nb + p) * (int64_t)nrt * kHeadDim;
+      f32x4 ld[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int p = p0 + j;
-          if (p < nb) {
-            const int64_t own = ((int64_t)b * H + h) * nb + p;
-            const int x = delta + 128 * p + 192;
-            if (x >= 0 && x < nrt) a8[j] += prow[(own * nrt + x) * kHeadDim + d];
-          }
-        }
+      for (int k = 0; k < 4; ++k) {
+        const int e = 4 * t + 1024 * k, x = x0 + (e >> 6);
+        ld[k] = (x >= 0 && x < nrt) ? *(const f32x4*)(base + (int64_t)x * kHeadDim + (e & 63))
+                                    : f32x4{};
       }
-    acc = ((a8[0] + a8[1]) + (a8[2] + a8[3])) + ((a8[4] + a8[5]) + (a8[6] + a8[7]));
-    acc = fmaf(v[(int64_t)h * kHeadDim + d], diag[(int64_t)h * (2 * L - 1) + delta + L - 1], acc);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] += ld[k];
+    }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int e = 4 * t + 1024 * k, row = row0 + (e >> 6), d = e & 63;
+    if (row >= nrel) continue;
+    const int delta = row - off;
+    f32x4 o = f32x4{};
+    if (delta > -L && delta < L) {
+      const float dg = diag[(int64_t)h * (2 * L - 1) + delta + L - 1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = fmaf(v[(int64_t)h * kHeadDim + d + i], dg, acc[k][i]) * s;
+    }
+    *(f32x4*)(dr + ((int64_t)h * nrel + row) * kHeadDim + d) = o;
   }
-  dr[idx] = acc * s;
 }
 
 // Fixed-order block reduction helper (256 threads).
@@ -174,8 +186,8 @@ hipError_t launch_agg_txl(const float* prow, const float* pkv, const float* diag
                           const float* v, int B, int H, int L, int nb, int nrt, int nrel,
                           int off, float s, bool fp32, float* dr, float* du, float* dv,
                           hipStream_t st) {
-  const int64_t n = (int64_t)H * nrel * kHeadDim;
-  hipLaunchKernelGGL(agg_txl_dr_kernel, dim3(nblk(n, 256)), dim3(256), 0, st, prow, diag, v, B, H,
+  const int nch = (nrel + 63) / 64;
+  hipLaunchKernelGGL(agg_txl_dr_kernel, dim3(H * nch), dim3(256), 0, st, prow, diag, v, B, H,
                      L, nb, nrt, nrel, off, s, dr);
   if (fp32)
     hipLaunchKernelGGL((agg_txl_dv_kernel<float>), dim3(H * kHeadDim), dim3(256), 0, st, diag,

@@ -103,7 +103,7 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-_KNAME = re.compile(r"(fwd|bwd)_kernel(?:_1wg)?<([^>]*)>")
+_KNAME = re.compile(r"(fwd|bwd)_kernel(?:_\dwg)?<([^>]*)>")
 
 
 def pass_of_kernel(name):

@@ -96,7 +96,7 @@ def kernel_source_sha():
     """Hash of every kernel source file: counters taken on other sources are stale."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h")):
+        if f.endswith((".hip", ".h")) and not f.startswith("relpos_probe"):
             h.update(f.encode())
             with open(os.path.join(CSRC, f), "rb") as fh:
                 h.update(fh.read())
@@ -190,6 +190,58 @@ def summarize_stats(stats_csv, out, cmd, title):
         f.write("\n".join(lines) + "\n")
 
 
+SQ_SET1 = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 "
+           "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_WAVE_CYCLES SQ_BUSY_CYCLES")
+SQ_SET2 = ("SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT "
+           "SQ_LDS_IDX_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_WAIT_ANY GRBM_GUI_ACTIVE")
+
+
+def summarize_sq(csv1, csv2, out, cmd, steps_per_wave=128):
+    """Per-kernel instruction mix (per wave and 64-row step) and pipe utilisation from the two
+    SQ counter runs.  GRBM_GUI_ACTIVE is summed over the 8 XCDs; MFMA-busy cycles are divided
+    by (GUI / 8) x 1024 SIMDs."""
+    data, cnt = {}, {}
+    for path in (csv1, csv2):
+        for r in _pmc_rows(path):
+            key = pass_of_kernel(r["Kernel_Name"])
+            if key is None:
+                continue
+            name = r["Kernel_Name"].replace("relpos::", "")
+            d = data.setdefault((key, name), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            cnt[(key, name, r["Counter_Name"])] = cnt.get((key, name, r["Counter_Name"]), 0) + 1
+    lines = ["# SQ counters per kernel (long-context workload, L=8192)", "",
+             "Commands (run from the repository root on one MI355X; two counter sets, one run each):",
+             "", "```", cmd, "```", "",
+             "Per wave and 64-row step (`/ step`: SQ_INSTS_* / SQ_WAVES / 128 steps; general passes "
+             "sweep only part of the steps, so theirs read low). `MFMA busy` = "
+             "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs). `VALU active` = "
+             "SQ_ACTIVE_INST_VALU x 4 on the same base. `wait` = SQ_WAIT_ANY / SQ_WAVE_CYCLES. "
+             "`bank conflicts` = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
+             "| pass | kernel | VALU / step | SALU / step | LDS / step | exp / step | MFMA ops / step | "
+             "MFMA busy | VALU active | wait | bank conflicts |",
+             "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for (key, name), d in sorted(data.items()):
+        g = lambda c: d.get(c, 0.0) / max(cnt.get((key, name, c), 0), 1)
+        waves = g("SQ_WAVES")
+        if waves <= 0:
+            continue
+        ws = waves * steps_per_wave
+        simd = g("GRBM_GUI_ACTIVE") / 8 * 1024
+        lines.append(
+            f"| {key[0]} {key[1]} | `{name[:48]}` | {g('SQ_INSTS_VALU') / ws:.0f} | "
+            f"{g('SQ_INSTS_SALU') / ws:.0f} | {g('SQ_INSTS_LDS') / ws:.0f} | "
+            f"{g('SQ_INSTS_VALU_TRANS_F32') / ws:.1f} | {g('SQ_INSTS_VALU_MFMA_MOPS_BF16') / ws / 64:.1f} | "
+            f"{g('SQ_VALU_MFMA_BUSY_CYCLES') / max(simd, 1):.3f} | "
+            f"{4 * g('SQ_ACTIVE_INST_VALU') / max(simd, 1):.3f} | "
+            f"{g('SQ_WAIT_ANY') / max(g('SQ_WAVE_CYCLES'), 1):.3f} | "
+            f"{g('SQ_LDS_BANK_CONFLICT') / max(g('SQ_LDS_IDX_ACTIVE'), 1):.3f} |")
+    lines += ["", "`MFMA ops / step` counts 32x32x16 bf16 MFMAs (MOPS_BF16 / 64).", "",
+              f"Kernel sources hash: `{kernel_source_sha()}`."]
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def recorded_traffic(mech, pass_name):
     """Calibrated HBM bytes per launch of (mech, pass), if counters exist for these sources."""
     sha = kernel_source_sha()
@@ -248,7 +300,23 @@ def step(mechs, hook=None):
             relpos_profile_events(None, None, RELPOS_PROF_OFF)
 
 
-def time_kernel(torch, mechs, mech, kid, reps=3):
+def measured_mfma_peak(torch):
+    """Sustained dense bf16 MFMA rate of this device (measurement-only probe library)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_relative_amd", "librelpos_probe.so"))
+    lib.relpos_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                           ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    blocks = 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    val = ctypes.c_double(0.0)
+    rc = lib.relpos_probe_mfma_bf16(500, blocks, ctypes.c_void_p(out.data_ptr()), ctypes.byref(val),
+                                    ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    if rc != 0:
+        raise RuntimeError(f"MFMA probe failed ({rc})")
+    return val.value
+
+
+def time_kernel(torch, mechs, mech, kid, reps=50):
     evs = []
     for _ in range(reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -259,7 +327,7 @@ def time_kernel(torch, mechs, mech, kid, reps=3):
     for a, b in evs:
         step([m for m in mechs if m["mech"] == mech], hook=(mech, kid, a, b))
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    return float(np.median([a.elapsed_time(b) for a, b in evs]))
 
 
 def cpu_baseline(budget_heads=1):
@@ -269,7 +337,7 @@ def cpu_baseline(budget_heads=1):
     from oracle import relpos_oracle as orc
     cores = len(os.sched_getaffinity(0))
     threads = int(os.environ.get("OMP_NUM_THREADS", cores))
-    tot_s, tot_f = 0.0, 0.0
+    tot_s, tot_f, fwd_s, bwd_s = 0.0, 0.0, 0.0, 0.0
     for mech in MECH_ORDER:
         case = make_config(CFG_NAME[mech])
         p = orc.Params(**case["params"])
@@ -278,15 +346,19 @@ def cpu_baseline(budget_heads=1):
         B, H, L, d = case["shape"]
         fl = pass_flops(mech, 1, budget_heads, L, d, cfg["window"][0], cfg["window"][1],
                         cfg.get("rel_span", 0))
-        t0 = time.time()
         for h in range(budget_heads):
+            t0 = time.time()
             orc.forward_rows(p, case["q"], case["k"], case["v"], tab, 0, h)
+            t1 = time.time()
             orc.backward_head(p, case["q"], case["k"], case["v"], tab, case["dout"], 0, h)
-        tot_s += time.time() - t0
+            t2 = time.time()
+            fwd_s += t1 - t0
+            bwd_s += t2 - t1
+            tot_s += t2 - t0
         tot_f += fl["fwd"] + fl["bwd"]
         del case, tab
     return {"value": tot_f / tot_s / 1e12, "unit": "TFLOP/s", "cores": min(cores, threads),
-            "kind": "oracle",
+            "kind": "oracle", "fwd_seconds": fwd_s, "bwd_seconds": bwd_s,
             "sample": f"forward + backward of {budget_heads} (batch, head) slice(s) of each of the "
                       f"four mechanisms at L=8192 (fp64 NumPy oracle), {tot_s:.1f} s"}
 
@@ -303,6 +375,7 @@ def main():
                     help="run one plain device copy of this size first (counter calibration)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("SET1_CSV", "SET2_CSV"))
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--out")
     ap.add_argument("--cmd", default="")
@@ -313,6 +386,9 @@ def main():
         return
     if args.summarize_stats:
         summarize_stats(args.summarize_stats, args.out, args.cmd, args.title)
+        return
+    if args.summarize_sq:
+        summarize_sq(*args.summarize_sq, args.out, args.cmd)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -350,7 +426,13 @@ def main():
         torch.cuda.synchronize()
         peak_all = torch.cuda.max_memory_allocated() - base
         mechs.append(m)
+        B_, H_, L_, d_ = m["case"]["shape"]
+        io = B_ * H_ * L_ * d_ * 2 * 8 + B_ * H_ * L_ * 4 * 2   # q k v o dout dq dk dv (bf16), lse, D
+        tab = sum(t.size for t in m["case"]["tables"].values()) * (2 + 4)   # tables + fp32 grads
         per_mech[mech] = {"peak_mem_fwd_GiB": peak_fwd / 2**30, "peak_mem_fwd_bwd_GiB": peak_all / 2**30,
+                          "analytic_min_GiB": (io + tab) / 2**30,
+                          "workspace_fwd_GiB": m["ws_f"].numel() / 2**30,
+                          "workspace_bwd_GiB": m["ws_b"].numel() / 2**30,
                           "naive_fp32_bias_GiB": 4 * m["case"]["shape"][0] * m["case"]["shape"][1] * m["case"]["shape"][2] ** 2 / 2**30}
         print(f"[bench] built {mech}", file=sys.stderr, flush=True)
 
@@ -401,10 +483,12 @@ def main():
     dom_flops = dm["flops"][dom_kernel]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     traffic, traffic_src = recorded_traffic(dom_mech, dom_kernel)
+    peak_meas = measured_mfma_peak(torch)
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "kernel": f"{dom_kernel} pass kernel, {dom_mech}", "avg_ms": dom_ms,
                 "flops_per_launch": dom_flops, "traffic_source": traffic_src,
+                "peak_measured": peak_meas, "frac_of_measured": achieved / peak_meas,
                 "kernel_source_sha": kernel_source_sha()}
 
     cpu = None

@@ -4,9 +4,9 @@ Only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg may import 
 package.  The HIP library never calls it and shares no code with it.
 """
 from .relpos_oracle import (MECHS, Params, allowed_mask, backward, backward_head, bias_rows,
-                            forward, forward_rows, index_maps, scores_rows, t5_bucket,
+                            dq_rows, forward, forward_rows, index_maps, scores_rows, t5_bucket,
                             t5_bucket_by_offset, table_shapes, txl_rows)
 
 __all__ = ["MECHS", "Params", "allowed_mask", "backward", "backward_head", "bias_rows",
-           "forward", "forward_rows", "index_maps", "scores_rows", "t5_bucket",
+           "dq_rows", "forward", "forward_rows", "index_maps", "scores_rows", "t5_bucket",
            "t5_bucket_by_offset", "table_shapes", "txl_rows"]

@@ -334,6 +334,35 @@ def backward_head(p: Params, q, k, v, tables: dict, dO, b: int, h: int):
     return dq, dk, dV, g
 
 
+def dq_rows(p: Params, q, k, v, tables: dict, dO, b: int, h: int, rows):
+    """dQ at the given query rows of one (batch, head): the query-side gradient restricted
+    to those rows (same formulas as backward_head, whose row i depends only on row i of S,
+    P and dP).  Cheap at any length: O(len(rows) * L * d)."""
+    L = q.shape[2]
+    s = p.s()
+    rows = np.asarray(rows, dtype=np.int64)
+    qh, kh, vh, doh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _f64(dO[b, h])
+    S = scores_rows(p, qh, kh, tables, h, rows)
+    P, _ = _softmax_rows(S)
+    dP = doh[rows] @ vh.T
+    D = np.sum(P * dP, axis=1)
+    dS = P * (dP - D[:, None])
+    idx = index_maps(rows, L, p)
+    dq = s * (dS @ kh)
+    if p.mech == "shaw":
+        w = _f64(tables["w"])
+        dq += s * (_pair_scatter(dS, idx["row"], w.shape[0]) @ w)
+    elif p.mech == "txl":
+        r = _f64(tables["r"])[h]
+        dq += s * (_pair_scatter(dS, idx["row"], r.shape[0]) @ r)
+    elif p.mech == "deberta":
+        kr = _f64(tables["kr"])
+        dq += s * (_pair_scatter(dS, idx["c2p"], kr.shape[0]) @ kr)
+    elif p.mech != "t5":
+        raise ValueError(p.mech)
+    return dq
+
+
 def backward(p: Params, q, k, v, tables: dict, dO):
     """Full backward: dq, dk, dv [B, H, L, d] and table gradients (summed over every
     (batch, head) that reads the table; per-head tables keep their head axis)."""

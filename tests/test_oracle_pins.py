@@ -224,6 +224,44 @@ def test_gradients_match_central_differences(mech, mask):
         assert np.max(np.abs(fd - grad)) <= 1e-6 * scale, name
 
 
+@pytest.mark.parametrize("mech", orc.MECHS)
+@pytest.mark.parametrize("mask", ["none", "causal", "local"])
+def test_dq_rows_matches_central_differences(mech, mask):
+    """Pin: the per-row dQ (used at lengths where the full backward is too large) against
+    central differences of the forward pass on the selected query rows, h = 1e-6."""
+    c, p = _case(mech, L=7, d=3, B=1, H=2, window=MASKS[mask], span=2, nb=6, md=5,
+                 bidir=(mask != "causal"), table_std=0.6)
+    q, k, v, tab, do = _f64(c)
+    rows = np.array([0, 3, 6])
+    h_ = 1e-6
+    for hh in range(2):
+        got = orc.dq_rows(p, q, k, v, tab, do, 0, hh, rows)
+        for a, i in enumerate(rows):
+            for e in range(q.shape[-1]):
+                old = q[0, hh, i, e]
+                q[0, hh, i, e] = old + h_
+                lp = _loss(p, q, k, v, tab, do)
+                q[0, hh, i, e] = old - h_
+                lm = _loss(p, q, k, v, tab, do)
+                q[0, hh, i, e] = old
+                fd = (lp - lm) / (2 * h_)
+                assert abs(fd - got[a, e]) <= 1e-6 * max(1.0, abs(fd)), (hh, i, e)
+
+
+@pytest.mark.parametrize("mech", orc.MECHS)
+@pytest.mark.parametrize("mask", ["none", "causal", "local"])
+def test_dq_rows_is_a_row_subset_of_the_full_backward(mech, mask):
+    """Pin: on a longer case, dq_rows over scattered rows equals those rows of the full
+    backward (itself pinned by central differences)."""
+    c, p = _case(mech, L=40, d=8, B=1, H=2, window=MASKS[mask], span=5, nb=10, md=20,
+                 bidir=(mask != "causal"), table_std=0.6)
+    q, k, v, tab, do = _f64(c)
+    rows = np.array([0, 1, 7, 19, 20, 38, 39])
+    dq, _, _, _ = orc.backward_head(p, q, k, v, tab, do, 0, 1)
+    got = orc.dq_rows(p, q, k, v, tab, do, 0, 1, rows)
+    assert np.allclose(got, dq[rows], rtol=1e-12, atol=1e-12)
+
+
 # ------------------------------------------------------------------------ invariants
 
 @pytest.mark.parametrize("mech", orc.MECHS)

@@ -363,12 +363,65 @@ def cpu_baseline(budget_heads=1):
                       f"four mechanisms at L=8192 (fp64 NumPy oracle), {tot_s:.1f} s"}
 
 
+STRESS_SETTINGS = {"t5": dict(num_buckets=32, max_distance=1024), "shaw": dict(rel_span=256),
+                   "deberta": dict(rel_span=512), "txl": {}}
+
+
+def run_stress(torch, lengths, reps=10):
+    """Fixed token budget B * L = 32768 (H = 8, d = 64, bf16, bidirectional) at several
+    lengths: forward and backward time, algorithmic TFLOP/s, peak memory and workspace."""
+    from exact_attention_relative_amd import runner, relpos_attn_fwd
+    from exact_attention_relative_amd.inputs import make_case
+    out = []
+    for mech in MECH_ORDER:
+        for L in lengths:
+            B = max(1, 32768 // L)
+            c = make_case(mech, B, 8, L, 64, dtype="bf16", window=(-1, -1), seed=L,
+                          sub=MECH_ORDER.index(mech), **STRESS_SETTINGS[mech])
+            desc = runner.desc_for(c)
+            torch.cuda.synchronize()
+            base = torch.cuda.memory_allocated()
+            dev = runner.to_device(c)
+            ws_f, _ = runner.workspace(desc, 0)
+            ws_b, _ = runner.workspace(desc, 1)
+            o = torch.empty_like(dev["q"])
+            lse = torch.empty(dev["q"].shape[:-1], dtype=torch.float32, device="cuda")
+            grads = runner.alloc_grads(desc, dev)
+            fwd = lambda: relpos_attn_fwd(desc, dev["q"], dev["k"], dev["v"], *runner.slots(dev), o,
+                                          lse, ws_f, ws_f.numel())
+            bwd = lambda: runner.backward(desc, dev, o, lse, ws=ws_b, grads=grads)
+            torch.cuda.reset_peak_memory_stats()
+            fwd(); bwd()
+            torch.cuda.synchronize()
+            peak = torch.cuda.max_memory_allocated() - base
+            tf, tb = [], []
+            for _ in range(reps):
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record(); fwd(); e[1].record(); bwd(); e[2].record()
+                torch.cuda.synchronize()
+                tf.append(e[0].elapsed_time(e[1]))
+                tb.append(e[1].elapsed_time(e[2]))
+            fl = pass_flops(mech, B, 8, L, 64, -1, -1, STRESS_SETTINGS[mech].get("rel_span", 0))
+            mf, mb = float(np.median(tf)), float(np.median(tb))
+            out.append({"mech": mech, "B": B, "L": L, "fwd_ms": mf, "bwd_ms": mb,
+                        "fwd_TFLOPs": fl["fwd"] / mf / 1e9, "bwd_TFLOPs": fl["bwd"] / mb / 1e9,
+                        "peak_mem_GiB": peak / 2**30, "workspace_bwd_GiB": ws_b.numel() / 2**30,
+                        "naive_fp32_bias_GiB": B * 8 * L * L * 4 / 2**30})
+            print(f"[stress] {mech} L={L}: fwd {mf:.2f} ms, bwd {mb:.2f} ms", file=sys.stderr,
+                  flush=True)
+            del dev, ws_f, ws_b, o, lse, grads
+            torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stress", default=None, metavar="L1,L2,...",
+                    help="length stress at a fixed token budget (prints its own JSON line)")
     ap.add_argument("--only", default=None,
                     help="comma-separated mechanisms (profiling runs; the value then covers only them)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -400,6 +453,11 @@ def main():
     from exact_attention_relative_amd import (RELPOS_PROF_BWD_DKDV, RELPOS_PROF_BWD_DQ,
                                               RELPOS_PROF_FWD)
     torch.cuda.init()
+    if args.stress:
+        lengths = [int(x) for x in args.stress.split(",") if x]
+        print(json.dumps({"stress": run_stress(torch, lengths), "tokens_per_batch": 32768,
+                          "heads": 8, "head_dim": 64, "dtype": "bf16", "data": "synthetic"}))
+        return
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * 2**20 // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")

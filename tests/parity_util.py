@@ -53,3 +53,35 @@ def rel_l2(a, b):
 
 def to_np(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def halfulp_bf16(x):
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    return np.where(ax > 0, 2.0 ** (e - 8), 2.0 ** -133)
+
+
+def check_row_sum_invariant(mech, case, o, tg):
+    O = to_np(o)
+    dO = case["dout"].astype(np.float64)
+    q = case["q"].astype(np.float64)
+    s = 1.0 / np.sqrt(3 * 64) if mech == "deberta" else 1.0 / 8.0
+    # Each row of dS sums to dO_i . (O_i - O_i stored) because D is formed from the stored bf16
+    # O; |that| <= e_i = sum_c |dO_ic| halfulp(O_ic), so the table gradients' sums over rows
+    # are bounded by the matching weighted sums of e_i.
+    e = np.sum(np.abs(dO) * halfulp_bf16(O), axis=-1)          # [B, H, L]
+    slack = 1.25
+    if mech == "t5":
+        bound = e.sum(axis=(0, 2))                                # per head
+        got = np.abs(tg["beta"].sum(axis=1))
+        assert np.all(got <= slack * bound + 1e-4 * np.abs(tg["beta"]).max()), (got, bound)
+    elif mech in ("shaw", "deberta"):
+        name = "w" if mech == "shaw" else "kr"
+        bound = s * np.einsum("bhl,bhld->d", e, np.abs(q))
+        got = np.abs(tg[name].sum(axis=0))
+        assert np.all(got <= slack * bound + 1e-4 * np.abs(tg[name]).max()), (got, bound)
+    elif mech == "txl":
+        v = case["tables"]["v"].astype(np.float64)
+        bound = s * np.einsum("bhl,bhld->hd", e, np.abs(q + v[None, :, None, :]))
+        got = np.abs(tg["r"].sum(axis=1))
+        assert np.all(got <= slack * bound + 1e-4 * np.abs(tg["r"]).max()), (got.max(), bound.min())

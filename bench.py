@@ -367,16 +367,18 @@ STRESS_SETTINGS = {"t5": dict(num_buckets=32, max_distance=1024), "shaw": dict(r
                    "deberta": dict(rel_span=512), "txl": {}}
 
 
-def run_stress(torch, lengths, reps=10):
-    """Fixed token budget B * L = 32768 (H = 8, d = 64, bf16, bidirectional) at several
-    lengths: forward and backward time, algorithmic TFLOP/s, peak memory and workspace."""
+def run_stress(torch, lengths, reps=10, windows=None):
+    """Fixed token budget B * L = 32768 (H = 8, d = 64, bf16) at several lengths, or at
+    L = 8192 with several symmetric local windows: forward and backward time, algorithmic
+    TFLOP/s (pairs inside the window only), peak memory and workspace."""
     from exact_attention_relative_amd import runner, relpos_attn_fwd
     from exact_attention_relative_amd.inputs import make_case
     out = []
+    cases = [(L, -1) for L in lengths] if windows is None else [(8192, w) for w in windows]
     for mech in MECH_ORDER:
-        for L in lengths:
+        for L, win in cases:
             B = max(1, 32768 // L)
-            c = make_case(mech, B, 8, L, 64, dtype="bf16", window=(-1, -1), seed=L,
+            c = make_case(mech, B, 8, L, 64, dtype="bf16", window=(win, win), seed=L + max(win, 0),
                           sub=MECH_ORDER.index(mech), **STRESS_SETTINGS[mech])
             desc = runner.desc_for(c)
             torch.cuda.synchronize()
@@ -401,13 +403,13 @@ def run_stress(torch, lengths, reps=10):
                 torch.cuda.synchronize()
                 tf.append(e[0].elapsed_time(e[1]))
                 tb.append(e[1].elapsed_time(e[2]))
-            fl = pass_flops(mech, B, 8, L, 64, -1, -1, STRESS_SETTINGS[mech].get("rel_span", 0))
+            fl = pass_flops(mech, B, 8, L, 64, win, win, STRESS_SETTINGS[mech].get("rel_span", 0))
             mf, mb = float(np.median(tf)), float(np.median(tb))
-            out.append({"mech": mech, "B": B, "L": L, "fwd_ms": mf, "bwd_ms": mb,
+            out.append({"mech": mech, "B": B, "L": L, "window": win, "fwd_ms": mf, "bwd_ms": mb,
                         "fwd_TFLOPs": fl["fwd"] / mf / 1e9, "bwd_TFLOPs": fl["bwd"] / mb / 1e9,
                         "peak_mem_GiB": peak / 2**30, "workspace_bwd_GiB": ws_b.numel() / 2**30,
                         "naive_fp32_bias_GiB": B * 8 * L * L * 4 / 2**30})
-            print(f"[stress] {mech} L={L}: fwd {mf:.2f} ms, bwd {mb:.2f} ms", file=sys.stderr,
+            print(f"[stress] {mech} L={L} window={win}: fwd {mf:.2f} ms, bwd {mb:.2f} ms", file=sys.stderr,
                   flush=True)
             del dev, ws_f, ws_b, o, lse, grads
             torch.cuda.empty_cache()
@@ -422,6 +424,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stress", default=None, metavar="L1,L2,...",
                     help="length stress at a fixed token budget (prints its own JSON line)")
+    ap.add_argument("--windows", default=None, metavar="W1,W2,...",
+                    help="symmetric local windows at L=8192 (prints its own JSON line)")
     ap.add_argument("--only", default=None,
                     help="comma-separated mechanisms (profiling runs; the value then covers only them)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -456,6 +460,11 @@ def main():
     if args.stress:
         lengths = [int(x) for x in args.stress.split(",") if x]
         print(json.dumps({"stress": run_stress(torch, lengths), "tokens_per_batch": 32768,
+                          "heads": 8, "head_dim": 64, "dtype": "bf16", "data": "synthetic"}))
+        return
+    if args.windows:
+        wins = [int(x) for x in args.windows.split(",") if x]
+        print(json.dumps({"windows": run_stress(torch, [], windows=wins), "L": 8192, "B": 4,
                           "heads": 8, "head_dim": 64, "dtype": "bf16", "data": "synthetic"}))
         return
     if args.copy_calibration_mib > 0:

@@ -57,16 +57,18 @@ __global__ void agg_diag_kernel(const float* __restrict__ pdiag, int B, int H, i
   diag[idx] = acc;
 }
 
-// T-XL dr[h][row][d] = s (sum_{b, key block} part[own][delta + 128 p + 192][d] + v_h[d] diag_h[delta]).
+// T-XL dr[h][row][d] = s (sum_{b, key block} part[own][x][d] + v_h[d] diag_h[delta]).
 // The partials come from the dK/dV pass: owner (b, h, p) holds offset delta at row
-// delta + 128 p + 192.  One workgroup per (head, 64 consecutive offsets): for every owner the
-// 64 rows it holds for those offsets are one contiguous 16 KB block, read whole and added in
-// a fixed owner order.
+// x = delta + 128 p + 192 - rbase(p), where rbase = 0 for a full sweep and, with a two-sided
+// window, the first row of the owner's sweep (its first 64-row step + 65).  One workgroup
+// per (head, 64 consecutive offsets): for every owner the 64 rows it holds for those offsets
+// are one contiguous 16 KB block, read whole and added in a fixed owner order.
 __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict__ prow,
                                                          const float* __restrict__ diag,
                                                          const float* __restrict__ v, int B, int H,
-                                                         int L, int nb, int nrt, int nrel, int off,
-                                                         float s, float* __restrict__ dr) {
+                                                         int L, int nb, int nrt, int wl, int wr,
+                                                         int nrel, int off, float s,
+                                                         float* __restrict__ dr) {
   const int nch = (nrel + 63) / 64;
   const int h = blockIdx.x / nch, row0 = 64 * (blockIdx.x % nch);
   const int t = threadIdx.x;
@@ -74,7 +76,8 @@ __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict
   f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
   for (int b = 0; b < B; ++b)
     for (int p = 0; p < nb; ++p) {
-      const int x0 = delta0 + 128 * p + 192;
+      const int rbase = (wl >= 0 && wr >= 0) ? (max(0, 128 * p - wr) / 64) * 64 + 65 : 0;
+      const int x0 = delta0 + 128 * p + 192 - rbase;
       if (x0 + 63 < 0 || x0 >= nrt) continue;   // no row of this owner in the block
       const float* base = prow + (((int64_t)b * H + h) * nb + p) * (int64_t)nrt * kHeadDim;
       f32x4 ld[4];
@@ -183,12 +186,12 @@ hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int
 }
 
 hipError_t launch_agg_txl(const float* prow, const float* pkv, const float* diag, const void* r,
-                          const float* v, int B, int H, int L, int nb, int nrt, int nrel,
-                          int off, float s, bool fp32, float* dr, float* du, float* dv,
+                          const float* v, int B, int H, int L, int nb, int nrk, int wl, int wr,
+                          int nrel, int off, float s, bool fp32, float* dr, float* du, float* dv,
                           hipStream_t st) {
   const int nch = (nrel + 63) / 64;
   hipLaunchKernelGGL(agg_txl_dr_kernel, dim3(H * nch), dim3(256), 0, st, prow, diag, v, B, H,
-                     L, nb, nrt, nrel, off, s, dr);
+                     L, nb, nrk, wl, wr, nrel, off, s, dr);
   if (fp32)
     hipLaunchKernelGGL((agg_txl_dv_kernel<float>), dim3(H * kHeadDim), dim3(256), 0, st, diag,
                        (const float*)r, L, nrel, off, s, dv);

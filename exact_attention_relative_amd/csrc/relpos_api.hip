@@ -5,6 +5,8 @@
 #include <vector>
 
 #include "../../include/relpos_attn.h"
+#include <algorithm>
+
 #include "relpos_kernels.h"
 
 using namespace relpos;
@@ -150,7 +152,16 @@ int make_plan(const relpos_desc* d, Plan* p) {
   const int k = d->rel_span;
   if (d->mech == RELPOS_SHAW) p->part_q_stride = (int64_t)(2 * k + 1) * kHeadDim;
   if (d->mech == RELPOS_DEBERTA) p->part_q_stride = p->part_k_stride = (int64_t)(2 * k) * kHeadDim;
-  if (d->mech == RELPOS_TXL) p->part_q_stride = (int64_t)p->nrt * kHeadDim;
+  if (d->mech == RELPOS_TXL) {
+    // key-side r partial: rows for every offset, or with a two-sided window only the rows of
+    // the owner's sweep (at most wl + wr + 382)
+    int64_t rows_k = p->nrt;
+    if (d->window_left >= 0 && d->window_right >= 0) {
+      const int64_t wrows = ((int64_t)d->window_left + d->window_right + 382 + 63) / 64 * 64;
+      rows_k = std::min<int64_t>(rows_k, wrows);
+    }
+    p->part_q_stride = rows_k * kHeadDim;
+  }
   if (p->part_q_stride) p->off_part_q = take(sizeof(float) * own * p->part_q_stride);
   if (p->part_k_stride) p->off_part_k = take(sizeof(float) * own * p->part_k_stride);
   if (d->mech == RELPOS_T5 || d->mech == RELPOS_TXL) {
@@ -440,7 +451,8 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
     case RELPOS_TXL:
       e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, p.nrt, diag, s);
       if (e == hipSuccess)
-        e = launch_agg_txl(a.part_q, a.part_kv, diag, rel_a, bias_b, p.B, p.H, p.L, p.nb, p.nrt,
+        e = launch_agg_txl(a.part_q, a.part_kv, diag, rel_a, bias_b, p.B, p.H, p.L, p.nb,
+                           (int)(p.part_q_stride / kHeadDim), desc->window_left, desc->window_right,
                            p.nrel, p.txl_off, p.scale, p.fp32, drel_a, dbias_a, dbias_b, s);
       break;
   }

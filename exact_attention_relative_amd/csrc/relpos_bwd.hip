@@ -224,8 +224,11 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   }
   // T-XL r partial of the key-side pass: row b0 + 65 + t holds window row t of step base b0
   // (offset delta = b0 - A0 - 127 + t), i.e. row delta + A0 + 192
+  // With a two-sided window the partial keeps only the rows of this sweep, from row bt0 + 65.
   float* ptg = nullptr;
-  if constexpr (V::TG1) ptg = a.part_q + owner * a.part_q_stride;
+  const int nrk = (int)(a.part_q_stride / kHeadDim);
+  const int rb = (sh.wl >= 0 && sh.wr >= 0) ? bt0 + 65 : 0;
+  if constexpr (V::TG1) ptg = a.part_q + owner * a.part_q_stride - (int64_t)rb * kHeadDim;
   float* pdiag = nullptr;
   if constexpr (V::DIAG) pdiag = a.part_qv + owner * (int64_t)nrt;
 
@@ -247,10 +250,10 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     }
   }
   if constexpr (V::TG1) {
-    // rows written by the sweep: [bt0 + 65, bt_last + 256]
-    for (int64_t e = tid; e < (int64_t)nrt * kHeadDim; e += 256) {
-      const int row = (int)(e / kHeadDim);
-      if (!(nsteps > 0 && row >= bt0 + 65 && row <= bt_last + 256)) ptg[e] = 0.f;
+    // rows written by the sweep: [bt0 + 65, bt_last + 256] (ptg is offset by rb rows)
+    for (int64_t e = tid; e < (int64_t)nrk * kHeadDim; e += 256) {
+      const int row = (int)(e / kHeadDim) + rb;
+      if (!(nsteps > 0 && row >= bt0 + 65 && row <= bt_last + 256)) ptg[(int64_t)rb * kHeadDim + e] = 0.f;
     }
   }
   if constexpr (V::DIAG) {

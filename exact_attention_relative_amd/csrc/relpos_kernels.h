@@ -115,7 +115,8 @@ hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool
 hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int nbk, float* dbeta,
                          hipStream_t st);
 hipError_t launch_agg_txl(const float* prow, const float* pkv, const float* diag, const void* r,
-                          const float* v, int B, int H, int L, int nb, int nrt, int nrel,
+                          const float* v, int B, int H, int L, int nb, int nrk, int wl, int wr,
+                          int nrel,
                           int off, float s, bool fp32, float* dr, float* du, float* dv,
                           hipStream_t st);
 

@@ -69,6 +69,8 @@ def score(p, q, k, tables, h, i, j):
         kr = tables["kr"][_clamp(i - j + kk, 0, 2 * kk - 1)]
         qr = tables["qr"][_clamp(j - i + kk, 0, 2 * kk - 1)]
         return s * (_dot(qi, kj) + _dot(qi, kr) + _dot(kj, qr))
+    if p.mech == "alibi":
+        return s * _dot(qi, kj) - float(tables["slopes"][h]) * abs(i - j)
     raise ValueError(p.mech)
 
 

@@ -24,6 +24,12 @@ mechanism:
     T-XL     S_ij = s * ((q_i + u_h) . k_j + (q_i + v_h) . r_h[i - j])
     DeBERTa  S_ij = s * (q_i . k_j + q_i . Kr[c2p(i,j)] + k_j . Qr[p2c(i,j)])
              c2p(i,j) = clamp(i - j + k, 0, 2k - 1),  p2c(i,j) = clamp(j - i + k, 0, 2k - 1)
+    ALiBi    B_ij = -m_h * |i - j|                             (slope per head, unscaled)
+
+ALiBi is not one of the authors' four; the explainer names it among the models the method
+suits (section on engineering trade-offs and where it applies).  Its plainest reading is the
+original linear distance penalty with one slope per head, added like T5's bias; its gradient
+is dm_h = -sum of dS_ij |i - j|.
 
 Default scale s = 1/sqrt(d), and 1/sqrt(3d) for DeBERTa.  The backward pass is
 written as explicit formulas (no autograd): dV = P^T dO, dP = dO V^T,
@@ -46,7 +52,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-MECHS = ("t5", "shaw", "txl", "deberta")
+MECHS = ("t5", "shaw", "txl", "deberta")     # the authors' four
+ALL_MECHS = MECHS + ("alibi",)
 
 
 @dataclass
@@ -165,6 +172,8 @@ def index_maps(rows: np.ndarray, L: int, p: Params) -> dict:
     if p.mech == "deberta":
         k = p.rel_span
         return {"c2p": np.clip(delta + k, 0, 2 * k - 1), "p2c": np.clip(rel + k, 0, 2 * k - 1)}
+    if p.mech == "alibi":
+        return {"dist": np.abs(delta)}
     raise ValueError(p.mech)
 
 
@@ -206,6 +215,9 @@ def bias_rows(p: Params, q: np.ndarray, k: np.ndarray, tables: dict, h: int,
         c2p = np.take_along_axis(G1, idx["c2p"], axis=1)
         p2c = G2[np.arange(L)[None, :], idx["p2c"]]
         return s * (c2p + p2c)
+    if p.mech == "alibi":
+        m = float(_f64(tables["slopes"])[h])
+        return -m * idx["dist"].astype(np.float64)
     raise ValueError(p.mech)
 
 
@@ -266,6 +278,8 @@ def table_shapes(p: Params, H: int, L: int, d: int) -> dict:
         return {"r": (H, txl_rows(L, p), d), "u": (H, d), "v": (H, d)}
     if p.mech == "deberta":
         return {"kr": (2 * p.rel_span, d), "qr": (2 * p.rel_span, d)}
+    if p.mech == "alibi":
+        return {"slopes": (H,)}
     raise ValueError(p.mech)
 
 
@@ -329,6 +343,10 @@ def backward_head(p: Params, q, k, v, tables: dict, dO, b: int, h: int):
         dk = s * (dS.T @ qh) + s * (N2 @ qr)
         g["kr"] = s * (N1.T @ qh)
         g["qr"] = s * (N2.T @ kh)
+    elif p.mech == "alibi":
+        dq = s * (dS @ kh)
+        dk = s * (dS.T @ qh)
+        g["slopes"] = -np.sum(dS * idx["dist"])
     else:
         raise ValueError(p.mech)
     return dq, dk, dV, g
@@ -358,7 +376,7 @@ def dq_rows(p: Params, q, k, v, tables: dict, dO, b: int, h: int, rows):
     elif p.mech == "deberta":
         kr = _f64(tables["kr"])
         dq += s * (_pair_scatter(dS, idx["c2p"], kr.shape[0]) @ kr)
-    elif p.mech != "t5":
+    elif p.mech not in ("t5", "alibi"):
         raise ValueError(p.mech)
     return dq
 
@@ -376,7 +394,8 @@ def backward(p: Params, q, k, v, tables: dict, dO):
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h], g = backward_head(p, q, k, v, tables, dO, b, h)
             for name, val in g.items():
-                if len(shapes[name]) >= 1 and shapes[name][0] == H and name in ("beta", "r", "u", "v"):
+                per_head = name in ("beta", "r", "u", "v", "slopes")
+                if len(shapes[name]) >= 1 and shapes[name][0] == H and per_head:
                     grads[name][h] += val
                 else:
                     grads[name] += val

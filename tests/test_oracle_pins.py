@@ -74,7 +74,7 @@ def test_t5_bucket_monotone_and_range():
 
 # ------------------------------------------------------------------------ index maps
 
-@pytest.mark.parametrize("mech", orc.MECHS)
+@pytest.mark.parametrize("mech", orc.ALL_MECHS)
 @pytest.mark.parametrize("mask", ["none", "causal"])
 def test_index_maps_depend_only_on_offset(mech, mask):
     """Pin: every table index is a function of i - j alone (idx[i][j] == idx[i+1][j+1])."""
@@ -109,7 +109,7 @@ def test_index_map_clamps_closed_form():
 
 # ------------------------------------------------------------------------ brute force
 
-@pytest.mark.parametrize("mech", orc.MECHS)
+@pytest.mark.parametrize("mech", orc.ALL_MECHS)
 @pytest.mark.parametrize("mask", list(MASKS))
 def test_vectorised_matches_scalar_brute_force(mech, mask):
     """Pin: pure-Python per-pair loops at L <= 8 agree with the vectorised oracle to 1e-12."""
@@ -130,7 +130,7 @@ def _zero_tables(c):
     return {n: np.zeros_like(t, dtype=np.float64) for n, t in c["tables"].items()}
 
 
-@pytest.mark.parametrize("mech", orc.MECHS)
+@pytest.mark.parametrize("mech", orc.ALL_MECHS)
 @pytest.mark.parametrize("mask", list(MASKS))
 def test_zero_tables_reduce_to_sdpa(mech, mask):
     """Pin: with every table zero the oracle is plain attention; forward and all three
@@ -151,6 +151,34 @@ def test_zero_tables_reduce_to_sdpa(mech, mask):
     np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-11)
     np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-11)
     np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_alibi_matches_sdpa_with_an_explicit_bias(mask):
+    """Pin: ALiBi equals torch's scaled_dot_product_attention with the float mask
+    -m_h |i - j| (and -inf outside the window), forward and autograd gradients of q, k, v and
+    the slopes, in float64."""
+    c, p = _case("alibi", L=24, d=8, B=2, H=3, window=MASKS[mask], bidir=(mask != "causal"),
+                 table_std=0.5)
+    q, k, v, tab, do = _f64(c)
+    O, _ = orc.forward(p, q, k, v, tab)
+    dq, dk, dv, g = orc.backward(p, q, k, v, tab, do)
+    L = q.shape[2]
+    i = torch.arange(L, dtype=torch.float64)
+    dist = (i[:, None] - i[None, :]).abs()
+    m = torch.from_numpy(tab["slopes"].copy()).requires_grad_(True)
+    allowed = torch.from_numpy(orc.allowed_mask(np.arange(L), L, p))
+    bias = -m[:, None, None] * dist[None]
+    mask_f = torch.where(allowed[None], bias, torch.full_like(bias, -math.inf))
+    tq, tk, tv = (torch.from_numpy(x).requires_grad_(True) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask_f[None],
+                                                           scale=p.s())
+    ref.backward(torch.from_numpy(do))
+    np.testing.assert_allclose(O, ref.detach().numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(g["slopes"], m.grad.numpy(), rtol=0, atol=1e-10)
 
 
 def test_txl_position_free_is_attention_on_q_plus_u():
@@ -198,7 +226,7 @@ def _loss(p, q, k, v, tab, do):
     return float(np.sum(O * do))
 
 
-@pytest.mark.parametrize("mech", orc.MECHS)
+@pytest.mark.parametrize("mech", orc.ALL_MECHS)
 @pytest.mark.parametrize("mask", ["none", "causal"])
 def test_gradients_match_central_differences(mech, mask):
     """Pin: every gradient element (q, k, v and every table) against central differences
@@ -224,7 +252,7 @@ def test_gradients_match_central_differences(mech, mask):
         assert np.max(np.abs(fd - grad)) <= 1e-6 * scale, name
 
 
-@pytest.mark.parametrize("mech", orc.MECHS)
+@pytest.mark.parametrize("mech", orc.ALL_MECHS)
 @pytest.mark.parametrize("mask", ["none", "causal", "local"])
 def test_dq_rows_matches_central_differences(mech, mask):
     """Pin: the per-row dQ (used at lengths where the full backward is too large) against
@@ -248,7 +276,7 @@ def test_dq_rows_matches_central_differences(mech, mask):
                 assert abs(fd - got[a, e]) <= 1e-6 * max(1.0, abs(fd)), (hh, i, e)
 
 
-@pytest.mark.parametrize("mech", orc.MECHS)
+@pytest.mark.parametrize("mech", orc.ALL_MECHS)
 @pytest.mark.parametrize("mask", ["none", "causal", "local"])
 def test_dq_rows_is_a_row_subset_of_the_full_backward(mech, mask):
     """Pin: on a longer case, dq_rows over scattered rows equals those rows of the full

@@ -66,7 +66,7 @@ def flop_counts(mech, B, H, L, d, wl, wr, span):
     per_row = np.maximum(hi - lo + 1, 0)
     n_pairs = int(per_row.sum()) * B * H
     i = np.arange(L)
-    if mech == "t5":
+    if mech in ("t5", "alibi"):
         rel = 0
     elif mech == "txl":
         rel = n_pairs
@@ -364,7 +364,8 @@ def cpu_baseline(budget_heads=1):
 
 
 STRESS_SETTINGS = {"t5": dict(num_buckets=32, max_distance=1024), "shaw": dict(rel_span=256),
-                   "deberta": dict(rel_span=512), "txl": {}}
+                   "deberta": dict(rel_span=512), "txl": {}, "alibi": {}}
+STRESS_MECHS = MECH_ORDER + ("alibi",)
 
 
 def run_stress(torch, lengths, reps=10, windows=None):
@@ -375,11 +376,11 @@ def run_stress(torch, lengths, reps=10, windows=None):
     from exact_attention_relative_amd.inputs import make_case
     out = []
     cases = [(L, -1) for L in lengths] if windows is None else [(8192, w) for w in windows]
-    for mech in MECH_ORDER:
+    for mech in STRESS_MECHS:
         for L, win in cases:
             B = max(1, 32768 // L)
             c = make_case(mech, B, 8, L, 64, dtype="bf16", window=(win, win), seed=L + max(win, 0),
-                          sub=MECH_ORDER.index(mech), **STRESS_SETTINGS[mech])
+                          sub=STRESS_MECHS.index(mech), **STRESS_SETTINGS[mech])
             desc = runner.desc_for(c)
             torch.cuda.synchronize()
             base = torch.cuda.memory_allocated()

@@ -13,9 +13,10 @@ import os
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librelpos_attn.so")
 
-RELPOS_T5, RELPOS_SHAW, RELPOS_TXL, RELPOS_DEBERTA = 0, 1, 2, 3
+RELPOS_T5, RELPOS_SHAW, RELPOS_TXL, RELPOS_DEBERTA, RELPOS_ALIBI = 0, 1, 2, 3, 4
 RELPOS_BF16, RELPOS_FP32 = 0, 1
-MECH_IDS = {"t5": RELPOS_T5, "shaw": RELPOS_SHAW, "txl": RELPOS_TXL, "deberta": RELPOS_DEBERTA}
+MECH_IDS = {"t5": RELPOS_T5, "shaw": RELPOS_SHAW, "txl": RELPOS_TXL, "deberta": RELPOS_DEBERTA,
+            "alibi": RELPOS_ALIBI}
 
 RELPOS_OK = 0
 RELPOS_E_INVALID = -1

@@ -161,6 +161,21 @@ __global__ void agg_txl_du_kernel(const float* __restrict__ pkv, int B, int H, i
   du[idx] = acc * s;
 }
 
+// ALiBi dm[h] = -sum_delta |delta| diag_h[delta]: one workgroup per head, each thread a fixed
+// strided subset of offsets, then the fixed-order block reduction.
+__global__ void agg_alibi_kernel(const float* __restrict__ diag, int L, float* __restrict__ dm) {
+  __shared__ float sh[256];
+  const int h = blockIdx.x;
+  const int n = 2 * L - 1;
+  float acc = 0.f;
+  for (int x = threadIdx.x; x < n; x += 256) {
+    const int delta = x - (L - 1);
+    acc = fmaf((float)(delta < 0 ? -delta : delta), diag[(int64_t)h * n + x], acc);
+  }
+  const float tot = block_sum(acc, sh);
+  if (threadIdx.x == 0) dm[h] = -tot;
+}
+
 static inline int nblk(int64_t n, int t) { return (int)((n + t - 1) / t); }
 
 hipError_t launch_agg_rows(const float* part, int64_t stride, int nown, int64_t nelem, float scale,
@@ -176,6 +191,11 @@ hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool
   const int64_t n = (int64_t)H * (2 * L - 1);
   hipLaunchKernelGGL(agg_diag_kernel, dim3(nblk(n, 256)), dim3(256), 0, st, pdiag, B, H, L, nb,
                      rev ? 1 : 0, nrt, diag);
+  return hipGetLastError();
+}
+
+hipError_t launch_agg_alibi(const float* diag, int H, int L, float* dm, hipStream_t st) {
+  hipLaunchKernelGGL(agg_alibi_kernel, dim3(H), dim3(256), 0, st, diag, L, dm);
   return hipGetLastError();
 }
 

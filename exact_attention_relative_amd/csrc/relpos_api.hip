@@ -91,7 +91,7 @@ struct Plan {
 
 int make_plan(const relpos_desc* d, Plan* p) {
   if (!d) return RELPOS_E_INVALID;
-  if (d->mech < RELPOS_T5 || d->mech > RELPOS_DEBERTA) return RELPOS_E_INVALID;
+  if (d->mech < RELPOS_T5 || d->mech > RELPOS_ALIBI) return RELPOS_E_INVALID;
   if (d->dtype != RELPOS_BF16 && d->dtype != RELPOS_FP32) return RELPOS_E_INVALID;
   if (d->batch < 0 || d->heads < 1 || d->seqlen < 0 || d->head_dim < 1) return RELPOS_E_INVALID;
   if (d->window_left < -1 || d->window_right < -1) return RELPOS_E_INVALID;
@@ -120,6 +120,7 @@ int make_plan(const relpos_desc* d, Plan* p) {
       if (d->rel_span < 1 || d->rel_span > (1 << 26)) return RELPOS_E_INVALID;
       break;
     case RELPOS_TXL:
+    case RELPOS_ALIBI:
       break;
   }
   p->nrel = (d->window_right == 0) ? L : 2 * L - 1;
@@ -131,7 +132,8 @@ int make_plan(const relpos_desc* d, Plan* p) {
   const size_t rows = (size_t)p->B * p->H * L;
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes); return o; };
-  if (d->mech == RELPOS_T5) {
+  const bool lut_path = d->mech == RELPOS_T5 || d->mech == RELPOS_ALIBI;
+  if (lut_path) {
     p->off_bucket = take(sizeof(int32_t) * (size_t)(L > 0 ? 2 * L - 1 : 1));
     p->off_lut = take(sizeof(float) * (size_t)p->H * (L > 0 ? 2 * L - 1 : 1));
   }
@@ -164,7 +166,7 @@ int make_plan(const relpos_desc* d, Plan* p) {
   }
   if (p->part_q_stride) p->off_part_q = take(sizeof(float) * own * p->part_q_stride);
   if (p->part_k_stride) p->off_part_k = take(sizeof(float) * own * p->part_k_stride);
-  if (d->mech == RELPOS_T5 || d->mech == RELPOS_TXL) {
+  if (lut_path || d->mech == RELPOS_TXL) {
     p->off_part_qv = take(sizeof(float) * own * p->nrt);
     p->off_diag = take(sizeof(float) * (size_t)p->H * (L > 0 ? 2 * L - 1 : 1));
   }
@@ -195,6 +197,11 @@ hipError_t run_prep(const relpos_desc* d, const Plan& p, const void* q, const vo
     e = launch_index_map(MECH_T5, L, 0, 0, 0, p.t5, (int32_t*)(ws + p.off_bucket), nullptr, st);
     if (e != hipSuccess) return e;
     e = launch_t5_lut(bias_a, p.H, L, d->num_buckets, 1.0f / p.scale, p.t5, (float*)(ws + p.off_lut), st);
+  } else if (d->mech == RELPOS_ALIBI) {
+    // distinct "bucket" per offset and sign: no tile is single-valued, every tile adds the LUT
+    e = launch_index_map(MECH_ALIBI, L, 0, 0, 0, p.t5, (int32_t*)(ws + p.off_bucket), nullptr, st);
+    if (e != hipSuccess) return e;
+    e = launch_alibi_lut(bias_a, p.H, L, 1.0f / p.scale, (float*)(ws + p.off_lut), st);
   } else if (d->mech == RELPOS_SHAW) {
     // end A (j - i >= k) reads w[2k], end B (j - i <= -k) reads w[0]
     RowDotArgs r{q, rows, L, p.H, rel_a, 0, 2 * d->rel_span, 0, 2, (float*)(ws + p.off_rowc)};
@@ -223,7 +230,7 @@ AttnShape make_shape(const relpos_desc* d, const Plan& p) {
   s.L = p.L;
   s.wl = d->window_left;
   s.wr = d->window_right;
-  s.mech = d->mech;
+  s.mech = d->mech == RELPOS_ALIBI ? MECH_T5 : d->mech;   // ALiBi uses the LUT path
   s.span = d->rel_span;
   s.nrel = p.nrel;
   s.txl_off = p.txl_off;
@@ -237,6 +244,7 @@ int check_tables(const relpos_desc* d, const void* rel_a, const void* rel_b, con
   bool need_ra = false, need_rb = false, need_ba = false, need_bb = false;
   switch (d->mech) {
     case RELPOS_T5: need_ba = true; break;
+    case RELPOS_ALIBI: need_ba = true; break;
     case RELPOS_SHAW: need_ra = true; break;
     case RELPOS_TXL: need_ra = need_ba = need_bb = true; break;
     case RELPOS_DEBERTA: need_ra = need_rb = true; break;
@@ -312,7 +320,7 @@ int relpos_index_map(const relpos_desc* desc, int32_t* out_a, int32_t* out_b, vo
   if (!out_a || !aligned16(out_a)) return RELPOS_E_INVALID;
   if ((desc->mech == RELPOS_DEBERTA) != (out_b != nullptr)) return RELPOS_E_INVALID;
   if (out_b && !aligned16(out_b)) return RELPOS_E_INVALID;
-  hipError_t e = launch_index_map(desc->mech, p.L, desc->rel_span, p.nrel, p.txl_off, p.t5, out_a,
+  hipError_t e = launch_index_map(desc->mech == RELPOS_ALIBI ? MECH_ALIBI : desc->mech, p.L, desc->rel_span, p.nrel, p.txl_off, p.t5, out_a,
                                   out_b, (hipStream_t)stream);
   return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
 }
@@ -339,7 +347,7 @@ int relpos_attn_fwd(const relpos_desc* desc, const void* q, const void* k, const
   a.q = q; a.k = k; a.v = v;
   a.rel_a = rel_a; a.rel_b = rel_b;
   a.o = o; a.lse = lse;
-  if (desc->mech == RELPOS_T5) {
+  if (desc->mech == RELPOS_T5 || desc->mech == RELPOS_ALIBI) {
     a.lut = (const float*)(ws + p.off_lut);
     a.bucket = (const int*)(ws + p.off_bucket);
   }
@@ -378,6 +386,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
     const size_t H = (size_t)p.H, L = (size_t)p.L, k2 = 2 * (size_t)desc->rel_span;
     switch (desc->mech) {
       case RELPOS_T5: n_ba = H * desc->num_buckets; break;
+      case RELPOS_ALIBI: n_ba = H; break;
       case RELPOS_SHAW: n_a = (k2 + 1) * kHeadDim; break;
       case RELPOS_TXL: n_a = H * p.nrel * kHeadDim; n_ba = n_bb = H * kHeadDim; break;
       case RELPOS_DEBERTA: n_a = n_b = k2 * kHeadDim; break;
@@ -407,7 +416,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
   a.dsum = (const float*)(ws + p.off_dsum);
   a.rel_a = rel_a; a.rel_b = rel_b;
   a.bias_a = bias_a; a.bias_b = bias_b;
-  if (desc->mech == RELPOS_T5) {
+  if (desc->mech == RELPOS_T5 || desc->mech == RELPOS_ALIBI) {
     a.lut = (const float*)(ws + p.off_lut);
     a.bucket = (const int*)(ws + p.off_bucket);
   }
@@ -439,6 +448,10 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
     case RELPOS_T5:
       e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, p.nrt, diag, s);
       if (e == hipSuccess) e = launch_agg_t5(diag, a.bucket, p.H, p.L, desc->num_buckets, dbias_a, s);
+      break;
+    case RELPOS_ALIBI:
+      e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, p.nrt, diag, s);
+      if (e == hipSuccess) e = launch_agg_alibi(diag, p.H, p.L, dbias_a, s);
       break;
     case RELPOS_SHAW:
       e = launch_agg_rows(a.part_q, p.part_q_stride, p.owners, p.part_q_stride, p.scale, drel_a, s);

@@ -9,6 +9,9 @@
 namespace relpos {
 
 enum { MECH_T5 = 0, MECH_SHAW = 1, MECH_TXL = 2, MECH_DEBERTA = 3 };
+// ALiBi runs the attention kernels' T5 path (a per-offset LUT); only the preparation and
+// aggregation kernels see this value.
+constexpr int MECH_ALIBI = 4;
 
 constexpr int kHeadDim = 64;
 constexpr int kMaxThresholds = 64;
@@ -103,6 +106,9 @@ struct RowDotArgs {
 };
 hipError_t launch_rowdot(const RowDotArgs& a, bool x_fp32, bool y_fp32, hipStream_t stream);
 
+// ALiBi LUT: lut[h][delta + L - 1] = -m_h |delta| * inv_scale
+hipError_t launch_alibi_lut(const float* slopes, int H, int L, float inv_scale, float* lut,
+                            hipStream_t stream);
 hipError_t launch_t5_lut(const float* beta, int H, int L, int nb, float inv_scale, const T5Map& m,
                          float* lut, hipStream_t stream);
 hipError_t launch_index_map(int mech, int L, int span, int nrel, int txl_off, const T5Map& m,
@@ -112,6 +118,8 @@ hipError_t launch_agg_rows(const float* part, int64_t stride, int nown, int64_t 
                            float* out, hipStream_t st);
 hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool rev, int nrt,
                            float* diag, hipStream_t st);
+// ALiBi dm[h] = -sum over offsets |delta| diag_h[delta] (fixed order)
+hipError_t launch_agg_alibi(const float* diag, int H, int L, float* dm, hipStream_t st);
 hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int nbk, float* dbeta,
                          hipStream_t st);
 hipError_t launch_agg_txl(const float* prow, const float* pkv, const float* diag, const void* r,

@@ -27,6 +27,25 @@ hipError_t launch_t5_lut(const float* beta, int H, int L, int nb, float inv_scal
   return hipGetLastError();
 }
 
+// ALiBi: the bias of offset delta in y units (the kernels scale the LUT by s)
+__global__ void alibi_lut_kernel(const float* __restrict__ slopes, int H, int L, float inv_scale,
+                                 float* __restrict__ lut) {
+  const int n = 2 * L - 1;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)n * H) return;
+  const int h = (int)(idx / n);
+  const int delta = (int)(idx % n) - (L - 1);
+  lut[idx] = -slopes[h] * (float)(delta < 0 ? -delta : delta) * inv_scale;
+}
+
+hipError_t launch_alibi_lut(const float* slopes, int H, int L, float inv_scale, float* lut,
+                            hipStream_t stream) {
+  const int64_t total = (int64_t)(2 * L - 1) * H;
+  hipLaunchKernelGGL(alibi_lut_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     slopes, H, L, inv_scale, lut);
+  return hipGetLastError();
+}
+
 __global__ void index_map_kernel(int mech, int L, int span, int nrel, int txl_off, T5Map m,
                                  int32_t* __restrict__ out_a, int32_t* __restrict__ out_b) {
   const int x = blockIdx.x * blockDim.x + threadIdx.x;
@@ -34,6 +53,7 @@ __global__ void index_map_kernel(int mech, int L, int span, int nrel, int txl_of
   const int delta = x - (L - 1);
   int ra;
   if (mech == MECH_T5) ra = t5_bucket_dev(delta, m);
+  else if (mech == MECH_ALIBI) ra = delta < 0 ? -delta : delta;   // distinct per offset and sign
   else ra = row_side_row(mech, delta, span, nrel, txl_off);
   out_a[x] = ra;
   if (out_b) out_b[x] = p2c_row(delta, span);

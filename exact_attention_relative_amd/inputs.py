@@ -16,7 +16,9 @@ Recipe (the pages publish no shapes; the workloads below stand in for their
     w_m = 10000^(-2m/512), m < 256, at every table offset delta, and
     W_r [512, H d] ~ N(0, 1/512); head h takes columns h d .. h d + d - 1;
   * DeBERTa Kr = P W_r^k and Qr = P W_r^q with P [2k, d] ~ N(0, table_std^2) and
-    W_r^{k,q} [d, d] ~ N(0, 1/d) (row-vector convention).
+    W_r^{k,q} [d, d] ~ N(0, 1/d) (row-vector convention);
+  * ALiBi slopes m_h = 2^(-8 (h + 1) / H), the original geometric sequence (no draw;
+    parity variants scale them by 1 + 4 table_std).
   The projections are input preparation, done in float64 and rounded to the input
   dtype; the attention library takes r, Kr, Qr as given.
 """
@@ -129,6 +131,11 @@ def make_case(mech: str, B: int, H: int, L: int, d: int, *, dtype: str = "bf16",
         tables["kr"] = round_bf16(kr) if dtype == "bf16" else kr
         tables["qr"] = round_bf16(qr) if dtype == "bf16" else qr
         raw.update(P=P, w_q=wq, w_k=wk)
+    elif mech == "alibi":
+        # the geometric per-head slopes 2^(-8 (h + 1) / H) of the original ALiBi recipe
+        tables["slopes"] = np.array([2.0 ** (-8.0 * (h + 1) / H) for h in range(H)], dtype=np.float32)
+        if table_std is not None:   # parity variants: larger, head-varied slopes
+            tables["slopes"] = tables["slopes"] * np.float32(1.0 + 4.0 * table_std)
     else:
         raise ValueError(mech)
     params = dict(mech=mech, head_dim=d, window_left=wl, window_right=wr,

@@ -14,6 +14,7 @@ SLOTS = {
     "shaw": {"rel_a": "w"},
     "txl": {"rel_a": "r", "bias_a": "u", "bias_b": "v"},
     "deberta": {"rel_a": "kr", "rel_b": "qr"},
+    "alibi": {"bias_a": "slopes"},
 }
 # gradient slot of each table
 GRAD_SLOTS = {"rel_a": "drel_a", "rel_b": "drel_b", "bias_a": "dbias_a", "bias_b": "dbias_b"}
@@ -43,7 +44,7 @@ def to_device(case: dict, device="cuda") -> dict:
     if case.get("dout") is not None:
         dev["dout"] = tensor_from_f32(case["dout"], dt, device)
     for slot, name in SLOTS[mech].items():
-        fp32_table = name in ("beta", "u", "v")
+        fp32_table = name in ("beta", "u", "v", "slopes")
         dev[slot] = tensor_from_f32(case["tables"][name], "fp32" if fp32_table else dt, device)
     return dev
 

@@ -19,7 +19,12 @@
  *   RELPOS_DEBERTA  S_ij = s (q_i . k_j + q_i . Kr[clamp(i - j + k, 0, 2k - 1)]
  *                                       + k_j . Qr[clamp(j - i + k, 0, 2k - 1)])
  *                   (rel_a = Kr, rel_b = Qr)
+ *   RELPOS_ALIBI    B_ij = -m_h |i - j|                                  (bias_a = m)
  *
+ * ALiBi is a fifth, scalar-offset mechanism: the zicq.com explainer names it among the models
+ * the method suits (section on engineering trade-offs and where it applies); the authors do
+ * not list it.  Its term is the linear distance penalty with one slope per head, added
+ * unscaled like T5's bias.
  * T5 buckets follow the published T5 log-bucket map with an exact floor (bidirectional maps put
  * keys after the query in the upper half).  T-XL tables hold offsets 0..L-1 (row = i - j) when
  * the mask is causal (window_right == 0) and -(L-1)..L-1 (row = i - j + L - 1) otherwise.
@@ -34,6 +39,7 @@
  *   T5 beta  [heads, num_buckets] float        Shaw w     [2k+1, head_dim] dtype (shared)
  *   T-XL r   [heads, Nrel, head_dim] dtype     T-XL u, v  [heads, head_dim] float
  *   DeBERTa Kr, Qr [2k, head_dim] dtype (shared across heads)
+ *   ALiBi m  [heads] float
  * Every table gradient is float with the table's shape and is OVERWRITTEN (not accumulated).
  * Unused table / gradient slots must be NULL.
  *
@@ -57,7 +63,10 @@
 extern "C" {
 #endif
 
-typedef enum { RELPOS_T5 = 0, RELPOS_SHAW = 1, RELPOS_TXL = 2, RELPOS_DEBERTA = 3 } relpos_mech;
+typedef enum {
+  RELPOS_T5 = 0, RELPOS_SHAW = 1, RELPOS_TXL = 2, RELPOS_DEBERTA = 3,
+  RELPOS_ALIBI = 4  /* B_ij = -m_h |i - j| with per-head slopes m (bias_a, fp32 [H]), unscaled */
+} relpos_mech;
 typedef enum { RELPOS_BF16 = 0, RELPOS_FP32 = 1 } relpos_dtype;
 
 enum {
@@ -96,7 +105,8 @@ int relpos_attn_fwd(const relpos_desc* desc, const void* q, const void* k, const
 
 /* Backward from (q, k, v, o, lse, dout): writes dq, dk, dv and the table gradients
  * (T5: dbias_a = dbeta; Shaw: drel_a = dw; T-XL: drel_a = dr, dbias_a = du, dbias_b = dv;
- * DeBERTa: drel_a = dKr, drel_b = dQr).  Table gradients are reduced over every (batch, head)
+ * DeBERTa: drel_a = dKr, drel_b = dQr; ALiBi: dbias_a = dm, the slopes' gradient).
+ * Table gradients are reduced over every (batch, head)
  * that reads the table, in a fixed order, without atomics (offset-sharded partials followed
  * by a second aggregation pass).  bf16 only: dtype RELPOS_FP32 returns RELPOS_E_UNSUPPORTED
  * before any launch. */
@@ -108,7 +118,8 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
 
 /* Index maps the kernels use, computed on the device: for every offset delta = i - j in
  * [-(L-1), L-1], out_a[delta + L - 1] is the table row of that offset (T5 bucket, Shaw row,
- * T-XL row or -1 when the table has no such row, DeBERTa c2p row) and, for DeBERTa only,
+ * T-XL row or -1 when the table has no such row, DeBERTa c2p row, ALiBi distance |delta|)
+ * and, for DeBERTa only,
  * out_b[delta + L - 1] is the p2c row (out_b must be NULL otherwise).  Both int32 device
  * buffers of 2L - 1 entries. */
 int relpos_index_map(const relpos_desc* desc, int32_t* out_a, int32_t* out_b, void* stream);

@@ -8,7 +8,7 @@ from parity_util import MASKS, TOL, case, oracle_backward, rel_l2, to_np
 
 pytestmark = pytest.mark.gpu
 
-MECHS = ["t5", "shaw", "txl", "deberta"]
+MECHS = ["t5", "shaw", "txl", "deberta", "alibi"]
 
 
 def _run(c):

@@ -8,7 +8,7 @@ from oracle import relpos_oracle as orc
 
 pytestmark = pytest.mark.gpu
 
-MECHS = ["t5", "shaw", "txl", "deberta"]
+MECHS = ["t5", "shaw", "txl", "deberta", "alibi"]
 
 
 def _run_fwd(c):
@@ -104,7 +104,7 @@ def test_forward_deterministic(mech):
     ("t5", "none", dict(nb=32, md=128)), ("t5", "causal", dict(nb=32, md=1024)),
     ("t5", "none", dict(nb=32, md=1024)), ("t5", "none", dict(nb=16, md=40)),
     ("shaw", "none", {}), ("shaw", "causal", {}), ("txl", "none", {}), ("txl", "causal", {}),
-    ("deberta", "none", {}), ("deberta", "local", {})])
+    ("deberta", "none", {}), ("deberta", "local", {}), ("alibi", "none", {}), ("alibi", "causal", {})])
 def test_index_maps_bit_exact(mech, mask, extra):
     """Bucket / clamp rows of every offset |i - j| < L, computed by the library on the GPU."""
     import torch
@@ -122,7 +122,7 @@ def test_index_maps_bit_exact(mech, mask, extra):
     rows_i = np.where(deltas >= 0, deltas, 0)
     cols_j = rows_i - deltas
     maps = orc.index_maps(np.arange(L), L, p)
-    key = {"t5": "bucket", "shaw": "row", "txl": "row", "deberta": "c2p"}[mech]
+    key = {"t5": "bucket", "shaw": "row", "txl": "row", "deberta": "c2p", "alibi": "dist"}[mech]
     exp_a = maps[key][rows_i, cols_j]
     if mech == "txl":
         nrel = orc.txl_rows(L, p)

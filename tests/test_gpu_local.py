@@ -14,17 +14,17 @@ from oracle import relpos_oracle as orc
 pytestmark = pytest.mark.gpu
 
 SETTINGS = {"t5": dict(num_buckets=32, max_distance=1024), "shaw": dict(rel_span=256),
-            "deberta": dict(rel_span=512), "txl": {}}
+            "deberta": dict(rel_span=512), "txl": {}, "alibi": {}}
 
 
 @pytest.mark.parametrize("window", [(256, 256), (512, 0)])
-@pytest.mark.parametrize("mech", ["t5", "shaw", "deberta", "txl"])
+@pytest.mark.parametrize("mech", ["t5", "shaw", "deberta", "txl", "alibi"])
 def test_local_window_L8192(mech, window):
     import torch
     from exact_attention_relative_amd import runner
     from exact_attention_relative_amd.inputs import make_case
     c = make_case(mech, 1, 1, 8192, 64, dtype="bf16", window=window, seed=17,
-                  sub=orc.MECHS.index(mech), **SETTINGS[mech])
+                  sub=orc.ALL_MECHS.index(mech), **SETTINGS[mech])
     print(f"local {mech} window={window}", flush=True)
     desc = runner.desc_for(c)
     dev = runner.to_device(c)

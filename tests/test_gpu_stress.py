@@ -19,13 +19,13 @@ from oracle import relpos_oracle as orc
 pytestmark = pytest.mark.gpu
 
 SETTINGS = {"t5": dict(num_buckets=32, max_distance=1024), "shaw": dict(rel_span=256),
-            "deberta": dict(rel_span=512), "txl": {}}
+            "deberta": dict(rel_span=512), "txl": {}, "alibi": {}}
 
 
 def _case(mech, L):
     from exact_attention_relative_amd.inputs import make_case
     return make_case(mech, 1, 2, L, 64, dtype="bf16", window=(-1, -1), seed=L + 3,
-                     sub=orc.MECHS.index(mech), **SETTINGS[mech])
+                     sub=orc.ALL_MECHS.index(mech), **SETTINGS[mech])
 
 
 def _rows(L):
@@ -34,7 +34,7 @@ def _rows(L):
 
 
 @pytest.mark.parametrize("L", [16384, 32768])
-@pytest.mark.parametrize("mech", ["t5", "shaw", "deberta", "txl"])
+@pytest.mark.parametrize("mech", ["t5", "shaw", "deberta", "txl", "alibi"])
 def test_long_sequence(mech, L):
     import torch
     from exact_attention_relative_amd import runner

@@ -11,6 +11,7 @@ import pytest
 import torch
 
 from oracle import brute
+from oracle import projection as prj
 from oracle import relpos_oracle as orc
 from exact_attention_relative_amd.inputs import make_case
 
@@ -394,3 +395,50 @@ def test_bias_is_toeplitz_for_constant_rows():
         k[:] = k[:, :, :1, :]
         Bm = orc.bias_rows(p, q[0, 0], k[0, 0], tab, 0, np.arange(14))
         np.testing.assert_allclose(Bm[1:, 1:], Bm[:-1, :-1], rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------------------ projections
+
+def test_projection_matches_scalar_loops():
+    """Pin: the table projection and its gradients against pure-Python loops."""
+    rng = np.random.default_rng(5)
+    N, F, H, d = 5, 4, 3, 2
+    X = rng.standard_normal((N, F))
+    W = rng.standard_normal((F, H * d))
+    G = rng.standard_normal((H, N, d))
+    rel = prj.project(X, W, H, d)
+    dX, dW = prj.project_backward(X, W, G)
+    for h in range(H):
+        for n in range(N):
+            for c in range(d):
+                ref = sum(X[n][f] * W[f][h * d + c] for f in range(F))
+                assert abs(rel[h, n, c] - ref) < 1e-12
+    for f in range(F):
+        for col in range(H * d):
+            ref = sum(X[n][f] * G[col // d][n][col % d] for n in range(N))
+            assert abs(dW[f, col] - ref) < 1e-12
+    for n in range(N):
+        for f in range(F):
+            ref = sum(G[h][n][c] * W[f][h * d + c] for h in range(H) for c in range(d))
+            assert abs(dX[n, f] - ref) < 1e-12
+
+
+def test_projection_gradients_match_central_differences():
+    """Pin: dX and dW of loss = sum(rel * G) against central differences, h = 1e-6."""
+    rng = np.random.default_rng(6)
+    N, F, H, d = 4, 3, 2, 3
+    X = rng.standard_normal((N, F))
+    W = rng.standard_normal((F, H * d))
+    G = rng.standard_normal((H, N, d))
+    dX, dW = prj.project_backward(X, W, G)
+    h_ = 1e-6
+    for arr, grad in ((X, dX), (W, dW)):
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h_
+            lp = float(np.sum(prj.project(X, W, H, d) * G))
+            arr[idx] = old - h_
+            lm = float(np.sum(prj.project(X, W, H, d) * G))
+            arr[idx] = old
+            assert abs((lp - lm) / (2 * h_) - grad[idx]) < 1e-7
+

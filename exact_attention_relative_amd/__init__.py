@@ -25,7 +25,8 @@ RELPOS_E_WORKSPACE = -3
 RELPOS_E_LAUNCH = -4
 
 EXPORTED = ("relpos_attn_workspace_size", "relpos_attn_fwd", "relpos_attn_bwd",
-            "relpos_index_map", "relpos_profile_events", "relpos_status_string", "relpos_version")
+            "relpos_index_map", "relpos_profile_events", "relpos_status_string", "relpos_version",
+            "relpos_project_fwd", "relpos_project_workspace_size", "relpos_project_bwd")
 RELPOS_PROF_OFF, RELPOS_PROF_FWD, RELPOS_PROF_BWD_DQ, RELPOS_PROF_BWD_DKDV = 0, 1, 2, 3
 
 
@@ -37,6 +38,12 @@ class relpos_desc(ctypes.Structure):
                 ("rel_span", ctypes.c_int32), ("num_buckets", ctypes.c_int32),
                 ("max_distance", ctypes.c_int32), ("bidirectional", ctypes.c_int32),
                 ("scale", ctypes.c_float)]
+
+
+class relpos_proj_desc(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("rows", ctypes.c_int64),
+                ("in_features", ctypes.c_int64), ("heads", ctypes.c_int64),
+                ("head_dim", ctypes.c_int64)]
 
 
 class RelposError(RuntimeError):
@@ -72,6 +79,13 @@ def load_library(path: str | None = None):
     lib.relpos_profile_events.restype = i32
     lib.relpos_status_string.argtypes = [i32]
     lib.relpos_status_string.restype = ctypes.c_char_p
+    pp = ctypes.POINTER(relpos_proj_desc)
+    lib.relpos_project_fwd.argtypes = [pp, vp, vp, vp, vp]
+    lib.relpos_project_fwd.restype = i32
+    lib.relpos_project_workspace_size.argtypes = [pp, ctypes.POINTER(sz)]
+    lib.relpos_project_workspace_size.restype = i32
+    lib.relpos_project_bwd.argtypes = [pp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.relpos_project_bwd.restype = i32
     lib.relpos_version.argtypes = []
     lib.relpos_version.restype = i32
     if path is None:
@@ -86,6 +100,11 @@ def make_desc(mech, batch, heads, seqlen, head_dim=64, dtype="bf16", window=(-1,
                        int(batch), int(heads), int(seqlen), int(head_dim),
                        int(window[0]), int(window[1]), int(rel_span), int(num_buckets),
                        int(max_distance), 1 if bidirectional else 0, float(scale))
+
+
+def make_proj_desc(rows, in_features, heads, head_dim, dtype="bf16"):
+    return relpos_proj_desc(RELPOS_FP32 if dtype in ("fp32", RELPOS_FP32) else RELPOS_BF16,
+                            int(rows), int(in_features), int(heads), int(head_dim))
 
 
 def _ptr(t):
@@ -166,4 +185,31 @@ def relpos_profile_events(start_event, stop_event, kernel: int) -> int:
         return e.cuda_event
     st = load_library().relpos_profile_events(raw(start_event), raw(stop_event), int(kernel))
     _check(st, "relpos_profile_events")
+    return st
+
+
+def relpos_project_fwd(desc, X, W, rel, stream=None, check=True) -> int:
+    st = load_library().relpos_project_fwd(ctypes.byref(desc), _ptr(X), _ptr(W), _ptr(rel),
+                                           _stream(stream))
+    if check:
+        _check(st, "relpos_project_fwd")
+    return st
+
+
+def relpos_project_workspace_size(desc) -> int:
+    out = ctypes.c_size_t(0)
+    _check(load_library().relpos_project_workspace_size(ctypes.byref(desc), ctypes.byref(out)),
+           "relpos_project_workspace_size")
+    return out.value
+
+
+def relpos_project_bwd(desc, X, W, drel, dX, dW, workspace, workspace_bytes=None, stream=None,
+                       check=True) -> int:
+    wsb = workspace_bytes if workspace_bytes is not None else (
+        0 if workspace is None else workspace.numel() * workspace.element_size())
+    st = load_library().relpos_project_bwd(ctypes.byref(desc), _ptr(X), _ptr(W), _ptr(drel),
+                                           _ptr(dX), _ptr(dW), _ptr(workspace), wsb,
+                                           _stream(stream))
+    if check:
+        _check(st, "relpos_project_bwd")
     return st

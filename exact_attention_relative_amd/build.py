@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librelpos_attn.so")
-SOURCES = ["relpos_api.hip", "relpos_prep.hip", "relpos_fwd.hip", "relpos_bwd.hip", "relpos_agg.hip"]
+SOURCES = ["relpos_api.hip", "relpos_prep.hip", "relpos_fwd.hip", "relpos_bwd.hip", "relpos_agg.hip",
+           "relpos_proj.hip"]
 # measurement-only MFMA throughput probe, a library of its own
 PROBE_LIB = os.path.join(PKG, "librelpos_probe.so")
 PROBE_SOURCES = ["relpos_probe.hip"]

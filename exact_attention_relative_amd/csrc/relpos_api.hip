@@ -272,6 +272,33 @@ hipError_t timed(int which, hipStream_t st, F launch) {
   return e;
 }
 
+// ------------------------------------------------------------------ projections
+struct ProjPlan {
+  bool fp32;
+  int N, F, H, d, kslices;
+  size_t ws_bytes;
+};
+
+int make_proj_plan(const relpos_proj_desc* d, ProjPlan* p) {
+  if (!d) return RELPOS_E_INVALID;
+  if (d->dtype != RELPOS_BF16 && d->dtype != RELPOS_FP32) return RELPOS_E_INVALID;
+  if (d->rows < 0 || d->rows > (1 << 24)) return RELPOS_E_INVALID;
+  if (d->in_features < 8 || d->in_features > 65536 || d->in_features % 8) return RELPOS_E_INVALID;
+  if (d->heads < 1 || d->head_dim < 8 || d->head_dim % 8) return RELPOS_E_INVALID;
+  if (d->heads * d->head_dim > 65536) return RELPOS_E_INVALID;
+  p->fp32 = d->dtype == RELPOS_FP32;
+  p->N = (int)d->rows;
+  p->F = (int)d->in_features;
+  p->H = (int)d->heads;
+  p->d = (int)d->head_dim;
+  // enough workgroups for the dW product to fill the chip, each slice at least 512 rows
+  const int tiles = ((p->F + 63) / 64) * ((p->H * p->d + 63) / 64);
+  p->kslices = std::max(1, std::min(512 / tiles, (p->N + 511) / 512));
+  p->ws_bytes = p->kslices > 1
+                    ? align_up((size_t)p->kslices * p->F * p->H * p->d * sizeof(float)) : 0;
+  return RELPOS_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -469,6 +496,46 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
                            p.nrel, p.txl_off, p.scale, p.fp32, drel_a, dbias_a, dbias_b, s);
       break;
   }
+  return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
+}
+
+int relpos_project_fwd(const relpos_proj_desc* desc, const void* X, const void* W, void* rel,
+                       void* stream) {
+  ProjPlan p;
+  int st = make_proj_plan(desc, &p);
+  if (st != RELPOS_OK) return st;
+  if (p.N == 0) return RELPOS_OK;
+  for (const void* ptr : {X, W, (const void*)rel})
+    if (!ptr || !aligned16(ptr)) return RELPOS_E_INVALID;
+  hipError_t e = launch_project_fwd(X, W, rel, p.N, p.F, p.H, p.d, p.fp32, (hipStream_t)stream);
+  return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
+}
+
+int relpos_project_workspace_size(const relpos_proj_desc* desc, size_t* bytes) {
+  if (!bytes) return RELPOS_E_INVALID;
+  ProjPlan p;
+  int st = make_proj_plan(desc, &p);
+  if (st != RELPOS_OK) return st;
+  *bytes = p.ws_bytes;
+  return RELPOS_OK;
+}
+
+int relpos_project_bwd(const relpos_proj_desc* desc, const void* X, const void* W,
+                       const float* drel, float* dX, float* dW, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  ProjPlan p;
+  int st = make_proj_plan(desc, &p);
+  if (st != RELPOS_OK) return st;
+  if (!dX && !dW) return RELPOS_OK;
+  for (const void* ptr : {X, W, (const void*)drel})
+    if (p.N > 0 && (!ptr || !aligned16(ptr))) return RELPOS_E_INVALID;
+  if (dX && !aligned16(dX)) return RELPOS_E_INVALID;
+  if (dW && !aligned16(dW)) return RELPOS_E_INVALID;
+  if (dW && !X) return RELPOS_E_INVALID;
+  if (dW && p.ws_bytes && !ws_ok(workspace, workspace_bytes, p.ws_bytes))
+    return RELPOS_E_WORKSPACE;
+  hipError_t e = launch_project_bwd(X, W, drel, dX, dW, (float*)workspace, p.kslices, p.N, p.F,
+                                    p.H, p.d, p.fp32, (hipStream_t)stream);
   return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
 }
 

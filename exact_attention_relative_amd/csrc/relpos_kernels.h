@@ -128,6 +128,17 @@ hipError_t launch_agg_txl(const float* prow, const float* pkv, const float* diag
                           int off, float s, bool fp32, float* dr, float* du, float* dv,
                           hipStream_t st);
 
+// Relation-table projections: rel [H, N, d] = X [N, F] . W [F, H d] (dtype of X and W; rel
+// written in that dtype), and the backward dX = dY . W^T [N, F], dW = X^T . dY [F, H d] (fp32)
+// with dY(n, h d + c) = drel[h][n][c].  dW sums `kslices` fp32 slices of the n range held in
+// `partials` ([kslices, F, H d]; unused when kslices == 1).  Either of dX / dW may be null.
+// F, d multiples of 8; pointers 16-byte aligned.
+hipError_t launch_project_fwd(const void* X, const void* W, void* rel, int N, int F, int H, int d,
+                              bool fp32, hipStream_t st);
+hipError_t launch_project_bwd(const void* X, const void* W, const float* drel, float* dX, float* dW,
+                              float* partials, int kslices, int N, int F, int H, int d, bool fp32,
+                              hipStream_t st);
+
 // D_n = dO_n . O_n over rows of length 64
 hipError_t launch_dsum(const void* o, const void* dout, int64_t nrows, bool fp32, float* dsum,
                        hipStream_t stream);

@@ -145,6 +145,25 @@ def make_case(mech: str, B: int, H: int, L: int, d: int, *, dtype: str = "bf16",
                 dtype=dtype, shape=shp)
 
 
+def make_projection_case(N: int, F: int, H: int, d: int, *, dtype: str = "bf16",
+                         basis: str = "normal", seed: int = 0, sub: int | None = None) -> dict:
+    """Draw a relation-table projection workload: the basis X [N, F], the weight W [F, H d]
+    (both rounded to bf16 when dtype is bf16) and an fp32 table gradient drel [H, N, d].
+
+    basis "sinusoid": the sin | cos features of offsets -(N-1)//2 .. N-1-(N-1)//2 (T-XL's R,
+    values in [-1, 1], F even); "normal": N(0, 0.02^2) rows (a learned DeBERTa P)."""
+    rng = _rng(seed, sub)
+    if basis == "sinusoid":
+        offsets = np.arange(N, dtype=np.int64) - (N - 1) // 2
+        X = sinusoid(offsets, F).astype(np.float32)
+        X = round_bf16(X) if dtype == "bf16" else X
+    else:
+        X = _normal(rng, (N, F), 0.02, dtype)
+    W = _normal(rng, (F, H * d), 1.0 / math.sqrt(F), dtype)
+    drel = rng.standard_normal((H, N, d), dtype=np.float32) * np.float32(1e-3)
+    return dict(X=np.ascontiguousarray(X), W=W, drel=drel, shape=(N, F, H, d), dtype=dtype)
+
+
 def make_config(name: str, **overrides) -> dict:
     cfg = dict(CONFIGS[name])
     cfg.update(overrides)

@@ -124,6 +124,41 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
  * buffers of 2L - 1 entries. */
 int relpos_index_map(const relpos_desc* desc, int32_t* out_a, int32_t* out_b, void* stream);
 
+/* Relation-table projections.  The T-XL table r and the DeBERTa tables Kr, Qr are projections
+ * of a position basis in the original mechanisms (T-XL: r = R W_r, R the sinusoid features of
+ * every offset; DeBERTa: Kr = P W_r^k and Qr = P W_r^q); the zicq.com explainer's section on
+ * reusing query-key relation products covers these "basis times weight" terms.  With X the basis
+ * [N, F] and W [F, H d] (head h owns columns h d .. h d + d - 1):
+ *
+ *   relpos_project_fwd   rel[h][n][c] = sum_f X[n][f] W[f][h d + c]        -> [H, N, d], dtype
+ *   relpos_project_bwd   dX[n][f]     = sum_{h,c} drel[h][n][c] W[f][h d + c]   [N, F] float
+ *                        dW[f][h d+c] = sum_n X[n][f] drel[h][n][c]             [F, H d] float
+ *
+ * rel has exactly the layout relpos_attn_fwd reads for rel_a / rel_b (T-XL: H heads, N = Nrel;
+ * DeBERTa: H = 1, N = 2k), and drel the layout relpos_attn_bwd writes for drel_a / drel_b, so the
+ * projection chains with the attention calls without copies.  Products run on the matrix cores
+ * with fp32 accumulation; fp32 operands are split into two bf16 parts (three products), giving
+ * close to fp32 accuracy.  dW is reduced over n in fixed slices, in a fixed order (deterministic);
+ * the slices' partial sums live in the workspace (relpos_project_workspace_size; may be 0).
+ * Either of dX / dW may be NULL (not computed; T-XL's R is fixed, so dX is usually not needed).
+ * Outputs are OVERWRITTEN.  Requirements: 0 <= N <= 2^24, 8 <= F <= 65536 and 8 <= d with F, d
+ * multiples of 8, H d <= 65536; every pointer 16-byte aligned, the workspace 256-byte aligned.
+ * Ownership, streams and errors as for the attention calls. */
+typedef struct relpos_proj_desc {
+  int32_t dtype;        /* relpos_dtype of X, W and rel */
+  int64_t rows;         /* N: basis rows */
+  int64_t in_features;  /* F */
+  int64_t heads;        /* H */
+  int64_t head_dim;     /* d */
+} relpos_proj_desc;
+
+int relpos_project_fwd(const relpos_proj_desc* desc, const void* X, const void* W, void* rel,
+                       void* stream);
+int relpos_project_workspace_size(const relpos_proj_desc* desc, size_t* bytes);
+int relpos_project_bwd(const relpos_proj_desc* desc, const void* X, const void* W,
+                       const float* drel, float* dX, float* dW, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* Profiling hook for benchmarks.  When `kernel` is RELPOS_PROF_FWD, RELPOS_PROF_BWD_DQ or
  * RELPOS_PROF_BWD_DKDV, later calls record `start_event` on their stream just before enqueueing
  * that kernel and `stop_event` just after it (both hipEvent_t created by the caller).

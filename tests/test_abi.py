@@ -130,3 +130,55 @@ def test_fwd_rejects_bad_pointers_without_launching():
 def test_missing_library_is_an_error(tmp_path):
     with pytest.raises(RuntimeError):
         ear.load_library(str(tmp_path / "nope.so"))
+
+
+# ------------------------------------------------------------------------ projections
+def _proj_ws(desc):
+    out = ctypes.c_size_t(0)
+    st = ear.load_library().relpos_project_workspace_size(ctypes.byref(desc), ctypes.byref(out))
+    return st, out.value
+
+
+@pytest.mark.parametrize("kw", [dict(rows=-1), dict(rows=(1 << 24) + 1), dict(in_features=12),
+                                dict(in_features=0), dict(heads=0), dict(head_dim=4),
+                                dict(head_dim=12), dict(heads=2048, head_dim=64),
+                                dict(dtype=3)])
+def test_projection_invalid_descriptors(kw):
+    base = dict(rows=100, in_features=64, heads=2, head_dim=64)
+    base.update(kw)
+    raw_dtype = base.pop("dtype", None)
+    desc = ear.make_proj_desc(**base)
+    if raw_dtype is not None:
+        desc.dtype = raw_dtype
+    assert _proj_ws(desc)[0] == ear.RELPOS_E_INVALID
+
+
+def test_projection_workspace_sizes():
+    # short bases need no slices; the T-XL basis of L = 8192 (16383 offsets, d_model 512) is
+    # reduced over 8 slices of [512, 512] fp32 partials
+    assert _proj_ws(ear.make_proj_desc(300, 64, 1, 64)) == (0, 0)
+    assert _proj_ws(ear.make_proj_desc(0, 64, 1, 64)) == (0, 0)
+    assert _proj_ws(ear.make_proj_desc(16383, 512, 8, 64)) == (0, 8 * 512 * 512 * 4)
+    assert _proj_ws(ear.make_proj_desc(1024, 64, 1, 64)) == (0, 2 * 64 * 64 * 4)
+
+
+def test_projection_rejects_bad_pointers_without_launching():
+    lib = ear.load_library()
+    buf = ctypes.create_string_buffer(1 << 16)
+    base = (ctypes.addressof(buf) + 255) & ~255
+    desc = ear.make_proj_desc(100, 64, 1, 64)
+    assert lib.relpos_project_fwd(ctypes.byref(desc), None, base, base, None) == ear.RELPOS_E_INVALID
+    assert lib.relpos_project_fwd(ctypes.byref(desc), base, base + 8, base, None) == ear.RELPOS_E_INVALID
+    assert lib.relpos_project_bwd(ctypes.byref(desc), base, base, None, base, base, None, 0,
+                                  None) == ear.RELPOS_E_INVALID
+    assert lib.relpos_project_bwd(ctypes.byref(desc), base, base, base, base + 4, None, None, 0,
+                                  None) == ear.RELPOS_E_INVALID
+    # nothing requested, or nothing to project: success without a launch
+    assert lib.relpos_project_bwd(ctypes.byref(desc), base, base, base, None, None, None, 0,
+                                  None) == ear.RELPOS_OK
+    empty = ear.make_proj_desc(0, 64, 1, 64)
+    assert lib.relpos_project_fwd(ctypes.byref(empty), None, None, None, None) == ear.RELPOS_OK
+    # dW of a long basis needs the slice workspace
+    big = ear.make_proj_desc(16383, 512, 8, 64)
+    assert lib.relpos_project_bwd(ctypes.byref(big), base, base, base, None, base, base, 16,
+                                  None) == ear.RELPOS_E_WORKSPACE

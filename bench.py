@@ -96,7 +96,7 @@ def kernel_source_sha():
     """Hash of every kernel source file: counters taken on other sources are stale."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".h")) and not f.startswith("relpos_probe"):
+        if f.endswith((".hip", ".h")) and not f.startswith(("relpos_probe", "relpos_proj")):
             h.update(f.encode())
             with open(os.path.join(CSRC, f), "rb") as fh:
                 h.update(fh.read())
@@ -417,6 +417,71 @@ def run_stress(torch, lengths, reps=10, windows=None):
     return out
 
 
+PROJ_SHAPES = (("txl_L8192_causal", 8192, 512, 8, 64, "sinusoid", 0),
+               ("txl_L8192_full", 16383, 512, 8, 64, "sinusoid", None),
+               ("deberta_span512", 1024, 64, 2, 64, "normal", None))
+
+
+def run_projections(torch, reps=20, per=20):
+    """The relation-table projections around the attention calls (T-XL r = R W_r; DeBERTa
+    Kr | Qr = P [W_r^k | W_r^q]) at the long-context shapes: forward, dW alone (T-XL's R is
+    fixed) and dX + dW, bf16 and fp32 operands; per call, the median over `reps` replays
+    of a graph of `per` calls."""
+    import exact_attention_relative_amd as ear
+    from exact_attention_relative_amd.inputs import make_projection_case
+    from exact_attention_relative_amd.runner import tensor_from_f32
+    out = []
+    for name, N, F, H, d, basis, first in PROJ_SHAPES:
+        for dt in ("bf16", "fp32"):
+            c = make_projection_case(N, F, H, d, dtype=dt, basis=basis, first_offset=first, seed=1)
+            X, W = tensor_from_f32(c["X"], dt), tensor_from_f32(c["W"], dt)
+            drel = tensor_from_f32(c["drel"], "fp32")
+            desc = ear.make_proj_desc(N, F, H, d, dtype=dt)
+            rel = torch.empty((H, N, d), device="cuda",
+                              dtype=torch.bfloat16 if dt == "bf16" else torch.float32)
+            dX = torch.empty((N, F), device="cuda")
+            dW = torch.empty((F, H * d), device="cuda")
+            n = ear.relpos_project_workspace_size(desc)
+            ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+            calls = {"fwd": lambda: ear.relpos_project_fwd(desc, X, W, rel),
+                     "bwd_dW": lambda: ear.relpos_project_bwd(desc, X, W, drel, None, dW, ws, n),
+                     "bwd_dX_dW": lambda: ear.relpos_project_bwd(desc, X, W, drel, dX, dW, ws, n)}
+            e = 2 if dt == "bf16" else 4
+            flops = {"fwd": 2.0 * N * F * H * d, "bwd_dW": 2.0 * N * F * H * d,
+                     "bwd_dX_dW": 4.0 * N * F * H * d}
+            nbytes = {"fwd": e * (N * F + F * H * d + N * H * d),
+                      "bwd_dW": e * (N * F) + 4 * (N * H * d + F * H * d),
+                      "bwd_dX_dW": e * (N * F + F * H * d) + 4 * (N * H * d + N * F + F * H * d)}
+            row = {"shape": name, "N": N, "F": F, "H": H, "d": d, "dtype": dt,
+                   "dW_slices": max(1, n // (F * H * d * 4))}
+            for k, fn in calls.items():
+                # device time only: `per` calls back to back in a captured graph, so host
+                # marshalling between calls does not idle the GPU inside the timed region
+                fn()
+                torch.cuda.synchronize()
+                graph = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(graph):
+                    for _ in range(per):
+                        fn()
+                graph.replay()
+                torch.cuda.synchronize()
+                evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                       for _ in range(reps)]
+                for a, b in evs:
+                    a.record(); graph.replay(); b.record()
+                torch.cuda.synchronize()
+                ms = float(np.median([a.elapsed_time(b) for a, b in evs])) / per
+                del graph
+                row[k + "_us"] = ms * 1e3
+                row[k + "_TFLOPs"] = flops[k] / ms / 1e9
+                row[k + "_GBs"] = nbytes[k] / ms / 1e6
+            print(f"[proj] {name} {dt}: fwd {row['fwd_us']:.1f} us, dW {row['bwd_dW_us']:.1f} us, "
+                  f"dX+dW {row['bwd_dX_dW_us']:.1f} us", file=sys.stderr, flush=True)
+            out.append(row)
+            del X, W, drel, rel, dX, dW, ws
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -427,6 +492,8 @@ def main():
                     help="length stress at a fixed token budget (prints its own JSON line)")
     ap.add_argument("--windows", default=None, metavar="W1,W2,...",
                     help="symmetric local windows at L=8192 (prints its own JSON line)")
+    ap.add_argument("--projections", action="store_true",
+                    help="time the relation-table projections (prints its own JSON line)")
     ap.add_argument("--only", default=None,
                     help="comma-separated mechanisms (profiling runs; the value then covers only them)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -467,6 +534,9 @@ def main():
         wins = [int(x) for x in args.windows.split(",") if x]
         print(json.dumps({"windows": run_stress(torch, [], windows=wins), "L": 8192, "B": 4,
                           "heads": 8, "head_dim": 64, "dtype": "bf16", "data": "synthetic"}))
+        return
+    if args.projections:
+        print(json.dumps({"projections": run_projections(torch), "data": "synthetic"}))
         return
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * 2**20 // 4

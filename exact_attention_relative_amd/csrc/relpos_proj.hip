@@ -8,8 +8,10 @@
 //   C(m, n) = sum_k A(m, k) B(n, k),   each index i of an operand at (i / split) s + (i % split) c
 //
 // (the head split turns the [H, N, d] table into the [N, H d] matrix the products need).
-// 64 x 64 output tile per workgroup (4 waves, one 32 x 32 MFMA block each), k in steps of 32
-// staged through LDS with both operands stored k-contiguous.  fp32 operands are split into
+// 128 x 128 output tile per workgroup (4 waves, 2 x 2 MFMA blocks of 32 x 32 each), k in steps of 64
+// staged through LDS with both operands stored k-contiguous (operands contiguous along m or n
+// are transposed on the way in); the next step's global loads are in flight during the
+// current step's products.  fp32 operands are split into
 // (hi, lo) bf16 planes (three products per MFMA step).  The long-k product (dW) is split over
 // k into fixed slices whose fp32 partials are summed in slice order: deterministic.
 #include "relpos_device.h"
@@ -19,23 +21,36 @@ namespace relpos {
 
 namespace {
 
-constexpr int PT = 64;        // output tile
-constexpr int PK = 32;        // k step
-constexpr int PSTR = PK + 8;  // LDS row stride (elements)
+constexpr int PT = 128;       // output tile (PT x PT per workgroup)
+constexpr int SUB = 64;       // staging sub-tile rows
+constexpr int PK = 64;        // k step
+constexpr int PSTR = PK + 16; // LDS row stride (elements): 40 words, conflict-free with the swizzle
 constexpr int NOSPLIT = 1 << 30;
 
-// index i -> (i / split) * s + (i % split) * c
+// index i -> (i / split) * s + (i % split) * c, for 0 <= i < 2^31.  The quotient uses a
+// multiply-shift divider fixed on the host (q = (umulhi(i, mul) + i) >> shift with
+// shift = ceil(log2 split), mul = floor(2^32 (2^shift - split) / split) + 1), exact for every
+// i < 2^31 and split <= 2^30: address arithmetic stays off the slow integer-division path.
 struct Ix {
   int64_t c, s;
-  int split;
+  uint32_t split, mul, shift;
 };
+Ix mk(int64_t c, int64_t s, uint32_t split) {
+  uint32_t l = 0;
+  while ((1ull << l) < split) ++l;
+  const uint64_t mul = (((1ull << 32) * ((1ull << l) - split)) / split) + 1;
+  return Ix{c, s, split, (uint32_t)mul, l};
+}
 __device__ __forceinline__ int64_t ix(const Ix& m, int i) {
-  return (int64_t)(i / m.split) * m.s + (int64_t)(i % m.split) * m.c;
+  const uint32_t u = (uint32_t)i;
+  const uint32_t q = (__umulhi(u, m.mul) + u) >> m.shift;
+  const uint32_t r = u - q * m.split;
+  return (int64_t)q * m.s + (int64_t)r * m.c;
 }
 
 // An operand in tile coordinates: A as (m, k), B as (n, k).  Exactly one of the two indices
 // has unit stride within its split (k_contig: along k), and 8-element groups along it never
-// cross a split (splits and tile extents along it are multiples of 8).
+// cross a split (splits and extents along it are multiples of 8).
 struct Operand {
   const void* p;
   Ix row, k;
@@ -53,86 +68,217 @@ struct GemmArgs {
   int64_t c_slice;
 };
 
-// 8 elements from element offset e, consecutive in memory, as floats
-__device__ __forceinline__ void load8v(const Operand& o, int64_t e, float x[8]) {
-  if (o.fp32) load8((const float*)o.p + e, x);
-  else load8((const uint16_t*)o.p + e, x);
+// 8 consecutive elements as loaded (no conversion yet)
+template <bool F32> struct Raw;
+template <> struct Raw<false> { u32x4 v; };
+template <> struct Raw<true> { f32x4 a, b; };
+
+template <bool F32>
+__device__ __forceinline__ void raw_load(const void* p, int64_t e, Raw<F32>& r) {
+  if constexpr (F32) {
+    r.a = *(const f32x4*)((const float*)p + e);
+    r.b = *(const f32x4*)((const float*)p + e + 4);
+  } else {
+    r.v = *(const u32x4*)((const uint16_t*)p + e);
+  }
 }
 
-// Stage a [64 tile rows] x [32 k] tile into NP planes of [64][PSTR] bf16, k contiguous.
-template <int NP>
-__device__ __forceinline__ void stage_tile(uint16_t* t, const Operand& o, int row0, int nrows,
-                                           int k0, int kend) {
+// element i of a raw group as a float, zero when the group was out of range
+template <bool F32>
+__device__ __forceinline__ float raw_elem(const Raw<F32>& r, bool ok, int i) {
+  float x;
+  if constexpr (F32) x = i < 4 ? r.a[i] : r.b[i - 4];
+  else x = __uint_as_float((i & 1) ? (r.v[i >> 1] & 0xFFFF0000u) : (r.v[i >> 1] << 16));
+  return ok ? x : 0.f;
+}
+
+// One thread's share (two groups of 8) of a [64 tile rows] x [64 k] operand sub-tile.
+// k-contiguous (KC): row tid / 4, k 16 (tid % 4) + 8 h.  Otherwise: k row 2 (tid / 8) + h,
+// tile rows 8 (tid % 8) .. +7 (8 lanes cover 64 contiguous elements of one k row).
+// Every load is issued unconditionally (an out-of-range group reads the operand's first 8
+// elements and is masked to zero later), so all of a step's loads are in flight together.
+template <bool F32, bool KC>
+__device__ __forceinline__ void load_stage(const Operand& o, int row0, int nrows, int k0, int kend,
+                                           Raw<F32> r[2], bool ok[2]) {
   const int tid = threadIdx.x;
-  const int plane = PT * PSTR;
-  float x[8];
-  if (o.k_contig) {
-    // thread -> (row, 8 consecutive k)
-    const int row = tid >> 2, kk = (tid & 3) * 8;
-    if (row0 + row < nrows && k0 + kk < kend) {
-      load8v(o, ix(o.row, row0 + row) + ix(o.k, k0 + kk), x);
-    } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+  for (int h = 0; h < 2; ++h) {
+    int row, k;
+    if constexpr (KC) { row = row0 + (tid >> 2); k = k0 + (tid & 3) * 16 + 8 * h; }
+    else { row = row0 + (tid & 7) * 8; k = k0 + 2 * (tid >> 3) + h; }
+    ok[h] = row < nrows && k < kend;
+    raw_load<F32>(o.p, ok[h] ? ix(o.row, row) + ix(o.k, k) : 0, r[h]);
+  }
+}
+
+// Registers -> 64 rows of an LDS tile [NP planes][PT rows][PSTR], k contiguous.  The
+// transposing path writes k pairs as 32-bit words; rows are visited in the order i ^ (tid % 8)
+// so that the 64 lanes of a store hit distinct banks.  bf16 operands are copied bit for bit
+// (their low plane is zero).
+template <int NP, bool F32, bool KC>
+__device__ __forceinline__ void store_stage(uint16_t* t, const Raw<F32> r[2], const bool ok[2]) {
+  const int tid = threadIdx.x;
+  constexpr int plane = PT * PSTR;   // t points at row 0 or 64 of a [PT][PSTR] plane
+  if constexpr (KC) {
+    const int row = tid >> 2, kk = (tid & 3) * 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint16_t* dst = t + row * PSTR + kk + 8 * h;
+      if constexpr (!F32) {
+        u32x4 v = r[h].v;
+        if (!ok[h]) v = u32x4{0u, 0u, 0u, 0u};
+        *(u32x4*)dst = v;
+        if constexpr (NP == 2) *(u32x4*)(dst + plane) = u32x4{0u, 0u, 0u, 0u};
+      } else {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = raw_elem<F32>(r[h], ok[h], i);
+        Op<NP> v = op_from_f32<NP>(x);
+#pragma unroll
+        for (int p = 0; p < NP; ++p) *(bf16x8*)(dst + p * plane) = v.p[p];
+      }
     }
-    Op<NP> v = op_from_f32<NP>(x);
-#pragma unroll
-    for (int p = 0; p < NP; ++p) *(bf16x8*)(t + p * plane + row * PSTR + kk) = v.p[p];
   } else {
-    // thread -> (k, 8 consecutive rows), scattered into the k-contiguous layout
-    const int kk = tid >> 3, row = (tid & 7) * 8;
-    if (k0 + kk < kend && row0 + row < nrows) {
-      load8v(o, ix(o.row, row0 + row) + ix(o.k, k0 + kk), x);
-    } else {
+    const int mg = tid & 7, kp = tid >> 3;
+    // words[p][u]: plane p of the k pair (k row 2 kp, 2 kp + 1) of tile row 8 mg + u
+    uint32_t words[NP][8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.f;
+    for (int u = 0; u < 8; ++u) {
+      if constexpr (!F32) {
+        const uint32_t a = __float_as_uint(raw_elem<F32>(r[0], ok[0], u)) >> 16;
+        const uint32_t b = __float_as_uint(raw_elem<F32>(r[1], ok[1], u)) & 0xFFFF0000u;
+        words[0][u] = a | b;
+        if constexpr (NP == 2) words[1][u] = 0u;
+      } else {
+        uint16_t ha, la, hb, lb;
+        split_bf16(raw_elem<F32>(r[0], ok[0], u), ha, la);
+        split_bf16(raw_elem<F32>(r[1], ok[1], u), hb, lb);
+        words[0][u] = (uint32_t)ha | ((uint32_t)hb << 16);
+        if constexpr (NP == 2) words[1][u] = (uint32_t)la | ((uint32_t)lb << 16);
+      }
+    }
+    // words[p][j] <- words[p][j ^ mg] by three conditional butterfly stages
+#pragma unroll
+    for (int b = 1; b < 8; b <<= 1) {
+      const bool sw = (mg & b) != 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (u & b) continue;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          const uint32_t lo = words[p][u], hi = words[p][u | b];
+          words[p][u] = sw ? hi : lo;
+          words[p][u | b] = sw ? lo : hi;
+        }
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint16_t h, l;
-      split_bf16(x[i], h, l);
-      t[(row + i) * PSTR + kk] = h;
-      if constexpr (NP == 2) t[plane + (row + i) * PSTR + kk] = l;
+    for (int j = 0; j < 8; ++j) {
+      const int e = (8 * mg + (j ^ mg)) * PSTR + 2 * kp;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) *(uint32_t*)(t + p * plane + e) = words[p][j];
     }
   }
 }
 
-template <int NP>
+// AF / BF: operand A / B is fp32 (else bf16); AKC / BKC: k-contiguous.  fp32 anywhere means
+// two bf16 planes (hi, lo) per operand and three products per step.
+template <bool AF, bool AKC, bool BF, bool BKC>
 __global__ __launch_bounds__(256) void proj_gemm_kernel(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t as[NP * PT * PSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t bs[NP * PT * PSTR];
+  constexpr int NP = (AF || BF) ? 2 : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t stage_lds[2 * NP * PT * PSTR];
+  uint16_t* as = stage_lds;
+  uint16_t* bs = stage_lds + NP * PT * PSTR;
   const int tiles_n = (g.N + PT - 1) / PT;
   const int tiles = ((g.M + PT - 1) / PT) * tiles_n;
-  const int slice = blockIdx.x / tiles;
-  const int tile = blockIdx.x % tiles;
+  // consecutive ids (the n tiles of one m tile, which share A rows) run on one XCD's L2
+  const int id = xcd_remap(blockIdx.x, gridDim.x);
+  const int slice = id / tiles;
+  const int tile = id % tiles;
   const int m0 = (tile / tiles_n) * PT, n0 = (tile % tiles_n) * PT;
   const int kper = ((g.K + g.kslices - 1) / g.kslices + PK - 1) / PK * PK;
   const int kb = slice * kper, ke = min(g.K, kb + kper);
   const int w = wave_index(), lane = threadIdx.x & 63, l32 = lane & 31, kh = lane >> 5;
-  const int wm = w >> 1, wn = w & 1;
-  f32x16 acc = {};
-  for (int k0 = kb; k0 < ke; k0 += PK) {
-    __syncthreads();
-    stage_tile<NP>(as, g.a, m0, g.M, k0, ke);
-    stage_tile<NP>(bs, g.b, n0, g.N, k0, ke);
-    __syncthreads();
+  const int wm = w >> 1, wn = w & 1;   // wave block: rows 64 wm.., cols 64 wn.. (2 x 2 MFMA blocks)
+  f32x16 acc[2][2] = {};
+  Raw<AF> ra[2][2];
+  Raw<BF> rb[2][2];
+  bool oka[2][2], okb[2][2];
+  if (kb < ke) {
 #pragma unroll
-    for (int kk = 0; kk < PK; kk += 16) {
-      Op<NP> ao = op_from_lds<NP>(as, PT * PSTR, (wm * 32 + l32) * PSTR + kk + 8 * kh);
-      Op<NP> bo = op_from_lds<NP>(bs, PT * PSTR, (wn * 32 + l32) * PSTR + kk + 8 * kh);
-      mma<NP>(acc, ao, bo);   // acc[m][n], n on the lanes
+    for (int u = 0; u < 2; ++u) {
+      load_stage<AF, AKC>(g.a, m0 + SUB * u, g.M, kb, ke, ra[u], oka[u]);
+      load_stage<BF, BKC>(g.b, n0 + SUB * u, g.N, kb, ke, rb[u], okb[u]);
     }
   }
-  // acc register r: m = wm 32 + 8 (r / 4) + 4 kh + r % 4, n = wn 32 + l32
-  const int n = n0 + wn * 32 + l32;
-  if (n >= g.N) return;
+  for (int k0 = kb; k0 < ke; k0 += PK) {
+    __syncthreads();
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int m = m0 + wm * 32 + 8 * (r >> 2) + 4 * kh + (r & 3);
-    if (m >= g.M) continue;
-    const int64_t o = ix(g.cm, m) + ix(g.cn, n);
-    if (g.c16) g.c16[o] = f2bf_bits(acc[r]);
-    else g.c[(int64_t)slice * g.c_slice + o] = acc[r];
+    for (int u = 0; u < 2; ++u) {
+      store_stage<NP, AF, AKC>(as + SUB * u * PSTR, ra[u], oka[u]);
+      store_stage<NP, BF, BKC>(bs + SUB * u * PSTR, rb[u], okb[u]);
+    }
+    __syncthreads();
+    if (k0 + PK < ke) {   // next step's loads fly while this step's products run
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        load_stage<AF, AKC>(g.a, m0 + SUB * u, g.M, k0 + PK, ke, ra[u], oka[u]);
+        load_stage<BF, BKC>(g.b, n0 + SUB * u, g.N, k0 + PK, ke, rb[u], okb[u]);
+      }
+    }
+#pragma unroll
+    for (int kk = 0; kk < PK; kk += 16) {
+      Op<NP> ao[2], bo[2];
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        ao[b] = op_from_lds<NP>(as, PT * PSTR, (wm * 64 + 32 * b + l32) * PSTR + kk + 8 * kh);
+        bo[b] = op_from_lds<NP>(bs, PT * PSTR, (wn * 64 + 32 * b + l32) * PSTR + kk + 8 * kh);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma<NP>(acc[i][j], ao[i], bo[j]);   // n on the lanes
+    }
+  }
+  // Epilogue through LDS, one 32-column half of each wave's 64 x 64 block at a time: the
+  // accumulators (acc[i][j] register r: m = 64 wm + 32 i + 8 (r / 4) + 4 kh + r % 4,
+  // n = 64 wn + 32 j + l32) go to a wave-private [64][CSTR] fp32 patch, and each lane then
+  // writes 8 consecutive n of one row with vector stores (C is contiguous along n in 8-groups).
+  constexpr int CSTR = 40;
+  static_assert(4 * 64 * CSTR * 4 <= 2 * PT * PSTR * 2, "C patch fits the A / B staging area");
+  float* patch = reinterpret_cast<float*>(as) + w * 64 * CSTR;   // as and bs are contiguous
+  float* cbase = g.c16 ? nullptr : g.c + (int64_t)slice * g.c_slice;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    __syncthreads();   // previous readers of the staging area are done
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        patch[(32 * i + 8 * (r >> 2) + 4 * kh + (r & 3)) * CSTR + l32] = acc[i][j][r];
+    __syncthreads();
+    const int q = lane & 3, n = n0 + wn * 64 + 32 * j + 8 * q;
+    if (n >= g.N) continue;
+    const int64_t on = ix(g.cn, n);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int row = (lane >> 2) + 16 * t, m = m0 + wm * 64 + row;
+      if (m >= g.M) continue;
+      const float* src = patch + row * CSTR + 8 * q;
+      const f32x4 lo = *(const f32x4*)src, hi = *(const f32x4*)(src + 4);
+      const int64_t o = ix(g.cm, m) + on;
+      if (g.c16) {
+        u32x4 v;
+        v[0] = pack_bf16x2(lo[0], lo[1]);
+        v[1] = pack_bf16x2(lo[2], lo[3]);
+        v[2] = pack_bf16x2(hi[0], hi[1]);
+        v[3] = pack_bf16x2(hi[2], hi[3]);
+        *(u32x4*)(g.c16 + o) = v;
+      } else {
+        *(f32x4*)(cbase + o) = lo;
+        *(f32x4*)(cbase + o + 4) = hi;
+      }
+    }
   }
 }
 
@@ -146,12 +292,25 @@ __global__ void slice_sum_kernel(const float* __restrict__ part, int S, int64_t 
   out[i] = acc;
 }
 
+template <bool AF, bool AKC, bool BF, bool BKC>
+void launch_gemm(const GemmArgs& g, dim3 grid, hipStream_t st) {
+  hipLaunchKernelGGL((proj_gemm_kernel<AF, AKC, BF, BKC>), grid, dim3(256), 0, st, g);
+}
+
+// The three products: forward (A k-contiguous, B not; one dtype), dX (both k-contiguous, A
+// fp32) and dW (neither, B fp32).
 hipError_t run_gemm(GemmArgs g, hipStream_t st) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   const int tiles = ((g.M + PT - 1) / PT) * ((g.N + PT - 1) / PT);
   const dim3 grid((unsigned)(tiles * g.kslices));
-  if (g.a.fp32 || g.b.fp32) hipLaunchKernelGGL(proj_gemm_kernel<2>, grid, dim3(256), 0, st, g);
-  else hipLaunchKernelGGL(proj_gemm_kernel<1>, grid, dim3(256), 0, st, g);
+  const bool af = g.a.fp32, ak = g.a.k_contig, bf = g.b.fp32, bk = g.b.k_contig;
+  if (!af && ak && !bf && !bk) launch_gemm<false, true, false, false>(g, grid, st);
+  else if (af && ak && bf && !bk) launch_gemm<true, true, true, false>(g, grid, st);
+  else if (af && ak && !bf && bk) launch_gemm<true, true, false, true>(g, grid, st);
+  else if (af && ak && bf && bk) launch_gemm<true, true, true, true>(g, grid, st);
+  else if (!af && !ak && bf && !bk) launch_gemm<false, false, true, false>(g, grid, st);
+  else if (af && !ak && bf && !bk) launch_gemm<true, false, true, false>(g, grid, st);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -161,11 +320,11 @@ hipError_t run_gemm(GemmArgs g, hipStream_t st) {
 hipError_t launch_project_fwd(const void* X, const void* W, void* rel, int N, int F, int H, int d,
                               bool fp32, hipStream_t st) {
   GemmArgs g{};
-  g.a = Operand{X, Ix{F, 0, NOSPLIT}, Ix{1, 0, NOSPLIT}, fp32, true};        // X[n_row][f]
-  g.b = Operand{W, Ix{1, 0, NOSPLIT}, Ix{H * d, 0, NOSPLIT}, fp32, false};   // W[f][col], n = col
+  g.a = Operand{X, mk(F, 0, NOSPLIT), mk(1, 0, NOSPLIT), fp32, true};        // X[n_row][f]
+  g.b = Operand{W, mk(1, 0, NOSPLIT), mk(H * d, 0, NOSPLIT), fp32, false};   // W[f][col], n = col
   if (fp32) g.c = (float*)rel; else g.c16 = (uint16_t*)rel;
-  g.cm = Ix{d, 0, NOSPLIT};                       // rel[col / d][n_row][col % d]
-  g.cn = Ix{1, (int64_t)N * d, d};
+  g.cm = mk(d, 0, NOSPLIT);                       // rel[col / d][n_row][col % d]
+  g.cn = mk(1, (int64_t)N * d, d);
   g.M = N; g.N = H * d; g.K = F; g.kslices = 1;
   return run_gemm(g, st);
 }
@@ -177,22 +336,22 @@ hipError_t launch_project_bwd(const void* X, const void* W, const float* drel, f
   hipError_t e = hipSuccess;
   if (dX) {
     GemmArgs g{};
-    g.a = Operand{drel, Ix{d, 0, NOSPLIT}, Ix{1, (int64_t)N * d, d}, true, true};   // m = n_row, k = col
-    g.b = Operand{W, Ix{H * d, 0, NOSPLIT}, Ix{1, 0, NOSPLIT}, fp32, true};          // n = f, k = col
+    g.a = Operand{drel, mk(d, 0, NOSPLIT), mk(1, (int64_t)N * d, d), true, true};   // m = n_row, k = col
+    g.b = Operand{W, mk(H * d, 0, NOSPLIT), mk(1, 0, NOSPLIT), fp32, true};          // n = f, k = col
     g.c = dX;
-    g.cm = Ix{F, 0, NOSPLIT};
-    g.cn = Ix{1, 0, NOSPLIT};
+    g.cm = mk(F, 0, NOSPLIT);
+    g.cn = mk(1, 0, NOSPLIT);
     g.M = N; g.N = F; g.K = H * d; g.kslices = 1;
     e = run_gemm(g, st);
     if (e != hipSuccess) return e;
   }
   if (dW) {
     GemmArgs g{};
-    g.a = Operand{X, Ix{1, 0, NOSPLIT}, Ix{F, 0, NOSPLIT}, fp32, false};             // m = f, k = n_row
-    g.b = Operand{drel, Ix{1, (int64_t)N * d, d}, Ix{d, 0, NOSPLIT}, true, false};   // n = col, k = n_row
+    g.a = Operand{X, mk(1, 0, NOSPLIT), mk(F, 0, NOSPLIT), fp32, false};             // m = f, k = n_row
+    g.b = Operand{drel, mk(1, (int64_t)N * d, d), mk(d, 0, NOSPLIT), true, false};   // n = col, k = n_row
     g.c = kslices > 1 ? partials : dW;
-    g.cm = Ix{H * d, 0, NOSPLIT};
-    g.cn = Ix{1, 0, NOSPLIT};
+    g.cm = mk(H * d, 0, NOSPLIT);
+    g.cn = mk(1, 0, NOSPLIT);
     g.M = F; g.N = H * d; g.K = N; g.kslices = kslices; g.c_slice = (int64_t)F * H * d;
     e = run_gemm(g, st);
     if (e != hipSuccess || kslices <= 1) return e;

@@ -146,15 +146,18 @@ def make_case(mech: str, B: int, H: int, L: int, d: int, *, dtype: str = "bf16",
 
 
 def make_projection_case(N: int, F: int, H: int, d: int, *, dtype: str = "bf16",
-                         basis: str = "normal", seed: int = 0, sub: int | None = None) -> dict:
+                         basis: str = "normal", first_offset: int | None = None, seed: int = 0,
+                         sub: int | None = None) -> dict:
     """Draw a relation-table projection workload: the basis X [N, F], the weight W [F, H d]
     (both rounded to bf16 when dtype is bf16) and an fp32 table gradient drel [H, N, d].
 
-    basis "sinusoid": the sin | cos features of offsets -(N-1)//2 .. N-1-(N-1)//2 (T-XL's R,
-    values in [-1, 1], F even); "normal": N(0, 0.02^2) rows (a learned DeBERTa P)."""
+    basis "sinusoid": the sin | cos features of N consecutive offsets from `first_offset`
+    (default -(N-1)//2, the full span; 0 for the causal table), T-XL's R with values in
+    [-1, 1] and F even; "normal": N(0, 0.02^2) rows (a learned DeBERTa P)."""
     rng = _rng(seed, sub)
     if basis == "sinusoid":
-        offsets = np.arange(N, dtype=np.int64) - (N - 1) // 2
+        start = -((N - 1) // 2) if first_offset is None else first_offset
+        offsets = np.arange(N, dtype=np.int64) + start
         X = sinusoid(offsets, F).astype(np.float32)
         X = round_bf16(X) if dtype == "bf16" else X
     else:

@@ -136,7 +136,10 @@ int relpos_index_map(const relpos_desc* desc, int32_t* out_a, int32_t* out_b, vo
  *
  * rel has exactly the layout relpos_attn_fwd reads for rel_a / rel_b (T-XL: H heads, N = Nrel;
  * DeBERTa: H = 1, N = 2k), and drel the layout relpos_attn_bwd writes for drel_a / drel_b, so the
- * projection chains with the attention calls without copies.  Products run on the matrix cores
+ * projection chains with the attention calls without copies.  DeBERTa's two tables come from one
+ * call with W = [W_r^k | W_r^q] as two heads (Kr = rel[0], Qr = rel[1]); when relpos_attn_bwd
+ * writes drel_a and drel_b into the two halves of one [2, 2k, d] buffer, one backward call
+ * gives dP summed over both projections and [dW_r^k | dW_r^q].  Products run on the matrix cores
  * with fp32 accumulation; fp32 operands are split into two bf16 parts (three products), giving
  * close to fp32 accuracy.  dW is reduced over n in fixed slices, in a fixed order (deterministic);
  * the slices' partial sums live in the workspace (relpos_project_workspace_size; may be 0).

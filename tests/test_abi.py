@@ -155,10 +155,10 @@ def test_projection_invalid_descriptors(kw):
 
 def test_projection_workspace_sizes():
     # short bases need no slices; the T-XL basis of L = 8192 (16383 offsets, d_model 512) is
-    # reduced over 8 slices of [512, 512] fp32 partials
+    # reduced over 16 slices of [512, 512] fp32 partials
     assert _proj_ws(ear.make_proj_desc(300, 64, 1, 64)) == (0, 0)
     assert _proj_ws(ear.make_proj_desc(0, 64, 1, 64)) == (0, 0)
-    assert _proj_ws(ear.make_proj_desc(16383, 512, 8, 64)) == (0, 8 * 512 * 512 * 4)
+    assert _proj_ws(ear.make_proj_desc(16383, 512, 8, 64)) == (0, 16 * 512 * 512 * 4)
     assert _proj_ws(ear.make_proj_desc(1024, 64, 1, 64)) == (0, 2 * 64 * 64 * 4)
 
 

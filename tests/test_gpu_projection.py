@@ -10,9 +10,10 @@ follow from the arithmetic, element by element, with A = the same products over 
   operand), about 2^-16 A, plus fp32 accumulation: |got - ref| <= 1e-4 A.
 
 Shapes: a ragged one (N, F, H d not multiples of the 64-wide tiles, d = 40 splitting heads
-inside a tile), the DeBERTa table basis (2k = 1024 rows, F = 512, one shared head), the T-XL
-basis of L = 8192 (16383 offsets, sinusoid features of width 512, 8 heads of 64), a long
-basis reduced over many dW slices, and a single row."""
+inside a tile); the DeBERTa bases of spans 256 and 512 (2k rows of width d = 64, with W_r^k and
+W_r^q side by side as two heads, so one call gives Kr and Qr); the T-XL bases of L = 8192
+(sinusoid features of width 512, 8 heads of 64), causal (8192 offsets) and full-span (16383);
+a long basis reduced over many dW slices; and a single row."""
 
 import numpy as np
 import pytest
@@ -23,19 +24,21 @@ from oracle import projection as prj
 pytestmark = pytest.mark.gpu
 
 SHAPES = {
-    "ragged": ((300, 136, 3, 40), "normal"),
-    "deberta_2k1024": ((1024, 512, 1, 64), "normal"),
-    "txl_L8192": ((16383, 512, 8, 64), "sinusoid"),
-    "long_slices": ((5000, 64, 1, 64), "normal"),
-    "one_row": ((1, 8, 1, 8), "normal"),
+    "ragged": ((300, 136, 3, 40), "normal", None),
+    "deberta_span256": ((512, 64, 2, 64), "normal", None),
+    "deberta_span512": ((1024, 64, 2, 64), "normal", None),
+    "txl_L8192_causal": ((8192, 512, 8, 64), "sinusoid", 0),
+    "txl_L8192_full": ((16383, 512, 8, 64), "sinusoid", None),
+    "long_slices": ((5000, 64, 1, 64), "normal", None),
+    "one_row": ((1, 8, 1, 8), "normal", None),
 }
 
 
 def _case(name, dtype, seed=5):
     from exact_attention_relative_amd.inputs import make_projection_case
-    (N, F, H, d), basis = SHAPES[name]
-    return make_projection_case(N, F, H, d, dtype=dtype, basis=basis, seed=seed,
-                                sub=list(SHAPES).index(name))
+    (N, F, H, d), basis, first = SHAPES[name]
+    return make_projection_case(N, F, H, d, dtype=dtype, basis=basis, first_offset=first,
+                                seed=seed, sub=list(SHAPES).index(name))
 
 
 def _dev(c):
@@ -103,7 +106,7 @@ def test_project_backward(name, dtype):
 def test_project_backward_is_deterministic_and_grads_are_independent():
     """Repeated calls agree bit for bit; asking for dW alone or dX alone gives the same bits."""
     import torch
-    c = _case("txl_L8192", "bf16")
+    c = _case("txl_L8192_full", "bf16")
     X, W, drel = _dev(c)
     dX1, dW1 = _run_bwd(c, X, W, drel)
     dX2, dW2 = _run_bwd(c, X, W, drel)
@@ -164,4 +167,49 @@ def test_txl_projection_chained_with_attention():
     assert np.max(np.abs(to_np(o) - O_ref)) <= tol["o"]
     _, _, _, gref = orc.backward(p, c["q"], c["k"], c["v"], tab, c["dout"])
     _, dW_ref = prj.project_backward(pc["X"], pc["W"], gref["r"])
+    assert rel_l2(to_np(dW), dW_ref) <= tol["grad"], rel_l2(to_np(dW), dW_ref)
+
+
+def test_deberta_projection_chained_with_attention():
+    """Kr | Qr = P [W_r^k | W_r^q] in one call (two heads) feed the DeBERTa attention as rel_a,
+    rel_b; its table gradients, written into the two halves of one [2, 2k, d] buffer, give dP
+    (summed over both projections) and [dW_r^k | dW_r^q] in one backward call.  Checked against
+    the oracle at L = 512, span 128, B = 1, H = 2."""
+    import torch
+    import exact_attention_relative_amd as ear
+    from exact_attention_relative_amd import runner
+    from exact_attention_relative_amd.inputs import make_case, make_projection_case
+    from oracle import relpos_oracle as orc
+    L, H, d, span = 512, 2, 64, 128
+    c = make_case("deberta", 1, H, L, d, dtype="bf16", seed=31, rel_span=span)
+    pc = make_projection_case(2 * span, d, 2, d, dtype="bf16", seed=32)
+    X, W, _ = _dev(pc)
+    pdesc = ear.make_proj_desc(2 * span, d, 2, d, dtype="bf16")
+    rel = torch.empty((2, 2 * span, d), dtype=torch.bfloat16, device="cuda")
+    ear.relpos_project_fwd(pdesc, X, W, rel)
+    desc = runner.desc_for(c)
+    dev = runner.to_device(c)
+    dev["rel_a"], dev["rel_b"] = rel[0], rel[1]
+    o, lse = runner.forward(desc, dev)
+    drel = torch.empty((2, 2 * span, d), device="cuda")
+    grads = runner.alloc_grads(desc, dev)
+    grads["drel_a"], grads["drel_b"] = drel[0], drel[1]
+    runner.backward(desc, dev, o, lse, grads=grads)
+    dP = torch.empty((2 * span, d), device="cuda")
+    dW = torch.empty((d, 2 * d), device="cuda")
+    n = ear.relpos_project_workspace_size(pdesc)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device="cuda")
+    ear.relpos_project_bwd(pdesc, X, W, drel, dP, dW, ws, n)
+    torch.cuda.synchronize()
+
+    p = orc.Params(**c["params"])
+    tab = {n_: t.astype(np.float64) for n_, t in c["tables"].items()}
+    kq = prj.project(pc["X"], pc["W"], 2, d)
+    tab["kr"], tab["qr"] = kq[0], kq[1]
+    O_ref, _ = orc.forward(p, c["q"], c["k"], c["v"], tab)
+    tol = TOL["bf16"]
+    assert np.max(np.abs(to_np(o) - O_ref)) <= tol["o"]
+    _, _, _, gref = orc.backward(p, c["q"], c["k"], c["v"], tab, c["dout"])
+    dP_ref, dW_ref = prj.project_backward(pc["X"], pc["W"], np.stack([gref["kr"], gref["qr"]]))
+    assert rel_l2(to_np(dP), dP_ref) <= tol["grad"], rel_l2(to_np(dP), dP_ref)
     assert rel_l2(to_np(dW), dW_ref) <= tol["grad"], rel_l2(to_np(dW), dW_ref)

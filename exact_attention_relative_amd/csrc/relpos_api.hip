@@ -291,9 +291,9 @@ int make_proj_plan(const relpos_proj_desc* d, ProjPlan* p) {
   p->F = (int)d->in_features;
   p->H = (int)d->heads;
   p->d = (int)d->head_dim;
-  // about one 128 x 128 dW tile-slice per compute unit, each slice at least 512 rows
+  // about one 128 x 128 dW tile-slice per compute unit, each slice at least one 64-row k step
   const int tiles = ((p->F + 127) / 128) * ((p->H * p->d + 127) / 128);
-  p->kslices = std::max(1, std::min(256 / tiles, (p->N + 511) / 512));
+  p->kslices = std::max(1, std::min(256 / tiles, (p->N + 63) / 64));
   p->ws_bytes = p->kslices > 1
                     ? align_up((size_t)p->kslices * p->F * p->H * p->d * sizeof(float)) : 0;
   return RELPOS_OK;

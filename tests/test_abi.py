@@ -154,12 +154,15 @@ def test_projection_invalid_descriptors(kw):
 
 
 def test_projection_workspace_sizes():
-    # short bases need no slices; the T-XL basis of L = 8192 (16383 offsets, d_model 512) is
-    # reduced over 16 slices of [512, 512] fp32 partials
-    assert _proj_ws(ear.make_proj_desc(300, 64, 1, 64)) == (0, 0)
+    # dW is split over the basis rows into at most 256 / (128 x 128 tiles) slices of at least 64
+    # rows; one slice needs no workspace.  The T-XL basis of L = 8192 (16383 offsets, d_model
+    # 512) uses 16 slices of [512, 512] fp32 partials.
+    assert _proj_ws(ear.make_proj_desc(64, 64, 1, 64)) == (0, 0)
     assert _proj_ws(ear.make_proj_desc(0, 64, 1, 64)) == (0, 0)
+    assert _proj_ws(ear.make_proj_desc(300, 64, 1, 64)) == (0, 5 * 64 * 64 * 4)
     assert _proj_ws(ear.make_proj_desc(16383, 512, 8, 64)) == (0, 16 * 512 * 512 * 4)
-    assert _proj_ws(ear.make_proj_desc(1024, 64, 1, 64)) == (0, 2 * 64 * 64 * 4)
+    assert _proj_ws(ear.make_proj_desc(1024, 64, 2, 64)) == (0, 16 * 64 * 128 * 4)
+    assert _proj_ws(ear.make_proj_desc(100000, 4096, 1, 4096)) == (0, 0)   # 1024 tiles
 
 
 def test_projection_rejects_bad_pointers_without_launching():

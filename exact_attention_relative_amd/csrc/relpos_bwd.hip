@@ -704,15 +704,30 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           }
         }
         float sums[2] = {0.f, 0.f};
+        if constexpr (MECH == MECH_TXL) {
+          // Lane l sums diagonal t = l (rows 0 .. min(l, 31)) and, for l < 32, diagonal
+          // t = l + 64 (rows l + 1 .. 31): one element of every row, rows in ascending order,
+          // so the 32 reads are independent and issue back to back (every T-XL tile runs this)
+          const float* gd = gs + (63 - lane);   // row n of diagonal l: gd[n * GS2 + n]
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int t = lane + 64 * half;
-          if (t < 96) {
-            // diagonal t runs through rows n with 0 <= n + 63 - t < 64
-            const int n0 = max(0, t - 63), n1 = min(WROWS - 1, t);
-            float sum = 0.f;
-            for (int n = n0; n <= n1; ++n) sum += gs[n * GS2 + n + 63 - t];
-            sums[half] = sum;
+          for (int n = 0; n < WROWS; ++n) {
+            const bool first = n <= lane;
+            const float v = gd[n * GS2 + n - (first ? 0 : 64)];
+            sums[0] += first ? v : 0.f;
+            sums[1] += first ? 0.f : v;
+          }
+        } else {
+          // T5 reaches this only on its multi-bucket tiles: the compact loop, same order
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int t = lane + 64 * half;
+            if (t < 96) {
+              // diagonal t runs through rows n with 0 <= n + 63 - t < 64
+              const int n0 = max(0, t - 63), n1 = min(WROWS - 1, t);
+              float sum = 0.f;
+              for (int n = n0; n <= n1; ++n) sum += gs[n * GS2 + n + 63 - t];
+              sums[half] = sum;
+            }
           }
         }
         wave_lds_sync();   // this wave's reads of its buffer precede the writes to its padding

@@ -45,15 +45,24 @@ __global__ void agg_diag_kernel(const float* __restrict__ pdiag, int B, int H, i
   if (idx >= (int64_t)H * n) return;
   const int h = (int)(idx / n);
   const int delta = (int)(idx % n) - (L - 1);
+  // owners q = b nb + p in ascending order, eight loads in flight, added in that order
+  constexpr int G = 8;
+  const int nq = B * nb;
   float acc = 0.f;
-  for (int b = 0; b < B; ++b)
-    for (int p = 0; p < nb; ++p) {
+  for (int q0 = 0; q0 < nq; q0 += G) {
+    float ld[G];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int q = q0 + u;
       int64_t own;
       int base;
-      owner_of(b, h, p, H, nb, rev != 0, L, own, base);
+      owner_of(q / nb, h, q % nb, H, nb, rev != 0, L, own, base);
       const int x = delta - base;
-      if (x >= 0 && x < nrt) acc += pdiag[own * nrt + x];
+      ld[u] = (q < nq && x >= 0 && x < nrt) ? pdiag[own * nrt + x] : 0.f;
     }
+#pragma unroll
+    for (int u = 0; u < G; ++u) acc += ld[u];
+  }
   diag[idx] = acc;
 }
 
@@ -74,22 +83,30 @@ __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict
   const int t = threadIdx.x;
   const int delta0 = row0 - off;
   f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
-  for (int b = 0; b < B; ++b)
-    for (int p = 0; p < nb; ++p) {
+  // owners q = b nb + p in ascending order, four at a time: the 16 loads of a group are in
+  // flight together, then added owner by owner (the order of the sum does not change)
+  constexpr int G = 4;
+  const int nq = B * nb;
+  for (int q0 = 0; q0 < nq; q0 += G) {
+    f32x4 ld[G][4];
+#pragma unroll
+    for (int u = 0; u < G; ++u) {
+      const int q = q0 + u, b = q / nb, p = q % nb;
       const int rbase = (wl >= 0 && wr >= 0) ? (max(0, 128 * p - wr) / 64) * 64 + 65 : 0;
       const int x0 = delta0 + 128 * p + 192 - rbase;
-      if (x0 + 63 < 0 || x0 >= nrt) continue;   // no row of this owner in the block
       const float* base = prow + (((int64_t)b * H + h) * nb + p) * (int64_t)nrt * kHeadDim;
-      f32x4 ld[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int e = 4 * t + 1024 * k, x = x0 + (e >> 6);
-        ld[k] = (x >= 0 && x < nrt) ? *(const f32x4*)(base + (int64_t)x * kHeadDim + (e & 63))
-                                    : f32x4{};
+        ld[u][k] = (q < nq && x >= 0 && x < nrt)
+                       ? *(const f32x4*)(base + (int64_t)x * kHeadDim + (e & 63)) : f32x4{};
       }
-#pragma unroll
-      for (int k = 0; k < 4; ++k) acc[k] += ld[k];
     }
+#pragma unroll
+    for (int u = 0; u < G; ++u)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc[k] += ld[u][k];
+  }
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int e = 4 * t + 1024 * k, row = row0 + (e >> 6), d = e & 63;

@@ -88,8 +88,17 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     pk.load(kg, jt0, L);
     pv.load(vg, jt0, L);
   }
+  // T-XL: the window slides by 64 offsets per key tile, so it is kept circular (rotation
+  // xrot) and only the 64 new table rows, their v.r values and the next keys' u.k are read
+  // per tile, into registers one tile ahead
+  TilePrefetch<T> pw;
+  float pvr = 0.f, puk = 0.f;
+  const T* rtab = nullptr;
+  if constexpr (MECH == MECH_TXL) rtab = (const T*)a.rel_a + (int64_t)h * sh.nrel * kHeadDim;
 
   for (int j0 = jt0; j0 <= j_hi; j0 += BOTH) {
+    // circular T-XL window: row x of step s sits at physical row (x - 64 s) mod 192
+    const int xrot = (MECH == MECH_TXL) ? ((3 - ((j0 - jt0) / BOTH) % 3) % 3) * BOTH : 0;
     // ---- tile classification (offset-aware scheduling) ----
     // wave tile offsets delta = i - j in [dlo, dhi]
     const int dlo = qw0 - (j0 + BOTH - 1), dhi = qw0 + WROWS - 1 - j0;
@@ -124,6 +133,13 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
         const int d = wg_dlo + x;   // window row x <-> delta = i0 - j0 - 63 + x
         vec_s[x] = (d > -L && d < L) ? a.lut[(int64_t)h * (2 * L - 1) + d + L - 1] : 0.f;
       }
+    } else if (MECH == MECH_TXL && j0 != jt0) {
+      // window rows 0..63 are new: physical rows xrot .. xrot + 63 (the rows that left)
+      pw.store_at(win, WIN * TSTR, xrot);
+      if (tid < BOTH) {
+        *win_vec(win, xrot + tid) = pvr;
+        kvec_s[tid] = puk;
+      }
     } else if (wg_general) {
       const int toff = sh.txl_off, nrel = sh.nrel;
       const T* tab = (const T*)a.rel_a;
@@ -136,10 +152,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
           const int r = row_side_row(MECH, wg_dlo + x, span, nrel, toff);
           *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
         }
+        if (tid < BOTH) kvec_s[tid] = (j0 + tid < L) ? a.uk[(int64_t)bh * L + j0 + tid] : 0.f;
       }
-    }
-    if constexpr (MECH == MECH_TXL) {
-      if (tid < BOTH) kvec_s[tid] = (j0 + tid < L) ? a.uk[(int64_t)bh * L + j0 + tid] : 0.f;
     }
     if constexpr (MECH == MECH_DEBERTA) {
       if (tid < 2 * BOTH) {
@@ -150,6 +164,17 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     if (j0 + BOTH <= j_hi) {
       pk.load(kg, j0 + BOTH, L);
       pv.load(vg, j0 + BOTH, L);
+      if constexpr (MECH == MECH_TXL) {
+        // next tile's new window rows: offsets wg_dlo - 64 .. wg_dlo - 1
+        const int r0 = wg_dlo - BOTH + sh.txl_off;
+        pw.load_range(rtab, r0, 0, sh.nrel);
+        pvr = 0.f;
+        puk = 0.f;
+        if (tid < BOTH) {
+          if (r0 + tid >= 0 && r0 + tid < sh.nrel) pvr = a.vr[(int64_t)h * sh.nrel + r0 + tid];
+          if (j0 + BOTH + tid < L) puk = a.uk[(int64_t)bh * L + j0 + BOTH + tid];
+        }
+      }
     }
     __syncthreads();
 
@@ -183,7 +208,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     } else if constexpr (MECH == MECH_TXL) {
       if (!wave_none) {
         f32x16 g[3];
-        row_products<NP, true>(g, win, WROWS * w, qop);
+        row_products<NP, true, true>(g, win, WROWS * w, qop, xrot);
         row_skew_add(sc, g, gs);
       }
     } else if constexpr (MECH == MECH_DEBERTA) {

@@ -62,9 +62,13 @@ struct TilePrefetch {
   static constexpr int NCH = sizeof(T) == 2 ? 2 : 4;   // 16-byte chunks per thread
   u32x4 v[NCH];
   __device__ __forceinline__ void load(const T* base, int row0, int nvalid) {
+    load_range(base, row0, 0, nvalid);
+  }
+  // rows row0 .. row0 + 63 of base, zero outside [lo, hi)
+  __device__ __forceinline__ void load_range(const T* base, int row0, int lo, int hi) {
     const int t = threadIdx.x;
     const int r = t >> 2, c = (t & 3) * 16;
-    if (row0 + r < nvalid) {
+    if (row0 + r >= lo && row0 + r < hi) {
       const u32x4* g = (const u32x4*)(base + (int64_t)(row0 + r) * kHeadDim + c);
 #pragma unroll
       for (int i = 0; i < NCH; ++i) v[i] = g[i];
@@ -73,15 +77,16 @@ struct TilePrefetch {
       for (int i = 0; i < NCH; ++i) v[i] = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  __device__ __forceinline__ void store(uint16_t* tile) const {
+  __device__ __forceinline__ void store(uint16_t* tile) const { store_at(tile, BOTH * TSTR, 0); }
+  // into rows p0 .. p0 + 63 of a tile of NP planes `plane` elements apart
+  __device__ __forceinline__ void store_at(uint16_t* tile, int plane, int p0) const {
     const int t = threadIdx.x;
-    const int e = (t >> 2) * TSTR + (t & 3) * 16;
+    const int e = (p0 + (t >> 2)) * TSTR + (t & 3) * 16;
     if constexpr (NCH == 2) {
       *(u32x4*)(tile + e) = v[0];
       *(u32x4*)(tile + e + 8) = v[1];
     } else {
       // fp32: split into (hi, lo) bf16 planes
-      const int plane = BOTH * TSTR;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         u32x4 h, l;
@@ -173,11 +178,18 @@ __device__ __forceinline__ void put_block(float* gs, const f32x16& g, int bb, in
   }
 }
 
+// Physical row of window row x in a circular window rotated by xrot (a multiple of 64).
+__device__ __forceinline__ int wrow(int x, int xrot) {
+  const int p = x + xrot;
+  return p >= WIN ? p - WIN : p;
+}
+
 // Row side, all three 32-offset blocks of products in registers (optionally + the per-row
-// value kept in the window's padding, win_vec).
-template <int NP, bool ADDVEC>
+// value kept in the window's padding, win_vec).  With ROT the window is circular: row x
+// sits at physical row wrow(x, xrot).
+template <int NP, bool ADDVEC, bool ROT = false>
 __device__ __forceinline__ void row_products(f32x16 g[3], const uint16_t* win, int w0,
-                                             const Op<NP> xop[4]) {
+                                             const Op<NP> xop[4], int xrot = 0) {
   const int lane = __lane_id();
   const int l32 = lane & 31, kh = lane >> 5;
 #pragma unroll
@@ -186,14 +198,16 @@ __device__ __forceinline__ void row_products(f32x16 g[3], const uint16_t* win, i
     if constexpr (ADDVEC) {   // the MFMA accumulates on top of the per-row value
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v4 = win_vec4(win, w0 + 32 * bb + 8 * q4 + 4 * kh);
+        const int x = w0 + 32 * bb + 8 * q4 + 4 * kh;
+        const f32x4 v4 = win_vec4(win, ROT ? wrow(x, xrot) : x);
 #pragma unroll
         for (int i = 0; i < 4; ++i) g[bb][4 * q4 + i] = v4[i];
       }
     }
+    const int prow = ROT ? wrow(w0 + 32 * bb + l32, xrot) : w0 + 32 * bb + l32;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
+      Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, prow * TSTR + 16 * c + 8 * kh);
       mma<NP>(g[bb], aop, xop[c]);
     }
   }

@@ -297,6 +297,9 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 
   for (int step = 0; step < nsteps; ++step) {
     const int b0 = bt0 + step * BOTH;
+    // query-side T-XL: the row window slides by 64 offsets per step and is kept circular,
+    // window row x of step s at physical row (x - 64 s) mod 192
+    const int xrot = V::GSREL ? ((3 - step % 3) % 3) * BOTH : 0;
     if constexpr (V::LIGHT) {
       if (step >= g_first && step <= g_last) continue;   // left to the general pass
     }
@@ -371,17 +374,27 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       }
     }
     // row side staged now when there is no column side
-    if constexpr (V::ROW && !V::COL) {
+    if constexpr (V::GSREL) {
+      // every T-XL tile is general; after the first step only rows 0..63 are new
+      auto rowfn = [&](int x) { return V::row_of(cwin - 63 + x, span, nrel, toff); };
+      if (step == 0) {
+        stage_window<T, NP>(win, trow, rowfn);
+        for (int x = tid; x < WIN; x += 256) {
+          const int r = rowfn(x);
+          *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+        }
+      } else {
+        stage_window_rows<T, NP>(win, trow, rowfn, 0, xrot);
+        if (tid < BOTH) {
+          const int r = rowfn(tid);
+          *win_vec(win, xrot + tid) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+        }
+      }
+    } else if constexpr (V::ROW && !V::COL) {
       if (wg_general) {
         stage_window<T, NP>(win, trow, [&](int x) {
           return V::row_of(cwin - 63 + x, span, nrel, toff);
         });
-        if constexpr (MECH == MECH_TXL) {
-          for (int x = tid; x < WIN; x += 256) {
-            const int r = V::row_of(cwin - 63 + x, span, nrel, toff);
-            *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
-          }
-        }
       }
     }
     // column side first (its window is replaced by the row-side window afterwards)
@@ -441,7 +454,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           lconst = (rcls == 1) ? rcA : rcB;
         } else if constexpr (V::ROW) {
           f32x16 g[3];
-          row_products<NP, MECH == MECH_TXL>(g, win, WROWS * w, xop);
+          if constexpr (V::GSREL) row_products<NP, true, true>(g, win, WROWS * w, xop, xrot);
+          else row_products<NP, MECH == MECH_TXL>(g, win, WROWS * w, xop);
           row_skew_add(sc, g, gs);
         }
       }
@@ -698,7 +712,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             Op<NP> eop = op_from_f32<NP>(e8);
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
-              Op<NP> wt = op_rows_tr<NP>(win, WIN * TSTR, TSTR, WROWS * w + 16 * cc, 32 * db);
+              Op<NP> wt = op_rows_tr_rot<NP>(win, WIN * TSTR, TSTR, WROWS * w + 16 * cc, 32 * db,
+                                             xrot);
               mma<NP>(gacc[db], wt, eop);
             }
           }

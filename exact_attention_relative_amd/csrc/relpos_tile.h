@@ -131,6 +131,26 @@ __device__ __forceinline__ void stage_window(uint16_t* win, const T* table, F ro
   }
 }
 
+// Window rows x0 .. x0 + 63 into physical rows p0 .. p0 + 63 (a circular window's new rows);
+// window row x reads table row rowfn(x) (< 0 = zero row).
+template <typename T, int NP, typename F>
+__device__ __forceinline__ void stage_window_rows(uint16_t* win, const T* table, F rowfn, int x0,
+                                                  int p0) {
+  const int t = threadIdx.x;
+  const int c = (t & 3) * 16;
+  const int plane = WIN * TSTR;
+  const int row = rowfn(x0 + (t >> 2));
+  const int e = (p0 + (t >> 2)) * TSTR + c;
+  if (row >= 0) {
+    const T* g = table + (int64_t)row * kHeadDim + c;
+    lds_store8<T>(win, plane, e, g);
+    lds_store8<T>(win, plane, e + 8, g + 8);
+  } else {
+    lds_zero8<NP>(win, plane, e);
+    lds_zero8<NP>(win, plane, e + 8);
+  }
+}
+
 // ---------------------------------------------------------------------------------------
 // Wave products.  `lane` operands: Op<NP> x[4] for the wave's 32 lane-side rows (lane % 32
 // = row, k = d chunk c: 16 c + 8 (lane / 32) .. + 7).
@@ -316,6 +336,19 @@ __device__ __forceinline__ Op<NP> op_rows_tr(const uint16_t* tile, int plane, in
   const int col = col0 + 16 * (g & 1) + 4 * (i & 3);
   const int r = row0 + 4 * kh + (i >> 2);
   return op_tr_from_lds<NP>(tile, plane, r * stride + col, (r + 8) * stride + col);
+}
+
+// op_rows_tr over a circular window rotated by xrot: each of the lane's two rows is wrapped.
+template <int NP>
+__device__ __forceinline__ Op<NP> op_rows_tr_rot(const uint16_t* tile, int plane, int stride,
+                                                 int row0, int col0, int xrot) {
+  const int lane = __lane_id();
+  const int g = lane >> 4, i = lane & 15;
+  const int kh = g >> 1;
+  const int col = col0 + 16 * (g & 1) + 4 * (i & 3);
+  const int r = row0 + 4 * kh + (i >> 2);
+  return op_tr_from_lds<NP>(tile, plane, wrow(r, xrot) * stride + col,
+                            wrow(r + 8, xrot) * stride + col);
 }
 
 // Operand from an fp32 register block in accumulator layout: 16 consecutive other-side

@@ -299,7 +299,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     const int b0 = bt0 + step * BOTH;
     // query-side T-XL: the row window slides by 64 offsets per step and is kept circular,
     // window row x of step s at physical row (x - 64 s) mod 192
-    const int xrot = V::GSREL ? ((3 - step % 3) % 3) * BOTH : 0;
+    // key-side T-XL: the column window slides up by 64 per step, row x at (x + 64 s) mod 192
+    const int xrot = V::GSREL ? ((3 - step % 3) % 3) * BOTH : V::TG1 ? (step % 3) * BOTH : 0;
     if constexpr (V::LIGHT) {
       if (step >= g_first && step <= g_last) continue;   // left to the general pass
     }
@@ -398,18 +399,30 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       }
     }
     // column side first (its window is replaced by the row-side window afterwards)
-    if constexpr (V::COL) {
+    if constexpr (V::TG1) {
+      // column window row x <-> mu = b - a = (b0 - A0 - 127) + x; after the first step only
+      // rows 128..191 are new, at physical rows wrow(128, xrot) ..
+      auto colfn = [&](int x) { return V::col_of((b0 - A0 - (BLANE - 1)) + x, span, nrel, toff); };
+      if (step == 0) {
+        stage_window<T, NP>(win, tcol, colfn);
+        for (int x = tid; x < WIN; x += 256) {
+          const int r = colfn(x);
+          *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+        }
+      } else {
+        const int p0 = wrow(2 * BOTH, xrot);
+        stage_window_rows<T, NP>(win, tcol, colfn, 2 * BOTH, p0);
+        if (tid < BOTH) {
+          const int r = colfn(2 * BOTH + tid);
+          *win_vec(win, p0 + tid) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+        }
+      }
+    } else if constexpr (V::COL) {
       if (wg_general) {
         stage_window<T, NP>(win, tcol, [&](int x) {
           // column window row x <-> mu = b - a = (b0 - A0 - 127) + x
           return V::col_of((b0 - A0 - (BLANE - 1)) + x, span, nrel, toff);
         });
-        if constexpr (MECH == MECH_TXL) {
-          for (int x = tid; x < WIN; x += 256) {
-            const int r = V::col_of((b0 - A0 - (BLANE - 1)) + x, span, nrel, toff);
-            *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
-          }
-        }
       }
     }
     // issue the next step's tile reads (after this step's staging reads have been consumed)
@@ -433,6 +446,9 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       if (!wave_none) {
         if (V::CLIP && ccls != 0) {
           add_other_vec(sc, ovec_s + (ccls == 1 ? 0 : 1), 2);
+        } else if constexpr (V::TG1) {
+          col_skew_add<NP, true, true>(sc, win, (BLANE - WROWS) - WROWS * w, 0, ys, gs, xrot);
+          col_skew_add<NP, true, true>(sc, win, (BLANE - WROWS) - WROWS * w, 1, ys, gs, xrot);
         } else if (V::COL && wg_general) {
           col_skew_add<NP, MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 0, ys, gs);
           col_skew_add<NP, MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 1, ys, gs);

@@ -258,11 +258,12 @@ __device__ __forceinline__ void row_skew_add(f32x16 s[2], const f32x16 g[3], flo
 }
 
 // Column side for other block ob: products Win[w0 + t'] . Y[32 ob + n] for t' in
-// [32 ob, 32 ob + 64), then s[ob][r] += H[y - 32 ob][y - n + 31].
+// [32 ob, 32 ob + 64), then s[ob][r] += H[y - 32 ob][y - n + 31].  With ROT the window is
+// circular (row x at physical row wrow(x, xrot)).
 // The other-side operands are re-read from the streamed tile (fewer live registers).
-template <int NP, bool ADDVEC>
+template <int NP, bool ADDVEC, bool ROT = false>
 __device__ __forceinline__ void col_skew_add(f32x16 s[2], const uint16_t* win, int w0, int ob,
-                                             const uint16_t* ytile, float* gs) {
+                                             const uint16_t* ytile, float* gs, int xrot = 0) {
   const int lane = __lane_id();
   const int l32 = lane & 31, kh = lane >> 5;
   f32x16 h[2];
@@ -273,14 +274,16 @@ __device__ __forceinline__ void col_skew_add(f32x16 s[2], const uint16_t* win, i
     if constexpr (ADDVEC) {   // the MFMA accumulates on top of the per-row value
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v4 = win_vec4(win, w0 + 32 * bb + 8 * q4 + 4 * kh);
+        const int x = w0 + 32 * bb + 8 * q4 + 4 * kh;
+        const f32x4 v4 = win_vec4(win, ROT ? wrow(x, xrot) : x);
 #pragma unroll
         for (int j = 0; j < 4; ++j) h[i][4 * q4 + j] = v4[j];
       }
     }
+    const int prow = ROT ? wrow(w0 + 32 * bb + l32, xrot) : w0 + 32 * bb + l32;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, (w0 + 32 * bb + l32) * TSTR + 16 * c + 8 * kh);
+      Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, prow * TSTR + 16 * c + 8 * kh);
       Op<NP> yop = op_from_lds<NP>(ytile, BOTH * TSTR, (32 * ob + l32) * TSTR + 16 * c + 8 * kh);
       mma<NP>(h[i], aop, yop);
     }

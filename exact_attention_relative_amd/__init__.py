@@ -37,7 +37,7 @@ class relpos_desc(ctypes.Structure):
                 ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
                 ("rel_span", ctypes.c_int32), ("num_buckets", ctypes.c_int32),
                 ("max_distance", ctypes.c_int32), ("bidirectional", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("max_partial_bytes", ctypes.c_int64)]
 
 
 class relpos_proj_desc(ctypes.Structure):
@@ -94,12 +94,14 @@ def load_library(path: str | None = None):
 
 
 def make_desc(mech, batch, heads, seqlen, head_dim=64, dtype="bf16", window=(-1, -1),
-              rel_span=0, num_buckets=32, max_distance=128, bidirectional=True, scale=0.0):
+              rel_span=0, num_buckets=32, max_distance=128, bidirectional=True, scale=0.0,
+              max_partial_bytes=0):
     return relpos_desc(MECH_IDS[mech] if isinstance(mech, str) else int(mech),
                        RELPOS_FP32 if dtype in ("fp32", RELPOS_FP32) else RELPOS_BF16,
                        int(batch), int(heads), int(seqlen), int(head_dim),
                        int(window[0]), int(window[1]), int(rel_span), int(num_buckets),
-                       int(max_distance), 1 if bidirectional else 0, float(scale))
+                       int(max_distance), 1 if bidirectional else 0, float(scale),
+                       int(max_partial_bytes))
 
 
 def make_proj_desc(rows, in_features, heads, head_dim, dtype="bf16"):

@@ -67,34 +67,47 @@ __global__ void agg_diag_kernel(const float* __restrict__ pdiag, int B, int H, i
 }
 
 // T-XL dr[h][row][d] = s (sum_{b, key block} part[own][x][d] + v_h[d] diag_h[delta]).
-// The partials come from the dK/dV pass: owner (b, h, p) holds offset delta at row
+// The partials come from the dK/dV pass: owner (slice, p) holds offset delta at row
 // x = delta + 128 p + 192 - rbase(p), where rbase = 0 for a full sweep and, with a two-sided
 // window, the first row of the owner's sweep (its first 64-row step + 65).  One workgroup
 // per (head, 64 consecutive offsets): for every owner the 64 rows it holds for those offsets
-// are one contiguous 16 KB block, read whole and added in a fixed owner order.
+// are one contiguous 16 KB block, read whole and added in a fixed owner order.  The slices are
+// processed in groups [s0, s0 + ns) (slot i nb + p for slice s0 + i): the first group starts
+// from zero, later groups from the raw sums already in dr, and the last applies v . diag and s.
 __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict__ prow,
                                                          const float* __restrict__ diag,
-                                                         const float* __restrict__ v, int B, int H,
+                                                         const float* __restrict__ v, int H,
                                                          int L, int nb, int nrt, int wl, int wr,
-                                                         int nrel, int off, float s,
+                                                         int nrel, int off, float s, int s0,
+                                                         int ns, int first, int last,
                                                          float* __restrict__ dr) {
   const int nch = (nrel + 63) / 64;
   const int h = blockIdx.x / nch, row0 = 64 * (blockIdx.x % nch);
   const int t = threadIdx.x;
   const int delta0 = row0 - off;
   f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
-  // owners q = b nb + p in ascending order, four at a time: the 16 loads of a group are in
+  if (!first) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int e = 4 * t + 1024 * k, row = row0 + (e >> 6);
+      if (row < nrel) acc[k] = *(const f32x4*)(dr + ((int64_t)h * nrel + row) * kHeadDim + (e & 63));
+    }
+  }
+  // this head's slices in the group: local i = i0, i0 + H, ...
+  const int i0 = ((h - s0) % H + H) % H;
+  const int nh = i0 < ns ? (ns - i0 + H - 1) / H : 0;
+  // owners q = j nb + p in ascending order, four at a time: the 16 loads of a group are in
   // flight together, then added owner by owner (the order of the sum does not change)
   constexpr int G = 4;
-  const int nq = B * nb;
+  const int nq = nh * nb;
   for (int q0 = 0; q0 < nq; q0 += G) {
     f32x4 ld[G][4];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const int q = q0 + u, b = q / nb, p = q % nb;
+      const int q = q0 + u, j = q / nb, p = q % nb;
       const int rbase = (wl >= 0 && wr >= 0) ? (max(0, 128 * p - wr) / 64) * 64 + 65 : 0;
       const int x0 = delta0 + 128 * p + 192 - rbase;
-      const float* base = prow + (((int64_t)b * H + h) * nb + p) * (int64_t)nrt * kHeadDim;
+      const float* base = prow + ((int64_t)(i0 + j * H) * nb + p) * (int64_t)nrt * kHeadDim;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int e = 4 * t + 1024 * k, x = x0 + (e >> 6);
@@ -111,12 +124,15 @@ __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict
   for (int k = 0; k < 4; ++k) {
     const int e = 4 * t + 1024 * k, row = row0 + (e >> 6), d = e & 63;
     if (row >= nrel) continue;
-    const int delta = row - off;
-    f32x4 o = f32x4{};
-    if (delta > -L && delta < L) {
-      const float dg = diag[(int64_t)h * (2 * L - 1) + delta + L - 1];
+    f32x4 o = acc[k];
+    if (last) {
+      const int delta = row - off;
+      o = f32x4{};
+      if (delta > -L && delta < L) {
+        const float dg = diag[(int64_t)h * (2 * L - 1) + delta + L - 1];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = fmaf(v[(int64_t)h * kHeadDim + d + i], dg, acc[k][i]) * s;
+        for (int i = 0; i < 4; ++i) o[i] = fmaf(v[(int64_t)h * kHeadDim + d + i], dg, acc[k][i]) * s;
+      }
     }
     *(f32x4*)(dr + ((int64_t)h * nrel + row) * kHeadDim + d) = o;
   }
@@ -222,13 +238,18 @@ hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int
   return hipGetLastError();
 }
 
-hipError_t launch_agg_txl(const float* prow, const float* pkv, const float* diag, const void* r,
-                          const float* v, int B, int H, int L, int nb, int nrk, int wl, int wr,
-                          int nrel, int off, float s, bool fp32, float* dr, float* du, float* dv,
-                          hipStream_t st) {
+hipError_t launch_agg_txl_dr(const float* prow, const float* diag, const float* v, int H, int L,
+                             int nb, int nrk, int wl, int wr, int nrel, int off, float s, int s0,
+                             int ns, bool first, bool last, float* dr, hipStream_t st) {
   const int nch = (nrel + 63) / 64;
-  hipLaunchKernelGGL(agg_txl_dr_kernel, dim3(H * nch), dim3(256), 0, st, prow, diag, v, B, H,
-                     L, nb, nrk, wl, wr, nrel, off, s, dr);
+  hipLaunchKernelGGL(agg_txl_dr_kernel, dim3(H * nch), dim3(256), 0, st, prow, diag, v, H, L, nb,
+                     nrk, wl, wr, nrel, off, s, s0, ns, first ? 1 : 0, last ? 1 : 0, dr);
+  return hipGetLastError();
+}
+
+hipError_t launch_agg_txl_uv(const float* pkv, const float* diag, const void* r, int B, int H,
+                             int L, int nb, int nrel, int off, float s, bool fp32, float* du,
+                             float* dv, hipStream_t st) {
   if (fp32)
     hipLaunchKernelGGL((agg_txl_dv_kernel<float>), dim3(H * kHeadDim), dim3(256), 0, st, diag,
                        (const float*)r, L, nrel, off, s, dv);

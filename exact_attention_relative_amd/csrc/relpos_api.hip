@@ -86,6 +86,7 @@ struct Plan {
   size_t off_part_q, off_part_k, off_part_qv, off_part_kv, off_diag, off_xpart, off_vpart, off_cab;
   int64_t part_q_stride, part_k_stride;
   int nb, nrt, owners;
+  int txl_group;   // T-XL key-side pass: (batch, head) slices per group
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -96,6 +97,7 @@ int make_plan(const relpos_desc* d, Plan* p) {
   if (d->batch < 0 || d->heads < 1 || d->seqlen < 0 || d->head_dim < 1) return RELPOS_E_INVALID;
   if (d->window_left < -1 || d->window_right < -1) return RELPOS_E_INVALID;
   if (!(isfinite(d->scale)) || d->scale < 0.f) return RELPOS_E_INVALID;
+  if (d->max_partial_bytes < 0) return RELPOS_E_INVALID;
   if (d->head_dim != kHeadDim) return RELPOS_E_UNSUPPORTED;
   if (d->seqlen > (1 << 28) || d->heads > (1 << 20) || d->batch > (1 << 20)) return RELPOS_E_UNSUPPORTED;
   const int64_t nqb = (d->seqlen + 127) / 128;
@@ -163,8 +165,17 @@ int make_plan(const relpos_desc* d, Plan* p) {
       rows_k = std::min<int64_t>(rows_k, wrows);
     }
     p->part_q_stride = rows_k * kHeadDim;
+    // the r partials of one group of slices must fit under the cap
+    const int64_t cap = d->max_partial_bytes > 0 ? d->max_partial_bytes : (int64_t)8 << 30;
+    const int64_t per_slice = (int64_t)p->nb * p->part_q_stride * (int64_t)sizeof(float);
+    const int64_t nbh = (int64_t)p->B * p->H;
+    p->txl_group = (int)std::max<int64_t>(1, std::min<int64_t>(nbh, cap / std::max<int64_t>(per_slice, 1)));
   }
-  if (p->part_q_stride) p->off_part_q = take(sizeof(float) * own * p->part_q_stride);
+  if (d->mech == RELPOS_TXL) {
+    p->off_part_q = take(sizeof(float) * (size_t)p->txl_group * p->nb * p->part_q_stride);
+  } else if (p->part_q_stride) {
+    p->off_part_q = take(sizeof(float) * own * p->part_q_stride);
+  }
   if (p->part_k_stride) p->off_part_k = take(sizeof(float) * own * p->part_k_stride);
   if (lut_path || d->mech == RELPOS_TXL) {
     p->off_part_qv = take(sizeof(float) * own * p->nrt);
@@ -317,7 +328,7 @@ int relpos_profile_events(void* start_event, void* stop_event, int kernel) {
   return RELPOS_OK;
 }
 
-int relpos_version(void) { return 100; }
+int relpos_version(void) { return 101; }
 
 const char* relpos_status_string(int status) {
   switch (status) {
@@ -466,11 +477,31 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
 
   e = timed(RELPOS_PROF_BWD_DQ, s, [&] { return launch_bwd_dq(a, p.fp32, s); });
   if (e != hipSuccess) return RELPOS_E_LAUNCH;
+  const bool rev = desc->window_right == 0;
+  float* diag = p.off_diag ? (float*)(ws + p.off_diag) : nullptr;
+  if (desc->mech == RELPOS_TXL) {
+    // the per-offset sums of the query-side pass, then the key-side pass group by group, each
+    // group's r partials folded into dr before the next group reuses them
+    e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, p.nrt, diag, s);
+    const int nbh = p.B * p.H, G = p.txl_group;
+    for (int s0 = 0; s0 < nbh && e == hipSuccess; s0 += G) {
+      a.bh0 = s0;
+      a.nbh = std::min(G, nbh - s0);
+      e = timed(RELPOS_PROF_BWD_DKDV, s, [&] { return launch_bwd_dkdv(a, p.fp32, s); });
+      if (e == hipSuccess)
+        e = launch_agg_txl_dr(a.part_q, diag, bias_b, p.H, p.L, p.nb,
+                              (int)(p.part_q_stride / kHeadDim), desc->window_left,
+                              desc->window_right, p.nrel, p.txl_off, p.scale, s0, a.nbh, s0 == 0,
+                              s0 + G >= nbh, drel_a, s);
+    }
+    if (e == hipSuccess)
+      e = launch_agg_txl_uv(a.part_kv, diag, rel_a, p.B, p.H, p.L, p.nb, p.nrel, p.txl_off,
+                            p.scale, p.fp32, dbias_a, dbias_b, s);
+    return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
+  }
   e = timed(RELPOS_PROF_BWD_DKDV, s, [&] { return launch_bwd_dkdv(a, p.fp32, s); });
   if (e != hipSuccess) return RELPOS_E_LAUNCH;
 
-  const bool rev = desc->window_right == 0;
-  float* diag = p.off_diag ? (float*)(ws + p.off_diag) : nullptr;
   switch (desc->mech) {
     case RELPOS_T5:
       e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, p.nrt, diag, s);
@@ -488,12 +519,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
       if (e == hipSuccess)
         e = launch_agg_rows(a.part_k, p.part_k_stride, p.owners, p.part_k_stride, p.scale, drel_b, s);
       break;
-    case RELPOS_TXL:
-      e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, p.nrt, diag, s);
-      if (e == hipSuccess)
-        e = launch_agg_txl(a.part_q, a.part_kv, diag, rel_a, bias_b, p.B, p.H, p.L, p.nb,
-                           (int)(p.part_q_stride / kHeadDim), desc->window_left, desc->window_right,
-                           p.nrel, p.txl_off, p.scale, p.fp32, drel_a, dbias_a, dbias_b, s);
+    default:
       break;
   }
   return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;

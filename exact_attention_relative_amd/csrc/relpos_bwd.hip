@@ -123,7 +123,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int nb = (L + BLANE - 1) / BLANE;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   int blk = bid % nb;
-  const int bh = bid / nb;
+  const int bh = a.bh0 + bid / nb;
   if (sh.wr == 0) blk = (DIR == 0) ? nb - 1 - blk : blk;   // causal: longest first
   const int h = bh % sh.H;
   const int A0 = blk * BLANE;
@@ -134,7 +134,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int span = sh.span, nrel = sh.nrel, toff = sh.txl_off;
   const float s = sh.scale, c = s * kLog2e;
   const int64_t bh_off = (int64_t)bh * L * kHeadDim;
-  const int64_t owner = (int64_t)bid;   // partial slot of this workgroup
+  const int64_t owner = (int64_t)a.bh0 * nb + bid;   // partial slot of this workgroup
 
   const T* xg = (const T*)(DIR == 0 ? a.q : a.k) + bh_off;
   const T* x2g = (const T*)(DIR == 0 ? a.dout : a.v) + bh_off;
@@ -228,7 +228,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   float* ptg = nullptr;
   const int nrk = (int)(a.part_q_stride / kHeadDim);
   const int rb = (sh.wl >= 0 && sh.wr >= 0) ? bt0 + 65 : 0;
-  if constexpr (V::TG1) ptg = a.part_q + owner * a.part_q_stride - (int64_t)rb * kHeadDim;
+  // (slots of the r partial count from the launch's first slice)
+  if constexpr (V::TG1) ptg = a.part_q + (int64_t)bid * a.part_q_stride - (int64_t)rb * kHeadDim;
   float* pdiag = nullptr;
   if constexpr (V::DIAG) pdiag = a.part_qv + owner * (int64_t)nrt;
 
@@ -999,7 +1000,8 @@ static void launch_one(const BwdArgs& a, dim3 grid, hipStream_t stream) {
 template <int DIR>
 static hipError_t launch_bwd_dir(const BwdArgs& a, hipStream_t stream) {
   const int nb = (a.sh.L + BLANE - 1) / BLANE;
-  const dim3 grid((unsigned)(nb * a.sh.B * a.sh.H));
+  const int nbh = a.nbh > 0 ? a.nbh : a.sh.B * a.sh.H;
+  const dim3 grid((unsigned)(nb * nbh));
   switch (a.sh.mech) {
     case MECH_T5: launch_one<MECH_T5, DIR>(a, grid, stream); break;
     case MECH_SHAW: launch_one<MECH_SHAW, DIR>(a, grid, stream); break;

@@ -55,6 +55,8 @@ struct FwdArgs {
 
 struct BwdArgs {
   AttnShape sh;
+  int bh0;             // first (batch, head) slice of this launch (b-major: b H + h)
+  int nbh;             // slices in this launch (0 = all B H)
   const void* q;
   const void* k;
   const void* v;
@@ -122,11 +124,17 @@ hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool
 hipError_t launch_agg_alibi(const float* diag, int H, int L, float* dm, hipStream_t st);
 hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int nbk, float* dbeta,
                          hipStream_t st);
-hipError_t launch_agg_txl(const float* prow, const float* pkv, const float* diag, const void* r,
-                          const float* v, int B, int H, int L, int nb, int nrk, int wl, int wr,
-                          int nrel,
-                          int off, float s, bool fp32, float* dr, float* du, float* dv,
-                          hipStream_t st);
+// T-XL dr from the key-side r partials of the slice group [s0, s0 + ns) (partial slot of slice
+// s0 + i, key block p: i nb + p), summed in ascending (slice, block) order.  Groups are added in
+// order: the first overwrites dr, later ones add to it; dr holds raw sums until the last group,
+// which adds v . diag and scales by s.
+hipError_t launch_agg_txl_dr(const float* prow, const float* diag, const float* v, int H, int L,
+                             int nb, int nrk, int wl, int wr, int nrel, int off, float s, int s0,
+                             int ns, bool first, bool last, float* dr, hipStream_t st);
+// T-XL dv (v . r diagonal term) and du (from the key-side per-owner sums of dS^T k)
+hipError_t launch_agg_txl_uv(const float* pkv, const float* diag, const void* r, int B, int H,
+                             int L, int nb, int nrel, int off, float s, bool fp32, float* du,
+                             float* dv, hipStream_t st);
 
 // Relation-table projections: rel [H, N, d] = X [N, F] . W [F, H d] (dtype of X and W; rel
 // written in that dtype), and the backward dX = dY . W^T [N, F], dW = X^T . dY [F, H d] (fp32)

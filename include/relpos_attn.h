@@ -92,6 +92,11 @@ typedef struct relpos_desc {
   int32_t max_distance;   /* T5: > num_buckets / 4 (bidirectional) or num_buckets / 2 */
   int32_t bidirectional;  /* T5: 1 = separate buckets for keys after the query */
   float scale;            /* 0 = default */
+  int64_t max_partial_bytes; /* T-XL backward: cap on the key-side r-partial workspace, which
+                                grows as L^2 / 2 bytes per (batch, head); the slices are then
+                                processed in fixed groups that fit under it (at least one slice
+                                per group).  0 = 8 GiB.  Results depend on the group size only
+                                through the (fixed) order of the fp32 sums. */
 } relpos_desc;
 
 /* Bytes of workspace the forward (pass 0) or backward (pass 1) call needs. */

@@ -64,6 +64,7 @@ def _ws(desc, pass_=0):
     (dict(rel_span=0), ear.RELPOS_E_INVALID),
     (dict(scale=-1.0), ear.RELPOS_E_INVALID),
     (dict(scale=float("nan")), ear.RELPOS_E_INVALID),
+    (dict(max_partial_bytes=-1), ear.RELPOS_E_INVALID),
 ])
 def test_invalid_descriptors(kw, expected):
     base = dict(mech="shaw", batch=2, heads=4, seqlen=100, head_dim=64, rel_span=8)
@@ -99,6 +100,21 @@ def test_workspace_sizes_scale_with_shape():
         s1, b = _ws(d, 1)
         assert s0 == s1 == 0 and b >= f > 0
     assert _ws(ear.make_desc("shaw", 1, 1, 10, rel_span=2), 2)[0] == ear.RELPOS_E_INVALID
+
+
+def test_txl_partial_cap_groups_slices():
+    """The T-XL key-side r partials take L^2 / 2 bytes per (batch, head) slice; a cap makes the
+    backward process the slices in groups, and the workspace shrinks to one group's partials
+    (never below one slice)."""
+    def ws(cap):
+        return _ws(ear.make_desc("txl", 2, 3, 1000, max_partial_bytes=cap), 1)
+    st, full = ws(0)
+    nb, rows = (1000 + 127) // 128, 1000 + 256
+    per_slice = nb * rows * 64 * 4
+    assert st == 0 and full >= 6 * per_slice
+    for cap, group in ((per_slice, 1), (2 * per_slice + 5, 2), (4 * per_slice, 4), (1, 1)):
+        st, n = ws(cap)
+        assert st == 0 and n == full - (6 - group) * per_slice, (cap, group)
 
 
 def test_fwd_rejects_bad_pointers_without_launching():

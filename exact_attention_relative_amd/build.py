@@ -16,7 +16,10 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librelpos_attn.so")
 SOURCES = ["relpos_api.hip", "relpos_prep.hip", "relpos_fwd.hip", "relpos_bwd.hip", "relpos_agg.hip",
-           "relpos_proj.hip"]
+           "relpos_proj.hip", "relpos_bwd_txl_key.hip"]
+# per-source options: the T-XL key-side pass schedules with the register-pressure trackers
+# (fewer spills at its 256-register budget)
+EXTRA_FLAGS = {"relpos_bwd_txl_key.hip": ["-mllvm", "-amdgpu-use-amdgpu-trackers=1"]}
 # measurement-only MFMA throughput probe, a library of its own
 PROBE_LIB = os.path.join(PKG, "librelpos_probe.so")
 PROBE_SOURCES = ["relpos_probe.hip"]
@@ -30,7 +33,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(PKG, "..", "include"), "-c",
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-I", os.path.join(PKG, "..", "include"), "-c",
            os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

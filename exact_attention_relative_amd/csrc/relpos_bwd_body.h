@@ -1,0 +1,975 @@
+#pragma once
+// Backward kernels.  One template, instantiated twice per mechanism:
+//   DIR 0: lane side = queries (128 per workgroup), keys streamed: dQ and the query-side table
+//          gradients (Shaw w, T-XL r and its diagonal sums, DeBERTa Kr, T5 diagonal sums).
+//   DIR 1: lane side = keys, queries streamed: dK, dV and the key-side table gradient
+//          (DeBERTa Qr), plus the T-XL u gradient.
+// Both recompute S and P = exp(S - LSE) per tile exactly as the forward does and form
+// dS = P (dP - D) in fp32.  Relation products are reused in both directions (abstract,
+// item 2).  Table gradients follow offset-based gradient sharding (abstract, item 3; zicq.com
+// explainer, section on offset-based gradient sharding): each workgroup accumulates, per
+// offset, the sum over its own rows in registers and writes every offset of its partial
+// exactly once; a second pass (relpos_agg.hip) merges the partials in a fixed order.  No
+// atomics anywhere, so results are bitwise reproducible.
+//
+// Shaw / DeBERTa: per step, dS is scattered into a workgroup buffer E[t][x] indexed by window
+// offset t and lane-side row x (the band t = x - y + 63 of the 64 streamed rows y).  Then
+//   dX_rel += Win^T E^T                     (per wave, its 96-offset window)
+//   dTable_window[t] += sum_x E[t][x] X[x]  (workgroup GEMM, 3 tiles per wave)
+// The window slides by 64 offsets per step, so a wave's three 32-offset accumulators shift by
+// two positions each step and the one that leaves the window is final: it is written out.
+// T-XL (full span, every tile general) splits the same work over the two passes so that each
+// fits two workgroups per CU: the dQ pass reads dX_rel's skewed operand straight from the
+// wave's fp32 dS buffer, and the dK/dV pass runs the table GEMM over its streamed query tile,
+//   dr_window[t] += sum_y E2[t][y] Q[y],   E2[t][y] = dS[y][x], t = y - x + 127,
+// with E2 in the space of the column-side skew buffer.
+#include "relpos_tile.h"
+
+namespace relpos {
+
+constexpr int ESTR16 = 136;   // bf16 E row stride (elements)
+constexpr int ESTRT = 200;    // bf16 E2T row stride (elements): 192 window offsets + pad
+static_assert(BOTH * ESTRT * 2 <= NWAVE * WROWS * GS2 * 4, "E2T fits the column-skew buffer");
+
+// PART 0: the whole sweep.  PART 1 (light): only the steps whose workgroup tile is clipped
+// (every offset beyond the span), without any relation-product machinery, writing fp32 partial
+// dX / dV and the end-row sums.  PART 2: only the contiguous range of general steps, merging
+// the light pass's partials into the final outputs.
+template <int MECH, int DIR, int PART>
+struct BV {
+  static constexpr bool HAS_ROW = DIR == 0 ? MECH != MECH_T5 : MECH == MECH_DEBERTA;
+  static constexpr bool HAS_COL = DIR == 0 ? MECH == MECH_DEBERTA : MECH != MECH_T5;
+  static constexpr bool LIGHT = PART == 1;
+  static constexpr bool FAT = PART == 2;
+  static constexpr bool ROW = HAS_ROW && !LIGHT;
+  static constexpr bool COL = HAS_COL && !LIGHT;
+  static constexpr bool TXL = MECH == MECH_TXL;
+  static constexpr bool CLIP = MECH == MECH_SHAW || MECH == MECH_DEBERTA;
+  static constexpr bool DIAG = DIR == 0 && (MECH == MECH_T5 || MECH == MECH_TXL);
+  static constexpr bool EBUF = ROW && !TXL;          // shared E buffer + lane-side table GEMM
+  static constexpr bool GSREL = TXL && DIR == 0;      // dX_rel from the wave's fp32 dS buffer
+  static constexpr bool TG1 = TXL && DIR == 1;        // table GEMM over the streamed rows
+  static constexpr bool WINB = ROW || COL;
+  static constexpr bool GSB = ROW || COL || DIAG;
+
+  // row-side table row of lane offset lam = a - b
+  __device__ static int row_of(int lam, int span, int nrel, int off) {
+    if (DIR == 0) return row_side_row(MECH, lam, span, nrel, off);
+    return clampi(lam + span, 0, 2 * span - 1);   // DeBERTa p2c: lam = j - i
+  }
+  // column-side table row of other offset mu = b - a
+  __device__ static int col_of(int mu, int span, int nrel, int off) {
+    if (DIR == 0) return clampi(mu + span, 0, 2 * span - 1);   // DeBERTa p2c: mu = j - i
+    return row_side_row(MECH, mu, span, nrel, off);             // mu = i - j
+  }
+  // offsets <= TA share end row A, >= TB share end row B (Shaw / DeBERTa only)
+  __device__ static int TA(int span) { return -span; }
+  __device__ static int TB(int span) { return MECH == MECH_SHAW ? span : span - 1; }
+  __device__ static int rowA(int span) { return MECH == MECH_SHAW ? 2 * span : 0; }
+  __device__ static int rowB(int span) { return MECH == MECH_SHAW ? 0 : 2 * span - 1; }
+};
+
+// A operand with the k order of op_rows_tr / op_from_acc (slot j < 4: k = 4 kh + j,
+// slot 4 + j: k = 8 + 4 kh + j) read from 16 consecutive bf16 of a row at element e.
+__device__ __forceinline__ Op<1> op_from_lds_perm(const uint16_t* base, int e) {
+  const int kh = __lane_id() >> 5;
+  u32x2 lo = *(const u32x2*)(base + e + 4 * kh);
+  u32x2 hi = *(const u32x2*)(base + e + 8 + 4 * kh);
+  u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+  Op<1> o;
+  o.p[0] = u4_to_bf8(v);
+  return o;
+}
+
+// Zero the slots of an op_from_lds_perm operand (row t, columns ybase + perm k) outside the
+// band y <= t <= y + 127.
+__device__ __forceinline__ void band_mask(Op<1>& o, int t, int ybase) {
+  const int kh = __lane_id() >> 5;
+  u32x4 v = __builtin_bit_cast(u32x4, o.p[0]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s0 = 2 * i, s1 = 2 * i + 1;
+    const int y0 = ybase + (s0 < 4 ? 4 * kh + s0 : 8 + 4 * kh + s0 - 4);
+    const int y1 = ybase + (s1 < 4 ? 4 * kh + s1 : 8 + 4 * kh + s1 - 4);
+    const uint32_t m = ((unsigned)(t - y0) <= 127u ? 0x0000FFFFu : 0u) |
+                       ((unsigned)(t - y1) <= 127u ? 0xFFFF0000u : 0u);
+    v[i] &= m;
+  }
+  o.p[0] = u4_to_bf8(v);
+}
+
+// ----------------------------------------------------------------------------- kernel
+template <int MECH, int DIR, int PART>
+__device__ __forceinline__ void bwd_body(const BwdArgs& a) {
+  using V = BV<MECH, DIR, PART>;
+  typedef uint16_t T;
+  constexpr int NP = 1;
+  __shared__ __attribute__((aligned(16))) uint16_t ys[BOTH * TSTR];     // K (dir 0) / Q (dir 1)
+  __shared__ __attribute__((aligned(16))) uint16_t y2s[BOTH * TSTR];    // V (dir 0) / dO (dir 1)
+  __shared__ __attribute__((aligned(16))) uint16_t win[V::WINB ? WIN * TSTR : 8];
+  // the skewed reads of the dX_rel operand reach up to 32 floats beyond a wave's buffer
+  constexpr int GSG = V::GSREL ? 32 : 0;
+  __shared__ __attribute__((aligned(16))) float gsb_raw[V::GSB ? NWAVE * WROWS * GS2 + 2 * GSG : 4];
+  __shared__ __attribute__((aligned(16))) uint16_t ebuf[V::EBUF ? WIN * ESTR16 : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t xs[V::EBUF ? BLANE * TSTR : 8];   // lane rows X
+  __shared__ __attribute__((aligned(16))) float vec_s[MECH == MECH_T5 ? WIN : 4];  // T5 LUT slice
+  constexpr int NOVEC = (MECH == MECH_TXL && DIR == 0) ? BOTH : (V::CLIP && V::HAS_COL ? 2 * BOTH : 4);
+  __shared__ __attribute__((aligned(16))) float ovec_s[NOVEC];   // per-other-row constants
+  __shared__ __attribute__((aligned(16))) float lsd_s[DIR == 1 ? 2 * BOTH : 4];   // LSE*log2e, D per query
+  __shared__ __attribute__((aligned(16))) float endc[V::CLIP && V::ROW ? 2 * BLANE : 4];
+  float* const gsb = gsb_raw + GSG;
+
+  const AttnShape sh = a.sh;
+  const int L = sh.L;
+  const int nb = (L + BLANE - 1) / BLANE;
+  const int bid = xcd_remap(blockIdx.x, gridDim.x);
+  int blk = bid % nb;
+  const int bh = a.bh0 + bid / nb;
+  if (sh.wr == 0) blk = (DIR == 0) ? nb - 1 - blk : blk;   // causal: longest first
+  const int h = bh % sh.H;
+  const int A0 = blk * BLANE;
+  const int tid = threadIdx.x;
+  const int w = wave_index(), lane = tid & 63, l32 = lane & 31, kh = lane >> 5;
+  const int aw0 = A0 + WROWS * w;
+  const int my_a = aw0 + l32;
+  const int span = sh.span, nrel = sh.nrel, toff = sh.txl_off;
+  const float s = sh.scale, c = s * kLog2e;
+  const int64_t bh_off = (int64_t)bh * L * kHeadDim;
+  const int64_t owner = (int64_t)a.bh0 * nb + bid;   // partial slot of this workgroup
+
+  const T* xg = (const T*)(DIR == 0 ? a.q : a.k) + bh_off;
+  const T* x2g = (const T*)(DIR == 0 ? a.dout : a.v) + bh_off;
+  const T* yg = (const T*)(DIR == 0 ? a.k : a.q) + bh_off;
+  const T* y2g = (const T*)(DIR == 0 ? a.v : a.dout) + bh_off;
+  const T* trow = (const T*)(DIR == 0 ? a.rel_a : a.rel_b);   // row-side table
+  const T* tcol = (const T*)(DIR == 0 ? a.rel_b : a.rel_a);   // column-side table
+  if constexpr (MECH == MECH_TXL) {
+    if (DIR == 0) trow += (int64_t)h * nrel * kHeadDim;
+    else tcol += (int64_t)h * nrel * kHeadDim;
+  }
+  const float* rc_g = DIR == 0 ? a.rowc : a.keyc;   // lane rows . row table ends (A, B)
+  const float* oc_g = DIR == 0 ? a.keyc : a.rowc;   // other rows . column table ends (A, B)
+
+  // ---- lane-side registers ----
+  Op<NP> xop[4], x2op[4];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc) {
+    if (my_a < L) {
+      xop[cc] = op_from_global<T>(xg + (int64_t)my_a * kHeadDim + 16 * cc + 8 * kh);
+      x2op[cc] = op_from_global<T>(x2g + (int64_t)my_a * kHeadDim + 16 * cc + 8 * kh);
+    } else {
+      float z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      xop[cc] = op_from_f32<NP>(z);
+      x2op[cc] = xop[cc];
+    }
+  }
+  float lse2 = __builtin_inff(), dsum_l = 0.f;   // dir 0: per lane
+  if (DIR == 0 && my_a < L) {
+    lse2 = a.lse[(int64_t)bh * L + my_a] * kLog2e;
+    dsum_l = a.dsum[(int64_t)bh * L + my_a];
+    if (!(lse2 > kNegInf)) lse2 = __builtin_inff();   // empty row: P = 0
+  }
+  float rcA = 0.f, rcB = 0.f;
+  if constexpr (V::CLIP && V::HAS_ROW) {
+    if (my_a < L) {
+      rcA = rc_g[((int64_t)bh * L + my_a) * 2 + 0];
+      rcB = rc_g[((int64_t)bh * L + my_a) * 2 + 1];
+    }
+  }
+  float ukl = 0.f;   // dir 1 T-XL: u . k of this lane's key
+  if constexpr (MECH == MECH_TXL && DIR == 1) {
+    if (my_a < L) ukl = a.uk[(int64_t)bh * L + my_a];
+  }
+
+  // ---- sweep range over the other side ----
+  int b_lo = 0, b_hi = L - 1;
+  if (DIR == 0) {
+    if (sh.wl >= 0) b_lo = max(0, A0 - sh.wl);
+    if (sh.wr >= 0) b_hi = min(L - 1, A0 + BLANE - 1 + sh.wr);
+  } else {
+    if (sh.wr >= 0) b_lo = max(0, A0 - sh.wr);
+    if (sh.wl >= 0) b_hi = min(L - 1, A0 + BLANE - 1 + sh.wl);
+  }
+  const int bt_all = (b_lo / BOTH) * BOTH;
+  const int nsteps_all = (b_hi >= b_lo) ? (b_hi - bt_all) / BOTH + 1 : 0;
+  // workgroup tile of step base b0 needs relation products (some offset not clipped)
+  auto wg_gen = [&](int b0) {
+    if constexpr (V::CLIP) {
+      const int ta = V::TA(span), tb = V::TB(span);
+      const int wlo = A0 - b0 - 63, whi = A0 - b0 + 127;
+      const bool gr = V::HAS_ROW && !(whi <= ta || wlo >= tb);
+      const bool gc = V::HAS_COL && !(-wlo <= ta || -whi >= tb);
+      return gr || gc;
+    }
+    return true;
+  };
+  // the general steps form one contiguous range (the window slides monotonically)
+  int g_first = nsteps_all, g_last = -1;
+  if constexpr (PART != 0) {
+    for (int s2 = 0; s2 < nsteps_all; ++s2)
+      if (wg_gen(bt_all + s2 * BOTH)) { g_first = min(g_first, s2); g_last = s2; }
+  }
+  const int bt0 = V::FAT ? bt_all + g_first * BOTH : bt_all;
+  const int nsteps = V::FAT ? (g_last >= g_first ? g_last - g_first + 1 : 0) : nsteps_all;
+  const int bt_last = bt0 + (nsteps - 1) * BOTH;
+
+  // ---- partial layouts ----
+  // lane offsets lam of this workgroup lie in [lam_base, lam_base + nrt)
+  const int lam_base = A0 - L - 64;
+  const int nrt = L + 256;
+  float* prow = nullptr;     // row-side table partial
+  int prow_rows = 0;
+  if constexpr (V::EBUF) {
+    prow_rows = (MECH == MECH_SHAW) ? 2 * span + 1 : 2 * span;
+    prow = (DIR == 0 ? a.part_q : a.part_k) + owner * (DIR == 0 ? a.part_q_stride : a.part_k_stride);
+  }
+  // T-XL r partial of the key-side pass: row b0 + 65 + t holds window row t of step base b0
+  // (offset delta = b0 - A0 - 127 + t), i.e. row delta + A0 + 192
+  // With a two-sided window the partial keeps only the rows of this sweep, from row bt0 + 65.
+  float* ptg = nullptr;
+  const int nrk = (int)(a.part_q_stride / kHeadDim);
+  const int rb = (sh.wl >= 0 && sh.wr >= 0) ? bt0 + 65 : 0;
+  // (slots of the r partial count from the launch's first slice)
+  if constexpr (V::TG1) ptg = a.part_q + (int64_t)bid * a.part_q_stride - (int64_t)rb * kHeadDim;
+  float* pdiag = nullptr;
+  if constexpr (V::DIAG) pdiag = a.part_qv + owner * (int64_t)nrt;
+
+  // lane offsets the sweep writes: every window row of every step, [A0 - b0 - 63, A0 - b0 + 128],
+  // for the table partial; the diagonal sums stop one short (the last window row has no pairs)
+  const int cov_lo = A0 - bt_last - 63, cov_hi = A0 - bt0 + 128, cov_hi_diag = cov_hi - 1;
+
+  // ---- zero what the sweep will not write ----
+  if constexpr (V::EBUF) {
+    for (int64_t e = tid; e < (int64_t)prow_rows * kHeadDim; e += 256) {
+      const int row = (int)(e / kHeadDim);
+      // end rows are written by the end-row pass; interior rows iff their offset is covered
+      int lam;
+      if constexpr (MECH == MECH_SHAW) lam = span - row;   // dir 0 only: row = clamp(-lam) + k
+      else lam = row - span;                               // row = clamp(lam + k)
+      const bool end = row == V::rowA(span) || row == V::rowB(span);
+      const bool covered = end || (nsteps > 0 && lam >= cov_lo && lam <= cov_hi);
+      if (!covered) prow[e] = 0.f;
+    }
+  }
+  if constexpr (V::TG1) {
+    // rows written by the sweep: [bt0 + 65, bt_last + 256] (ptg is offset by rb rows)
+    for (int64_t e = tid; e < (int64_t)nrk * kHeadDim; e += 256) {
+      const int row = (int)(e / kHeadDim) + rb;
+      if (!(nsteps > 0 && row >= bt0 + 65 && row <= bt_last + 256)) ptg[(int64_t)rb * kHeadDim + e] = 0.f;
+    }
+  }
+  if constexpr (V::DIAG) {
+    for (int e = tid; e < nrt; e += 256) {
+      const int lam = lam_base + e;
+      if (!(nsteps > 0 && lam >= cov_lo && lam <= cov_hi_diag)) pdiag[e] = 0.f;
+    }
+  }
+  if constexpr (V::EBUF) {
+    const int n16 = (WIN * ESTR16) / 8;
+    u32x4 z = {0u, 0u, 0u, 0u};
+    for (int e = tid; e < n16; e += 256) *(u32x4*)(ebuf + 8 * e) = z;
+  }
+  if constexpr (V::EBUF) {
+    stage64<T, NP>(xs, xg, A0, L);
+    stage64<T, NP>(xs + BOTH * TSTR, xg, A0 + BOTH, L);
+  }
+
+  // ---- accumulators ----
+  f32x16 gacc[2] = {f32x16{}, f32x16{}};    // dX (content + relation), dir 1: dK
+  f32x16 vacc[2] = {f32x16{}, f32x16{}};    // dir 1: dV
+  f32x16 racc[3] = {f32x16{}, f32x16{}, f32x16{}};   // row-side table window accumulators
+  float cA = 0.f, cB = 0.f;                  // clipped-end sums of dS (lane row)
+  float colsum = 0.f;                        // dir 1 T-XL: sum_i dS_ij
+  float dcarry = 0.f;                        // diagonal sum of offsets lam = tid (mod 256)
+  const int gdb = w & 1, gp = w >> 1;        // GEMM tiles of this wave: d-block, t-block parity
+
+  float* gs = gsb + (V::GSB ? w * WROWS * GS2 : 0);
+  uint16_t* e16 = ebuf;
+
+  // the next step's streamed tiles are read into registers while the current step computes
+  auto step_base = [&](int st) { return bt0 + st * BOTH; };
+  auto step_skipped = [&](int st) { return V::LIGHT && st >= g_first && st <= g_last; };
+  int next = 0;
+  while (next < nsteps && step_skipped(next)) ++next;
+  TilePrefetch<T> py, py2;
+  if (!V::TG1 && next < nsteps) {
+    py.load(yg, step_base(next), L);
+    py2.load(y2g, step_base(next), L);
+  }
+
+  for (int step = 0; step < nsteps; ++step) {
+    const int b0 = bt0 + step * BOTH;
+    // query-side T-XL: the row window slides by 64 offsets per step and is kept circular,
+    // window row x of step s at physical row (x - 64 s) mod 192
+    // key-side T-XL: the column window slides up by 64 per step, row x at (x + 64 s) mod 192
+    const int xrot = V::GSREL ? ((3 - step % 3) % 3) * BOTH : V::TG1 ? (step % 3) * BOTH : 0;
+    if constexpr (V::LIGHT) {
+      if (step >= g_first && step <= g_last) continue;   // left to the general pass
+    }
+    const int cwin = A0 - b0;             // workgroup window row t <-> lam = cwin - 63 + t
+    const int lamlo = aw0 - b0 - 63, lamhi = aw0 + 31 - b0;
+    // delta = i - j range of the wave tile
+    const int dlo = DIR == 0 ? lamlo : -lamhi, dhi = DIR == 0 ? lamhi : -lamlo;
+    bool wave_none = (b0 >= L) || (aw0 >= L);
+    if (sh.wl >= 0 && dlo > sh.wl) wave_none = true;
+    if (sh.wr >= 0 && -dhi > sh.wr) wave_none = true;
+    const bool wave_full = (b0 + BOTH <= L) && (aw0 + WROWS <= L) &&
+                           (sh.wl < 0 || dhi <= sh.wl) && (sh.wr < 0 || -dlo <= sh.wr);
+    // ---- tile classes ----
+    int rcls = 0, ccls = 0;   // 0 general, 1 = all end A, 2 = all end B
+    bool wg_general = true;
+    if constexpr (V::CLIP) {
+      const int ta = V::TA(span), tb = V::TB(span);
+      if constexpr (V::HAS_ROW) {
+        if (lamhi <= ta) rcls = 1; else if (lamlo >= tb) rcls = 2;
+      }
+      if constexpr (V::HAS_COL) {
+        if (-lamlo <= ta) ccls = 1; else if (-lamhi >= tb) ccls = 2;
+      }
+      wg_general = wg_gen(b0);
+    }
+    int t5cls = 0;
+    if constexpr (MECH == MECH_T5) {
+      const int lo = clampi(dlo, 1 - L, L - 1), hi = clampi(dhi, 1 - L, L - 1);
+      if ((lo >= 0 || hi < 0) && a.bucket[lo + L - 1] == a.bucket[hi + L - 1]) t5cls = 1;
+      // the workgroup needs the E buffer when any of its waves is not single-bucket
+      const int wlo = DIR == 0 ? cwin - 63 : -(cwin + 127), whi = DIR == 0 ? cwin + 127 : -(cwin - 63);
+      const int l2 = clampi(wlo, 1 - L, L - 1), h2 = clampi(whi, 1 - L, L - 1);
+      wg_general = !((l2 >= 0 || h2 < 0) && a.bucket[l2 + L - 1] == a.bucket[h2 + L - 1]);
+    }
+
+    // ---- stage ----
+    __syncthreads();
+    if constexpr (V::TG1) {   // registers are the limit here: stage directly
+      stage64<T, NP>(ys, yg, b0, L);
+      stage64<T, NP>(y2s, y2g, b0, L);
+    } else {
+      py.store(ys);
+      py2.store(y2s);
+    }
+    if constexpr (MECH == MECH_T5) {
+      for (int x = tid; x < WIN; x += 256) {
+        const int lam = cwin - 63 + x;
+        const int d = DIR == 0 ? lam : -lam;
+        vec_s[x] = (d > -L && d < L) ? a.lut[(int64_t)h * (2 * L - 1) + d + L - 1] : 0.f;
+      }
+    }
+    if constexpr (MECH == MECH_TXL && DIR == 0) {
+      if (tid < BOTH) ovec_s[tid] = (b0 + tid < L) ? a.uk[(int64_t)bh * L + b0 + tid] : 0.f;
+    }
+    if constexpr (V::CLIP && V::HAS_COL) {
+      if (tid < 2 * BOTH) {
+        const int yy = b0 + (tid >> 1);
+        ovec_s[tid] = (yy < L) ? oc_g[((int64_t)bh * L + yy) * 2 + (tid & 1)] : 0.f;
+      }
+    }
+    if constexpr (DIR == 1) {
+      if (tid < BOTH) {
+        const int yy = b0 + tid;
+        float l2 = __builtin_inff(), dd = 0.f;
+        if (yy < L) {
+          l2 = a.lse[(int64_t)bh * L + yy] * kLog2e;
+          if (!(l2 > kNegInf)) l2 = __builtin_inff();
+          dd = a.dsum[(int64_t)bh * L + yy];
+        }
+        lsd_s[tid] = l2;
+        lsd_s[BOTH + tid] = dd;
+      }
+    }
+    // row side staged now when there is no column side
+    if constexpr (V::GSREL) {
+      // every T-XL tile is general; after the first step only rows 0..63 are new
+      auto rowfn = [&](int x) { return V::row_of(cwin - 63 + x, span, nrel, toff); };
+      if (step == 0) {
+        stage_window<T, NP>(win, trow, rowfn);
+        for (int x = tid; x < WIN; x += 256) {
+          const int r = rowfn(x);
+          *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+        }
+      } else {
+        stage_window_rows<T, NP>(win, trow, rowfn, 0, xrot);
+        if (tid < BOTH) {
+          const int r = rowfn(tid);
+          *win_vec(win, xrot + tid) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+        }
+      }
+    } else if constexpr (V::ROW && !V::COL) {
+      if (wg_general) {
+        stage_window<T, NP>(win, trow, [&](int x) {
+          return V::row_of(cwin - 63 + x, span, nrel, toff);
+        });
+      }
+    }
+    // column side first (its window is replaced by the row-side window afterwards)
+    if constexpr (V::TG1) {
+      // column window row x <-> mu = b - a = (b0 - A0 - 127) + x; after the first step only
+      // rows 128..191 are new, at physical rows wrow(128, xrot) ..
+      auto colfn = [&](int x) { return V::col_of((b0 - A0 - (BLANE - 1)) + x, span, nrel, toff); };
+      if (step == 0) {
+        stage_window<T, NP>(win, tcol, colfn);
+        for (int x = tid; x < WIN; x += 256) {
+          const int r = colfn(x);
+          *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+        }
+      } else {
+        const int p0 = wrow(2 * BOTH, xrot);
+        stage_window_rows<T, NP>(win, tcol, colfn, 2 * BOTH, p0);
+        if (tid < BOTH) {
+          const int r = colfn(2 * BOTH + tid);
+          *win_vec(win, p0 + tid) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+        }
+      }
+    } else if constexpr (V::COL) {
+      if (wg_general) {
+        stage_window<T, NP>(win, tcol, [&](int x) {
+          // column window row x <-> mu = b - a = (b0 - A0 - 127) + x
+          return V::col_of((b0 - A0 - (BLANE - 1)) + x, span, nrel, toff);
+        });
+      }
+    }
+    // issue the next step's tile reads (after this step's staging reads have been consumed)
+    next = step + 1;
+    while (next < nsteps && step_skipped(next)) ++next;
+    if (!V::TG1 && next < nsteps) {
+      py.load(yg, step_base(next), L);
+      py2.load(y2g, step_base(next), L);
+    }
+    __syncthreads();
+
+    f32x16 sc[2];
+    Op<NP> yop[2][4];
+    if (!wave_none) {
+      // T-XL query side: the scores start from u.k of each streamed key
+      if constexpr (MECH == MECH_TXL && DIR == 0) other_dot_lane<NP, true>(sc, ys, xop, yop, ovec_s);
+      else other_dot_lane<NP>(sc, ys, xop, yop);
+    }
+    float lconst = 0.f;   // per-lane additive term (y units)
+    if constexpr (V::HAS_COL) {
+      if (!wave_none) {
+        if (V::CLIP && ccls != 0) {
+          add_other_vec(sc, ovec_s + (ccls == 1 ? 0 : 1), 2);
+        } else if constexpr (V::TG1) {
+          col_skew_add<NP, true, true>(sc, win, (BLANE - WROWS) - WROWS * w, 0, ys, gs, xrot);
+          col_skew_add<NP, true, true>(sc, win, (BLANE - WROWS) - WROWS * w, 1, ys, gs, xrot);
+        } else if (V::COL && wg_general) {
+          col_skew_add<NP, MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 0, ys, gs);
+          col_skew_add<NP, MECH == MECH_TXL>(sc, win, (BLANE - WROWS) - WROWS * w, 1, ys, gs);
+        }
+      }
+    }
+    if constexpr (V::ROW && V::COL) {
+      if (wg_general) {
+        __syncthreads();   // column-side window reads done
+        stage_window<T, NP>(win, trow, [&](int x) {
+          return V::row_of(cwin - 63 + x, span, nrel, toff);
+        });
+        __syncthreads();
+      }
+    }
+    if constexpr (V::HAS_ROW) {
+      if (!wave_none) {
+        if (V::CLIP && rcls != 0) {
+          lconst = (rcls == 1) ? rcA : rcB;
+        } else if constexpr (V::ROW) {
+          f32x16 g[3];
+          if constexpr (V::GSREL) row_products<NP, true, true>(g, win, WROWS * w, xop, xrot);
+          else row_products<NP, MECH == MECH_TXL>(g, win, WROWS * w, xop);
+          row_skew_add(sc, g, gs);
+        }
+      }
+    }
+    if constexpr (MECH == MECH_T5) {
+      if (!wave_none) {
+        if (t5cls == 1) {
+          const int lo = clampi(DIR == 0 ? lamlo : -lamhi, 1 - L, L - 1);
+          const int lamx = DIR == 0 ? lo : -lo;
+          lconst = vec_s[lamx - (cwin - 63)];
+        } else {
+          add_offset_vec(sc, vec_s, WROWS * w);
+        }
+      }
+    }
+    if constexpr (MECH == MECH_TXL) {
+      if (!wave_none) {
+        if (DIR == 1) lconst = ukl;
+      }
+    }
+
+    f32x16 ds[2];
+    Op<NP> dso[4];   // dS as bf16 MFMA operands (16 other-side rows each)
+    if (!wave_none) {
+      // query-side pass: dP first, its MFMAs run while the exponentials below are computed
+      Op<NP> y2op[2][4];
+      f32x16 dp[2];
+      if constexpr (DIR == 0) other_dot_lane<NP>(dp, y2s, x2op, y2op);
+      // ---- P ----  (key-side pass: LSE of the streamed queries, 4 rows per read)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 l4 = {lse2, lse2, lse2, lse2};
+          if constexpr (DIR == 1) l4 = *(const f32x4*)(lsd_s + 32 * b + 8 * g + 4 * kh);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sc[b][4 * g + i] = fast_exp2(fmaf(sc[b][4 * g + i], c, lconst * c - l4[i]));
+        }
+      if (!wave_full) {
+        const int wlx = sh.wl < 0 ? L : sh.wl, wrx = sh.wr < 0 ? L : sh.wr;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
+            const int ii = DIR == 0 ? my_a : b0 + y;
+            const int jj = DIR == 0 ? b0 + y : my_a;
+            sc[b][r] = pair_ok(ii, jj, L, wlx, wrx) ? sc[b][r] : 0.f;
+          }
+      }
+      if constexpr (DIR == 1) other_dot_lane<NP>(dp, y2s, x2op, y2op);
+      // ---- dS ----
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 d4 = {dsum_l, dsum_l, dsum_l, dsum_l};
+          if constexpr (DIR == 1) d4 = *(const f32x4*)(lsd_s + BOTH + 32 * b + 8 * g + 4 * kh);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ds[b][4 * g + i] = sc[b][4 * g + i] * (dp[b][4 * g + i] - d4[i]);
+        }
+      if constexpr (MECH == MECH_TXL && DIR == 1) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) colsum += ds[b][r];
+      }
+      // ---- content gradients (P and dS packed to bf16 once; the fp32 copies can die) ----
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) dso[cc] = op_from_acc<NP>(ds, cc);
+      if constexpr (DIR == 1) {
+        Op<NP> po[4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) po[cc] = op_from_acc<NP>(sc, cc);
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+            Op<NP> yt = op_rows_tr<NP>(y2s, BOTH * TSTR, TSTR, 16 * cc, 32 * db);
+            mma<NP>(vacc[db], yt, po[cc]);
+          }
+      }
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          Op<NP> yt = op_rows_tr<NP>(ys, BOTH * TSTR, TSTR, 16 * cc, 32 * db);
+          mma<NP>(gacc[db], yt, dso[cc]);
+        }
+    }
+
+    // ---- offset-sharded row-side gradients ----
+    if constexpr (V::CLIP && V::HAS_ROW) {
+      if (!(V::EBUF && wg_general) && !wave_none) {
+        // the whole wave tile reads one end row
+        float tot = 0.f;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tot += ds[b][r];
+        if (rcls == 1) cA += tot; else cB += tot;
+      }
+    }
+    if constexpr (V::EBUF) {
+      const bool use_e = wg_general;
+      if (use_e) {
+        __syncthreads();   // skew buffers and previous E reads are done
+        // scatter the band; clipped elements go to the end-row sums instead
+        const int xcol = WROWS * w + l32;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
+            const int t = xcol - y + 63;
+            float v = wave_none ? 0.f : ds[b][r];
+            if constexpr (V::CLIP) {
+              const int lam = cwin - 63 + t;
+              if (lam <= V::TA(span)) { cA += v; v = 0.f; }
+              else if (lam >= V::TB(span)) { cB += v; v = 0.f; }
+            }
+            e16[t * ESTR16 + xcol] = f2bf_bits(v);
+          }
+        __syncthreads();
+      }
+
+      if constexpr (V::ROW) {
+        // slide the window accumulators by two blocks; the block leaving the window is final
+        if (step > 0) {
+          const int pc = cwin + BOTH;   // previous step's window base (lam = pc - 63 + t)
+          const int a2 = gp + 4;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int t = 32 * a2 + 8 * (r >> 2) + 4 * kh + (r & 3);
+            const int lam = pc - 63 + t;
+            const int d = 32 * gdb + l32;
+            if (lam > V::TA(span) && lam < V::TB(span)) {
+              const int row = V::row_of(lam, span, nrel, toff);
+              prow[(int64_t)row * kHeadDim + d] = racc[2][r];
+            }
+          }
+          racc[2] = racc[1];
+          racc[1] = racc[0];
+          racc[0] = f32x16{};
+        }
+        if (wg_general) {
+          // dX_rel += Win^T E^T over this wave's 96 offsets
+#pragma unroll
+          for (int cc = 0; cc < 6; ++cc) {
+            Op<NP> eop = op_rows_tr<NP>(e16, WIN * ESTR16, ESTR16, WROWS * w + 16 * cc, WROWS * w);
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+              Op<NP> wt = op_rows_tr<NP>(win, WIN * TSTR, TSTR, WROWS * w + 16 * cc, 32 * db);
+              mma<NP>(gacc[db], wt, eop);
+            }
+          }
+          // workgroup GEMM: racc[i] (t-block gp + 2 i, d-block gdb) += E[t][x] X[x][d]
+#pragma unroll
+          for (int i = 0; i < 3; ++i) {
+            const int ab = gp + 2 * i;
+            const int c_lo = max(0, 2 * ab - 4), c_hi = min(7, 2 * ab + 1);
+            for (int cq = c_lo; cq <= c_hi; ++cq) {
+              Op<NP> eop = op_from_lds_perm(e16, (32 * ab + l32) * ESTR16 + 16 * cq);
+              Op<NP> xop2 = op_rows_tr<NP>(xs, BLANE * TSTR, TSTR, 16 * cq, 32 * gdb);
+              mma<NP>(racc[i], eop, xop2);
+            }
+          }
+        }
+      }
+
+    }
+
+    // ---- T-XL key side: dr window GEMM over the streamed query rows ----
+    if constexpr (V::TG1) {
+      // E2T[y][t] = dS[y][x] with t = y - x + 127, in the column-skew buffer's space: for one
+      // register, the 32 lanes of a half-wave write 32 consecutive t
+      uint16_t* e2t = (uint16_t*)gsb;
+      __syncthreads();   // every wave's column-skew reads are done
+      uint16_t* eb = e2t + (127 - (WROWS * w + l32) + 4 * kh) + 4 * kh * ESTRT;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        // operand slot i of dso[cc] is register 8 (cc % 2) + i of block cc / 2
+        const u32x4 wv = __builtin_bit_cast(u32x4, dso[cc].p[0]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int r = 8 * (cc & 1) + i;
+          const int yc = 32 * (cc >> 1) + 8 * (r >> 2) + (r & 3);   // y - 4 kh
+          const uint32_t word = wv[i >> 1];
+          const uint16_t bits = (uint16_t)((i & 1) ? (word >> 16) : (word & 0xFFFFu));
+          eb[yc * (ESTRT + 1)] = wave_none ? (uint16_t)0 : bits;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int ab = gp + 2 * i;
+        const int tlo = 32 * ab, thi = tlo + 31;
+#pragma unroll
+        for (int cq = 0; cq < 4; ++cq) {
+          const int ylo = 16 * cq, yhi = ylo + 15;
+          if (thi < ylo || tlo > yhi + 127) continue;   // no pair of this block and chunk
+          Op<NP> eop = op_rows_tr<NP>(e2t, 0, ESTRT, ylo, tlo);
+          if (!(tlo >= yhi && thi <= ylo + 127)) band_mask(eop, tlo + l32, ylo);
+          Op<NP> qop2 = op_rows_tr<NP>(ys, BOTH * TSTR, TSTR, ylo, 32 * gdb);
+          mma<NP>(racc[i], eop, qop2);
+        }
+      }
+      // block gp leaves the window with this step (the next window starts 64 offsets higher)
+      {
+        float* fb = ptg + (int64_t)(b0 + 65 + 32 * gp + 4 * kh) * kHeadDim + 32 * gdb + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = racc[0][r];
+      }
+      racc[0] = racc[1];
+      racc[1] = racc[2];
+      racc[2] = f32x16{};
+    }
+
+    // ---- per-offset fp32 sums of dS (T5 bias gradient; T-XL v term and v gradient) ----
+    if constexpr (V::DIAG) {
+      // a wave's 96 sums live in the padding columns of its dS buffer (4 per row)
+      auto wsum_at = [&](int ww, int t) {
+        return gsb + ww * WROWS * GS2 + (t >> 2) * GS2 + kHeadDim + (t & 3);
+      };
+      const bool single = (MECH == MECH_T5) && t5cls == 1;
+      if (!wave_none && !single) {
+        // dS[n][y] into the wave buffer, then sums along the diagonals t = n - y + 63
+        wave_lds_sync();
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            f32x4 v4 = {ds[b][4 * g4], ds[b][4 * g4 + 1], ds[b][4 * g4 + 2], ds[b][4 * g4 + 3]};
+            *(f32x4*)(gs + l32 * GS2 + 32 * b + 8 * g4 + 4 * kh) = v4;
+          }
+        wave_lds_sync();
+        if constexpr (V::GSREL) {
+          // dX_rel^T[d][x] += sum_t Win[32 w + t][d] E[x][t] with E[x][t] = dS[x][x + 63 - t]
+          // for t in [x, x + 63] (else 0), read along the skewed diagonal of the buffer
+          const float* grow = gs + l32 * GS2 + l32 + 63 - 4 * kh;
+#pragma unroll
+          for (int cc = 0; cc < 6; ++cc) {
+            float e8[8];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const int t0 = 16 * cc + 4 * kh + j, t1 = t0 + 8;
+              float v0 = grow[-(16 * cc + j)], v1 = grow[-(16 * cc + 8 + j)];
+              if (cc < 2) { v0 = t0 >= l32 ? v0 : 0.f; v1 = t1 >= l32 ? v1 : 0.f; }
+              if (cc > 3) { v0 = t0 <= l32 + 63 ? v0 : 0.f; v1 = t1 <= l32 + 63 ? v1 : 0.f; }
+              e8[j] = v0;
+              e8[4 + j] = v1;
+            }
+            Op<NP> eop = op_from_f32<NP>(e8);
+#pragma unroll
+            for (int db = 0; db < 2; ++db) {
+              Op<NP> wt = op_rows_tr_rot<NP>(win, WIN * TSTR, TSTR, WROWS * w + 16 * cc, 32 * db,
+                                             xrot);
+              mma<NP>(gacc[db], wt, eop);
+            }
+          }
+        }
+        float sums[2] = {0.f, 0.f};
+        if constexpr (MECH == MECH_TXL) {
+          // Lane l sums diagonal t = l (rows 0 .. min(l, 31)) and, for l < 32, diagonal
+          // t = l + 64 (rows l + 1 .. 31): one element of every row, rows in ascending order,
+          // so the 32 reads are independent and issue back to back (every T-XL tile runs this)
+          const float* gd = gs + (63 - lane);   // row n of diagonal l: gd[n * GS2 + n]
+#pragma unroll
+          for (int n = 0; n < WROWS; ++n) {
+            const bool first = n <= lane;
+            const float v = gd[n * GS2 + n - (first ? 0 : 64)];
+            sums[0] += first ? v : 0.f;
+            sums[1] += first ? 0.f : v;
+          }
+        } else {
+          // T5 reaches this only on its multi-bucket tiles: the compact loop, same order
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int t = lane + 64 * half;
+            if (t < 96) {
+              // diagonal t runs through rows n with 0 <= n + 63 - t < 64
+              const int n0 = max(0, t - 63), n1 = min(WROWS - 1, t);
+              float sum = 0.f;
+              for (int n = n0; n <= n1; ++n) sum += gs[n * GS2 + n + 63 - t];
+              sums[half] = sum;
+            }
+          }
+        }
+        wave_lds_sync();   // this wave's reads of its buffer precede the writes to its padding
+        *wsum_at(w, lane) = sums[0];
+        if (lane < 32) *wsum_at(w, 64 + lane) = sums[1];
+      } else {
+        // single bucket: the wave total goes to one offset of the tile (window row 63)
+        float tot = 0.f;
+        if (!wave_none) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) tot += ds[b][r];
+          tot += xhalf(tot);
+          for (int m = 1; m < 32; m <<= 1) tot += __shfl_xor(tot, m);
+        }
+        wave_lds_sync();
+        *wsum_at(w, lane) = (lane == 63) ? tot : 0.f;
+        if (lane < 32) *wsum_at(w, 64 + lane) = 0.f;
+      }
+      __syncthreads();
+      // thread tid carries the offsets lam = tid (mod 256): at most one window row per step
+      const int t = (tid - (cwin - 63)) & 255;
+      if (t < WIN - 1) {
+        float sum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NWAVE; ++ww) {
+          const int tt = t - 32 * ww;
+          if (tt >= 0 && tt < 96) sum += *wsum_at(ww, tt);
+        }
+        const int lam = cwin - 63 + t;
+        float val = dcarry + sum;
+        // offsets above the next window are final
+        if (step == nsteps - 1 || t >= 127) {
+          pdiag[lam - lam_base] = val;
+          val = 0.f;
+        }
+        dcarry = val;
+      }
+    }
+  }
+
+  // ---- final flush of the window accumulators ----
+  if constexpr (V::EBUF) {
+    if (nsteps > 0) {
+      const int pc = A0 - bt_last;
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        const int ab = gp + 2 * i;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * ab + 8 * (r >> 2) + 4 * kh + (r & 3);
+          const int lam = pc - 63 + t;
+          const int d = 32 * gdb + l32;
+          if (lam > V::TA(span) && lam < V::TB(span)) {
+            const int row = V::row_of(lam, span, nrel, toff);
+            prow[(int64_t)row * kHeadDim + d] = racc[i][r];
+          }
+        }
+      }
+    }
+  }
+  if constexpr (V::TG1) {
+    // blocks gp + 2 and gp + 4 of the last window (shifted into racc[0], racc[1])
+    if (nsteps > 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        float* fb = ptg + (int64_t)(bt_last + 65 + 32 * (gp + 2 + 2 * i) + 4 * kh) * kHeadDim +
+                    32 * gdb + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = racc[i][r];
+      }
+    }
+  }
+
+  // ---- light pass: hand the partial sums to the general pass ----
+  if constexpr (V::LIGHT) {
+    if constexpr (V::HAS_ROW) {
+      cA += xhalf(cA);
+      cB += xhalf(cB);
+    }
+    if (my_a < L) {
+      const int64_t rowoff = ((int64_t)bh * L + my_a) * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * kh;
+          f32x4 v4 = {gacc[db][4 * g], gacc[db][4 * g + 1], gacc[db][4 * g + 2], gacc[db][4 * g + 3]};
+          *(f32x4*)(a.xpart + rowoff + d) = v4;
+          if constexpr (DIR == 1) {
+            f32x4 w4 = {vacc[db][4 * g], vacc[db][4 * g + 1], vacc[db][4 * g + 2], vacc[db][4 * g + 3]};
+            *(f32x4*)(a.vpart + rowoff + d) = w4;
+          }
+        }
+      if (V::HAS_ROW && kh == 0) {
+        a.cab[((int64_t)bh * L + my_a) * 2 + 0] = cA;
+        a.cab[((int64_t)bh * L + my_a) * 2 + 1] = cB;
+      }
+    }
+    return;
+  }
+  if constexpr (V::FAT) {
+    if (my_a < L) {
+      const int64_t rowoff = ((int64_t)bh * L + my_a) * kHeadDim;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d = 32 * db + 8 * g + 4 * kh;
+          f32x4 v4 = *(const f32x4*)(a.xpart + rowoff + d);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gacc[db][4 * g + i] += v4[i];
+          if constexpr (DIR == 1) {
+            f32x4 w4 = *(const f32x4*)(a.vpart + rowoff + d);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vacc[db][4 * g + i] += w4[i];
+          }
+        }
+    }
+  }
+
+  // ---- end rows (clipped offsets): table gradient and lane gradient ----
+  if constexpr (V::CLIP && V::ROW) {
+    // cA / cB hold this lane's sum over its half of the other rows
+    cA += xhalf(cA);
+    cB += xhalf(cB);
+    if constexpr (V::FAT) {
+      if (my_a < L) {
+        cA += a.cab[((int64_t)bh * L + my_a) * 2 + 0];
+        cB += a.cab[((int64_t)bh * L + my_a) * 2 + 1];
+      }
+    }
+    if (kh == 0) {
+      endc[WROWS * w + l32] = (my_a < L) ? cA : 0.f;
+      endc[BLANE + WROWS * w + l32] = (my_a < L) ? cB : 0.f;
+    }
+    __syncthreads();
+    if (tid < 2 * kHeadDim) {
+      const int e = tid / kHeadDim, d = tid % kHeadDim;
+      float acc = 0.f;
+      for (int x = 0; x < BLANE; ++x) acc = fmaf(endc[e * BLANE + x], bf_bits2f(xs[x * TSTR + d]), acc);
+      const int row = e == 0 ? V::rowA(span) : V::rowB(span);
+      prow[(int64_t)row * kHeadDim + d] = acc;
+    }
+    // dX += cA T[rowA] + cB T[rowB]
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * db + 8 * (r >> 2) + 4 * kh + (r & 3);
+        const float ta = bf_bits2f(trow[(int64_t)V::rowA(span) * kHeadDim + d]);
+        const float tb = bf_bits2f(trow[(int64_t)V::rowB(span) * kHeadDim + d]);
+        gacc[db][r] = fmaf(cA, ta, fmaf(cB, tb, gacc[db][r]));
+      }
+  }
+
+  // ---- T-XL key side: dK += u * colsum; du partial = sum_j colsum_j k_j ----
+  if constexpr (MECH == MECH_TXL && DIR == 1) {
+    colsum += xhalf(colsum);
+    const float* u = a.bias_a + (int64_t)h * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * db + 8 * (r >> 2) + 4 * kh + (r & 3);
+        gacc[db][r] = fmaf(colsum, u[d], gacc[db][r]);
+      }
+    float* csum = lsd_s;   // the per-query vectors are dead after the sweep
+    __syncthreads();
+    if (kh == 0) csum[WROWS * w + l32] = (my_a < L) ? colsum : 0.f;
+    __syncthreads();
+    if (tid < kHeadDim) {
+      float acc = 0.f;
+      for (int x = 0; x < BLANE && A0 + x < L; ++x)
+        acc = fmaf(csum[x], bf_bits2f(xg[(int64_t)(A0 + x) * kHeadDim + tid]), acc);
+      a.part_kv[owner * kHeadDim + tid] = acc;
+    }
+  }
+
+  // ---- store dX (dQ or dK) and dV ----
+  if (my_a < L) {
+    T* gx = (T*)(DIR == 0 ? a.dq : a.dk) + bh_off + (int64_t)my_a * kHeadDim;
+    T* gv = (T*)a.dv + bh_off + (int64_t)my_a * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * db + 8 * g + 4 * kh;
+        u32x2 pk = {pack_bf16x2(gacc[db][4 * g] * s, gacc[db][4 * g + 1] * s),
+                    pack_bf16x2(gacc[db][4 * g + 2] * s, gacc[db][4 * g + 3] * s)};
+        *(u32x2*)(gx + d) = pk;
+        if constexpr (DIR == 1) {
+          u32x2 pv = {pack_bf16x2(vacc[db][4 * g], vacc[db][4 * g + 1]),
+                      pack_bf16x2(vacc[db][4 * g + 2], vacc[db][4 * g + 3])};
+          *(u32x2*)(gv + d) = pv;
+        }
+      }
+  }
+}
+
+// Variants whose LDS footprint leaves room for two workgroups per CU are compiled for two
+// waves per SIMD (at most 256 registers per lane); the others for one.
+template <int MECH, int DIR, int PART>
+__global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
+  bwd_body<MECH, DIR, PART>(a);
+}
+template <int MECH, int DIR, int PART>
+__global__ __launch_bounds__(256, 1) void bwd_kernel_1wg(BwdArgs a) {
+  bwd_body<MECH, DIR, PART>(a);
+}
+}  // namespace relpos

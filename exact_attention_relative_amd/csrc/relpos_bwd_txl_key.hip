@@ -1,0 +1,12 @@
+// The T-XL key-side backward pass (dK, dV and the r-window table GEMM), alone in this
+// translation unit so that it can be compiled with options of its own (the build adds the
+// AMDGPU scheduler's register-pressure trackers, which halve its spills).
+#include "relpos_bwd_body.h"
+
+namespace relpos {
+
+void launch_bwd_txl_key(const BwdArgs& a, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_kernel<MECH_TXL, 1, 0>), grid, dim3(256), 0, stream, a);
+}
+
+}  // namespace relpos

@@ -190,6 +190,29 @@ def summarize_stats(stats_csv, out, cmd, title):
         f.write("\n".join(lines) + "\n")
 
 
+def summarize_trace_by_grid(trace_csv, out, cmd, title, pattern):
+    """Mean / min duration per (kernel, grid size) of the kernels whose name contains `pattern`,
+    from a rocprofv3 kernel trace (one row per dispatch)."""
+    rows = _pmc_rows(trace_csv)
+    groups = {}
+    for r in rows:
+        if pattern not in r["Kernel_Name"]:
+            continue
+        name = r["Kernel_Name"].replace("relpos::", "").replace("(anonymous namespace)::", "")
+        name = re.sub(r"\(.*", "", name).replace("void ", "")
+        grid = int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1)
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups.setdefault((name, grid), []).append(dur)
+    lines = [f"# {title}", "", "Commands (run from the repository root on one MI355X):", "",
+             "```", cmd, "```", "",
+             "| kernel | workgroups | dispatches | mean (us) | min (us) |",
+             "|---|---:|---:|---:|---:|"]
+    for (name, grid), d in sorted(groups.items()):
+        lines.append(f"| `{name}` | {grid} | {len(d)} | {float(np.mean(d)):.1f} | {min(d):.1f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 SQ_SET1 = ("SQ_WAVES SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_LDS SQ_INSTS_VALU_TRANS_F32 "
            "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_WAVE_CYCLES SQ_BUSY_CYCLES")
 SQ_SET2 = ("SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS SQ_LDS_BANK_CONFLICT "
@@ -501,6 +524,8 @@ def main():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV")
     ap.add_argument("--summarize-sq", nargs=2, metavar=("SET1_CSV", "SET2_CSV"))
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("KERNEL_TRACE_CSV", "NAME_PATTERN"),
+                    help="per (kernel, grid) durations from a kernel trace")
     ap.add_argument("--copy-mib", type=int, default=1024)
     ap.add_argument("--out")
     ap.add_argument("--cmd", default="")
@@ -514,6 +539,10 @@ def main():
         return
     if args.summarize_sq:
         summarize_sq(*args.summarize_sq, args.out, args.cmd)
+        return
+    if args.summarize_trace:
+        trace_csv, pattern = args.summarize_trace
+        summarize_trace_by_grid(trace_csv, args.out, args.cmd, args.title, pattern)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "

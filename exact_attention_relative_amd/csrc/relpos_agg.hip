@@ -19,13 +19,23 @@ __device__ __forceinline__ float strided_sum(const float* __restrict__ p, int64_
   return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
 }
 
-// out[r * 64 + d] = scale * sum_{o < nown} part[o * stride + r * 64 + d]
-__global__ void agg_rows_kernel(const float* __restrict__ part, int64_t stride, int nown,
-                                int64_t nelem, float scale, float* __restrict__ out) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= nelem) return;
-  const float acc = nown > 0 ? strided_sum(part + e, stride, nown) : 0.f;
-  out[e] = acc * scale;
+// out[e] = scale * sum_{o < nown} part[o * stride + e]: 64 elements per workgroup, the owners
+// split over four thread groups (group g takes owners o = g mod 4, each with eight loads in
+// flight), whose sums are added in a fixed tree: ((g0 + g1) + (g2 + g3)).
+__global__ __launch_bounds__(256) void agg_rows_kernel(const float* __restrict__ part,
+                                                       int64_t stride, int nown, int64_t nelem,
+                                                       float scale, float* __restrict__ out) {
+  __shared__ float sh[4][64];
+  const int g = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t e = (int64_t)blockIdx.x * 64 + l;
+  float acc = 0.f;
+  if (e < nelem && g < nown) {
+    const int n = (nown - g + 3) / 4;   // owners g, g + 4, ...
+    acc = strided_sum(part + (int64_t)g * stride + e, 4 * stride, n);
+  }
+  sh[g][l] = acc;
+  __syncthreads();
+  if (g == 0 && e < nelem) out[e] = ((sh[0][l] + sh[1][l]) + (sh[2][l] + sh[3][l])) * scale;
 }
 
 // Owner (workgroup) of batch b, head h, block position p, and the first lane offset of its
@@ -214,7 +224,7 @@ static inline int nblk(int64_t n, int t) { return (int)((n + t - 1) / t); }
 hipError_t launch_agg_rows(const float* part, int64_t stride, int nown, int64_t nelem, float scale,
                            float* out, hipStream_t st) {
   if (nelem == 0) return hipSuccess;
-  hipLaunchKernelGGL(agg_rows_kernel, dim3(nblk(nelem, 256)), dim3(256), 0, st, part, stride, nown,
+  hipLaunchKernelGGL(agg_rows_kernel, dim3(nblk(nelem, 64)), dim3(256), 0, st, part, stride, nown,
                      nelem, scale, out);
   return hipGetLastError();
 }

@@ -360,7 +360,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if constexpr (V::CLIP && V::HAS_COL) {
       if (tid < 2 * BOTH) {
         const int yy = b0 + (tid >> 1);
-        ovec_s[tid] = (yy < L) ? oc_g[((int64_t)bh * L + yy) * 2 + (tid & 1)] : 0.f;
+        // end A values of the 64 streamed rows, then end B: each a contiguous vector
+        ovec_s[(tid & 1) * BOTH + (tid >> 1)] = (yy < L) ? oc_g[((int64_t)bh * L + yy) * 2 + (tid & 1)] : 0.f;
       }
     }
     if constexpr (DIR == 1) {
@@ -439,15 +440,23 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     f32x16 sc[2];
     Op<NP> yop[2][4];
     if (!wave_none) {
-      // T-XL query side: the scores start from u.k of each streamed key
-      if constexpr (MECH == MECH_TXL && DIR == 0) other_dot_lane<NP, true>(sc, ys, xop, yop, ovec_s);
-      else other_dot_lane<NP>(sc, ys, xop, yop);
+      if constexpr (MECH == MECH_TXL && DIR == 0) {
+        // T-XL query side: the scores start from u.k of each streamed key
+        other_dot_lane<NP, true>(sc, ys, xop, yop, ovec_s);
+      } else if constexpr (V::CLIP && V::HAS_COL) {
+        // a column-clipped wave tile starts its scores from the end-row constant of each
+        // streamed row
+        if (ccls != 0) other_dot_lane<NP, true>(sc, ys, xop, yop, ovec_s + (ccls == 1 ? 0 : BOTH));
+        else other_dot_lane<NP>(sc, ys, xop, yop);
+      } else {
+        other_dot_lane<NP>(sc, ys, xop, yop);
+      }
     }
     float lconst = 0.f;   // per-lane additive term (y units)
     if constexpr (V::HAS_COL) {
       if (!wave_none) {
         if (V::CLIP && ccls != 0) {
-          add_other_vec(sc, ovec_s + (ccls == 1 ? 0 : 1), 2);
+          // already in the accumulator start
         } else if constexpr (V::TG1) {
           col_skew_add<NP, true, true>(sc, win, (BLANE - WROWS) - WROWS * w, 0, ys, gs, xrot);
           col_skew_add<NP, true, true>(sc, win, (BLANE - WROWS) - WROWS * w, 1, ys, gs, xrot);

@@ -158,7 +158,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     if constexpr (MECH == MECH_DEBERTA) {
       if (tid < 2 * BOTH) {
         const int jj = j0 + (tid >> 1);
-        kvec_s[tid] = (jj < L) ? a.keyc[((int64_t)bh * L + jj) * 2 + (tid & 1)] : 0.f;
+        // end A values of the 64 keys, then end B: each a contiguous vector
+        kvec_s[(tid & 1) * BOTH + (tid >> 1)] = (jj < L) ? a.keyc[((int64_t)bh * L + jj) * 2 + (tid & 1)] : 0.f;
       }
     }
     if (j0 + BOTH <= j_hi) {
@@ -181,9 +182,16 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     f32x16 sc[2];
     Op<NP> kop[2][4];
     if (!wave_none) {
-      // T-XL: the scores start from u.k of each key
-      if constexpr (MECH == MECH_TXL) other_dot_lane<NP, true>(sc, ks, qop, kop, kvec_s);
-      else other_dot_lane<NP>(sc, ks, qop, kop);
+      if constexpr (MECH == MECH_TXL) {
+        // T-XL: the scores start from u.k of each key
+        other_dot_lane<NP, true>(sc, ks, qop, kop, kvec_s);
+      } else if constexpr (MECH == MECH_DEBERTA) {
+        // a clipped wave tile starts its scores from the keys' end-row constants
+        if (cls != 0) other_dot_lane<NP, true>(sc, ks, qop, kop, kvec_s + (cls == 2 ? 0 : BOTH));
+        else other_dot_lane<NP>(sc, ks, qop, kop);
+      } else {
+        other_dot_lane<NP>(sc, ks, qop, kop);
+      }
     }
     float rowconst = 0.f;
     // ---- relative terms (row side) ----
@@ -213,8 +221,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
       }
     } else if constexpr (MECH == MECH_DEBERTA) {
       if (!wave_none) {
-        if (cls == 2) { rowconst = rcB; add_other_vec(sc, kvec_s + 0, 2); }        // delta >= k
-        else if (cls == 1) { rowconst = rcA; add_other_vec(sc, kvec_s + 1, 2); }   // delta <= -k
+        if (cls == 2) rowconst = rcB;        // delta >= k (key term in the accumulator start)
+        else if (cls == 1) rowconst = rcA;   // delta <= -k
         else {
           f32x16 g[3];
           row_products<NP, false>(g, win, WROWS * w, qop);

@@ -313,19 +313,6 @@ __device__ __forceinline__ void add_offset_vec(f32x16 s[2], const float* vec, in
     }
 }
 
-// s[b][r] += vec[y * stride] (a per-other-row term, broadcast over lanes).
-__device__ __forceinline__ void add_other_vec(f32x16 s[2], const float* vec, int stride) {
-  const int lane = __lane_id();
-  const int kh = lane >> 5;
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
-      s[b][r] += vec[y * stride];
-    }
-}
-
 // Operand whose k index runs down 16 consecutive rows of an LDS tile (row-major, TSTR):
 // 32x32x16 A/B layout with m/n = column col0 + (lane % 32) and k = rows row0 + (8 i + 4 kh
 // + j) as the P / dS register permutation expects (slot j < 4: row0 + 4 kh + j, slot

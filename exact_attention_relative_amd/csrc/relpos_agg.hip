@@ -204,19 +204,16 @@ __global__ void agg_txl_du_kernel(const float* __restrict__ pkv, int B, int H, i
   du[idx] = acc * s;
 }
 
-// ALiBi dm[h] = -sum_delta |delta| diag_h[delta]: one workgroup per head, each thread a fixed
-// strided subset of offsets, then the fixed-order block reduction.
-__global__ void agg_alibi_kernel(const float* __restrict__ diag, int L, float* __restrict__ dm) {
-  __shared__ float sh[256];
-  const int h = blockIdx.x;
-  const int n = 2 * L - 1;
+// ALiBi dm[h] = -sum over the (batch, query block) owners of head h of their sums of
+// dS |i - j|, in ascending owner order.
+__global__ void agg_alibi_kernel(const float* __restrict__ part, int B, int H, int nb,
+                                 float* __restrict__ dm) {
+  const int h = blockIdx.x * blockDim.x + threadIdx.x;
+  if (h >= H) return;
   float acc = 0.f;
-  for (int x = threadIdx.x; x < n; x += 256) {
-    const int delta = x - (L - 1);
-    acc = fmaf((float)(delta < 0 ? -delta : delta), diag[(int64_t)h * n + x], acc);
-  }
-  const float tot = block_sum(acc, sh);
-  if (threadIdx.x == 0) dm[h] = -tot;
+  for (int b = 0; b < B; ++b)
+    for (int p = 0; p < nb; ++p) acc += part[((int64_t)b * H + h) * nb + p];
+  dm[h] = -acc;
 }
 
 static inline int nblk(int64_t n, int t) { return (int)((n + t - 1) / t); }
@@ -237,8 +234,8 @@ hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool
   return hipGetLastError();
 }
 
-hipError_t launch_agg_alibi(const float* diag, int H, int L, float* dm, hipStream_t st) {
-  hipLaunchKernelGGL(agg_alibi_kernel, dim3(H), dim3(256), 0, st, diag, L, dm);
+hipError_t launch_agg_alibi(const float* part, int B, int H, int nb, float* dm, hipStream_t st) {
+  hipLaunchKernelGGL(agg_alibi_kernel, dim3(nblk(H, 64)), dim3(64), 0, st, part, B, H, nb, dm);
   return hipGetLastError();
 }
 

@@ -241,7 +241,7 @@ AttnShape make_shape(const relpos_desc* d, const Plan& p) {
   s.L = p.L;
   s.wl = d->window_left;
   s.wr = d->window_right;
-  s.mech = d->mech == RELPOS_ALIBI ? MECH_T5 : d->mech;   // ALiBi uses the LUT path
+  s.mech = d->mech;   // RELPOS_* and MECH_* share their values
   s.span = d->rel_span;
   s.nrel = p.nrel;
   s.txl_off = p.txl_off;
@@ -389,6 +389,7 @@ int relpos_attn_fwd(const relpos_desc* desc, const void* q, const void* k, const
     a.lut = (const float*)(ws + p.off_lut);
     a.bucket = (const int*)(ws + p.off_bucket);
   }
+  if (desc->mech == RELPOS_ALIBI) a.slopes = bias_a;
   if (desc->mech == RELPOS_SHAW || desc->mech == RELPOS_DEBERTA) a.rowc = (const float*)(ws + p.off_rowc);
   if (desc->mech == RELPOS_DEBERTA) a.keyc = (const float*)(ws + p.off_keyc);
   if (desc->mech == RELPOS_TXL) {
@@ -508,8 +509,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
       if (e == hipSuccess) e = launch_agg_t5(diag, a.bucket, p.H, p.L, desc->num_buckets, dbias_a, s);
       break;
     case RELPOS_ALIBI:
-      e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, p.nrt, diag, s);
-      if (e == hipSuccess) e = launch_agg_alibi(diag, p.H, p.L, dbias_a, s);
+      e = launch_agg_alibi(a.part_qv, p.B, p.H, p.nb, dbias_a, s);
       break;
     case RELPOS_SHAW:
       e = launch_agg_rows(a.part_q, p.part_q_stride, p.owners, p.part_q_stride, p.scale, drel_a, s);

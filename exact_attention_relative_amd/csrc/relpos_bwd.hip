@@ -15,7 +15,8 @@ constexpr bool split_pass() {
 }
 template <int MECH, int DIR, int PART>
 constexpr bool two_wg() {
-  return MECH == MECH_T5 || MECH == MECH_TXL || (DIR == 1 && MECH == MECH_SHAW) || PART == 1;
+  return MECH == MECH_T5 || MECH == MECH_ALIBI || MECH == MECH_TXL || (DIR == 1 && MECH == MECH_SHAW) ||
+         PART == 1;
 }
 template <int MECH, int DIR, int PART>
 static void launch_part(const BwdArgs& a, dim3 grid, hipStream_t stream) {
@@ -46,6 +47,7 @@ static hipError_t launch_bwd_dir(const BwdArgs& a, hipStream_t stream) {
     case MECH_SHAW: launch_one<MECH_SHAW, DIR>(a, grid, stream); break;
     case MECH_TXL: launch_one<MECH_TXL, DIR>(a, grid, stream); break;
     case MECH_DEBERTA: launch_one<MECH_DEBERTA, DIR>(a, grid, stream); break;
+    case MECH_ALIBI: launch_one<MECH_ALIBI, DIR>(a, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

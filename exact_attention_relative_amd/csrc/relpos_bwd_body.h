@@ -37,8 +37,9 @@ static_assert(BOTH * ESTRT * 2 <= NWAVE * WROWS * GS2 * 4, "E2T fits the column-
 // the light pass's partials into the final outputs.
 template <int MECH, int DIR, int PART>
 struct BV {
-  static constexpr bool HAS_ROW = DIR == 0 ? MECH != MECH_T5 : MECH == MECH_DEBERTA;
-  static constexpr bool HAS_COL = DIR == 0 ? MECH == MECH_DEBERTA : MECH != MECH_T5;
+  static constexpr bool LUTP = MECH == MECH_T5 || MECH == MECH_ALIBI;   // per-offset bias LUT
+  static constexpr bool HAS_ROW = DIR == 0 ? !LUTP : MECH == MECH_DEBERTA;
+  static constexpr bool HAS_COL = DIR == 0 ? MECH == MECH_DEBERTA : !LUTP;
   static constexpr bool LIGHT = PART == 1;
   static constexpr bool FAT = PART == 2;
   static constexpr bool ROW = HAS_ROW && !LIGHT;
@@ -112,8 +113,12 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   __shared__ __attribute__((aligned(16))) float gsb_raw[V::GSB ? NWAVE * WROWS * GS2 + 2 * GSG : 4];
   __shared__ __attribute__((aligned(16))) uint16_t ebuf[V::EBUF ? WIN * ESTR16 : 8];
   __shared__ __attribute__((aligned(16))) uint16_t xs[V::EBUF ? BLANE * TSTR : 8];   // lane rows X
-  __shared__ __attribute__((aligned(16))) float vec_s[MECH == MECH_T5 ? WIN : 4];  // T5 LUT slice
-  constexpr int NOVEC = (MECH == MECH_TXL && DIR == 0) ? BOTH : (V::CLIP && V::HAS_COL ? 2 * BOTH : 4);
+  __shared__ __attribute__((aligned(16))) float vec_s[V::LUTP ? WIN : 4];  // bias LUT slice
+  // T-XL u.k / clipped end-row constants / ALiBi ramps +m y / s and -m y / s
+  constexpr int NOVEC = (MECH == MECH_TXL && DIR == 0)
+                            ? BOTH
+                            : ((V::CLIP && V::HAS_COL) || MECH == MECH_ALIBI ? 2 * BOTH : 4);
+  __shared__ float red_s[MECH == MECH_ALIBI ? NWAVE : 1];   // ALiBi: per-wave slope-gradient sums
   __shared__ __attribute__((aligned(16))) float ovec_s[NOVEC];   // per-other-row constants
   __shared__ __attribute__((aligned(16))) float lsd_s[DIR == 1 ? 2 * BOTH : 4];   // LSE*log2e, D per query
   __shared__ __attribute__((aligned(16))) float endc[V::CLIP && V::ROW ? 2 * BLANE : 4];
@@ -289,6 +294,19 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   // the next step's streamed tiles are read into registers while the current step computes
   auto step_base = [&](int st) { return bt0 + st * BOTH; };
   auto step_skipped = [&](int st) { return V::LIGHT && st >= g_first && st <= g_last; };
+  // ALiBi: on a wave tile on one side of the diagonal, -m |i - j| / s = (lane-row term) +
+  // (streamed-row term), the latter a ramp over the 64 streamed rows: the ramp starts the score
+  // accumulators and the lane-row term is the lane constant, so those tiles add nothing per
+  // element; straddling tiles read the per-offset LUT.  The query-side pass also accumulates
+  // dm = -sum dS |i - j| per lane (the slope gradient), without per-offset sums.
+  float am = 0.f, amacc = 0.f;
+  if constexpr (MECH == MECH_ALIBI) {
+    am = a.bias_a[h] / s;
+    if (tid < BOTH) {
+      ovec_s[tid] = am * (float)tid;
+      ovec_s[BOTH + tid] = -am * (float)tid;
+    }
+  }
   int next = 0;
   while (next < nsteps && step_skipped(next)) ++next;
   TilePrefetch<T> py, py2;
@@ -328,6 +346,13 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       }
       wg_general = wg_gen(b0);
     }
+    int acls = 0;            // ALiBi side of the diagonal: 1 every i >= j, 2 every i < j, 0 both
+    bool lut_needed = true;  // ALiBi: some wave of the workgroup straddles the diagonal
+    if constexpr (MECH == MECH_ALIBI) {
+      if (dlo >= 0) acls = 1; else if (dhi < 0) acls = 2;
+      const int wlo = DIR == 0 ? cwin - 63 : -(cwin + 127), whi = DIR == 0 ? cwin + 127 : -(cwin - 63);
+      lut_needed = wlo < 0 && whi >= 0;
+    }
     int t5cls = 0;
     if constexpr (MECH == MECH_T5) {
       const int lo = clampi(dlo, 1 - L, L - 1), hi = clampi(dhi, 1 - L, L - 1);
@@ -347,7 +372,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       py.store(ys);
       py2.store(y2s);
     }
-    if constexpr (MECH == MECH_T5) {
+    if constexpr (V::LUTP) {
+      if (lut_needed)
       for (int x = tid; x < WIN; x += 256) {
         const int lam = cwin - 63 + x;
         const int d = DIR == 0 ? lam : -lam;
@@ -448,6 +474,12 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         // streamed row
         if (ccls != 0) other_dot_lane<NP, true>(sc, ys, xop, yop, ovec_s + (ccls == 1 ? 0 : BOTH));
         else other_dot_lane<NP>(sc, ys, xop, yop);
+      } else if constexpr (MECH == MECH_ALIBI) {
+        // streamed-row ramp: +m y / s when the streamed rows are keys below the queries
+        // (query side, i >= j) or queries above the keys (key side, i < j), else -m y / s
+        const bool plus = (DIR == 0) == (acls == 1);
+        if (acls != 0) other_dot_lane<NP, true>(sc, ys, xop, yop, ovec_s + (plus ? 0 : BOTH));
+        else other_dot_lane<NP>(sc, ys, xop, yop);
       } else {
         other_dot_lane<NP>(sc, ys, xop, yop);
       }
@@ -503,6 +535,16 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         if (DIR == 1) lconst = ukl;
       }
     }
+    if constexpr (MECH == MECH_ALIBI) {
+      if (!wave_none) {
+        // lane-row term: -m (i - b0) / s or +m (i - b0) / s on the query side, the key side
+        // mirrored (its lane rows are keys)
+        const float da = am * (float)(my_a - b0);
+        if (acls == 1) lconst = DIR == 0 ? -da : da;
+        else if (acls == 2) lconst = DIR == 0 ? da : -da;
+        else add_offset_vec(sc, vec_s, WROWS * w);
+      }
+    }
 
     f32x16 ds[2];
     Op<NP> dso[4];   // dS as bf16 MFMA operands (16 other-side rows each)
@@ -550,6 +592,31 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int r = 0; r < 16; ++r) colsum += ds[b][r];
+      }
+      if constexpr (MECH == MECH_ALIBI && DIR == 0) {
+        // |i - j| = (my_a - b0) - y below the diagonal, y - (my_a - b0) above, with y the
+        // streamed row of the register (a constant plus 4 kh)
+        const float di = (float)(my_a - b0);
+        if (acls != 0) {
+          float rs = 0.f, yw = 0.f;
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              rs += ds[b][r];
+              yw = fmaf((float)(32 * b + 8 * (r >> 2) + (r & 3)), ds[b][r], yw);
+            }
+          yw = fmaf((float)(4 * kh), rs, yw);
+          amacc += (acls == 1) ? fmaf(di, rs, -yw) : fmaf(-di, rs, yw);
+        } else {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float y = (float)(32 * b + 8 * (r >> 2) + 4 * kh + (r & 3));
+              amacc = fmaf(fabsf(di - y), ds[b][r], amacc);
+            }
+        }
       }
       // ---- content gradients (P and dS packed to bf16 once; the fp32 copies can die) ----
 #pragma unroll
@@ -810,6 +877,15 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         dcarry = val;
       }
     }
+  }
+
+  // ---- ALiBi: this workgroup's share of sum dS |i - j|, in a fixed order ----
+  if constexpr (MECH == MECH_ALIBI && DIR == 0) {
+    float t = amacc + xhalf(amacc);
+    for (int m = 1; m < 32; m <<= 1) t += __shfl_xor(t, m);
+    if (lane == 0) red_s[w] = t;
+    __syncthreads();
+    if (tid == 0) a.part_qv[owner] = (red_s[0] + red_s[1]) + (red_s[2] + red_s[3]);
   }
 
   // ---- final flush of the window accumulators ----

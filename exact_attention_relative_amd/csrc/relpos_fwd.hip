@@ -14,15 +14,18 @@ namespace relpos {
 template <typename T, int MECH>
 __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   constexpr int NP = Elem<T>::NP;
-  constexpr bool REL = (MECH != MECH_T5);
-  constexpr bool VEC = (MECH == MECH_T5);
-  constexpr int KVEC = (MECH == MECH_DEBERTA) ? 2 * BOTH : (MECH == MECH_TXL ? BOTH : 1);
+  constexpr bool LUTP = (MECH == MECH_T5 || MECH == MECH_ALIBI);   // per-offset bias LUT path
+  constexpr bool REL = !LUTP;
+  constexpr bool VEC = LUTP;
+  constexpr int KVEC = (MECH == MECH_DEBERTA || MECH == MECH_ALIBI) ? 2 * BOTH
+                                                                    : (MECH == MECH_TXL ? BOTH : 1);
   __shared__ __attribute__((aligned(16))) uint16_t ks[NP * BOTH * TSTR];
   __shared__ __attribute__((aligned(16))) uint16_t vs[NP * BOTH * TSTR];
   __shared__ __attribute__((aligned(16))) uint16_t win[REL ? NP * WIN * TSTR : 8];
   __shared__ __attribute__((aligned(16))) float gsb[REL ? NWAVE * WROWS * GS2 : 4];
   __shared__ __attribute__((aligned(16))) float vec_s[VEC ? WIN : 4];   // T5 LUT slice
-  __shared__ __attribute__((aligned(16))) float kvec_s[KVEC];           // T-XL u.k / DeBERTa k.Qr ends
+  // T-XL u.k / DeBERTa k.Qr ends / ALiBi ramps +m y / s and -m y / s over a key tile
+  __shared__ __attribute__((aligned(16))) float kvec_s[KVEC];
 
   const AttnShape sh = a.sh;
   const int L = sh.L;
@@ -68,6 +71,19 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     if (my_i < L) {
       rcA = a.rowc[((int64_t)bh * L + my_i) * 2 + 0];
       rcB = a.rowc[((int64_t)bh * L + my_i) * 2 + 1];
+    }
+  }
+
+  // ALiBi: on a wave tile on one side of the diagonal, -m |i - j| / s = (row term) + (key
+  // term) with the key term a ramp over the tile's 64 keys: the ramp starts the score
+  // accumulators and the row term joins the row constant, so those tiles add nothing per
+  // element.  Tiles that straddle the diagonal read the per-offset LUT.
+  float am = 0.f;   // ALiBi: m / s
+  if constexpr (MECH == MECH_ALIBI) {
+    am = a.slopes[h] / s;
+    if (tid < BOTH) {
+      kvec_s[tid] = am * (float)tid;
+      kvec_s[BOTH + tid] = -am * (float)tid;
     }
   }
 
@@ -118,6 +134,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     } else if constexpr (MECH == MECH_DEBERTA) {
       if (dlo >= span) cls = 2; else if (dhi <= -span) cls = 1;
       wg_general = !((wg_dlo >= span) || (wg_dhi <= -span));
+    } else if constexpr (MECH == MECH_ALIBI) {
+      // side of the diagonal: 1 every i >= j, 2 every i < j, 0 both
+      if (dlo >= 0) cls = 1; else if (dhi < 0) cls = 2;
     } else if constexpr (MECH == MECH_T5) {
       // one bucket for the whole wave tile: the offsets lie on one side of 0 (where the
       // bucket map is monotone) and both ends share a bucket
@@ -128,7 +147,9 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     __syncthreads();  // previous tile's LDS reads are done
     pk.store(ks);
     pv.store(vs);
-    if constexpr (MECH == MECH_T5) {
+    if constexpr (LUTP) {
+      // (ALiBi reads the slice only on workgroup tiles that straddle the diagonal)
+      if (MECH != MECH_ALIBI || (wg_dlo < 0 && wg_dhi >= 0))
       for (int x = tid; x < WIN; x += 256) {
         const int d = wg_dlo + x;   // window row x <-> delta = i0 - j0 - 63 + x
         vec_s[x] = (d > -L && d < L) ? a.lut[(int64_t)h * (2 * L - 1) + d + L - 1] : 0.f;
@@ -189,6 +210,10 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
         // a clipped wave tile starts its scores from the keys' end-row constants
         if (cls != 0) other_dot_lane<NP, true>(sc, ks, qop, kop, kvec_s + (cls == 2 ? 0 : BOTH));
         else other_dot_lane<NP>(sc, ks, qop, kop);
+      } else if constexpr (MECH == MECH_ALIBI) {
+        // i >= j: -m (i - j0) / s + m (j - j0) / s; i < j: m (i - j0) / s - m (j - j0) / s
+        if (cls != 0) other_dot_lane<NP, true>(sc, ks, qop, kop, kvec_s + (cls == 1 ? 0 : BOTH));
+        else other_dot_lane<NP>(sc, ks, qop, kop);
       } else {
         other_dot_lane<NP>(sc, ks, qop, kop);
       }
@@ -202,6 +227,12 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
         } else {
           add_offset_vec(sc, vec_s, WROWS * w);
         }
+      }
+    } else if constexpr (MECH == MECH_ALIBI) {
+      if (!wave_none) {
+        if (cls == 1) rowconst = -am * (float)(my_i - j0);
+        else if (cls == 2) rowconst = am * (float)(my_i - j0);
+        else add_offset_vec(sc, vec_s, WROWS * w);
       }
     } else if constexpr (MECH == MECH_SHAW) {
       if (!wave_none) {
@@ -346,8 +377,8 @@ template <typename T, int MECH>
 __global__ __launch_bounds__(256, 1) void fwd_kernel_1wg(FwdArgs a) {
   fwd_body<T, MECH>(a);
 }
-// T5 keeps only K, V and a LUT slice in LDS (19 KB): three workgroups per CU when the
-// registers fit 168 per lane.
+// T5 and ALiBi keep only K, V and a LUT slice in LDS (19 KB): three workgroups per CU when
+// the registers fit 168 per lane.
 template <typename T, int MECH>
 __global__ __launch_bounds__(256, 3) void fwd_kernel_3wg(FwdArgs a) {
   fwd_body<T, MECH>(a);
@@ -355,7 +386,7 @@ __global__ __launch_bounds__(256, 3) void fwd_kernel_3wg(FwdArgs a) {
 
 template <typename T, int MECH>
 static void launch_one(const FwdArgs& a, dim3 grid, hipStream_t stream) {
-  if constexpr (Elem<T>::NP == 1 && MECH == MECH_T5)
+  if constexpr (Elem<T>::NP == 1 && (MECH == MECH_T5 || MECH == MECH_ALIBI))
     hipLaunchKernelGGL((fwd_kernel_3wg<T, MECH>), grid, dim3(256), 0, stream, a);
   else if constexpr (Elem<T>::NP == 1)
     hipLaunchKernelGGL((fwd_kernel<T, MECH>), grid, dim3(256), 0, stream, a);
@@ -372,6 +403,7 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
     case MECH_SHAW: launch_one<T, MECH_SHAW>(a, grid, stream); break;
     case MECH_TXL: launch_one<T, MECH_TXL>(a, grid, stream); break;
     case MECH_DEBERTA: launch_one<T, MECH_DEBERTA>(a, grid, stream); break;
+    case MECH_ALIBI: launch_one<T, MECH_ALIBI>(a, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -51,6 +51,7 @@ struct FwdArgs {
   const float* rowc;   // Shaw / DeBERTa: per-query clipped-end products, [B, H, L, 2]
   const float* keyc;   // DeBERTa: per-key clipped-end p2c products, [B, H, L, 2]
   const int* bucket;   // T5: bucket of every offset, [2L - 1]
+  const float* slopes; // ALiBi: m per head, [H]
 };
 
 struct BwdArgs {
@@ -120,8 +121,8 @@ hipError_t launch_agg_rows(const float* part, int64_t stride, int nown, int64_t 
                            float* out, hipStream_t st);
 hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool rev, int nrt,
                            float* diag, hipStream_t st);
-// ALiBi dm[h] = -sum over offsets |delta| diag_h[delta] (fixed order)
-hipError_t launch_agg_alibi(const float* diag, int H, int L, float* dm, hipStream_t st);
+// ALiBi dm[h] = -sum over the owners (b, query block) of head h of part[owner] (fixed order)
+hipError_t launch_agg_alibi(const float* part, int B, int H, int nb, float* dm, hipStream_t st);
 hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int nbk, float* dbeta,
                          hipStream_t st);
 // T-XL dr from the key-side r partials of the slice group [s0, s0 + ns) (partial slot of slice

@@ -85,6 +85,8 @@ __device__ __forceinline__ Op<1> op_from_lds_perm(const uint16_t* base, int e) {
 // Zero the slots of an op_from_lds_perm operand (row t, columns ybase + perm k) outside the
 // band y <= t <= y + 127.
 __device__ __forceinline__ void band_mask(Op<1>& o, int t, int ybase) {
+  // recomputed where used: hoisted out of the step loop, the masks would hold registers
+  asm volatile("" : "+v"(t));
   const int kh = __lane_id() >> 5;
   u32x4 v = __builtin_bit_cast(u32x4, o.p[0]);
 #pragma unroll
@@ -728,6 +730,11 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       // E2T[y][t] = dS[y][x] with t = y - x + 127, in the column-skew buffer's space: for one
       // register, the 32 lanes of a half-wave write 32 consecutive t
       uint16_t* e2t = (uint16_t*)gsb;
+      if (wave_none) {   // a wave with no pairs contributes zeros (wave-uniform)
+        const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) dso[cc].p[0] = u4_to_bf8(z);
+      }
       __syncthreads();   // every wave's column-skew reads are done
       uint16_t* eb = e2t + (127 - (WROWS * w + l32) + 4 * kh) + 4 * kh * ESTRT;
 #pragma unroll
@@ -739,8 +746,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           const int r = 8 * (cc & 1) + i;
           const int yc = 32 * (cc >> 1) + 8 * (r >> 2) + (r & 3);   // y - 4 kh
           const uint32_t word = wv[i >> 1];
-          const uint16_t bits = (uint16_t)((i & 1) ? (word >> 16) : (word & 0xFFFFu));
-          eb[yc * (ESTRT + 1)] = wave_none ? (uint16_t)0 : bits;
+          eb[yc * (ESTRT + 1)] = (uint16_t)((i & 1) ? (word >> 16) : (word & 0xFFFFu));
         }
       }
       __syncthreads();

@@ -38,6 +38,19 @@ __device__ __forceinline__ f32x4 win_vec4(const uint16_t* win, int x) {   // x %
 // ---------------------------------------------------------------------------------------
 // Staging (all 256 threads).  Tiles hold NP bf16 planes of [rows][TSTR].
 // ---------------------------------------------------------------------------------------
+// base + e elements.  By default the offset is taken in 32 bits (e < 2^32 / sizeof(T)), so the
+// address is the wave-uniform base in scalar registers plus one 32-bit vector register.  A
+// translation unit that defines RELPOS_STAGE_ADDR64 keeps 64-bit per-lane addresses: the T-XL
+// key-side pass, at its 256-register limit, is allocated better that way (measured).
+template <typename T>
+__device__ __forceinline__ const T* stage_addr(const T* base, int64_t e) {
+#ifdef RELPOS_STAGE_ADDR64
+  return base + e;
+#else
+  return (const T*)((const char*)base + (uint32_t)e * (uint32_t)sizeof(T));
+#endif
+}
+
 // 64 consecutive rows of a [*, 64] tensor; rows >= nvalid are zero.
 template <typename T, int NP>
 __device__ __forceinline__ void stage64(uint16_t* tile, const T* base, int row0, int nvalid) {
@@ -46,7 +59,7 @@ __device__ __forceinline__ void stage64(uint16_t* tile, const T* base, int row0,
   const int c = (t & 3) * 16;
   const int plane = BOTH * TSTR;
   if (row0 + r < nvalid) {
-    const T* g = base + (int64_t)(row0 + r) * kHeadDim + c;
+    const T* g = stage_addr(base, (int64_t)(row0 + r) * kHeadDim + c);
     lds_store8<T>(tile, plane, r * TSTR + c, g);
     lds_store8<T>(tile, plane, r * TSTR + c + 8, g + 8);
   } else {
@@ -69,7 +82,7 @@ struct TilePrefetch {
     const int t = threadIdx.x;
     const int r = t >> 2, c = (t & 3) * 16;
     if (row0 + r >= lo && row0 + r < hi) {
-      const u32x4* g = (const u32x4*)(base + (int64_t)(row0 + r) * kHeadDim + c);
+      const u32x4* g = (const u32x4*)stage_addr(base, (int64_t)(row0 + r) * kHeadDim + c);
 #pragma unroll
       for (int i = 0; i < NCH; ++i) v[i] = g[i];
     } else {
@@ -121,7 +134,7 @@ __device__ __forceinline__ void stage_window(uint16_t* win, const T* table, F ro
     const int x = x0 + (t >> 2);
     const int row = rowfn(x);
     if (row >= 0) {
-      const T* g = table + (int64_t)row * kHeadDim + c;
+      const T* g = stage_addr(table, (int64_t)row * kHeadDim + c);
       lds_store8<T>(win, plane, x * TSTR + c, g);
       lds_store8<T>(win, plane, x * TSTR + c + 8, g + 8);
     } else {
@@ -142,7 +155,7 @@ __device__ __forceinline__ void stage_window_rows(uint16_t* win, const T* table,
   const int row = rowfn(x0 + (t >> 2));
   const int e = (p0 + (t >> 2)) * TSTR + c;
   if (row >= 0) {
-    const T* g = table + (int64_t)row * kHeadDim + c;
+    const T* g = stage_addr(table, (int64_t)row * kHeadDim + c);
     lds_store8<T>(win, plane, e, g);
     lds_store8<T>(win, plane, e + 8, g + 8);
   } else {
@@ -203,6 +216,12 @@ __device__ __forceinline__ int wrow(int x, int xrot) {
   const int p = x + xrot;
   return p >= WIN ? p - WIN : p;
 }
+// Physical row of the first row of an aligned block of 16 or 32 window rows (x0 a multiple of
+// the block size, the same in every lane).  Such a block never wraps, since the rotation is a
+// multiple of 64, so its rows stay consecutive and the wrap is decided once, on the scalar unit.
+__device__ __forceinline__ int wrow_block(int x0, int xrot) {
+  return __builtin_amdgcn_readfirstlane(wrow(x0, xrot));
+}
 
 // Row side, all three 32-offset blocks of products in registers (optionally + the per-row
 // value kept in the window's padding, win_vec).  With ROT the window is circular: row x
@@ -215,16 +234,16 @@ __device__ __forceinline__ void row_products(f32x16 g[3], const uint16_t* win, i
 #pragma unroll
   for (int bb = 0; bb < 3; ++bb) {
     g[bb] = f32x16{};
+    const int pb = ROT ? wrow_block(w0 + 32 * bb, xrot) : w0 + 32 * bb;   // w0 % 32 == 0
     if constexpr (ADDVEC) {   // the MFMA accumulates on top of the per-row value
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int x = w0 + 32 * bb + 8 * q4 + 4 * kh;
-        const f32x4 v4 = win_vec4(win, ROT ? wrow(x, xrot) : x);
+        const f32x4 v4 = win_vec4(win, pb + 8 * q4 + 4 * kh);
 #pragma unroll
         for (int i = 0; i < 4; ++i) g[bb][4 * q4 + i] = v4[i];
       }
     }
-    const int prow = ROT ? wrow(w0 + 32 * bb + l32, xrot) : w0 + 32 * bb + l32;
+    const int prow = pb + l32;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, prow * TSTR + 16 * c + 8 * kh);
@@ -271,16 +290,16 @@ __device__ __forceinline__ void col_skew_add(f32x16 s[2], const uint16_t* win, i
   for (int i = 0; i < 2; ++i) {
     const int bb = ob + i;
     h[i] = f32x16{};
+    const int pb = ROT ? wrow_block(w0 + 32 * bb, xrot) : w0 + 32 * bb;   // w0 % 32 == 0
     if constexpr (ADDVEC) {   // the MFMA accumulates on top of the per-row value
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const int x = w0 + 32 * bb + 8 * q4 + 4 * kh;
-        const f32x4 v4 = win_vec4(win, ROT ? wrow(x, xrot) : x);
+        const f32x4 v4 = win_vec4(win, pb + 8 * q4 + 4 * kh);
 #pragma unroll
         for (int j = 0; j < 4; ++j) h[i][4 * q4 + j] = v4[j];
       }
     }
-    const int prow = ROT ? wrow(w0 + 32 * bb + l32, xrot) : w0 + 32 * bb + l32;
+    const int prow = pb + l32;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, prow * TSTR + 16 * c + 8 * kh);
@@ -328,17 +347,12 @@ __device__ __forceinline__ Op<NP> op_rows_tr(const uint16_t* tile, int plane, in
   return op_tr_from_lds<NP>(tile, plane, r * stride + col, (r + 8) * stride + col);
 }
 
-// op_rows_tr over a circular window rotated by xrot: each of the lane's two rows is wrapped.
+// op_rows_tr over a circular window rotated by xrot (row0 a multiple of 16, the same in every
+// lane: the 16 rows read form one block that does not wrap).
 template <int NP>
 __device__ __forceinline__ Op<NP> op_rows_tr_rot(const uint16_t* tile, int plane, int stride,
                                                  int row0, int col0, int xrot) {
-  const int lane = __lane_id();
-  const int g = lane >> 4, i = lane & 15;
-  const int kh = g >> 1;
-  const int col = col0 + 16 * (g & 1) + 4 * (i & 3);
-  const int r = row0 + 4 * kh + (i >> 2);
-  return op_tr_from_lds<NP>(tile, plane, wrow(r, xrot) * stride + col,
-                            wrow(r + 8, xrot) * stride + col);
+  return op_rows_tr<NP>(tile, plane, stride, wrow_block(row0, xrot), col0);
 }
 
 // Operand from an fp32 register block in accumulator layout: 16 consecutive other-side

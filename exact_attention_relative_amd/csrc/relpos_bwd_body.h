@@ -309,6 +309,43 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       ovec_s[BOTH + tid] = -am * (float)tid;
     }
   }
+  // Fat passes (one workgroup per compute unit, so no other workgroup hides their latency; and
+  // registers to spare): the next general step's windows and per-row values are read into
+  // registers one step ahead.
+  WindowPrefetch<T> pwc, pwr;
+  float pov = 0.f, pl2 = 0.f, pdd = 0.f;
+  auto colfn_at = [&](int b0x) {   // column window row x <-> mu = b - a = (b0 - A0 - 127) + x
+    return [=](int x) { return V::col_of((b0x - A0 - (BLANE - 1)) + x, span, nrel, toff); };
+  };
+  auto rowfn_at = [&](int b0x) {   // row window row x <-> lam = A0 - b0 - 63 + x
+    return [=](int x) { return V::row_of(A0 - b0x - 63 + x, span, nrel, toff); };
+  };
+  auto ov_load = [&](int b0x) {   // end A, end B values of the streamed rows (column side)
+    if (tid < 2 * BOTH) {
+      const int yy = b0x + (tid >> 1);
+      pov = (yy < L) ? oc_g[((int64_t)bh * L + yy) * 2 + (tid & 1)] : 0.f;
+    }
+  };
+  auto lsd_load = [&](int b0x) {   // key side: LSE log2(e) and D of the streamed queries
+    if (tid < BOTH) {
+      const int yy = b0x + tid;
+      pl2 = __builtin_inff();
+      pdd = 0.f;
+      if (yy < L) {
+        pl2 = a.lse[(int64_t)bh * L + yy] * kLog2e;
+        if (!(pl2 > kNegInf)) pl2 = __builtin_inff();
+        pdd = a.dsum[(int64_t)bh * L + yy];
+      }
+    }
+  };
+  if constexpr (V::FAT) {
+    if (nsteps > 0) {
+      if constexpr (V::COL) pwc.load(tcol, colfn_at(bt0));
+      if constexpr (V::ROW) pwr.load(trow, rowfn_at(bt0));
+      if constexpr (V::CLIP && V::HAS_COL) ov_load(bt0);
+      if constexpr (DIR == 1) lsd_load(bt0);
+    }
+  }
   int next = 0;
   while (next < nsteps && step_skipped(next)) ++next;
   TilePrefetch<T> py, py2;
@@ -386,13 +423,20 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       if (tid < BOTH) ovec_s[tid] = (b0 + tid < L) ? a.uk[(int64_t)bh * L + b0 + tid] : 0.f;
     }
     if constexpr (V::CLIP && V::HAS_COL) {
-      if (tid < 2 * BOTH) {
-        const int yy = b0 + (tid >> 1);
-        // end A values of the 64 streamed rows, then end B: each a contiguous vector
-        ovec_s[(tid & 1) * BOTH + (tid >> 1)] = (yy < L) ? oc_g[((int64_t)bh * L + yy) * 2 + (tid & 1)] : 0.f;
+      // end A values of the 64 streamed rows, then end B: each a contiguous vector
+      if constexpr (!V::FAT) ov_load(b0);
+      if (tid < 2 * BOTH) ovec_s[(tid & 1) * BOTH + (tid >> 1)] = pov;
+      if constexpr (V::FAT) {
+        if (step + 1 < nsteps) ov_load(b0 + BOTH);
       }
     }
-    if constexpr (DIR == 1) {
+    if constexpr (DIR == 1 && V::FAT) {
+      if (tid < BOTH) {
+        lsd_s[tid] = pl2;
+        lsd_s[BOTH + tid] = pdd;
+      }
+      if (step + 1 < nsteps) lsd_load(b0 + BOTH);
+    } else if constexpr (DIR == 1) {
       if (tid < BOTH) {
         const int yy = b0 + tid;
         float l2 = __builtin_inff(), dd = 0.f;
@@ -424,9 +468,12 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       }
     } else if constexpr (V::ROW && !V::COL) {
       if (wg_general) {
-        stage_window<T, NP>(win, trow, [&](int x) {
-          return V::row_of(cwin - 63 + x, span, nrel, toff);
-        });
+        if constexpr (V::FAT) {
+          pwr.store(win);
+          if (step + 1 < nsteps) pwr.load(trow, rowfn_at(b0 + BOTH));
+        } else {
+          stage_window<T, NP>(win, trow, rowfn_at(b0));
+        }
       }
     }
     // column side first (its window is replaced by the row-side window afterwards)
@@ -450,10 +497,12 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       }
     } else if constexpr (V::COL) {
       if (wg_general) {
-        stage_window<T, NP>(win, tcol, [&](int x) {
-          // column window row x <-> mu = b - a = (b0 - A0 - 127) + x
-          return V::col_of((b0 - A0 - (BLANE - 1)) + x, span, nrel, toff);
-        });
+        if constexpr (V::FAT) {
+          pwc.store(win);
+          if (step + 1 < nsteps) pwc.load(tcol, colfn_at(b0 + BOTH));
+        } else {
+          stage_window<T, NP>(win, tcol, colfn_at(b0));
+        }
       }
     }
     // issue the next step's tile reads (after this step's staging reads have been consumed)
@@ -503,9 +552,12 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if constexpr (V::ROW && V::COL) {
       if (wg_general) {
         __syncthreads();   // column-side window reads done
-        stage_window<T, NP>(win, trow, [&](int x) {
-          return V::row_of(cwin - 63 + x, span, nrel, toff);
-        });
+        if constexpr (V::FAT) {
+          pwr.store(win);
+          if (step + 1 < nsteps) pwr.load(trow, rowfn_at(b0 + BOTH));
+        } else {
+          stage_window<T, NP>(win, trow, rowfn_at(b0));
+        }
         __syncthreads();
       }
     }

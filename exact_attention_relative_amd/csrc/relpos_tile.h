@@ -31,8 +31,10 @@ constexpr int GS2 = 68;              // skew buffer row stride (floats): 64 offs
 __device__ __forceinline__ float* win_vec(uint16_t* win, int x) {
   return (float*)(win + (x >> 2) * TSTR + kHeadDim) + (x & 3);
 }
-__device__ __forceinline__ f32x4 win_vec4(const uint16_t* win, int x) {   // x % 4 == 0
-  return *(const f32x4*)(win + (x >> 2) * TSTR + kHeadDim);
+// Where the values of window rows pb + 4 kh .. + 3 start (pb % 8 == 0, the same in every lane);
+// rows pb + 8 q + 4 kh follow 2 q padded rows further on.
+__device__ __forceinline__ const uint16_t* win_vec4_base(const uint16_t* win, int pb, int kh) {
+  return win + ((pb >> 2) + kh) * TSTR + kHeadDim;
 }
 
 // ---------------------------------------------------------------------------------------
@@ -270,9 +272,10 @@ __device__ __forceinline__ void row_products(f32x16 g[3], const uint16_t* win, i
     g[bb] = f32x16{};
     const int pb = ROT ? wrow_block(w0 + 32 * bb, xrot) : w0 + 32 * bb;   // w0 % 32 == 0
     if constexpr (ADDVEC) {   // the MFMA accumulates on top of the per-row value
+      const uint16_t* vb = win_vec4_base(win, pb, kh);
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v4 = win_vec4(win, pb + 8 * q4 + 4 * kh);
+        const f32x4 v4 = *(const f32x4*)(vb + 2 * q4 * TSTR);
 #pragma unroll
         for (int i = 0; i < 4; ++i) g[bb][4 * q4 + i] = v4[i];
       }
@@ -326,9 +329,12 @@ __device__ __forceinline__ void col_skew_add(f32x16 s[2], const uint16_t* win, i
     h[i] = f32x16{};
     const int pb = ROT ? wrow_block(w0 + 32 * bb, xrot) : w0 + 32 * bb;   // w0 % 32 == 0
     if constexpr (ADDVEC) {   // the MFMA accumulates on top of the per-row value
+      // (addressed row by row: with win_vec4_base the T-XL key-side pass, at its register
+      // limit, is scheduled worse; measured)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
-        const f32x4 v4 = win_vec4(win, pb + 8 * q4 + 4 * kh);
+        const int x = pb + 8 * q4 + 4 * kh;
+        const f32x4 v4 = *(const f32x4*)(win + (x >> 2) * TSTR + kHeadDim);
 #pragma unroll
         for (int j = 0; j < 4; ++j) h[i][4 * q4 + j] = v4[j];
       }

@@ -290,6 +290,26 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   float dcarry = 0.f;                        // diagonal sum of offsets lam = tid (mod 256)
   const int gdb = w & 1, gp = w >> 1;        // GEMM tiles of this wave: d-block, t-block parity
 
+  // Store one window accumulator block to the table partial: register r holds offset
+  // lam0 + 8 (r / 4) + r % 4, column 32 gdb + l32.  Only interior offsets are stored (clipped
+  // ones belong to the end rows); when the whole block is interior its 16 rows are consecutive
+  // table rows, stored from one base without per-element tests.
+  auto flush_block = [&](const f32x16& acc, int lam0) {
+    const int d = 32 * gdb + l32;
+    constexpr int rstep = (MECH == MECH_SHAW && DIR == 0) ? -1 : 1;   // table row per unit lam
+    if (lam0 > V::TA(span) && lam0 + 27 < V::TB(span)) {
+      float* fb = prow + (uint32_t)(V::row_of(lam0, span, nrel, toff) * kHeadDim + d);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) fb[rstep * (8 * (r >> 2) + (r & 3)) * kHeadDim] = acc[r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lam = lam0 + 8 * (r >> 2) + (r & 3);
+        if (lam > V::TA(span) && lam < V::TB(span))
+          prow[(int64_t)V::row_of(lam, span, nrel, toff) * kHeadDim + d] = acc[r];
+      }
+    }
+  };
   float* gs = gsb + (V::GSB ? w * WROWS * GS2 : 0);
   uint16_t* e16 = ebuf;
 
@@ -735,17 +755,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         // slide the window accumulators by two blocks; the block leaving the window is final
         if (step > 0) {
           const int pc = cwin + BOTH;   // previous step's window base (lam = pc - 63 + t)
-          const int a2 = gp + 4;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int t = 32 * a2 + 8 * (r >> 2) + 4 * kh + (r & 3);
-            const int lam = pc - 63 + t;
-            const int d = 32 * gdb + l32;
-            if (lam > V::TA(span) && lam < V::TB(span)) {
-              const int row = V::row_of(lam, span, nrel, toff);
-              prow[(int64_t)row * kHeadDim + d] = racc[2][r];
-            }
-          }
+          flush_block(racc[2], pc - 63 + 32 * (gp + 4) + 4 * kh);
           racc[2] = racc[1];
           racc[1] = racc[0];
           racc[0] = f32x16{};
@@ -951,19 +961,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if (nsteps > 0) {
       const int pc = A0 - bt_last;
 #pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int ab = gp + 2 * i;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * ab + 8 * (r >> 2) + 4 * kh + (r & 3);
-          const int lam = pc - 63 + t;
-          const int d = 32 * gdb + l32;
-          if (lam > V::TA(span) && lam < V::TB(span)) {
-            const int row = V::row_of(lam, span, nrel, toff);
-            prow[(int64_t)row * kHeadDim + d] = racc[i][r];
-          }
-        }
-      }
+      for (int i = 0; i < 3; ++i) flush_block(racc[i], pc - 63 + 32 * (gp + 2 * i) + 4 * kh);
     }
   }
   if constexpr (V::TG1) {

@@ -47,33 +47,42 @@ __device__ __forceinline__ void owner_of(int b, int h, int p, int H, int nb, boo
   lam_base = blk * 128 - L - 64;
 }
 
-// diag[h][delta + L - 1] = sum over (b, block) of the per-offset dS sums
-__global__ void agg_diag_kernel(const float* __restrict__ pdiag, int B, int H, int L, int nb,
-                                int rev, int nrt, float* __restrict__ diag) {
-  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+// diag[h][delta + L - 1] = sum over (b, block) of the per-offset dS sums.  One workgroup per
+// 64 consecutive (head, offset) entries: thread t takes entry t % 64 and the owners of group
+// t / 64 (a quarter of them, consecutive, in ascending order, 16 loads in flight); the four
+// group sums are then added in group order.
+__global__ __launch_bounds__(256) void agg_diag_kernel(const float* __restrict__ pdiag, int B,
+                                                       int H, int L, int nb, int rev, int nrt,
+                                                       float* __restrict__ diag) {
+  __shared__ float sh[4][64];
+  const int t = threadIdx.x, j = t & 63, g = t >> 6;
+  const int64_t idx = (int64_t)blockIdx.x * 64 + j;
   const int n = 2 * L - 1;
-  if (idx >= (int64_t)H * n) return;
-  const int h = (int)(idx / n);
-  const int delta = (int)(idx % n) - (L - 1);
-  // owners q = b nb + p in ascending order, eight loads in flight, added in that order
-  constexpr int G = 8;
-  const int nq = B * nb;
+  const bool valid = idx < (int64_t)H * n;
+  const int h = valid ? (int)(idx / n) : 0;
+  const int delta = valid ? (int)(idx % n) - (L - 1) : 0;
+  constexpr int G = 16;
+  const int nq = B * nb, per = (nq + 3) / 4;
+  const int qa = g * per, qb = min(nq, qa + per);
+  // owner q = b nb + p, tracked incrementally (no division per load)
+  int b = qa / nb, p = qa - (qa / nb) * nb;
   float acc = 0.f;
-  for (int q0 = 0; q0 < nq; q0 += G) {
+  for (int q0 = qa; q0 < qb; q0 += G) {
     float ld[G];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const int q = q0 + u;
-      int64_t own;
-      int base;
-      owner_of(q / nb, h, q % nb, H, nb, rev != 0, L, own, base);
-      const int x = delta - base;
-      ld[u] = (q < nq && x >= 0 && x < nrt) ? pdiag[own * nrt + x] : 0.f;
+      const int blk = rev ? nb - 1 - p : p;
+      const int64_t own = ((int64_t)b * H + h) * nb + p;
+      const int x = delta - (blk * 128 - L - 64);
+      ld[u] = (valid && q0 + u < qb && x >= 0 && x < nrt) ? pdiag[own * nrt + x] : 0.f;
+      if (++p == nb) { p = 0; ++b; }
     }
 #pragma unroll
     for (int u = 0; u < G; ++u) acc += ld[u];
   }
-  diag[idx] = acc;
+  sh[g][j] = acc;
+  __syncthreads();
+  if (t < 64 && valid) diag[idx] = ((sh[0][t] + sh[1][t]) + sh[2][t]) + sh[3][t];
 }
 
 // T-XL dr[h][row][d] = s (sum_{b, key block} part[own][x][d] + v_h[d] diag_h[delta]).
@@ -176,32 +185,58 @@ __global__ void agg_t5_kernel(const float* __restrict__ diag, const int* __restr
 
 // T-XL dv[h][d] = s sum_delta diag_h[delta] r_h[row(delta)][d]
 template <typename T>
-__global__ void agg_txl_dv_kernel(const float* __restrict__ diag, const T* __restrict__ r, int L,
-                                  int nrel, int off, float s, float* __restrict__ dv) {
-  __shared__ float sh[256];
-  const int h = blockIdx.x / kHeadDim, d = blockIdx.x % kHeadDim;
+__global__ __launch_bounds__(1024) void agg_txl_dv_kernel(const float* __restrict__ diag,
+                                                          const T* __restrict__ r, int L, int nrel,
+                                                          int off, float s, float* __restrict__ dv) {
+  // one workgroup per (head, 8 columns): thread t takes the offsets t, t + 1024, ..., reading 8
+  // consecutive columns of each table row; then a fixed-order tree over the 1024 threads
+  __shared__ float sh[8][1024];
+  const int h = blockIdx.x >> 3, d0 = 8 * (blockIdx.x & 7);
+  const int t = threadIdx.x;
   const int n = 2 * L - 1;
-  float acc = 0.f;
-  for (int x = threadIdx.x; x < n; x += 256) {
-    const int delta = x - (L - 1);
-    const int row = delta + off;
-    if (row >= 0 && row < nrel)
-      acc = fmaf(diag[(int64_t)h * n + x], Elem<T>::to_f(r[((int64_t)h * nrel + row) * kHeadDim + d]), acc);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int x = t; x < n; x += 1024) {
+    const int row = x - (L - 1) + off;
+    if (row >= 0 && row < nrel) {
+      float rv[8];
+      load8(r + ((int64_t)h * nrel + row) * kHeadDim + d0, rv);
+      const float dg = diag[(int64_t)h * n + x];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(dg, rv[i], acc[i]);
+    }
   }
-  const float tot = block_sum(acc, sh);
-  if (threadIdx.x == 0) dv[blockIdx.x] = tot * s;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) sh[i][t] = acc[i];
+  __syncthreads();
+  for (int st = 512; st > 0; st >>= 1) {
+    if (t < st) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sh[i][t] += sh[i][t + st];
+    }
+    __syncthreads();
+  }
+  if (t < 8) dv[(int64_t)h * kHeadDim + d0 + t] = sh[t][0] * s;
 }
 
-// T-XL du[h][d] = s sum_{b, block} part_kv[own][d]
-__global__ void agg_txl_du_kernel(const float* __restrict__ pkv, int B, int H, int nb, float s,
-                                  float* __restrict__ du) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= H * kHeadDim) return;
-  const int h = idx / kHeadDim, d = idx % kHeadDim;
+// T-XL du[h][d] = s sum_{b, block} part_kv[own][d]: one workgroup per head; thread t sums the
+// owners of group t / 64 (64 consecutive owners each, in order) for column t % 64, and the four
+// group sums are added in group order
+__global__ __launch_bounds__(256) void agg_txl_du_kernel(const float* __restrict__ pkv, int B,
+                                                         int H, int nb, float s,
+                                                         float* __restrict__ du) {
+  __shared__ float sh[4][kHeadDim];
+  const int h = blockIdx.x, t = threadIdx.x, d = t & 63, g = t >> 6;
+  const int nown = B * nb, per = (nown + 3) / 4;
+  const int q0 = g * per, q1 = min(nown, q0 + per);
   float acc = 0.f;
-  for (int b = 0; b < B; ++b)
-    for (int p = 0; p < nb; ++p) acc += pkv[(((int64_t)b * H + h) * nb + p) * kHeadDim + d];
-  du[idx] = acc * s;
+#pragma unroll 8
+  for (int q = q0; q < q1; ++q) {
+    const int b = q / nb, p = q - b * nb;
+    acc += pkv[(((int64_t)b * H + h) * nb + p) * kHeadDim + d];
+  }
+  sh[g][d] = acc;
+  __syncthreads();
+  if (t < kHeadDim) du[(int64_t)h * kHeadDim + t] = (((sh[0][t] + sh[1][t]) + sh[2][t]) + sh[3][t]) * s;
 }
 
 // ALiBi dm[h] = -sum over the (batch, query block) owners of head h of their sums of
@@ -229,7 +264,7 @@ hipError_t launch_agg_rows(const float* part, int64_t stride, int nown, int64_t 
 hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool rev, int nrt,
                            float* diag, hipStream_t st) {
   const int64_t n = (int64_t)H * (2 * L - 1);
-  hipLaunchKernelGGL(agg_diag_kernel, dim3(nblk(n, 256)), dim3(256), 0, st, pdiag, B, H, L, nb,
+  hipLaunchKernelGGL(agg_diag_kernel, dim3(nblk(n, 64)), dim3(256), 0, st, pdiag, B, H, L, nb,
                      rev ? 1 : 0, nrt, diag);
   return hipGetLastError();
 }
@@ -258,13 +293,12 @@ hipError_t launch_agg_txl_uv(const float* pkv, const float* diag, const void* r,
                              int L, int nb, int nrel, int off, float s, bool fp32, float* du,
                              float* dv, hipStream_t st) {
   if (fp32)
-    hipLaunchKernelGGL((agg_txl_dv_kernel<float>), dim3(H * kHeadDim), dim3(256), 0, st, diag,
+    hipLaunchKernelGGL((agg_txl_dv_kernel<float>), dim3(H * 8), dim3(1024), 0, st, diag,
                        (const float*)r, L, nrel, off, s, dv);
   else
-    hipLaunchKernelGGL((agg_txl_dv_kernel<uint16_t>), dim3(H * kHeadDim), dim3(256), 0, st, diag,
+    hipLaunchKernelGGL((agg_txl_dv_kernel<uint16_t>), dim3(H * 8), dim3(1024), 0, st, diag,
                        (const uint16_t*)r, L, nrel, off, s, dv);
-  hipLaunchKernelGGL(agg_txl_du_kernel, dim3(nblk(H * kHeadDim, 256)), dim3(256), 0, st, pkv, B, H,
-                     nb, s, du);
+  hipLaunchKernelGGL(agg_txl_du_kernel, dim3(H), dim3(256), 0, st, pkv, B, H, nb, s, du);
   return hipGetLastError();
 }
 

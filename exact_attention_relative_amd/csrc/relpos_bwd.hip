@@ -1,12 +1,16 @@
 // Backward launch logic: per mechanism and direction, the pass variants of relpos_bwd_body.h.
 // The T-XL key-side pass is instantiated in relpos_bwd_txl_key.hip, a translation unit of its
-// own compiled with the scheduler's register-pressure trackers, which spill less there.
+// own compiled with the scheduler's register-pressure trackers, which spill less there; the
+// query-side general passes of Shaw and DeBERTa in relpos_bwd_fat_q.hip, compiled with MFMA
+// accumulators kept in VGPRs.
 #include "relpos_bwd_body.h"
 
 namespace relpos {
 
 // relpos_bwd_txl_key.hip
 void launch_bwd_txl_key(const BwdArgs& a, dim3 grid, hipStream_t stream);
+// relpos_bwd_fat_q.hip: the query-side general passes of Shaw and DeBERTa
+void launch_bwd_fat_q(int mech, const BwdArgs& a, dim3 grid, hipStream_t stream);
 
 // Passes that carry relation-gradient machinery for clipped mechanisms run in two parts.
 template <int MECH, int DIR>
@@ -20,7 +24,9 @@ constexpr bool two_wg() {
 }
 template <int MECH, int DIR, int PART>
 static void launch_part(const BwdArgs& a, dim3 grid, hipStream_t stream) {
-  if constexpr (two_wg<MECH, DIR, PART>())
+  if constexpr (DIR == 0 && PART == 2)
+    launch_bwd_fat_q(MECH, a, grid, stream);
+  else if constexpr (two_wg<MECH, DIR, PART>())
     hipLaunchKernelGGL((bwd_kernel<MECH, DIR, PART>), grid, dim3(256), 0, stream, a);
   else
     hipLaunchKernelGGL((bwd_kernel_1wg<MECH, DIR, PART>), grid, dim3(256), 0, stream, a);

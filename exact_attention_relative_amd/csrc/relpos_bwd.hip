@@ -19,8 +19,8 @@ constexpr bool split_pass() {
 }
 template <int MECH, int DIR, int PART>
 constexpr bool two_wg() {
-  return MECH == MECH_T5 || MECH == MECH_ALIBI || MECH == MECH_TXL || (DIR == 1 && MECH == MECH_SHAW) ||
-         PART == 1;
+  return MECH == MECH_T5 || MECH == MECH_ALIBI || MECH == MECH_TXL || MECH == MECH_DEBERTA ||
+         (DIR == 1 && MECH == MECH_SHAW) || PART == 1;
 }
 template <int MECH, int DIR, int PART>
 static void launch_part(const BwdArgs& a, dim3 grid, hipStream_t stream) {

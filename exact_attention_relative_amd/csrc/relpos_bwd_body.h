@@ -47,9 +47,15 @@ struct BV {
   static constexpr bool TXL = MECH == MECH_TXL;
   static constexpr bool CLIP = MECH == MECH_SHAW || MECH == MECH_DEBERTA;
   static constexpr bool DIAG = DIR == 0 && (MECH == MECH_T5 || MECH == MECH_TXL);
-  static constexpr bool EBUF = ROW && !TXL;          // shared E buffer + lane-side table GEMM
-  static constexpr bool GSREL = TXL && DIR == 0;      // dX_rel from the wave's fp32 dS buffer
-  static constexpr bool TG1 = TXL && DIR == 1;        // table GEMM over the streamed rows
+  // DeBERTa general pass: the row-side dX_rel from the wave's dS buffer and the column-side
+  // table gradient over the streamed rows (no E buffer, so two workgroups fit per CU); the
+  // row-side table's interior rows come from the other direction's pass
+  static constexpr bool DFAT = MECH == MECH_DEBERTA && PART == 2;
+  static constexpr bool TQ = TXL && DIR == 0;         // T-XL query side (circular row window)
+  static constexpr bool TK = TXL && DIR == 1;         // T-XL key side (circular column window)
+  static constexpr bool EBUF = ROW && !TXL && !DFAT;  // shared E buffer + lane-side table GEMM
+  static constexpr bool GSREL = TQ || DFAT;           // dX_rel from the wave's fp32 dS buffer
+  static constexpr bool TG1 = TK || DFAT;             // table GEMM over the streamed rows
   static constexpr bool WINB = ROW || COL;
   static constexpr bool GSB = ROW || COL || DIAG;
 
@@ -119,11 +125,11 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   // T-XL u.k / clipped end-row constants / ALiBi ramps +m y / s and -m y / s
   constexpr int NOVEC = (MECH == MECH_TXL && DIR == 0)
                             ? BOTH
-                            : ((V::CLIP && V::HAS_COL) || MECH == MECH_ALIBI ? 2 * BOTH : 4);
+                            : ((V::CLIP && V::HAS_COL && !V::DFAT) || MECH == MECH_ALIBI ? 2 * BOTH : 4);
   __shared__ float red_s[MECH == MECH_ALIBI ? NWAVE : 1];   // ALiBi: per-wave slope-gradient sums
   __shared__ __attribute__((aligned(16))) float ovec_s[NOVEC];   // per-other-row constants
   __shared__ __attribute__((aligned(16))) float lsd_s[DIR == 1 ? 2 * BOTH : 4];   // LSE*log2e, D per query
-  __shared__ __attribute__((aligned(16))) float endc[V::CLIP && V::ROW ? 2 * BLANE : 4];
+  __shared__ __attribute__((aligned(16))) float endc[V::CLIP && V::ROW && !V::DFAT ? 2 * BLANE : 4];
   float* const gsb = gsb_raw + GSG;
 
   const AttnShape sh = a.sh;
@@ -177,7 +183,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if (!(lse2 > kNegInf)) lse2 = __builtin_inff();   // empty row: P = 0
   }
   float rcA = 0.f, rcB = 0.f;
-  if constexpr (V::CLIP && V::HAS_ROW) {
+  if constexpr (V::CLIP && V::HAS_ROW && !V::DFAT) {
     if (my_a < L) {
       rcA = rc_g[((int64_t)bh * L + my_a) * 2 + 0];
       rcB = rc_g[((int64_t)bh * L + my_a) * 2 + 1];
@@ -226,10 +232,15 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int nrt = L + 256;
   float* prow = nullptr;     // row-side table partial
   int prow_rows = 0;
-  if constexpr (V::EBUF) {
+  if constexpr (V::EBUF || V::DFAT) {
     prow_rows = (MECH == MECH_SHAW) ? 2 * span + 1 : 2 * span;
     prow = (DIR == 0 ? a.part_q : a.part_k) + owner * (DIR == 0 ? a.part_q_stride : a.part_k_stride);
   }
+  // DeBERTa general pass: column-side table partial (its interior rows; the end rows are the
+  // other direction's row-side end rows)
+  float* pcol = nullptr;
+  if constexpr (V::DFAT)
+    pcol = (DIR == 0 ? a.part_k : a.part_q) + owner * (DIR == 0 ? a.part_k_stride : a.part_q_stride);
   // T-XL r partial of the key-side pass: row b0 + 65 + t holds window row t of step base b0
   // (offset delta = b0 - A0 - 127 + t), i.e. row delta + A0 + 192
   // With a two-sided window the partial keeps only the rows of this sweep, from row bt0 + 65.
@@ -237,7 +248,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int nrk = (int)(a.part_q_stride / kHeadDim);
   const int rb = (sh.wl >= 0 && sh.wr >= 0) ? bt0 + 65 : 0;
   // (slots of the r partial count from the launch's first slice)
-  if constexpr (V::TG1) ptg = a.part_q + (int64_t)bid * a.part_q_stride - (int64_t)rb * kHeadDim;
+  if constexpr (V::TK) ptg = a.part_q + (int64_t)bid * a.part_q_stride - (int64_t)rb * kHeadDim;
   float* pdiag = nullptr;
   if constexpr (V::DIAG) pdiag = a.part_qv + owner * (int64_t)nrt;
 
@@ -258,7 +269,16 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       if (!covered) prow[e] = 0.f;
     }
   }
-  if constexpr (V::TG1) {
+  if constexpr (V::DFAT) {
+    // column offsets mu = b - a of every window row of every step are flushed (interior ones)
+    const int mlo = bt0 - A0 - (BLANE - 1), mhi = bt_last - A0 + BOTH;
+    for (int64_t e = tid; e < (int64_t)prow_rows * kHeadDim; e += 256) {
+      const int row = (int)(e / kHeadDim), mu = row - span;   // row = clamp(mu + k)
+      const bool end = row == V::rowA(span) || row == V::rowB(span);
+      if (!end && !(nsteps > 0 && mu >= mlo && mu <= mhi)) pcol[e] = 0.f;
+    }
+  }
+  if constexpr (V::TK) {
     // rows written by the sweep: [bt0 + 65, bt_last + 256] (ptg is offset by rb rows)
     for (int64_t e = tid; e < (int64_t)nrk * kHeadDim; e += 256) {
       const int row = (int)(e / kHeadDim) + rb;
@@ -307,6 +327,22 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         const int lam = lam0 + 8 * (r >> 2) + (r & 3);
         if (lam > V::TA(span) && lam < V::TB(span))
           prow[(int64_t)V::row_of(lam, span, nrel, toff) * kHeadDim + d] = acc[r];
+      }
+    }
+  };
+  // DeBERTa general pass: the same for the column-side table (offsets mu = b - a, table row
+  // mu + k, interior rows only)
+  auto flush_col = [&](const f32x16& acc, int mu0) {
+    const int d = 32 * gdb + l32;
+    if (mu0 > V::TA(span) && mu0 + 27 < V::TB(span)) {
+      float* fb = pcol + (uint32_t)((mu0 + span) * kHeadDim + d);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = acc[r];
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int mu = mu0 + 8 * (r >> 2) + (r & 3);
+        if (mu > V::TA(span) && mu < V::TB(span)) pcol[(uint32_t)((mu + span) * kHeadDim + d)] = acc[r];
       }
     }
   };
@@ -360,9 +396,9 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   };
   if constexpr (V::FAT) {
     if (nsteps > 0) {
-      if constexpr (V::COL) pwc.load(tcol, colfn_at(bt0));
-      if constexpr (V::ROW) pwr.load(trow, rowfn_at(bt0));
-      if constexpr (V::CLIP && V::HAS_COL) ov_load(bt0);
+      if constexpr (V::COL && !V::DFAT) pwc.load(tcol, colfn_at(bt0));
+      if constexpr (V::ROW && !V::DFAT) pwr.load(trow, rowfn_at(bt0));
+      if constexpr (V::CLIP && V::HAS_COL && !V::DFAT) ov_load(bt0);
       if constexpr (DIR == 1) lsd_load(bt0);
     }
   }
@@ -379,7 +415,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     // query-side T-XL: the row window slides by 64 offsets per step and is kept circular,
     // window row x of step s at physical row (x - 64 s) mod 192
     // key-side T-XL: the column window slides up by 64 per step, row x at (x + 64 s) mod 192
-    const int xrot = V::GSREL ? ((3 - step % 3) % 3) * BOTH : V::TG1 ? (step % 3) * BOTH : 0;
+    const int xrot = V::TQ ? ((3 - step % 3) % 3) * BOTH : V::TK ? (step % 3) * BOTH : 0;
     if constexpr (V::LIGHT) {
       if (step >= g_first && step <= g_last) continue;   // left to the general pass
     }
@@ -397,10 +433,10 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     bool wg_general = true;
     if constexpr (V::CLIP) {
       const int ta = V::TA(span), tb = V::TB(span);
-      if constexpr (V::HAS_ROW) {
+      if constexpr (V::HAS_ROW && !V::DFAT) {
         if (lamhi <= ta) rcls = 1; else if (lamlo >= tb) rcls = 2;
       }
-      if constexpr (V::HAS_COL) {
+      if constexpr (V::HAS_COL && !V::DFAT) {
         if (-lamlo <= ta) ccls = 1; else if (-lamhi >= tb) ccls = 2;
       }
       wg_general = wg_gen(b0);
@@ -442,7 +478,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if constexpr (MECH == MECH_TXL && DIR == 0) {
       if (tid < BOTH) ovec_s[tid] = (b0 + tid < L) ? a.uk[(int64_t)bh * L + b0 + tid] : 0.f;
     }
-    if constexpr (V::CLIP && V::HAS_COL) {
+    if constexpr (V::CLIP && V::HAS_COL && !V::DFAT) {
       // end A values of the 64 streamed rows, then end B: each a contiguous vector
       if constexpr (!V::FAT) ov_load(b0);
       if (tid < 2 * BOTH) ovec_s[(tid & 1) * BOTH + (tid >> 1)] = pov;
@@ -470,7 +506,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       }
     }
     // row side staged now when there is no column side
-    if constexpr (V::GSREL) {
+    if constexpr (V::TQ) {
       // every T-XL tile is general; after the first step only rows 0..63 are new
       auto rowfn = [&](int x) { return V::row_of(cwin - 63 + x, span, nrel, toff); };
       if (step == 0) {
@@ -497,7 +533,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       }
     }
     // column side first (its window is replaced by the row-side window afterwards)
-    if constexpr (V::TG1) {
+    if constexpr (V::TK) {
       // column window row x <-> mu = b - a = (b0 - A0 - 127) + x; after the first step only
       // rows 128..191 are new, at physical rows wrow(128, xrot) ..
       auto colfn = [&](int x) { return V::col_of((b0 - A0 - (BLANE - 1)) + x, span, nrel, toff); };
@@ -517,7 +553,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       }
     } else if constexpr (V::COL) {
       if (wg_general) {
-        if constexpr (V::FAT) {
+        if constexpr (V::FAT && !V::DFAT) {
           pwc.store(win);
           if (step + 1 < nsteps) pwc.load(tcol, colfn_at(b0 + BOTH));
         } else {
@@ -560,7 +596,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       if (!wave_none) {
         if (V::CLIP && ccls != 0) {
           // already in the accumulator start
-        } else if constexpr (V::TG1) {
+        } else if constexpr (V::TK) {
           col_skew_add<NP, true, true>(sc, win, (BLANE - WROWS) - WROWS * w, 0, ys, gs, xrot);
           col_skew_add<NP, true, true>(sc, win, (BLANE - WROWS) - WROWS * w, 1, ys, gs, xrot);
         } else if (V::COL && wg_general) {
@@ -572,7 +608,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if constexpr (V::ROW && V::COL) {
       if (wg_general) {
         __syncthreads();   // column-side window reads done
-        if constexpr (V::FAT) {
+        if constexpr (V::FAT && !V::DFAT) {
           pwr.store(win);
           if (step + 1 < nsteps) pwr.load(trow, rowfn_at(b0 + BOTH));
         } else {
@@ -587,7 +623,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           lconst = (rcls == 1) ? rcA : rcB;
         } else if constexpr (V::ROW) {
           f32x16 g[3];
-          if constexpr (V::GSREL) row_products<NP, true, true>(g, win, WROWS * w, xop, xrot);
+          if constexpr (V::TQ) row_products<NP, true, true>(g, win, WROWS * w, xop, xrot);
           else row_products<NP, MECH == MECH_TXL>(g, win, WROWS * w, xop);
           row_skew_add(sc, g, gs);
         }
@@ -692,6 +728,30 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             }
         }
       }
+      if constexpr (V::DFAT) {
+        // row-side clipped elements: their dX_rel comes through the window's end rows, and
+        // the end rows' table gradient needs their sums per lane row
+        if (lamlo <= V::TA(span) || lamhi >= V::TB(span)) {
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int lam = my_a - b0 - (32 * b + 8 * (r >> 2) + 4 * kh + (r & 3));
+              if (lam <= V::TA(span)) cA += ds[b][r];
+              else if (lam >= V::TB(span)) cB += ds[b][r];
+            }
+        }
+        // dS into the wave's buffer now (its skew reads are done), so that the fp32 copy dies
+        // before the content gradients; the row-side dX_rel reads it back after them
+        wave_lds_sync();
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            f32x4 v4 = {ds[b][4 * g4], ds[b][4 * g4 + 1], ds[b][4 * g4 + 2], ds[b][4 * g4 + 3]};
+            *(f32x4*)(gs + l32 * GS2 + 32 * b + 8 * g4 + 4 * kh) = v4;
+          }
+      }
       // ---- content gradients (P and dS packed to bf16 once; the fp32 copies can die) ----
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) dso[cc] = op_from_acc<NP>(ds, cc);
@@ -717,7 +777,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     }
 
     // ---- offset-sharded row-side gradients ----
-    if constexpr (V::CLIP && V::HAS_ROW) {
+    if constexpr (V::CLIP && V::HAS_ROW && !V::DFAT) {
       if (!(V::EBUF && wg_general) && !wave_none) {
         // the whole wave tile reads one end row
         float tot = 0.f;
@@ -787,7 +847,36 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 
     }
 
-    // ---- T-XL key side: dr window GEMM over the streamed query rows ----
+    // ---- DeBERTa general pass: row-side dX_rel from the wave's dS buffer ----
+    if constexpr (V::DFAT) {
+      if (!wave_none) {
+        wave_lds_sync();   // the wave's dS writes (before the content gradients) are visible
+        // dX_rel^T[d][x] += sum_t Win[32 w + t][d] E[x][t], E[x][t] = dS[x][x + 63 - t] for t
+        // in [x, x + 63] (else 0), read along the skewed diagonal of the buffer
+        const float* grow = gs + l32 * GS2 + l32 + 63 - 4 * kh;
+#pragma unroll
+        for (int cc = 0; cc < 6; ++cc) {
+          float e8[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int t0 = 16 * cc + 4 * kh + j, t1 = t0 + 8;
+            float v0 = grow[-(16 * cc + j)], v1 = grow[-(16 * cc + 8 + j)];
+            if (cc < 2) { v0 = t0 >= l32 ? v0 : 0.f; v1 = t1 >= l32 ? v1 : 0.f; }
+            if (cc > 3) { v0 = t0 <= l32 + 63 ? v0 : 0.f; v1 = t1 <= l32 + 63 ? v1 : 0.f; }
+            e8[j] = v0;
+            e8[4 + j] = v1;
+          }
+          Op<NP> eop = op_from_f32<NP>(e8);
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+            Op<NP> wt = op_rows_tr<NP>(win, WIN * TSTR, TSTR, WROWS * w + 16 * cc, 32 * db);
+            mma<NP>(gacc[db], wt, eop);
+          }
+        }
+      }
+    }
+
+    // ---- T-XL key side (and DeBERTa general pass): table GEMM over the streamed rows ----
     if constexpr (V::TG1) {
       // E2T[y][t] = dS[y][x] with t = y - x + 127, in the column-skew buffer's space: for one
       // register, the 32 lanes of a half-wave write 32 consecutive t
@@ -827,10 +916,12 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         }
       }
       // block gp leaves the window with this step (the next window starts 64 offsets higher)
-      {
+      if constexpr (V::TK) {
         float* fb = ptg + (int64_t)(b0 + 65 + 32 * gp + 4 * kh) * kHeadDim + 32 * gdb + l32;
 #pragma unroll
         for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = racc[0][r];
+      } else {
+        flush_col(racc[0], b0 - A0 - (BLANE - 1) + 32 * gp + 4 * kh);
       }
       racc[0] = racc[1];
       racc[1] = racc[2];
@@ -964,7 +1055,14 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       for (int i = 0; i < 3; ++i) flush_block(racc[i], pc - 63 + 32 * (gp + 2 * i) + 4 * kh);
     }
   }
-  if constexpr (V::TG1) {
+  if constexpr (V::DFAT) {
+    // blocks gp + 2 and gp + 4 of the last window (shifted into racc[0], racc[1])
+    if (nsteps > 0) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) flush_col(racc[i], bt_last - A0 - (BLANE - 1) + 32 * (gp + 2 + 2 * i) + 4 * kh);
+    }
+  }
+  if constexpr (V::TK) {
     // blocks gp + 2 and gp + 4 of the last window (shifted into racc[0], racc[1])
     if (nsteps > 0) {
 #pragma unroll
@@ -1025,7 +1123,47 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   }
 
   // ---- end rows (clipped offsets): table gradient and lane gradient ----
-  if constexpr (V::CLIP && V::ROW) {
+  if constexpr (V::DFAT) {
+    // cA / cB hold this lane's sum over its half of the other rows (this pass's clipped
+    // elements, whose dX_rel came through the window); the light pass's sums still owe their
+    // dX term
+    cA += xhalf(cA);
+    cB += xhalf(cB);
+    float lA = 0.f, lB = 0.f;
+    if (my_a < L) {
+      lA = a.cab[((int64_t)bh * L + my_a) * 2 + 0];
+      lB = a.cab[((int64_t)bh * L + my_a) * 2 + 1];
+    }
+    // end rows of the row-side table: sum over the lane rows of (cA + lA) X, with the lane rows
+    // and the sums staged in the (now free) dS buffers
+    float* ends = gsb;                                   // [2][BLANE]
+    uint16_t* xst = (uint16_t*)(gsb + 2 * BLANE);        // lane rows X, [BLANE][TSTR]
+    __syncthreads();
+    stage64<T, NP>(xst, xg, A0, L);
+    stage64<T, NP>(xst + BOTH * TSTR, xg, A0 + BOTH, L);
+    if (kh == 0) {
+      ends[WROWS * w + l32] = (my_a < L) ? cA + lA : 0.f;
+      ends[BLANE + WROWS * w + l32] = (my_a < L) ? cB + lB : 0.f;
+    }
+    __syncthreads();
+    if (tid < 2 * kHeadDim) {
+      const int e = tid / kHeadDim, d = tid % kHeadDim;
+      float acc = 0.f;
+      for (int x = 0; x < BLANE; ++x) acc = fmaf(ends[e * BLANE + x], bf_bits2f(xst[x * TSTR + d]), acc);
+      const int row = e == 0 ? V::rowA(span) : V::rowB(span);
+      prow[(int64_t)row * kHeadDim + d] = acc;
+    }
+    // dX += lA T[rowA] + lB T[rowB]
+#pragma unroll
+    for (int db = 0; db < 2; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int d = 32 * db + 8 * (r >> 2) + 4 * kh + (r & 3);
+        const float ta = bf_bits2f(trow[(int64_t)V::rowA(span) * kHeadDim + d]);
+        const float tb = bf_bits2f(trow[(int64_t)V::rowB(span) * kHeadDim + d]);
+        gacc[db][r] = fmaf(lA, ta, fmaf(lB, tb, gacc[db][r]));
+      }
+  } else if constexpr (V::CLIP && V::ROW) {
     // cA / cB hold this lane's sum over its half of the other rows
     cA += xhalf(cA);
     cB += xhalf(cB);

@@ -10,7 +10,7 @@ void launch_bwd_fat_q(int mech, const BwdArgs& a, dim3 grid, hipStream_t stream)
   if (mech == MECH_SHAW)
     hipLaunchKernelGGL((bwd_kernel_1wg<MECH_SHAW, 0, 2>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_kernel_1wg<MECH_DEBERTA, 0, 2>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_kernel<MECH_DEBERTA, 0, 2>), grid, dim3(256), 0, stream, a);
 }
 
 }  // namespace relpos

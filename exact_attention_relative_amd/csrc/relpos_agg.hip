@@ -2,7 +2,7 @@
 // gradient sharding: aggregate locally first, then merge): every table-gradient element sums
 // the per-workgroup partials in ascending owner order, and reductions over offsets use a fixed
 // tree, so the result is bitwise reproducible.  Outputs are overwritten.
-#include "relpos_device.h"
+#include "relpos_tile.h"
 
 namespace relpos {
 
@@ -47,10 +47,12 @@ __device__ __forceinline__ void owner_of(int b, int h, int p, int H, int nb, boo
   lam_base = blk * 128 - L - 64;
 }
 
-// diag[h][delta + L - 1] = sum over (b, block) of the per-offset dS sums.  One workgroup per
-// 64 consecutive (head, offset) entries: thread t takes entry t % 64 and the owners of group
-// t / 64 (a quarter of them, consecutive, in ascending order, 16 loads in flight); the four
-// group sums are then added in group order.
+// diag[h][delta + L - 1] = sum over (b, block, wave) of the per-offset dS sums (the query-side
+// pass writes one partial per wave: wave w of owner o at slot 4 o + w, its offsets counted from
+// the owner's lam_base + 32 w).  One workgroup per 64 consecutive (head, offset) entries: thread
+// t takes entry t % 64 and the partials of group t / 64 (a quarter of them, consecutive, in
+// ascending (owner, wave) order, 16 loads in flight); the four group sums are then added in
+// group order.
 __global__ __launch_bounds__(256) void agg_diag_kernel(const float* __restrict__ pdiag, int B,
                                                        int H, int L, int nb, int rev, int nrt,
                                                        float* __restrict__ diag) {
@@ -62,20 +64,23 @@ __global__ __launch_bounds__(256) void agg_diag_kernel(const float* __restrict__
   const int h = valid ? (int)(idx / n) : 0;
   const int delta = valid ? (int)(idx % n) - (L - 1) : 0;
   constexpr int G = 16;
-  const int nq = B * nb, per = (nq + 3) / 4;
+  const int nq = B * nb * NWAVE, per = (nq + 3) / 4;
   const int qa = g * per, qb = min(nq, qa + per);
-  // owner q = b nb + p, tracked incrementally (no division per load)
-  int b = qa / nb, p = qa - (qa / nb) * nb;
+  // partial q = (b nb + p) NWAVE + w, tracked incrementally (no division per load)
+  int w = qa % NWAVE, b = (qa / NWAVE) / nb, p = (qa / NWAVE) - b * nb;
   float acc = 0.f;
   for (int q0 = qa; q0 < qb; q0 += G) {
     float ld[G];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
       const int blk = rev ? nb - 1 - p : p;
-      const int64_t own = ((int64_t)b * H + h) * nb + p;
-      const int x = delta - (blk * 128 - L - 64);
-      ld[u] = (valid && q0 + u < qb && x >= 0 && x < nrt) ? pdiag[own * nrt + x] : 0.f;
-      if (++p == nb) { p = 0; ++b; }
+      const int64_t slot = (((int64_t)b * H + h) * nb + p) * NWAVE + w;
+      const int x = delta - (blk * 128 + 32 * w - L - 64);
+      ld[u] = (valid && q0 + u < qb && x >= 0 && x < nrt) ? pdiag[slot * nrt + x] : 0.f;
+      if (++w == NWAVE) {
+        w = 0;
+        if (++p == nb) { p = 0; ++b; }
+      }
     }
 #pragma unroll
     for (int u = 0; u < G; ++u) acc += ld[u];

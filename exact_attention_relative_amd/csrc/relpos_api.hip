@@ -178,7 +178,8 @@ int make_plan(const relpos_desc* d, Plan* p) {
   }
   if (p->part_k_stride) p->off_part_k = take(sizeof(float) * own * p->part_k_stride);
   if (lut_path || d->mech == RELPOS_TXL) {
-    p->off_part_qv = take(sizeof(float) * own * p->nrt);
+    // T5 / T-XL: per-offset sums, one partial of nrt floats per wave of each query-side owner
+    p->off_part_qv = take(sizeof(float) * own * p->nrt * 4);
     p->off_diag = take(sizeof(float) * (size_t)p->H * (L > 0 ? 2 * L - 1 : 1));
   }
   if (d->mech == RELPOS_TXL) p->off_part_kv = take(sizeof(float) * own * kHeadDim);

@@ -249,12 +249,14 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int rb = (sh.wl >= 0 && sh.wr >= 0) ? bt0 + 65 : 0;
   // (slots of the r partial count from the launch's first slice)
   if constexpr (V::TK) ptg = a.part_q + (int64_t)bid * a.part_q_stride - (int64_t)rb * kHeadDim;
+  // per-offset dS sums: one partial per wave (its lane offsets lie in [lam_base + 32 w,
+  // lam_base + 32 w + nrt)), in the owner's slot of NWAVE x nrt floats
   float* pdiag = nullptr;
-  if constexpr (V::DIAG) pdiag = a.part_qv + owner * (int64_t)nrt;
+  if constexpr (V::DIAG) pdiag = a.part_qv + owner * (int64_t)(NWAVE * nrt);
 
   // lane offsets the sweep writes: every window row of every step, [A0 - b0 - 63, A0 - b0 + 128],
-  // for the table partial; the diagonal sums stop one short (the last window row has no pairs)
-  const int cov_lo = A0 - bt_last - 63, cov_hi = A0 - bt0 + 128, cov_hi_diag = cov_hi - 1;
+  // for the table partial
+  const int cov_lo = A0 - bt_last - 63, cov_hi = A0 - bt0 + 128;
 
   // ---- zero what the sweep will not write ----
   if constexpr (V::EBUF) {
@@ -286,9 +288,11 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     }
   }
   if constexpr (V::DIAG) {
-    for (int e = tid; e < nrt; e += 256) {
-      const int lam = lam_base + e;
-      if (!(nsteps > 0 && lam >= cov_lo && lam <= cov_hi_diag)) pdiag[e] = 0.f;
+    // wave ww writes the offsets [A0 + 32 ww - bt_last - 63, A0 + 32 ww - bt0 + 32]
+    for (int e = tid; e < NWAVE * nrt; e += 256) {
+      const int ww = e / nrt, lam = lam_base + 32 * ww + (e - ww * nrt);
+      const int lo = A0 + 32 * ww - bt_last - 63, hi = A0 + 32 * ww - bt0 + 32;
+      if (!(nsteps > 0 && lam >= lo && lam <= hi)) pdiag[e] = 0.f;
     }
   }
   if constexpr (V::EBUF) {
@@ -307,7 +311,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   f32x16 racc[3] = {f32x16{}, f32x16{}, f32x16{}};   // row-side table window accumulators
   float cA = 0.f, cB = 0.f;                  // clipped-end sums of dS (lane row)
   float colsum = 0.f;                        // dir 1 T-XL: sum_i dS_ij
-  float dcarry = 0.f;                        // diagonal sum of offsets lam = tid (mod 256)
+  float dcarry = 0.f;                        // diagonal t = lane carried into the next step
   const int gdb = w & 1, gp = w >> 1;        // GEMM tiles of this wave: d-block, t-block parity
 
   // Store one window accumulator block to the table partial: register r holds offset
@@ -930,11 +934,9 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 
     // ---- per-offset fp32 sums of dS (T5 bias gradient; T-XL v term and v gradient) ----
     if constexpr (V::DIAG) {
-      // a wave's 96 sums live in the padding columns of its dS buffer (4 per row)
-      auto wsum_at = [&](int ww, int t) {
-        return gsb + ww * WROWS * GS2 + (t >> 2) * GS2 + kHeadDim + (t & 3);
-      };
       const bool single = (MECH == MECH_T5) && t5cls == 1;
+      // lane l: sums[0] = diagonal t = l, sums[1] = diagonal t = l + 64 (l < 32)
+      float sums[2] = {0.f, 0.f};
       if (!wave_none && !single) {
         // dS[n][y] into the wave buffer, then sums along the diagonals t = n - y + 63
         wave_lds_sync();
@@ -971,7 +973,6 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             }
           }
         }
-        float sums[2] = {0.f, 0.f};
         if constexpr (MECH == MECH_TXL) {
           // Lane l sums diagonal t = l (rows 0 .. min(l, 31)) and, for l < 32, diagonal
           // t = l + 64 (rows l + 1 .. 31): one element of every row, rows in ascending order,
@@ -998,11 +999,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             }
           }
         }
-        wave_lds_sync();   // this wave's reads of its buffer precede the writes to its padding
-        *wsum_at(w, lane) = sums[0];
-        if (lane < 32) *wsum_at(w, 64 + lane) = sums[1];
       } else {
-        // single bucket: the wave total goes to one offset of the tile (window row 63)
+        // single bucket: the wave total goes to one offset of the tile (diagonal 63)
         float tot = 0.f;
         if (!wave_none) {
 #pragma unroll
@@ -1012,29 +1010,18 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           tot += xhalf(tot);
           for (int m = 1; m < 32; m <<= 1) tot += __shfl_xor(tot, m);
         }
-        wave_lds_sync();
-        *wsum_at(w, lane) = (lane == 63) ? tot : 0.f;
-        if (lane < 32) *wsum_at(w, 64 + lane) = 0.f;
+        sums[0] = (lane == 63) ? tot : 0.f;
       }
-      __syncthreads();
-      // thread tid carries the offsets lam = tid (mod 256): at most one window row per step
-      const int t = (tid - (cwin - 63)) & 255;
-      if (t < WIN - 1) {
-        float sum = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NWAVE; ++ww) {
-          const int tt = t - 32 * ww;
-          if (tt >= 0 && tt < 96) sum += *wsum_at(ww, tt);
-        }
-        const int lam = cwin - 63 + t;
-        float val = dcarry + sum;
-        // offsets above the next window are final
-        if (step == nsteps - 1 || t >= 127) {
-          pdiag[lam - lam_base] = val;
-          val = 0.f;
-        }
-        dcarry = val;
-      }
+      // Diagonal t of this step is diagonal t + 64 of the next for t < 32: lanes 0..31 carry
+      // sums[0] into their next sums[1]; the wave's 64 offsets t = 32 .. 95 are final (lane
+      // 32 + i: t = 32 + i from sums[0]; lane i: t = 64 + i from sums[1] and the carry), and
+      // after the last step also t = 0 .. 31.  No workgroup barrier: each wave writes its own
+      // partial.
+      const float fin = (lane >= 32) ? sums[0] : sums[1] + dcarry;
+      dcarry = (lane < 32) ? sums[0] : 0.f;
+      float* pw = pdiag + w * nrt + (aw0 - b0 - 63) - (lam_base + 32 * w);
+      pw[(lane >= 32) ? lane : 64 + lane] = fin;
+      if (step == nsteps - 1 && lane < 32) pw[lane] = dcarry;
     }
   }
 

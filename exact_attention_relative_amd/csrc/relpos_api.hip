@@ -185,10 +185,11 @@ int make_plan(const relpos_desc* d, Plan* p) {
   if (d->mech == RELPOS_TXL) p->off_part_kv = take(sizeof(float) * own * kHeadDim);
   if (d->mech == RELPOS_SHAW || d->mech == RELPOS_DEBERTA) {
     // split passes: clipped-step partials handed from the light kernel to the general one
+    // (dX, the end-row sums, and dV on the key side)
     p->off_xpart = take(sizeof(float) * rows * kHeadDim);
     p->off_cab = take(sizeof(float) * rows * 2);
+    p->off_vpart = take(sizeof(float) * rows * kHeadDim);
   }
-  if (d->mech == RELPOS_DEBERTA) p->off_vpart = take(sizeof(float) * rows * kHeadDim);
   p->bwd_bytes = off;
   return RELPOS_OK;
 }

@@ -1,8 +1,7 @@
 // Backward launch logic: per mechanism and direction, the pass variants of relpos_bwd_body.h.
 // The T-XL key-side pass is instantiated in relpos_bwd_txl_key.hip, a translation unit of its
 // own compiled with the scheduler's register-pressure trackers, which spill less there; the
-// query-side general passes of Shaw and DeBERTa in relpos_bwd_fat_q.hip, compiled with MFMA
-// accumulators kept in VGPRs.
+// query-side general passes of Shaw and DeBERTa in relpos_bwd_fat_q.hip.
 #include "relpos_bwd_body.h"
 
 namespace relpos {
@@ -12,24 +11,17 @@ void launch_bwd_txl_key(const BwdArgs& a, dim3 grid, hipStream_t stream);
 // relpos_bwd_fat_q.hip: the query-side general passes of Shaw and DeBERTa
 void launch_bwd_fat_q(int mech, const BwdArgs& a, dim3 grid, hipStream_t stream);
 
-// Passes that carry relation-gradient machinery for clipped mechanisms run in two parts.
+// Shaw and DeBERTa run in two parts: a light pass over the clipped steps, then the general pass.
 template <int MECH, int DIR>
 constexpr bool split_pass() {
-  return (MECH == MECH_SHAW && DIR == 0) || MECH == MECH_DEBERTA;
-}
-template <int MECH, int DIR, int PART>
-constexpr bool two_wg() {
-  return MECH == MECH_T5 || MECH == MECH_ALIBI || MECH == MECH_TXL || MECH == MECH_DEBERTA ||
-         (DIR == 1 && MECH == MECH_SHAW) || PART == 1;
+  return MECH == MECH_SHAW || MECH == MECH_DEBERTA;
 }
 template <int MECH, int DIR, int PART>
 static void launch_part(const BwdArgs& a, dim3 grid, hipStream_t stream) {
   if constexpr (DIR == 0 && PART == 2)
     launch_bwd_fat_q(MECH, a, grid, stream);
-  else if constexpr (two_wg<MECH, DIR, PART>())
-    hipLaunchKernelGGL((bwd_kernel<MECH, DIR, PART>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_kernel_1wg<MECH, DIR, PART>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_kernel<MECH, DIR, PART>), grid, dim3(256), 0, stream, a);
 }
 template <int MECH, int DIR>
 static void launch_one(const BwdArgs& a, dim3 grid, hipStream_t stream) {

@@ -12,22 +12,25 @@
 // exactly once; a second pass (relpos_agg.hip) merges the partials in a fixed order.  No
 // atomics anywhere, so results are bitwise reproducible.
 //
-// Shaw / DeBERTa: per step, dS is scattered into a workgroup buffer E[t][x] indexed by window
-// offset t and lane-side row x (the band t = x - y + 63 of the 64 streamed rows y).  Then
-//   dX_rel += Win^T E^T                     (per wave, its 96-offset window)
-//   dTable_window[t] += sum_x E[t][x] X[x]  (workgroup GEMM, 3 tiles per wave)
-// The window slides by 64 offsets per step, so a wave's three 32-offset accumulators shift by
-// two positions each step and the one that leaves the window is final: it is written out.
-// T-XL (full span, every tile general) splits the same work over the two passes so that each
-// fits two workgroups per CU: the dQ pass reads dX_rel's skewed operand straight from the
-// wave's fp32 dS buffer, and the dK/dV pass runs the table GEMM over its streamed query tile,
-//   dr_window[t] += sum_y E2[t][y] Q[y],   E2[t][y] = dS[y][x], t = y - x + 127,
-// with E2 in the space of the column-side skew buffer.
+// Relation gradients of a table applied on one side (the row side: lane rows X times the table
+// row of offset lam = a - b) are split over the two passes so that each fits two workgroups per
+// CU.  The pass where the table is on the row side adds dX_rel = sum_b dS[a][b] T[row(lam)]
+// with the skewed operand read straight from the wave's fp32 dS buffer; the pass where it is
+// on the column side (the X rows are now the streamed rows) runs the table GEMM over its
+// streamed tile,
+//   dT_window[t] += sum_y E2[t][y] Y[y],   E2[t][y] = dS[y][x], t = y - x + 127,
+// with E2 in the space of the column-side skew buffer.  The window slides by 64 offsets per
+// step, so a wave's three 32-offset accumulators shift each step and the one that leaves the
+// window is final: it is written out.  T-XL (full span, every tile general) runs this over every
+// step.  Shaw and DeBERTa (clipped offsets) run each direction in two parts: a light pass over
+// the steps whose workgroup tile is clipped throughout (every element reads an end row, so the
+// relation term is a per-row constant) and a general pass over the rest; the table's interior
+// rows come from the column-side general pass, its two end rows (sums over the clipped
+// elements) from the row-side passes.
 #include "relpos_tile.h"
 
 namespace relpos {
 
-constexpr int ESTR16 = 136;   // bf16 E row stride (elements)
 constexpr int ESTRT = 200;    // bf16 E2T row stride (elements): 192 window offsets + pad
 static_assert(BOTH * ESTRT * 2 <= NWAVE * WROWS * GS2 * 4, "E2T fits the column-skew buffer");
 
@@ -47,15 +50,15 @@ struct BV {
   static constexpr bool TXL = MECH == MECH_TXL;
   static constexpr bool CLIP = MECH == MECH_SHAW || MECH == MECH_DEBERTA;
   static constexpr bool DIAG = DIR == 0 && (MECH == MECH_T5 || MECH == MECH_TXL);
-  // DeBERTa general pass: the row-side dX_rel from the wave's dS buffer and the column-side
-  // table gradient over the streamed rows (no E buffer, so two workgroups fit per CU); the
-  // row-side table's interior rows come from the other direction's pass
-  static constexpr bool DFAT = MECH == MECH_DEBERTA && PART == 2;
+  // General pass of Shaw / DeBERTa: the row-side dX_rel from the wave's dS buffer and the
+  // column-side table gradient over the streamed rows (no E buffer, so two workgroups fit per
+  // CU); a table's interior rows come from the pass where it is the column side, its end rows
+  // from the pass where it is the row side
+  static constexpr bool DFAT = CLIP && PART == 2;
   static constexpr bool TQ = TXL && DIR == 0;         // T-XL query side (circular row window)
   static constexpr bool TK = TXL && DIR == 1;         // T-XL key side (circular column window)
-  static constexpr bool EBUF = ROW && !TXL && !DFAT;  // shared E buffer + lane-side table GEMM
-  static constexpr bool GSREL = TQ || DFAT;           // dX_rel from the wave's fp32 dS buffer
-  static constexpr bool TG1 = TK || DFAT;             // table GEMM over the streamed rows
+  static constexpr bool GSREL = TQ || (DFAT && HAS_ROW);   // dX_rel from the wave's dS buffer
+  static constexpr bool TG1 = TK || (DFAT && HAS_COL);     // table GEMM over the streamed rows
   static constexpr bool WINB = ROW || COL;
   static constexpr bool GSB = ROW || COL || DIAG;
 
@@ -76,20 +79,8 @@ struct BV {
   __device__ static int rowB(int span) { return MECH == MECH_SHAW ? 0 : 2 * span - 1; }
 };
 
-// A operand with the k order of op_rows_tr / op_from_acc (slot j < 4: k = 4 kh + j,
-// slot 4 + j: k = 8 + 4 kh + j) read from 16 consecutive bf16 of a row at element e.
-__device__ __forceinline__ Op<1> op_from_lds_perm(const uint16_t* base, int e) {
-  const int kh = __lane_id() >> 5;
-  u32x2 lo = *(const u32x2*)(base + e + 4 * kh);
-  u32x2 hi = *(const u32x2*)(base + e + 8 + 4 * kh);
-  u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
-  Op<1> o;
-  o.p[0] = u4_to_bf8(v);
-  return o;
-}
-
-// Zero the slots of an op_from_lds_perm operand (row t, columns ybase + perm k) outside the
-// band y <= t <= y + 127.
+// Zero the slots of an op_rows_tr operand (row t; slot j < 4 is column ybase + 4 kh + j, slot
+// 4 + j column ybase + 8 + 4 kh + j) outside the band y <= t <= y + 127.
 __device__ __forceinline__ void band_mask(Op<1>& o, int t, int ybase) {
   // recomputed where used: hoisted out of the step loop, the masks would hold registers
   asm volatile("" : "+v"(t));
@@ -119,8 +110,6 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   // the skewed reads of the dX_rel operand reach up to 32 floats beyond a wave's buffer
   constexpr int GSG = V::GSREL ? 32 : 0;
   __shared__ __attribute__((aligned(16))) float gsb_raw[V::GSB ? NWAVE * WROWS * GS2 + 2 * GSG : 4];
-  __shared__ __attribute__((aligned(16))) uint16_t ebuf[V::EBUF ? WIN * ESTR16 : 8];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[V::EBUF ? BLANE * TSTR : 8];   // lane rows X
   __shared__ __attribute__((aligned(16))) float vec_s[V::LUTP ? WIN : 4];  // bias LUT slice
   // T-XL u.k / clipped end-row constants / ALiBi ramps +m y / s and -m y / s
   constexpr int NOVEC = (MECH == MECH_TXL && DIR == 0)
@@ -129,7 +118,6 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   __shared__ float red_s[MECH == MECH_ALIBI ? NWAVE : 1];   // ALiBi: per-wave slope-gradient sums
   __shared__ __attribute__((aligned(16))) float ovec_s[NOVEC];   // per-other-row constants
   __shared__ __attribute__((aligned(16))) float lsd_s[DIR == 1 ? 2 * BOTH : 4];   // LSE*log2e, D per query
-  __shared__ __attribute__((aligned(16))) float endc[V::CLIP && V::ROW && !V::DFAT ? 2 * BLANE : 4];
   float* const gsb = gsb_raw + GSG;
 
   const AttnShape sh = a.sh;
@@ -232,7 +220,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int nrt = L + 256;
   float* prow = nullptr;     // row-side table partial
   int prow_rows = 0;
-  if constexpr (V::EBUF || V::DFAT) {
+  if constexpr (V::DFAT) {
     prow_rows = (MECH == MECH_SHAW) ? 2 * span + 1 : 2 * span;
     prow = (DIR == 0 ? a.part_q : a.part_k) + owner * (DIR == 0 ? a.part_q_stride : a.part_k_stride);
   }
@@ -254,28 +242,13 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   float* pdiag = nullptr;
   if constexpr (V::DIAG) pdiag = a.part_qv + owner * (int64_t)(NWAVE * nrt);
 
-  // lane offsets the sweep writes: every window row of every step, [A0 - b0 - 63, A0 - b0 + 128],
-  // for the table partial
-  const int cov_lo = A0 - bt_last - 63, cov_hi = A0 - bt0 + 128;
-
   // ---- zero what the sweep will not write ----
-  if constexpr (V::EBUF) {
-    for (int64_t e = tid; e < (int64_t)prow_rows * kHeadDim; e += 256) {
-      const int row = (int)(e / kHeadDim);
-      // end rows are written by the end-row pass; interior rows iff their offset is covered
-      int lam;
-      if constexpr (MECH == MECH_SHAW) lam = span - row;   // dir 0 only: row = clamp(-lam) + k
-      else lam = row - span;                               // row = clamp(lam + k)
-      const bool end = row == V::rowA(span) || row == V::rowB(span);
-      const bool covered = end || (nsteps > 0 && lam >= cov_lo && lam <= cov_hi);
-      if (!covered) prow[e] = 0.f;
-    }
-  }
-  if constexpr (V::DFAT) {
+  if constexpr (V::DFAT && V::HAS_COL) {
     // column offsets mu = b - a of every window row of every step are flushed (interior ones)
     const int mlo = bt0 - A0 - (BLANE - 1), mhi = bt_last - A0 + BOTH;
     for (int64_t e = tid; e < (int64_t)prow_rows * kHeadDim; e += 256) {
-      const int row = (int)(e / kHeadDim), mu = row - span;   // row = clamp(mu + k)
+      // table row of mu: Shaw clamp(-mu) + k, DeBERTa clamp(mu + k)
+      const int row = (int)(e / kHeadDim), mu = (MECH == MECH_SHAW) ? span - row : row - span;
       const bool end = row == V::rowA(span) || row == V::rowB(span);
       if (!end && !(nsteps > 0 && mu >= mlo && mu <= mhi)) pcol[e] = 0.f;
     }
@@ -295,63 +268,38 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       if (!(nsteps > 0 && lam >= lo && lam <= hi)) pdiag[e] = 0.f;
     }
   }
-  if constexpr (V::EBUF) {
-    const int n16 = (WIN * ESTR16) / 8;
-    u32x4 z = {0u, 0u, 0u, 0u};
-    for (int e = tid; e < n16; e += 256) *(u32x4*)(ebuf + 8 * e) = z;
-  }
-  if constexpr (V::EBUF) {
-    stage64<T, NP>(xs, xg, A0, L);
-    stage64<T, NP>(xs + BOTH * TSTR, xg, A0 + BOTH, L);
-  }
 
   // ---- accumulators ----
   f32x16 gacc[2] = {f32x16{}, f32x16{}};    // dX (content + relation), dir 1: dK
   f32x16 vacc[2] = {f32x16{}, f32x16{}};    // dir 1: dV
-  f32x16 racc[3] = {f32x16{}, f32x16{}, f32x16{}};   // row-side table window accumulators
+  f32x16 racc[3] = {f32x16{}, f32x16{}, f32x16{}};   // table window accumulators
   float cA = 0.f, cB = 0.f;                  // clipped-end sums of dS (lane row)
   float colsum = 0.f;                        // dir 1 T-XL: sum_i dS_ij
   float dcarry = 0.f;                        // diagonal t = lane carried into the next step
   const int gdb = w & 1, gp = w >> 1;        // GEMM tiles of this wave: d-block, t-block parity
 
-  // Store one window accumulator block to the table partial: register r holds offset
-  // lam0 + 8 (r / 4) + r % 4, column 32 gdb + l32.  Only interior offsets are stored (clipped
-  // ones belong to the end rows); when the whole block is interior its 16 rows are consecutive
-  // table rows, stored from one base without per-element tests.
-  auto flush_block = [&](const f32x16& acc, int lam0) {
+  // Store one window accumulator block to the column-side table partial: register r holds
+  // offset mu0 + 8 (r / 4) + r % 4 (mu = b - a), column 32 gdb + l32.  Only interior offsets are
+  // stored (clipped ones belong to the end rows); when the whole block is interior its 16 rows
+  // are consecutive table rows (ascending for DeBERTa, row mu + k; descending for Shaw, k - mu),
+  // stored from one base without per-element tests.
+  auto flush_col = [&](const f32x16& acc, int mu0) {
     const int d = 32 * gdb + l32;
-    constexpr int rstep = (MECH == MECH_SHAW && DIR == 0) ? -1 : 1;   // table row per unit lam
-    if (lam0 > V::TA(span) && lam0 + 27 < V::TB(span)) {
-      float* fb = prow + (uint32_t)(V::row_of(lam0, span, nrel, toff) * kHeadDim + d);
+    constexpr int rstep = (MECH == MECH_SHAW) ? -1 : 1;
+    if (mu0 > V::TA(span) && mu0 + 27 < V::TB(span)) {
+      float* fb = pcol + (uint32_t)(V::col_of(mu0, span, nrel, toff) * kHeadDim + d);
 #pragma unroll
       for (int r = 0; r < 16; ++r) fb[rstep * (8 * (r >> 2) + (r & 3)) * kHeadDim] = acc[r];
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int lam = lam0 + 8 * (r >> 2) + (r & 3);
-        if (lam > V::TA(span) && lam < V::TB(span))
-          prow[(int64_t)V::row_of(lam, span, nrel, toff) * kHeadDim + d] = acc[r];
-      }
-    }
-  };
-  // DeBERTa general pass: the same for the column-side table (offsets mu = b - a, table row
-  // mu + k, interior rows only)
-  auto flush_col = [&](const f32x16& acc, int mu0) {
-    const int d = 32 * gdb + l32;
-    if (mu0 > V::TA(span) && mu0 + 27 < V::TB(span)) {
-      float* fb = pcol + (uint32_t)((mu0 + span) * kHeadDim + d);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = acc[r];
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
         const int mu = mu0 + 8 * (r >> 2) + (r & 3);
-        if (mu > V::TA(span) && mu < V::TB(span)) pcol[(uint32_t)((mu + span) * kHeadDim + d)] = acc[r];
+        if (mu > V::TA(span) && mu < V::TB(span))
+          pcol[(uint32_t)(V::col_of(mu, span, nrel, toff) * kHeadDim + d)] = acc[r];
       }
     }
   };
   float* gs = gsb + (V::GSB ? w * WROWS * GS2 : 0);
-  uint16_t* e16 = ebuf;
 
   // the next step's streamed tiles are read into registers while the current step computes
   auto step_base = [&](int st) { return bt0 + st * BOTH; };
@@ -369,10 +317,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       ovec_s[BOTH + tid] = -am * (float)tid;
     }
   }
-  // Fat passes (one workgroup per compute unit, so no other workgroup hides their latency; and
-  // registers to spare): the next general step's windows and per-row values are read into
-  // registers one step ahead.
-  WindowPrefetch<T> pwc, pwr;
+  // per-row values of the streamed rows: end-row constants (light key-side pass) and, in the
+  // key-side general pass, LSE and D read one step ahead
   float pov = 0.f, pl2 = 0.f, pdd = 0.f;
   auto colfn_at = [&](int b0x) {   // column window row x <-> mu = b - a = (b0 - A0 - 127) + x
     return [=](int x) { return V::col_of((b0x - A0 - (BLANE - 1)) + x, span, nrel, toff); };
@@ -398,13 +344,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       }
     }
   };
-  if constexpr (V::FAT) {
-    if (nsteps > 0) {
-      if constexpr (V::COL && !V::DFAT) pwc.load(tcol, colfn_at(bt0));
-      if constexpr (V::ROW && !V::DFAT) pwr.load(trow, rowfn_at(bt0));
-      if constexpr (V::CLIP && V::HAS_COL && !V::DFAT) ov_load(bt0);
-      if constexpr (DIR == 1) lsd_load(bt0);
-    }
+  if constexpr (V::FAT && DIR == 1) {
+    if (nsteps > 0) lsd_load(bt0);
   }
   int next = 0;
   while (next < nsteps && step_skipped(next)) ++next;
@@ -484,11 +425,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     }
     if constexpr (V::CLIP && V::HAS_COL && !V::DFAT) {
       // end A values of the 64 streamed rows, then end B: each a contiguous vector
-      if constexpr (!V::FAT) ov_load(b0);
+      ov_load(b0);
       if (tid < 2 * BOTH) ovec_s[(tid & 1) * BOTH + (tid >> 1)] = pov;
-      if constexpr (V::FAT) {
-        if (step + 1 < nsteps) ov_load(b0 + BOTH);
-      }
     }
     if constexpr (DIR == 1 && V::FAT) {
       if (tid < BOTH) {
@@ -527,14 +465,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         }
       }
     } else if constexpr (V::ROW && !V::COL) {
-      if (wg_general) {
-        if constexpr (V::FAT) {
-          pwr.store(win);
-          if (step + 1 < nsteps) pwr.load(trow, rowfn_at(b0 + BOTH));
-        } else {
-          stage_window<T, NP>(win, trow, rowfn_at(b0));
-        }
-      }
+      if (wg_general) stage_window<T, NP>(win, trow, rowfn_at(b0));
     }
     // column side first (its window is replaced by the row-side window afterwards)
     if constexpr (V::TK) {
@@ -556,14 +487,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         }
       }
     } else if constexpr (V::COL) {
-      if (wg_general) {
-        if constexpr (V::FAT && !V::DFAT) {
-          pwc.store(win);
-          if (step + 1 < nsteps) pwc.load(tcol, colfn_at(b0 + BOTH));
-        } else {
-          stage_window<T, NP>(win, tcol, colfn_at(b0));
-        }
-      }
+      if (wg_general) stage_window<T, NP>(win, tcol, colfn_at(b0));
     }
     // issue the next step's tile reads (after this step's staging reads have been consumed)
     next = step + 1;
@@ -612,12 +536,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if constexpr (V::ROW && V::COL) {
       if (wg_general) {
         __syncthreads();   // column-side window reads done
-        if constexpr (V::FAT && !V::DFAT) {
-          pwr.store(win);
-          if (step + 1 < nsteps) pwr.load(trow, rowfn_at(b0 + BOTH));
-        } else {
-          stage_window<T, NP>(win, trow, rowfn_at(b0));
-        }
+        stage_window<T, NP>(win, trow, rowfn_at(b0));
         __syncthreads();
       }
     }
@@ -732,7 +651,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             }
         }
       }
-      if constexpr (V::DFAT) {
+      if constexpr (V::DFAT && V::HAS_ROW) {
         // row-side clipped elements: their dX_rel comes through the window's end rows, and
         // the end rows' table gradient needs their sums per lane row
         if (lamlo <= V::TA(span) || lamhi >= V::TB(span)) {
@@ -780,10 +699,9 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         }
     }
 
-    // ---- offset-sharded row-side gradients ----
+    // ---- light pass: the whole wave tile reads one row-side end row ----
     if constexpr (V::CLIP && V::HAS_ROW && !V::DFAT) {
-      if (!(V::EBUF && wg_general) && !wave_none) {
-        // the whole wave tile reads one end row
+      if (!wave_none) {
         float tot = 0.f;
 #pragma unroll
         for (int b = 0; b < 2; ++b)
@@ -792,67 +710,9 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         if (rcls == 1) cA += tot; else cB += tot;
       }
     }
-    if constexpr (V::EBUF) {
-      const bool use_e = wg_general;
-      if (use_e) {
-        __syncthreads();   // skew buffers and previous E reads are done
-        // scatter the band; clipped elements go to the end-row sums instead
-        const int xcol = WROWS * w + l32;
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
-            const int t = xcol - y + 63;
-            float v = wave_none ? 0.f : ds[b][r];
-            if constexpr (V::CLIP) {
-              const int lam = cwin - 63 + t;
-              if (lam <= V::TA(span)) { cA += v; v = 0.f; }
-              else if (lam >= V::TB(span)) { cB += v; v = 0.f; }
-            }
-            e16[t * ESTR16 + xcol] = f2bf_bits(v);
-          }
-        __syncthreads();
-      }
 
-      if constexpr (V::ROW) {
-        // slide the window accumulators by two blocks; the block leaving the window is final
-        if (step > 0) {
-          const int pc = cwin + BOTH;   // previous step's window base (lam = pc - 63 + t)
-          flush_block(racc[2], pc - 63 + 32 * (gp + 4) + 4 * kh);
-          racc[2] = racc[1];
-          racc[1] = racc[0];
-          racc[0] = f32x16{};
-        }
-        if (wg_general) {
-          // dX_rel += Win^T E^T over this wave's 96 offsets
-#pragma unroll
-          for (int cc = 0; cc < 6; ++cc) {
-            Op<NP> eop = op_rows_tr<NP>(e16, WIN * ESTR16, ESTR16, WROWS * w + 16 * cc, WROWS * w);
-#pragma unroll
-            for (int db = 0; db < 2; ++db) {
-              Op<NP> wt = op_rows_tr<NP>(win, WIN * TSTR, TSTR, WROWS * w + 16 * cc, 32 * db);
-              mma<NP>(gacc[db], wt, eop);
-            }
-          }
-          // workgroup GEMM: racc[i] (t-block gp + 2 i, d-block gdb) += E[t][x] X[x][d]
-#pragma unroll
-          for (int i = 0; i < 3; ++i) {
-            const int ab = gp + 2 * i;
-            const int c_lo = max(0, 2 * ab - 4), c_hi = min(7, 2 * ab + 1);
-            for (int cq = c_lo; cq <= c_hi; ++cq) {
-              Op<NP> eop = op_from_lds_perm(e16, (32 * ab + l32) * ESTR16 + 16 * cq);
-              Op<NP> xop2 = op_rows_tr<NP>(xs, BLANE * TSTR, TSTR, 16 * cq, 32 * gdb);
-              mma<NP>(racc[i], eop, xop2);
-            }
-          }
-        }
-      }
-
-    }
-
-    // ---- DeBERTa general pass: row-side dX_rel from the wave's dS buffer ----
-    if constexpr (V::DFAT) {
+    // ---- general pass (Shaw / DeBERTa): row-side dX_rel from the wave's dS buffer ----
+    if constexpr (V::DFAT && V::HAS_ROW) {
       if (!wave_none) {
         wave_lds_sync();   // the wave's dS writes (before the content gradients) are visible
         // dX_rel^T[d][x] += sum_t Win[32 w + t][d] E[x][t], E[x][t] = dS[x][x + 63 - t] for t
@@ -1035,14 +895,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   }
 
   // ---- final flush of the window accumulators ----
-  if constexpr (V::EBUF) {
-    if (nsteps > 0) {
-      const int pc = A0 - bt_last;
-#pragma unroll
-      for (int i = 0; i < 3; ++i) flush_block(racc[i], pc - 63 + 32 * (gp + 2 * i) + 4 * kh);
-    }
-  }
-  if constexpr (V::DFAT) {
+  if constexpr (V::DFAT && V::HAS_COL) {
     // blocks gp + 2 and gp + 4 of the last window (shifted into racc[0], racc[1])
     if (nsteps > 0) {
 #pragma unroll
@@ -1110,7 +963,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   }
 
   // ---- end rows (clipped offsets): table gradient and lane gradient ----
-  if constexpr (V::DFAT) {
+  if constexpr (V::DFAT && V::ROW) {
     // cA / cB hold this lane's sum over its half of the other rows (this pass's clipped
     // elements, whose dX_rel came through the window); the light pass's sums still owe their
     // dX term
@@ -1149,38 +1002,6 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         const float ta = bf_bits2f(trow[(int64_t)V::rowA(span) * kHeadDim + d]);
         const float tb = bf_bits2f(trow[(int64_t)V::rowB(span) * kHeadDim + d]);
         gacc[db][r] = fmaf(lA, ta, fmaf(lB, tb, gacc[db][r]));
-      }
-  } else if constexpr (V::CLIP && V::ROW) {
-    // cA / cB hold this lane's sum over its half of the other rows
-    cA += xhalf(cA);
-    cB += xhalf(cB);
-    if constexpr (V::FAT) {
-      if (my_a < L) {
-        cA += a.cab[((int64_t)bh * L + my_a) * 2 + 0];
-        cB += a.cab[((int64_t)bh * L + my_a) * 2 + 1];
-      }
-    }
-    if (kh == 0) {
-      endc[WROWS * w + l32] = (my_a < L) ? cA : 0.f;
-      endc[BLANE + WROWS * w + l32] = (my_a < L) ? cB : 0.f;
-    }
-    __syncthreads();
-    if (tid < 2 * kHeadDim) {
-      const int e = tid / kHeadDim, d = tid % kHeadDim;
-      float acc = 0.f;
-      for (int x = 0; x < BLANE; ++x) acc = fmaf(endc[e * BLANE + x], bf_bits2f(xs[x * TSTR + d]), acc);
-      const int row = e == 0 ? V::rowA(span) : V::rowB(span);
-      prow[(int64_t)row * kHeadDim + d] = acc;
-    }
-    // dX += cA T[rowA] + cB T[rowB]
-#pragma unroll
-    for (int db = 0; db < 2; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int d = 32 * db + 8 * (r >> 2) + 4 * kh + (r & 3);
-        const float ta = bf_bits2f(trow[(int64_t)V::rowA(span) * kHeadDim + d]);
-        const float tb = bf_bits2f(trow[(int64_t)V::rowB(span) * kHeadDim + d]);
-        gacc[db][r] = fmaf(cA, ta, fmaf(cB, tb, gacc[db][r]));
       }
   }
 
@@ -1228,14 +1049,10 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   }
 }
 
-// Variants whose LDS footprint leaves room for two workgroups per CU are compiled for two
-// waves per SIMD (at most 256 registers per lane); the others for one.
+// Every variant fits two workgroups per CU (LDS at most 80 KiB) and is compiled for two waves
+// per SIMD (at most 256 registers per lane).
 template <int MECH, int DIR, int PART>
 __global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
-  bwd_body<MECH, DIR, PART>(a);
-}
-template <int MECH, int DIR, int PART>
-__global__ __launch_bounds__(256, 1) void bwd_kernel_1wg(BwdArgs a) {
   bwd_body<MECH, DIR, PART>(a);
 }
 }  // namespace relpos

@@ -125,40 +125,6 @@ struct TilePrefetch {
   }
 };
 
-// Register prefetch of a whole WIN-row bf16 window (window row x reads table row rowfn(x),
-// < 0 = zero row): this thread's rows 64 i + t / 4, 16 elements each.  load() issues the global
-// reads; store() writes them to LDS later.
-template <typename T>
-struct WindowPrefetch {
-  static_assert(sizeof(T) == 2, "bf16 windows");
-  u32x4 v[3][2];
-  template <typename F>
-  __device__ __forceinline__ void load(const T* table, F rowfn) {
-    const int t = threadIdx.x;
-    const int c = (t & 3) * 16;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int row = rowfn(64 * i + (t >> 2));
-      if (row >= 0) {
-        const u32x4* g = (const u32x4*)stage_addr(table, (int64_t)row * kHeadDim + c);
-        v[i][0] = g[0];
-        v[i][1] = g[1];
-      } else {
-        v[i][0] = v[i][1] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* win) const {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < 3; ++i) {
-      const int e = (64 * i + (t >> 2)) * TSTR + (t & 3) * 16;
-      *(u32x4*)(win + e) = v[i][0];
-      *(u32x4*)(win + e + 8) = v[i][1];
-    }
-  }
-};
-
 // WIN window rows; window row x reads table row rowfn(x) (< 0 = zero row).
 template <typename T, int NP, typename F>
 __device__ __forceinline__ void stage_window(uint16_t* win, const T* table, F rowfn) {

@@ -38,56 +38,65 @@ __global__ __launch_bounds__(256) void agg_rows_kernel(const float* __restrict__
   if (g == 0 && e < nelem) out[e] = ((sh[0][l] + sh[1][l]) + (sh[2][l] + sh[3][l])) * scale;
 }
 
-// Owner (workgroup) of batch b, head h, block position p, and the first lane offset of its
-// compact partial: the dQ pass visits blocks in reverse order under a causal mask.
-__device__ __forceinline__ void owner_of(int b, int h, int p, int H, int nb, bool rev, int L,
-                                         int64_t& own, int& lam_base) {
-  const int blk = rev ? nb - 1 - p : p;
-  own = ((int64_t)b * H + h) * nb + p;
-  lam_base = blk * 128 - L - 64;
-}
+__device__ __forceinline__ int floordiv32(int a) { return a >= 0 ? a / 32 : -((31 - a) / 32); }
 
-// diag[h][delta + L - 1] = sum over (b, block, wave) of the per-offset dS sums (the query-side
-// pass writes one partial per wave: wave w of owner o at slot 4 o + w, its offsets counted from
-// the owner's lam_base + 32 w).  One workgroup per 64 consecutive (head, offset) entries: thread
-// t takes entry t % 64 and the partials of group t / 64 (a quarter of them, consecutive, in
-// ascending (owner, wave) order, 16 loads in flight); the four group sums are then added in
-// group order.
+// diag[h][delta + L - 1] = sum over (b, block, wave) of the per-offset dS sums.  The query-side
+// pass writes one partial per wave: wave w of the workgroup at block blk (position p, blk = p or,
+// under a causal mask, nb - 1 - p) at slot ((b H + h) nb + p) NWAVE + w, its offsets counted
+// from 32 u - L - 64 with u = 4 blk + w.  One workgroup per (head, 64 consecutive offsets): only
+// the wave rows u that hold one of them are visited, in ascending (b, u) order split into four
+// consecutive quarters (thread group t / 64 takes one, 16 loads in flight, the address advanced
+// by a constant per step); the four group sums are then added in group order.
+template <bool REV>
 __global__ __launch_bounds__(256) void agg_diag_kernel(const float* __restrict__ pdiag, int B,
-                                                       int H, int L, int nb, int rev, int nrt,
+                                                       int H, int L, int nb, int nrt,
                                                        float* __restrict__ diag) {
   __shared__ float sh[4][64];
   const int t = threadIdx.x, j = t & 63, g = t >> 6;
-  const int64_t idx = (int64_t)blockIdx.x * 64 + j;
-  const int n = 2 * L - 1;
-  const bool valid = idx < (int64_t)H * n;
-  const int h = valid ? (int)(idx / n) : 0;
-  const int delta = valid ? (int)(idx % n) - (L - 1) : 0;
+  const int n = 2 * L - 1, nch = (n + 63) / 64;
+  const int h = blockIdx.x / nch, c0 = 64 * (blockIdx.x - h * nch);
+  const bool valid = c0 + j < n;
+  // lane offset delta = c0 + j - (L - 1) sits at x = lim - 32 u of wave row u, x in [0, nrt)
+  const int a0 = c0 - (L - 1) + L + 64, lim = a0 + j;
+  const int u_lo = max(0, floordiv32(a0 - nrt) + 1);
+  const int u_hi = min(NWAVE * nb - 1, floordiv32(a0 + 63));
+  const int nu = max(0, u_hi - u_lo + 1);
+  const int nq = B * nu, per = (nq + 3) / 4;
+  const int qa = min(nq, g * per), qb = min(nq, qa + per);
+  auto elem_of = [&](int bb, int uu) -> int64_t {
+    const int64_t own0 = ((int64_t)bb * H + h) * nb;
+    const int64_t slot = REV ? (own0 + nb - 1 - (uu >> 2)) * NWAVE + (uu & 3) : own0 * NWAVE + uu;
+    return slot * nrt + (lim - 32 * uu);
+  };
+  int b = nu > 0 ? qa / nu : 0, u = u_lo + (nu > 0 ? qa - b * nu : 0);
+  const float* ptr = pdiag + (qa < qb ? elem_of(b, u) : 0);
+  // the next wave row of the same block is the next slot (x 32 lower); under a causal mask the
+  // next block's first wave row lies 7 slots lower
+  const int64_t inc = (int64_t)nrt - 32, inc_rev = -(int64_t)7 * nrt - 32;
   constexpr int G = 16;
-  const int nq = B * nb * NWAVE, per = (nq + 3) / 4;
-  const int qa = g * per, qb = min(nq, qa + per);
-  // partial q = (b nb + p) NWAVE + w, tracked incrementally (no division per load)
-  int w = qa % NWAVE, b = (qa / NWAVE) / nb, p = (qa / NWAVE) - b * nb;
   float acc = 0.f;
   for (int q0 = qa; q0 < qb; q0 += G) {
     float ld[G];
 #pragma unroll
-    for (int u = 0; u < G; ++u) {
-      const int blk = rev ? nb - 1 - p : p;
-      const int64_t slot = (((int64_t)b * H + h) * nb + p) * NWAVE + w;
-      const int x = delta - (blk * 128 + 32 * w - L - 64);
-      ld[u] = (valid && q0 + u < qb && x >= 0 && x < nrt) ? pdiag[slot * nrt + x] : 0.f;
-      if (++w == NWAVE) {
-        w = 0;
-        if (++p == nb) { p = 0; ++b; }
+    for (int k = 0; k < G; ++k) {
+      const int x = lim - 32 * u;
+      ld[k] = (valid && q0 + k < qb && x >= 0 && x < nrt) ? *ptr : 0.f;
+      if (u == u_hi) {
+        ++b;
+        u = u_lo;
+        if (b < B) ptr = pdiag + elem_of(b, u);
+      } else {
+        ptr += (REV && (u & 3) == 3) ? inc_rev : inc;
+        ++u;
       }
     }
 #pragma unroll
-    for (int u = 0; u < G; ++u) acc += ld[u];
+    for (int k = 0; k < G; ++k) acc += ld[k];
   }
   sh[g][j] = acc;
   __syncthreads();
-  if (t < 64 && valid) diag[idx] = ((sh[0][t] + sh[1][t]) + sh[2][t]) + sh[3][t];
+  if (t < 64 && valid)
+    diag[(int64_t)h * n + c0 + t] = ((sh[0][t] + sh[1][t]) + sh[2][t]) + sh[3][t];
 }
 
 // T-XL dr[h][row][d] = s (sum_{b, key block} part[own][x][d] + v_h[d] diag_h[delta]).
@@ -117,20 +126,38 @@ __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict
       if (row < nrel) acc[k] = *(const f32x4*)(dr + ((int64_t)h * nrel + row) * kHeadDim + (e & 63));
     }
   }
+  // owner p holds these 64 offsets at its partial rows x0(p) .. x0(p) + 63; x0 does not decrease
+  // with p (with a two-sided window it is constant once 128 p > wr), so the owners that hold any
+  // of them form one range [p_lo, p_hi], the same for every slice
+  auto x0of = [&](int p) {
+    const int rbase = (wl >= 0 && wr >= 0) ? (max(0, 128 * p - wr) / 64) * 64 + 65 : 0;
+    return delta0 + 128 * p + 192 - rbase;
+  };
+  int lo = 0, hi = nb;   // p_lo: the first p with x0 + 63 >= 0
+  while (lo < hi) {
+    const int m = (lo + hi) >> 1;
+    if (x0of(m) + 63 >= 0) hi = m; else lo = m + 1;
+  }
+  const int p_lo = lo;
+  hi = nb;               // p_hi: the first p with x0 >= nrt
+  while (lo < hi) {
+    const int m = (lo + hi) >> 1;
+    if (x0of(m) >= nrt) hi = m; else lo = m + 1;
+  }
+  const int p_hi = lo;
   // this head's slices in the group: local i = i0, i0 + H, ...
   const int i0 = ((h - s0) % H + H) % H;
   const int nh = i0 < ns ? (ns - i0 + H - 1) / H : 0;
-  // owners q = j nb + p in ascending order, four at a time: the 16 loads of a group are in
+  // (slice, owner) pairs in ascending order, four at a time: the 16 loads of a group are in
   // flight together, then added owner by owner (the order of the sum does not change)
   constexpr int G = 4;
-  const int nq = nh * nb;
+  const int no = p_hi - p_lo, nq = nh * no;
   for (int q0 = 0; q0 < nq; q0 += G) {
     f32x4 ld[G][4];
 #pragma unroll
     for (int u = 0; u < G; ++u) {
-      const int q = q0 + u, j = q / nb, p = q % nb;
-      const int rbase = (wl >= 0 && wr >= 0) ? (max(0, 128 * p - wr) / 64) * 64 + 65 : 0;
-      const int x0 = delta0 + 128 * p + 192 - rbase;
+      const int q = q0 + u, j = q / no, p = p_lo + (q - j * no);
+      const int x0 = x0of(p);
       const float* base = prow + ((int64_t)(i0 + j * H) * nb + p) * (int64_t)nrt * kHeadDim;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -268,9 +295,14 @@ hipError_t launch_agg_rows(const float* part, int64_t stride, int nown, int64_t 
 
 hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool rev, int nrt,
                            float* diag, hipStream_t st) {
-  const int64_t n = (int64_t)H * (2 * L - 1);
-  hipLaunchKernelGGL(agg_diag_kernel, dim3(nblk(n, 64)), dim3(256), 0, st, pdiag, B, H, L, nb,
-                     rev ? 1 : 0, nrt, diag);
+  const int64_t nw = (int64_t)H * ((2 * L - 1 + 63) / 64);
+  if (L < 1 || nw == 0) return hipSuccess;
+  if (rev)
+    hipLaunchKernelGGL(agg_diag_kernel<true>, dim3((unsigned)nw), dim3(256), 0, st, pdiag, B, H,
+                       L, nb, nrt, diag);
+  else
+    hipLaunchKernelGGL(agg_diag_kernel<false>, dim3((unsigned)nw), dim3(256), 0, st, pdiag, B, H,
+                       L, nb, nrt, diag);
   return hipGetLastError();
 }
 

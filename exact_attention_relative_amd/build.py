@@ -16,11 +16,13 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librelpos_attn.so")
 SOURCES = ["relpos_api.hip", "relpos_prep.hip", "relpos_fwd.hip", "relpos_bwd.hip", "relpos_agg.hip",
-           "relpos_proj.hip", "relpos_bwd_txl_key.hip", "relpos_bwd_fat_q.hip"]
-# per-source options: the T-XL key-side pass schedules with the register-pressure trackers
-# (fewer spills at its 256-register budget); the query-side general passes of Shaw and DeBERTa
-# keep their MFMA accumulators in VGPRs (fewer copies between register files; measured)
+           "relpos_proj.hip", "relpos_bwd_txl_key.hip", "relpos_bwd_fat_q.hip", "relpos_bwd_trk.hip"]
+# per-source options: the T-XL passes and the key-side passes of Shaw and DeBERTa schedule with
+# the register-pressure trackers (fewer spills at the 256-register budget); the query-side
+# general passes of Shaw and DeBERTa keep their MFMA accumulators in VGPRs (fewer copies between
+# register files; measured)
 EXTRA_FLAGS = {"relpos_bwd_txl_key.hip": ["-mllvm", "-amdgpu-use-amdgpu-trackers=1"],
+               "relpos_bwd_trk.hip": ["-mllvm", "-amdgpu-use-amdgpu-trackers=1"],
                "relpos_bwd_fat_q.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 # measurement-only MFMA throughput probe, a library of its own
 PROBE_LIB = os.path.join(PKG, "librelpos_probe.so")

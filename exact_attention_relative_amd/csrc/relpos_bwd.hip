@@ -1,7 +1,8 @@
 // Backward launch logic: per mechanism and direction, the pass variants of relpos_bwd_body.h.
 // The T-XL key-side pass is instantiated in relpos_bwd_txl_key.hip, a translation unit of its
 // own compiled with the scheduler's register-pressure trackers, which spill less there; the
-// query-side general passes of Shaw and DeBERTa in relpos_bwd_fat_q.hip.
+// query-side general passes of Shaw and DeBERTa in relpos_bwd_fat_q.hip; the T-XL query-side
+// pass and the key-side passes of Shaw and DeBERTa in relpos_bwd_trk.hip.
 #include "relpos_bwd_body.h"
 
 namespace relpos {
@@ -10,6 +11,8 @@ namespace relpos {
 void launch_bwd_txl_key(const BwdArgs& a, dim3 grid, hipStream_t stream);
 // relpos_bwd_fat_q.hip: the query-side general passes of Shaw and DeBERTa
 void launch_bwd_fat_q(int mech, const BwdArgs& a, dim3 grid, hipStream_t stream);
+// relpos_bwd_trk.hip: passes compiled with the register-pressure trackers
+void launch_bwd_trk(int mech, int dir, int part, const BwdArgs& a, dim3 grid, hipStream_t stream);
 
 // Shaw and DeBERTa run in two parts: a light pass over the clipped steps, then the general pass.
 template <int MECH, int DIR>
@@ -20,6 +23,8 @@ template <int MECH, int DIR, int PART>
 static void launch_part(const BwdArgs& a, dim3 grid, hipStream_t stream) {
   if constexpr (DIR == 0 && PART == 2)
     launch_bwd_fat_q(MECH, a, grid, stream);
+  else if constexpr (DIR == 1 && PART != 0)
+    launch_bwd_trk(MECH, DIR, PART, a, grid, stream);
   else
     hipLaunchKernelGGL((bwd_kernel<MECH, DIR, PART>), grid, dim3(256), 0, stream, a);
 }
@@ -27,6 +32,8 @@ template <int MECH, int DIR>
 static void launch_one(const BwdArgs& a, dim3 grid, hipStream_t stream) {
   if constexpr (MECH == MECH_TXL && DIR == 1) {
     launch_bwd_txl_key(a, grid, stream);
+  } else if constexpr (MECH == MECH_TXL && DIR == 0) {
+    launch_bwd_trk(MECH, DIR, 0, a, grid, stream);
   } else if constexpr (split_pass<MECH, DIR>()) {
     launch_part<MECH, DIR, 1>(a, grid, stream);
     launch_part<MECH, DIR, 2>(a, grid, stream);

@@ -655,13 +655,18 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         // row-side clipped elements: their dX_rel comes through the window's end rows, and
         // the end rows' table gradient needs their sums per lane row
         if (lamlo <= V::TA(span) || lamhi >= V::TB(span)) {
+          // element y has lam = my_a - b0 - y: end A iff TA - lam = sa + y >= 0, end B iff
+          // lam - TB = sb - y >= 0.  The tests are sign bits of integer sums (no lane masks:
+          // the compiler would compute all 32 of a step at once and spill them)
+          const int sa = V::TA(span) - (my_a - b0) + 4 * kh, sb = (my_a - b0) - V::TB(span) - 4 * kh;
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int lam = my_a - b0 - (32 * b + 8 * (r >> 2) + 4 * kh + (r & 3));
-              if (lam <= V::TA(span)) cA += ds[b][r];
-              else if (lam >= V::TB(span)) cB += ds[b][r];
+              const int yc = 32 * b + 8 * (r >> 2) + (r & 3);   // y - 4 kh
+              const uint32_t bits = __float_as_uint(ds[b][r]);
+              cA += __uint_as_float(bits & ~(uint32_t)((sa + yc) >> 31));
+              cB += __uint_as_float(bits & ~(uint32_t)((sb - yc) >> 31));
             }
         }
         // dS into the wave's buffer now (its skew reads are done), so that the fp32 copy dies
@@ -718,15 +723,21 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         // dX_rel^T[d][x] += sum_t Win[32 w + t][d] E[x][t], E[x][t] = dS[x][x + 63 - t] for t
         // in [x, x + 63] (else 0), read along the skewed diagonal of the buffer
         const float* grow = gs + l32 * GS2 + l32 + 63 - 4 * kh;
+        // band tests against lq = l32 - 4 kh; lq is opaque to the compiler, so the tests are redone
+        // each step (hoisted out of the step loop, their lane masks spill the scalar registers)
+        int lq = l32 - 4 * kh;
+        asm volatile("" : "+v"(lq));
 #pragma unroll
         for (int cc = 0; cc < 6; ++cc) {
           float e8[8];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const int t0 = 16 * cc + 4 * kh + j, t1 = t0 + 8;
             float v0 = grow[-(16 * cc + j)], v1 = grow[-(16 * cc + 8 + j)];
-            if (cc < 2) { v0 = t0 >= l32 ? v0 : 0.f; v1 = t1 >= l32 ? v1 : 0.f; }
-            if (cc > 3) { v0 = t0 <= l32 + 63 ? v0 : 0.f; v1 = t1 <= l32 + 63 ? v1 : 0.f; }
+            if (cc < 2) { v0 = 16 * cc + j >= lq ? v0 : 0.f; v1 = 16 * cc + 8 + j >= lq ? v1 : 0.f; }
+            if (cc > 3) {
+              v0 = 16 * cc + j - 63 <= lq ? v0 : 0.f;
+              v1 = 16 * cc + 8 + j - 63 <= lq ? v1 : 0.f;
+            }
             e8[j] = v0;
             e8[4 + j] = v1;
           }
@@ -812,15 +823,21 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           // dX_rel^T[d][x] += sum_t Win[32 w + t][d] E[x][t] with E[x][t] = dS[x][x + 63 - t]
           // for t in [x, x + 63] (else 0), read along the skewed diagonal of the buffer
           const float* grow = gs + l32 * GS2 + l32 + 63 - 4 * kh;
+          // band tests against lq = l32 - 4 kh; lq is opaque to the compiler, so the tests are redone
+          // each step (hoisted out of the step loop, their lane masks spill the scalar registers)
+          int lq = l32 - 4 * kh;
+          asm volatile("" : "+v"(lq));
 #pragma unroll
           for (int cc = 0; cc < 6; ++cc) {
             float e8[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const int t0 = 16 * cc + 4 * kh + j, t1 = t0 + 8;
               float v0 = grow[-(16 * cc + j)], v1 = grow[-(16 * cc + 8 + j)];
-              if (cc < 2) { v0 = t0 >= l32 ? v0 : 0.f; v1 = t1 >= l32 ? v1 : 0.f; }
-              if (cc > 3) { v0 = t0 <= l32 + 63 ? v0 : 0.f; v1 = t1 <= l32 + 63 ? v1 : 0.f; }
+              if (cc < 2) { v0 = 16 * cc + j >= lq ? v0 : 0.f; v1 = 16 * cc + 8 + j >= lq ? v1 : 0.f; }
+              if (cc > 3) {
+                v0 = 16 * cc + j - 63 <= lq ? v0 : 0.f;
+                v1 = 16 * cc + 8 + j - 63 <= lq ? v1 : 0.f;
+              }
               e8[j] = v0;
               e8[4 + j] = v1;
             }
@@ -838,9 +855,11 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           // t = l + 64 (rows l + 1 .. 31): one element of every row, rows in ascending order,
           // so the 32 reads are independent and issue back to back (every T-XL tile runs this)
           const float* gd = gs + (63 - lane);   // row n of diagonal l: gd[n * GS2 + n]
+          int ln = lane;   // opaque: the tests n <= lane are redone each step, not hoisted
+          asm volatile("" : "+v"(ln));
 #pragma unroll
           for (int n = 0; n < WROWS; ++n) {
-            const bool first = n <= lane;
+            const bool first = n <= ln;
             const float v = gd[n * GS2 + n - (first ? 0 : 64)];
             sums[0] += first ? v : 0.f;
             sums[1] += first ? 0.f : v;

@@ -41,53 +41,77 @@ __global__ __launch_bounds__(256) void agg_rows_kernel(const float* __restrict__
 __device__ __forceinline__ int floordiv32(int a) { return a >= 0 ? a / 32 : -((31 - a) / 32); }
 
 // diag[h][delta + L - 1] = sum over (b, block, wave) of the per-offset dS sums.  The query-side
-// pass writes one partial per wave: wave w of the workgroup at block blk (position p, blk = p or,
-// under a causal mask, nb - 1 - p) at slot ((b H + h) nb + p) NWAVE + w, its offsets counted
-// from 32 u - L - 64 with u = 4 blk + w.  One workgroup per (head, 64 consecutive offsets): only
-// the wave rows u that hold one of them are visited, in ascending (b, u) order split into four
-// consecutive quarters (thread group t / 64 takes one, 16 loads in flight, the address advanced
-// by a constant per step); the four group sums are then added in group order.
-template <bool REV>
-__global__ __launch_bounds__(256) void agg_diag_kernel(const float* __restrict__ pdiag, int B,
-                                                       int H, int L, int nb, int nrt,
-                                                       float* __restrict__ diag) {
-  __shared__ float sh[4][64];
+// pass writes one partial row per wave: wave w of the workgroup at block blk (position p, blk = p
+// or, under a causal mask, nb - 1 - p) at slot ((b H + h) nb + p) NWAVE + w, offset delta at
+// index delta - (32 u - L - 64) - diag_xoff(blk) with u = 4 blk + w.  One workgroup per (head,
+// 64 consecutive offsets): only the wave rows u that can hold one of them are visited, in
+// ascending (b, u) order split into consecutive parts, one per thread group of 64 (four groups,
+// or sixteen for window-compact rows; 16 loads in flight; the address advances by a constant
+// per step within a block); the group sums are then added in group order.
+template <bool REV, bool COMPACT>
+__global__ __launch_bounds__(COMPACT ? 1024 : 256) void agg_diag_kernel(
+    const float* __restrict__ pdiag, int B, int H, int L, int nb, int wl, int wr,
+    float* __restrict__ diag) {
+  // thread groups of 64 (one per offset); compact rows: few workgroups hold data, so 16 groups
+  constexpr int NG = COMPACT ? 16 : 4;
+  __shared__ float sh[NG][64];
   const int t = threadIdx.x, j = t & 63, g = t >> 6;
   const int n = 2 * L - 1, nch = (n + 63) / 64;
   const int h = blockIdx.x / nch, c0 = 64 * (blockIdx.x - h * nch);
   const bool valid = c0 + j < n;
-  // lane offset delta = c0 + j - (L - 1) sits at x = lim - 32 u of wave row u, x in [0, nrt)
+  const int ndg = diag_width(L, wl, wr);
+  // lane offset delta = c0 + j - (L - 1) sits at x = lim - xs(u) of wave row u, with
+  // xs(u) = 32 u + diag_xoff(blk)
   const int a0 = c0 - (L - 1) + L + 64, lim = a0 + j;
-  const int u_lo = max(0, floordiv32(a0 - nrt) + 1);
-  const int u_hi = min(NWAVE * nb - 1, floordiv32(a0 + 63));
+  int u_lo, u_hi;
+  if (!COMPACT) {   // x = lim - 32 u in [0, ndg)
+    u_lo = max(0, floordiv32(a0 - ndg) + 1);
+    u_hi = min(NWAVE * nb - 1, floordiv32(a0 + 63));
+  } else {          // every block sweeps the offsets near the diagonal; none holds the rest
+    const int64_t d0 = c0 - (L - 1);
+    const bool any = d0 + 63 >= -((int64_t)wr + 320) && d0 <= (int64_t)wl + 320;
+    u_lo = 0;
+    u_hi = any ? NWAVE * nb - 1 : -1;
+  }
   const int nu = max(0, u_hi - u_lo + 1);
-  const int nq = B * nu, per = (nq + 3) / 4;
+  const int nq = B * nu, per = (nq + NG - 1) / NG;
   const int qa = min(nq, g * per), qb = min(nq, qa + per);
+  auto xs_of = [&](int uu) { return 32 * uu + (COMPACT ? diag_xoff(L, wl, wr, 128 * (uu >> 2)) : 0); };
   auto elem_of = [&](int bb, int uu) -> int64_t {
     const int64_t own0 = ((int64_t)bb * H + h) * nb;
     const int64_t slot = REV ? (own0 + nb - 1 - (uu >> 2)) * NWAVE + (uu & 3) : own0 * NWAVE + uu;
-    return slot * nrt + (lim - 32 * uu);
+    return slot * ndg + (lim - xs_of(uu));
   };
   int b = nu > 0 ? qa / nu : 0, u = u_lo + (nu > 0 ? qa - b * nu : 0);
   const float* ptr = pdiag + (qa < qb ? elem_of(b, u) : 0);
-  // the next wave row of the same block is the next slot (x 32 lower); under a causal mask the
-  // next block's first wave row lies 7 slots lower
-  const int64_t inc = (int64_t)nrt - 32, inc_rev = -(int64_t)7 * nrt - 32;
+  int xs = xs_of(u);
+  // the next wave row of the same block is the next slot (x 32 lower); full-sweep rows continue
+  // into the next block the same way (under a causal mask its first wave row lies 7 slots lower);
+  // compact rows restart at the block's own offset
+  const int64_t inc = (int64_t)ndg - 32, inc_rev = -(int64_t)7 * ndg - 32;
   constexpr int G = 16;
   float acc = 0.f;
   for (int q0 = qa; q0 < qb; q0 += G) {
     float ld[G];
 #pragma unroll
     for (int k = 0; k < G; ++k) {
-      const int x = lim - 32 * u;
-      ld[k] = (valid && q0 + k < qb && x >= 0 && x < nrt) ? *ptr : 0.f;
+      const int x = lim - xs;
+      ld[k] = (valid && q0 + k < qb && x >= 0 && x < ndg) ? *ptr : 0.f;
       if (u == u_hi) {
         ++b;
         u = u_lo;
-        if (b < B) ptr = pdiag + elem_of(b, u);
+        if (b < B) {
+          ptr = pdiag + elem_of(b, u);
+          xs = xs_of(u);
+        }
+      } else if (COMPACT && (u & 3) == 3) {
+        ++u;
+        ptr = pdiag + elem_of(b, u);
+        xs = xs_of(u);
       } else {
         ptr += (REV && (u & 3) == 3) ? inc_rev : inc;
         ++u;
+        xs += 32;
       }
     }
 #pragma unroll
@@ -95,8 +119,12 @@ __global__ __launch_bounds__(256) void agg_diag_kernel(const float* __restrict__
   }
   sh[g][j] = acc;
   __syncthreads();
-  if (t < 64 && valid)
-    diag[(int64_t)h * n + c0 + t] = ((sh[0][t] + sh[1][t]) + sh[2][t]) + sh[3][t];
+  if (t < 64 && valid) {
+    float sum = sh[0][t];
+#pragma unroll
+    for (int i = 1; i < NG; ++i) sum += sh[i][t];
+    diag[(int64_t)h * n + c0 + t] = sum;
+  }
 }
 
 // T-XL dr[h][row][d] = s (sum_{b, key block} part[own][x][d] + v_h[d] diag_h[delta]).
@@ -293,16 +321,20 @@ hipError_t launch_agg_rows(const float* part, int64_t stride, int nown, int64_t 
   return hipGetLastError();
 }
 
-hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool rev, int nrt,
-                           float* diag, hipStream_t st) {
+hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool rev, int wl,
+                           int wr, float* diag, hipStream_t st) {
   const int64_t nw = (int64_t)H * ((2 * L - 1 + 63) / 64);
   if (L < 1 || nw == 0) return hipSuccess;
-  if (rev)
-    hipLaunchKernelGGL(agg_diag_kernel<true>, dim3((unsigned)nw), dim3(256), 0, st, pdiag, B, H,
-                       L, nb, nrt, diag);
+  const bool compact = diag_width(L, wl, wr) != L + 256;
+  const dim3 grid((unsigned)nw), blk(compact ? 1024 : 256);
+  if (rev && compact)
+    hipLaunchKernelGGL((agg_diag_kernel<true, true>), grid, blk, 0, st, pdiag, B, H, L, nb, wl, wr, diag);
+  else if (rev)
+    hipLaunchKernelGGL((agg_diag_kernel<true, false>), grid, blk, 0, st, pdiag, B, H, L, nb, wl, wr, diag);
+  else if (compact)
+    hipLaunchKernelGGL((agg_diag_kernel<false, true>), grid, blk, 0, st, pdiag, B, H, L, nb, wl, wr, diag);
   else
-    hipLaunchKernelGGL(agg_diag_kernel<false>, dim3((unsigned)nw), dim3(256), 0, st, pdiag, B, H,
-                       L, nb, nrt, diag);
+    hipLaunchKernelGGL((agg_diag_kernel<false, false>), grid, blk, 0, st, pdiag, B, H, L, nb, wl, wr, diag);
   return hipGetLastError();
 }
 

@@ -178,8 +178,8 @@ int make_plan(const relpos_desc* d, Plan* p) {
   }
   if (p->part_k_stride) p->off_part_k = take(sizeof(float) * own * p->part_k_stride);
   if (lut_path || d->mech == RELPOS_TXL) {
-    // T5 / T-XL: per-offset sums, one partial of nrt floats per wave of each query-side owner
-    p->off_part_qv = take(sizeof(float) * own * p->nrt * 4);
+    // T5 / T-XL: per-offset sums, one partial row per wave of each query-side owner
+    p->off_part_qv = take(sizeof(float) * own * diag_width(L, d->window_left, d->window_right) * 4);
     p->off_diag = take(sizeof(float) * (size_t)p->H * (L > 0 ? 2 * L - 1 : 1));
   }
   if (d->mech == RELPOS_TXL) p->off_part_kv = take(sizeof(float) * own * kHeadDim);
@@ -485,7 +485,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
   if (desc->mech == RELPOS_TXL) {
     // the per-offset sums of the query-side pass, then the key-side pass group by group, each
     // group's r partials folded into dr before the next group reuses them
-    e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, p.nrt, diag, s);
+    e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, desc->window_left, desc->window_right, diag, s);
     const int nbh = p.B * p.H, G = p.txl_group;
     for (int s0 = 0; s0 < nbh && e == hipSuccess; s0 += G) {
       a.bh0 = s0;
@@ -507,7 +507,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
 
   switch (desc->mech) {
     case RELPOS_T5:
-      e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, p.nrt, diag, s);
+      e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, desc->window_left, desc->window_right, diag, s);
       if (e == hipSuccess) e = launch_agg_t5(diag, a.bucket, p.H, p.L, desc->num_buckets, dbias_a, s);
       break;
     case RELPOS_ALIBI:

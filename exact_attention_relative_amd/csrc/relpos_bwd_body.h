@@ -215,9 +215,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int bt_last = bt0 + (nsteps - 1) * BOTH;
 
   // ---- partial layouts ----
-  // lane offsets lam of this workgroup lie in [lam_base, lam_base + nrt)
+  // lane offsets lam of this workgroup lie in [lam_base, lam_base + L + 256)
   const int lam_base = A0 - L - 64;
-  const int nrt = L + 256;
   float* prow = nullptr;     // row-side table partial
   int prow_rows = 0;
   if constexpr (V::DFAT) {
@@ -237,10 +236,11 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int rb = (sh.wl >= 0 && sh.wr >= 0) ? bt0 + 65 : 0;
   // (slots of the r partial count from the launch's first slice)
   if constexpr (V::TK) ptg = a.part_q + (int64_t)bid * a.part_q_stride - (int64_t)rb * kHeadDim;
-  // per-offset dS sums: one partial per wave (its lane offsets lie in [lam_base + 32 w,
-  // lam_base + 32 w + nrt)), in the owner's slot of NWAVE x nrt floats
+  // per-offset dS sums: one partial row of ndg floats per wave (lane offset lam at index
+  // lam - (lam_base + 32 w) - dxo), in the owner's slot of NWAVE rows
+  const int ndg = diag_width(L, sh.wl, sh.wr), dxo = diag_xoff(L, sh.wl, sh.wr, A0);
   float* pdiag = nullptr;
-  if constexpr (V::DIAG) pdiag = a.part_qv + owner * (int64_t)(NWAVE * nrt);
+  if constexpr (V::DIAG) pdiag = a.part_qv + owner * (int64_t)(NWAVE * ndg);
 
   // ---- zero what the sweep will not write ----
   if constexpr (V::DFAT && V::HAS_COL) {
@@ -262,8 +262,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   }
   if constexpr (V::DIAG) {
     // wave ww writes the offsets [A0 + 32 ww - bt_last - 63, A0 + 32 ww - bt0 + 32]
-    for (int e = tid; e < NWAVE * nrt; e += 256) {
-      const int ww = e / nrt, lam = lam_base + 32 * ww + (e - ww * nrt);
+    for (int e = tid; e < NWAVE * ndg; e += 256) {
+      const int ww = e / ndg, lam = lam_base + 32 * ww + dxo + (e - ww * ndg);
       const int lo = A0 + 32 * ww - bt_last - 63, hi = A0 + 32 * ww - bt0 + 32;
       if (!(nsteps > 0 && lam >= lo && lam <= hi)) pdiag[e] = 0.f;
     }
@@ -898,7 +898,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       // partial.
       const float fin = (lane >= 32) ? sums[0] : sums[1] + dcarry;
       dcarry = (lane < 32) ? sums[0] : 0.f;
-      float* pw = pdiag + w * nrt + (aw0 - b0 - 63) - (lam_base + 32 * w);
+      float* pw = pdiag + w * ndg + (aw0 - b0 - 63) - (lam_base + 32 * w) - dxo;
       pw[(lane >= 32) ? lane : 64 + lane] = fin;
       if (step == nsteps - 1 && lane < 32) pw[lane] = dcarry;
     }

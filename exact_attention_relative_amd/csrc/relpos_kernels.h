@@ -16,6 +16,24 @@ constexpr int MECH_ALIBI = 4;
 constexpr int kHeadDim = 64;
 constexpr int kMaxThresholds = 64;
 
+// Per-offset dS partials of the query-side pass (T5, T-XL): one row of diag_width floats per
+// wave of each 128-row block.  A full sweep keeps every offset: wave w of the block at A0 stores
+// offset lam at lam - (A0 + 32 w - L - 64).  With a two-sided window the row keeps only the
+// offsets of the wave's own sweep, counted from its last 64-row tile: the index is lowered by
+// diag_xoff (at most wl + wr + 286 offsets; the compact form is used only when it is smaller).
+__host__ __device__ inline int diag_width(int L, int wl, int wr) {
+  const int64_t full = (int64_t)L + 256;
+  if (wl < 0 || wr < 0) return (int)full;
+  const int64_t w = ((int64_t)wl + wr + 286 + 63) / 64 * 64;
+  return (int)(w < full ? w : full);
+}
+__host__ __device__ inline int diag_xoff(int L, int wl, int wr, int A0) {
+  if (diag_width(L, wl, wr) == L + 256) return 0;
+  int64_t bhi = (int64_t)A0 + 127 + wr;   // last streamed row of the sweep
+  if (bhi > L - 1) bhi = L - 1;
+  return L + 1 - (int)(bhi / 64 * 64);
+}
+
 // T5 bucket map: magnitude n >= max_exact lands in max_exact + #{e : n >= thr[e]}.
 struct T5Map {
   int bidirectional;
@@ -119,8 +137,8 @@ hipError_t launch_index_map(int mech, int L, int span, int nrel, int txl_off, co
 // second-pass aggregation of the backward's offset-sharded partials
 hipError_t launch_agg_rows(const float* part, int64_t stride, int nown, int64_t nelem, float scale,
                            float* out, hipStream_t st);
-hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool rev, int nrt,
-                           float* diag, hipStream_t st);
+hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool rev, int wl,
+                           int wr, float* diag, hipStream_t st);
 // ALiBi dm[h] = -sum over the owners (b, query block) of head h of part[owner] (fixed order)
 hipError_t launch_agg_alibi(const float* part, int B, int H, int nb, float* dm, hipStream_t st);
 hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int nbk, float* dbeta,

@@ -350,6 +350,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   int next = 0;
   while (next < nsteps && step_skipped(next)) ++next;
   TilePrefetch<T> py, py2;
+  TilePrefetch<T> pwn;   // query-side T-XL: the next step's 64 new window rows
+  float pvr = 0.f;       // and their v.r values (threads 0..63)
   if (!V::TG1 && next < nsteps) {
     py.load(yg, step_base(next), L);
     py2.load(y2g, step_base(next), L);
@@ -458,11 +460,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
         }
       } else {
-        stage_window_rows<T, NP>(win, trow, rowfn, 0, xrot);
-        if (tid < BOTH) {
-          const int r = rowfn(tid);
-          *win_vec(win, xrot + tid) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
-        }
+        pwn.store_at(win, WIN * TSTR, xrot);
+        if (tid < BOTH) *win_vec(win, xrot + tid) = pvr;
       }
     } else if constexpr (V::ROW && !V::COL) {
       if (wg_general) stage_window<T, NP>(win, trow, rowfn_at(b0));
@@ -495,6 +494,16 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if (!V::TG1 && next < nsteps) {
       py.load(yg, step_base(next), L);
       py2.load(y2g, step_base(next), L);
+    }
+    if constexpr (V::TQ) {
+      if (step + 1 < nsteps) {
+        const int row0 = (cwin - BOTH) - 63 + toff;   // window rows 0..63 of the next step
+        pwn.load_range(trow, row0, 0, nrel);
+        if (tid < BOTH) {
+          const int r = row0 + tid;
+          pvr = (r >= 0 && r < nrel) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+        }
+      }
     }
     __syncthreads();
 

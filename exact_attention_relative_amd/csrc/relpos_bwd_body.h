@@ -344,11 +344,29 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       }
     }
   };
-  if constexpr (V::FAT && DIR == 1) {
-    if (nsteps > 0) lsd_load(bt0);
-  }
+  float plut = 0.f;   // T5 / ALiBi: this thread's LUT entry of the next step's window
+  auto lut_load = [&](int b0x) {
+    if (tid < WIN) {
+      const int lam = (A0 - b0x) - 63 + tid;
+      const int d = DIR == 0 ? lam : -lam;
+      plut = (d > -L && d < L) ? a.lut[(int64_t)h * (2 * L - 1) + d + L - 1] : 0.f;
+    }
+  };
+  // the next processed step's per-row values are read while the current step computes (not in
+  // the T-XL key-side pass, whose registers are the limit)
+  constexpr bool PF_LSD = DIR == 1 && !V::TK;
+  constexpr bool PF_OV = V::CLIP && V::HAS_COL && !V::DFAT;
+  auto scalars_load = [&](int b0x) {
+    if constexpr (PF_LSD) lsd_load(b0x);
+    if constexpr (PF_OV) ov_load(b0x);
+    if constexpr (V::LUTP) lut_load(b0x);
+  };
+  constexpr bool ANY_PF = PF_LSD || PF_OV || V::LUTP;
   int next = 0;
   while (next < nsteps && step_skipped(next)) ++next;
+  if constexpr (ANY_PF) {
+    if (next < nsteps) scalars_load(step_base(next));
+  }
   TilePrefetch<T> py, py2;
   TilePrefetch<T> pwn;   // query-side T-XL: the next step's 64 new window rows
   float pvr = 0.f;       // and their v.r values (threads 0..63)
@@ -415,27 +433,20 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       py2.store(y2s);
     }
     if constexpr (V::LUTP) {
-      if (lut_needed)
-      for (int x = tid; x < WIN; x += 256) {
-        const int lam = cwin - 63 + x;
-        const int d = DIR == 0 ? lam : -lam;
-        vec_s[x] = (d > -L && d < L) ? a.lut[(int64_t)h * (2 * L - 1) + d + L - 1] : 0.f;
-      }
+      if (lut_needed && tid < WIN) vec_s[tid] = plut;
     }
     if constexpr (MECH == MECH_TXL && DIR == 0) {
       if (tid < BOTH) ovec_s[tid] = (b0 + tid < L) ? a.uk[(int64_t)bh * L + b0 + tid] : 0.f;
     }
     if constexpr (V::CLIP && V::HAS_COL && !V::DFAT) {
       // end A values of the 64 streamed rows, then end B: each a contiguous vector
-      ov_load(b0);
       if (tid < 2 * BOTH) ovec_s[(tid & 1) * BOTH + (tid >> 1)] = pov;
     }
-    if constexpr (DIR == 1 && V::FAT) {
+    if constexpr (PF_LSD) {
       if (tid < BOTH) {
         lsd_s[tid] = pl2;
         lsd_s[BOTH + tid] = pdd;
       }
-      if (step + 1 < nsteps) lsd_load(b0 + BOTH);
     } else if constexpr (DIR == 1) {
       if (tid < BOTH) {
         const int yy = b0 + tid;
@@ -494,6 +505,9 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if (!V::TG1 && next < nsteps) {
       py.load(yg, step_base(next), L);
       py2.load(y2g, step_base(next), L);
+    }
+    if constexpr (ANY_PF) {
+      if (next < nsteps) scalars_load(step_base(next));
     }
     if constexpr (V::TQ) {
       if (step + 1 < nsteps) {

@@ -109,6 +109,17 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   // per tile, into registers one tile ahead
   TilePrefetch<T> pw;
   float pvr = 0.f, puk = 0.f;
+  // T5 / ALiBi: this thread's LUT entry of the next tile's window (window row x = tid)
+  float plut = 0.f;
+  auto lut_load = [&](int j0x) {
+    if (tid < WIN) {
+      const int d = i0 - (j0x + BOTH - 1) + tid;
+      plut = (d > -L && d < L) ? a.lut[(int64_t)h * (2 * L - 1) + d + L - 1] : 0.f;
+    }
+  };
+  if constexpr (LUTP) {
+    if (jt0 <= j_hi) lut_load(jt0);
+  }
   const T* rtab = nullptr;
   if constexpr (MECH == MECH_TXL) rtab = (const T*)a.rel_a + (int64_t)h * sh.nrel * kHeadDim;
 
@@ -149,11 +160,8 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     pv.store(vs);
     if constexpr (LUTP) {
       // (ALiBi reads the slice only on workgroup tiles that straddle the diagonal)
-      if (MECH != MECH_ALIBI || (wg_dlo < 0 && wg_dhi >= 0))
-      for (int x = tid; x < WIN; x += 256) {
-        const int d = wg_dlo + x;   // window row x <-> delta = i0 - j0 - 63 + x
-        vec_s[x] = (d > -L && d < L) ? a.lut[(int64_t)h * (2 * L - 1) + d + L - 1] : 0.f;
-      }
+      if ((MECH != MECH_ALIBI || (wg_dlo < 0 && wg_dhi >= 0)) && tid < WIN) vec_s[tid] = plut;
+      if (j0 + BOTH <= j_hi) lut_load(j0 + BOTH);
     } else if (MECH == MECH_TXL && j0 != jt0) {
       // window rows 0..63 are new: physical rows xrot .. xrot + 63 (the rows that left)
       pw.store_at(win, WIN * TSTR, xrot);

@@ -51,9 +51,9 @@ struct BV {
   static constexpr bool CLIP = MECH == MECH_SHAW || MECH == MECH_DEBERTA;
   static constexpr bool DIAG = DIR == 0 && (MECH == MECH_T5 || MECH == MECH_TXL);
   // General pass of Shaw / DeBERTa: the row-side dX_rel from the wave's dS buffer and the
-  // column-side table gradient over the streamed rows (no E buffer, so two workgroups fit per
-  // CU); a table's interior rows come from the pass where it is the column side, its end rows
-  // from the pass where it is the row side
+  // column-side table gradient over the streamed rows (no workgroup band buffer, so two
+  // workgroups fit per CU); a table's interior rows come from the pass where it is the column
+  // side, its end rows from the pass where it is the row side
   static constexpr bool DFAT = CLIP && PART == 2;
   static constexpr bool TQ = TXL && DIR == 0;         // T-XL query side (circular row window)
   static constexpr bool TK = TXL && DIR == 1;         // T-XL key side (circular column window)
@@ -317,8 +317,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       ovec_s[BOTH + tid] = -am * (float)tid;
     }
   }
-  // per-row values of the streamed rows: end-row constants (light key-side pass) and, in the
-  // key-side general pass, LSE and D read one step ahead
+  // per-row values of the streamed rows (end-row constants of the light key-side passes, LSE
+  // and D of the streamed queries), read one processed step ahead
   float pov = 0.f, pl2 = 0.f, pdd = 0.f;
   auto colfn_at = [&](int b0x) {   // column window row x <-> mu = b - a = (b0 - A0 - 127) + x
     return [=](int x) { return V::col_of((b0x - A0 - (BLANE - 1)) + x, span, nrel, toff); };
@@ -417,10 +417,6 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if constexpr (MECH == MECH_T5) {
       const int lo = clampi(dlo, 1 - L, L - 1), hi = clampi(dhi, 1 - L, L - 1);
       if ((lo >= 0 || hi < 0) && a.bucket[lo + L - 1] == a.bucket[hi + L - 1]) t5cls = 1;
-      // the workgroup needs the E buffer when any of its waves is not single-bucket
-      const int wlo = DIR == 0 ? cwin - 63 : -(cwin + 127), whi = DIR == 0 ? cwin + 127 : -(cwin - 63);
-      const int l2 = clampi(wlo, 1 - L, L - 1), h2 = clampi(whi, 1 - L, L - 1);
-      wg_general = !((l2 >= 0 || h2 < 0) && a.bucket[l2 + L - 1] == a.bucket[h2 + L - 1]);
     }
 
     // ---- stage ----

@@ -117,6 +117,24 @@ def test_txl_partial_cap_groups_slices():
         assert st == 0 and n == full - (6 - group) * per_slice, (cap, group)
 
 
+def test_t5_offset_partials_shrink_under_two_sided_window():
+    """The query-side pass keeps one row of per-offset dS sums per wave (four per 128-row block):
+    L + 256 offsets for a full sweep, or, under a two-sided window, only the wave's own sweep
+    (wl + wr + 286 offsets, in whole 64-float steps) when that is fewer."""
+    B, H, L = 2, 3, 1000
+    owners = B * H * ((L + 127) // 128)
+    st, full = _ws(ear.make_desc("t5", B, H, L), 1)
+    assert st == 0
+    for (wl, wr), rows in (((100, 37), 448), ((0, 0), 320), ((600, 600), L + 256),
+                           ((2000, 2000), L + 256)):
+        st, n = _ws(ear.make_desc("t5", B, H, L, window=(wl, wr)), 1)
+        assert st == 0 and full - n == owners * 4 * (L + 256 - rows) * 4, (wl, wr)
+    # one-sided windows sweep to the sequence end: no compaction
+    for w in ((-1, 0), (50, -1)):
+        st, n = _ws(ear.make_desc("t5", B, H, L, window=w, bidirectional=True), 1)
+        assert st == 0 and n == full, w
+
+
 def test_fwd_rejects_bad_pointers_without_launching():
     lib = ear.load_library()
     desc = ear.make_desc("shaw", 1, 1, 64, rel_span=4)

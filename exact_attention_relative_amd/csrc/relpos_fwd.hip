@@ -120,6 +120,17 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   if constexpr (LUTP) {
     if (jt0 <= j_hi) lut_load(jt0);
   }
+  // DeBERTa: end A / end B constants of the next tile's keys (threads 0..127)
+  float pkc = 0.f;
+  auto kc_load = [&](int j0x) {
+    if (tid < 2 * BOTH) {
+      const int jj = j0x + (tid >> 1);
+      pkc = (jj < L) ? a.keyc[((int64_t)bh * L + jj) * 2 + (tid & 1)] : 0.f;
+    }
+  };
+  if constexpr (MECH == MECH_DEBERTA) {
+    if (jt0 <= j_hi) kc_load(jt0);
+  }
   const T* rtab = nullptr;
   if constexpr (MECH == MECH_TXL) rtab = (const T*)a.rel_a + (int64_t)h * sh.nrel * kHeadDim;
 
@@ -185,15 +196,13 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
       }
     }
     if constexpr (MECH == MECH_DEBERTA) {
-      if (tid < 2 * BOTH) {
-        const int jj = j0 + (tid >> 1);
-        // end A values of the 64 keys, then end B: each a contiguous vector
-        kvec_s[(tid & 1) * BOTH + (tid >> 1)] = (jj < L) ? a.keyc[((int64_t)bh * L + jj) * 2 + (tid & 1)] : 0.f;
-      }
+      // end A values of the 64 keys, then end B: each a contiguous vector
+      if (tid < 2 * BOTH) kvec_s[(tid & 1) * BOTH + (tid >> 1)] = pkc;
     }
     if (j0 + BOTH <= j_hi) {
       pk.load(kg, j0 + BOTH, L);
       pv.load(vg, j0 + BOTH, L);
+      if constexpr (MECH == MECH_DEBERTA) kc_load(j0 + BOTH);
       if constexpr (MECH == MECH_TXL) {
         // next tile's new window rows: offsets wg_dlo - 64 .. wg_dlo - 1
         const int r0 = wg_dlo - BOTH + sh.txl_off;

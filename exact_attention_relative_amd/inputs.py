@@ -18,7 +18,11 @@ Recipe (the pages publish no shapes; the workloads below stand in for their
   * DeBERTa Kr = P W_r^k and Qr = P W_r^q with P [2k, d] ~ N(0, table_std^2) and
     W_r^{k,q} [d, d] ~ N(0, 1/d) (row-vector convention);
   * ALiBi slopes m_h = 2^(-8 (h + 1) / H), the original geometric sequence (no draw;
-    parity variants scale them by 1 + 4 table_std).
+    parity variants scale them by 1 + 4 table_std);
+  * relation-table layout: by default Shaw's w and DeBERTa's Kr, Qr are shared by every head
+    and T-XL has one r per head; rel_layout="per_head" draws one w / P per head (leading head
+    axis; T-XL unchanged) and rel_layout="shared" gives T-XL one r for every head (W_r
+    [512, d]; Shaw and DeBERTa unchanged).
   The projections are input preparation, done in float64 and rounded to the input
   dtype; the attention library takes r, Kr, Qr as given.
 """
@@ -93,7 +97,7 @@ def make_case(mech: str, B: int, H: int, L: int, d: int, *, dtype: str = "bf16",
               window=(-1, -1), seed: int = 0, sub: int | None = None, num_buckets: int = 32,
               max_distance: int = 128, bidirectional: bool | None = None, rel_span: int = 0,
               table_std: float | None = None, bias_std: float = 0.5, with_dout: bool = True,
-              **_ignored) -> dict:
+              rel_layout: str | None = None, **_ignored) -> dict:
     """Draw one workload.  Returns dict(q, k, v, dout, tables, params) of numpy arrays."""
     rng = _rng(seed, sub)
     wl, wr = window
@@ -111,19 +115,24 @@ def make_case(mech: str, B: int, H: int, L: int, d: int, *, dtype: str = "bf16",
     if mech == "t5":
         tables["beta"] = rng.standard_normal((H, num_buckets), dtype=np.float32) * np.float32(bias_std)
     elif mech == "shaw":
-        tables["w"] = _normal(rng, (2 * rel_span + 1, d), tstd, dtype)
+        lead = (H,) if rel_layout == "per_head" else ()
+        tables["w"] = _normal(rng, lead + (2 * rel_span + 1, d), tstd, dtype)
     elif mech == "txl":
         nrel = L if causal else 2 * L - 1
         offsets = np.arange(nrel) if causal else np.arange(-(L - 1), L)
-        w_r = rng.standard_normal((512, H * d), dtype=np.float32) * np.float32(1.0 / math.sqrt(512))
+        hr = 1 if rel_layout == "shared" else H
+        w_r = rng.standard_normal((512, hr * d), dtype=np.float32) * np.float32(1.0 / math.sqrt(512))
         r = (sinusoid(offsets) @ w_r.astype(np.float64)).astype(np.float32)
-        r = r.reshape(nrel, H, d).transpose(1, 0, 2)
+        r = r.reshape(nrel, hr, d).transpose(1, 0, 2)
+        if rel_layout == "shared":
+            r = r[0]
         tables["r"] = np.ascontiguousarray(round_bf16(r) if dtype == "bf16" else r)
         tables["u"] = rng.standard_normal((H, d), dtype=np.float32) * np.float32(tstd)
         tables["v"] = rng.standard_normal((H, d), dtype=np.float32) * np.float32(tstd)
         raw["w_r"] = w_r
     elif mech == "deberta":
-        P = _normal(rng, (2 * rel_span, d), tstd, dtype)
+        lead = (H,) if rel_layout == "per_head" else ()
+        P = _normal(rng, lead + (2 * rel_span, d), tstd, dtype)
         wq = rng.standard_normal((d, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(d))
         wk = rng.standard_normal((d, d), dtype=np.float32) * np.float32(1.0 / math.sqrt(d))
         kr = (P.astype(np.float64) @ wk.astype(np.float64)).astype(np.float32)

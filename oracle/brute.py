@@ -39,6 +39,11 @@ def _clamp(x, lo, hi):
     return lo if x < lo else hi if x > hi else x
 
 
+def _head_rows(tab, h):
+    """Head h's table: tab is a list of rows, or a list of per-head lists of rows."""
+    return tab[h] if isinstance(tab[0][0], list) else tab
+
+
 def score(p, q, k, tables, h, i, j):
     """S_ij for one (batch, head); q, k are lists of rows (lists of floats)."""
     L = len(k)
@@ -54,20 +59,20 @@ def score(p, q, k, tables, h, i, j):
                                                              p.bidirectional)])
     if p.mech == "shaw":
         kk = p.rel_span
-        w = tables["w"][_clamp(j - i, -kk, kk) + kk]
+        w = _head_rows(tables["w"], h)[_clamp(j - i, -kk, kk) + kk]
         return s * _dot(qi, kj) + s * _dot(qi, w)
     if p.mech == "txl":
         u = tables["u"][h]
         v = tables["v"][h]
         row = (i - j) if p.window_right == 0 else (i - j) + (L - 1)
-        r = tables["r"][h][row]
+        r = _head_rows(tables["r"], h)[row]
         qu = [a + c for a, c in zip(qi, u)]
         qv = [a + c for a, c in zip(qi, v)]
         return s * _dot(qu, kj) + s * _dot(qv, r)
     if p.mech == "deberta":
         kk = p.rel_span
-        kr = tables["kr"][_clamp(i - j + kk, 0, 2 * kk - 1)]
-        qr = tables["qr"][_clamp(j - i + kk, 0, 2 * kk - 1)]
+        kr = _head_rows(tables["kr"], h)[_clamp(i - j + kk, 0, 2 * kk - 1)]
+        qr = _head_rows(tables["qr"], h)[_clamp(j - i + kk, 0, 2 * kk - 1)]
         return s * (_dot(qi, kj) + _dot(qi, kr) + _dot(kj, qr))
     if p.mech == "alibi":
         return s * _dot(qi, kj) - float(tables["slopes"][h]) * abs(i - j)

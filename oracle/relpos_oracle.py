@@ -31,6 +31,12 @@ suits (section on engineering trade-offs and where it applies).  Its plainest re
 original linear distance penalty with one slope per head, added like T5's bias; its gradient
 is dm_h = -sum of dS_ij |i - j|.
 
+Which heads share a relation table is not on the pages.  The workloads share Shaw's w and
+DeBERTa's Kr, Qr across heads and give T-XL one r per head; either kind of table may instead
+come with a leading head axis (one table per head) or without it (one table every head
+reads).  The score of head h uses head h's table, and a shared table's gradient is the sum
+over every head that reads it.
+
 Default scale s = 1/sqrt(d), and 1/sqrt(3d) for DeBERTa.  The backward pass is
 written as explicit formulas (no autograd): dV = P^T dO, dP = dO V^T,
 D_i = sum_j P_ij dP_ij, dS = P * (dP - D), and every table gradient is the
@@ -185,6 +191,23 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
+# relation tables and their rank without a head axis; beta, u, v and slopes are always per head
+REL_TABLE_NDIM = {"w": 2, "r": 2, "kr": 2, "qr": 2}
+
+
+def has_head_axis(name: str, table) -> bool:
+    """True when `table` holds one table per head (leading head axis)."""
+    if name in REL_TABLE_NDIM:
+        return np.ndim(table) == REL_TABLE_NDIM[name] + 1
+    return True
+
+
+def head_table(tables: dict, name: str, h: int) -> np.ndarray:
+    """Head h's relation table (the table itself when every head shares it)."""
+    t = _f64(tables[name])
+    return t[h] if has_head_axis(name, t) else t
+
+
 def bias_rows(p: Params, q: np.ndarray, k: np.ndarray, tables: dict, h: int,
               rows: np.ndarray) -> np.ndarray:
     """Materialised additive term B[rows, :] for one (batch, head): q, k are [L, d]."""
@@ -195,11 +218,11 @@ def bias_rows(p: Params, q: np.ndarray, k: np.ndarray, tables: dict, h: int,
         beta = _f64(tables["beta"])[h]
         return beta[idx["bucket"]]
     if p.mech == "shaw":
-        w = _f64(tables["w"])
+        w = head_table(tables, "w", h)
         G = q[rows] @ w.T                                   # [rows, 2k+1]: q_i . w_c
         return s * np.take_along_axis(G, idx["row"], axis=1)
     if p.mech == "txl":
-        r = _f64(tables["r"])[h]
+        r = head_table(tables, "r", h)
         v = _f64(tables["v"])[h]
         u = _f64(tables["u"])[h]
         G = (q[rows] + v) @ r.T                             # [rows, Nrel]: (q_i + v) . r_c
@@ -208,8 +231,8 @@ def bias_rows(p: Params, q: np.ndarray, k: np.ndarray, tables: dict, h: int,
         content_u = s * (k @ u)[None, :]                    # s * u . k_j
         return pos + content_u
     if p.mech == "deberta":
-        kr = _f64(tables["kr"])
-        qr = _f64(tables["qr"])
+        kr = head_table(tables, "kr", h)
+        qr = head_table(tables, "qr", h)
         G1 = q[rows] @ kr.T                                 # [rows, 2k]: q_i . Kr_c
         G2 = k @ qr.T                                       # [L, 2k]:    k_j . Qr_c
         c2p = np.take_along_axis(G1, idx["c2p"], axis=1)
@@ -319,13 +342,13 @@ def backward_head(p: Params, q, k, v, tables: dict, dO, b: int, h: int):
         nb = p.num_buckets
         g["beta"] = np.bincount(idx["bucket"].ravel(), weights=dS.ravel(), minlength=nb)
     elif p.mech == "shaw":
-        w = _f64(tables["w"])
+        w = head_table(tables, "w", h)
         N = _pair_scatter(dS, idx["row"], w.shape[0])
         dq = s * (dS @ kh) + s * (N @ w)
         dk = s * (dS.T @ qh)
         g["w"] = s * (N.T @ qh)
     elif p.mech == "txl":
-        r = _f64(tables["r"])[h]
+        r = head_table(tables, "r", h)
         u = _f64(tables["u"])[h]
         vv = _f64(tables["v"])[h]
         N = _pair_scatter(dS, idx["row"], r.shape[0])
@@ -335,8 +358,8 @@ def backward_head(p: Params, q, k, v, tables: dict, dO, b: int, h: int):
         g["u"] = s * np.sum(dS @ kh, axis=0)
         g["v"] = s * np.sum(N @ r, axis=0)
     elif p.mech == "deberta":
-        kr = _f64(tables["kr"])
-        qr = _f64(tables["qr"])
+        kr = head_table(tables, "kr", h)
+        qr = head_table(tables, "qr", h)
         N1 = _pair_scatter(dS, idx["c2p"], kr.shape[0])
         N2 = _pair_scatter(dS, idx["p2c"], qr.shape[0], by_key=True)
         dq = s * (dS @ kh) + s * (N1 @ kr)
@@ -368,17 +391,27 @@ def dq_rows(p: Params, q, k, v, tables: dict, dO, b: int, h: int, rows):
     idx = index_maps(rows, L, p)
     dq = s * (dS @ kh)
     if p.mech == "shaw":
-        w = _f64(tables["w"])
+        w = head_table(tables, "w", h)
         dq += s * (_pair_scatter(dS, idx["row"], w.shape[0]) @ w)
     elif p.mech == "txl":
-        r = _f64(tables["r"])[h]
+        r = head_table(tables, "r", h)
         dq += s * (_pair_scatter(dS, idx["row"], r.shape[0]) @ r)
     elif p.mech == "deberta":
-        kr = _f64(tables["kr"])
+        kr = head_table(tables, "kr", h)
         dq += s * (_pair_scatter(dS, idx["c2p"], kr.shape[0]) @ kr)
     elif p.mech not in ("t5", "alibi"):
         raise ValueError(p.mech)
     return dq
+
+
+def add_table_grads(grads: dict, g: dict, tables: dict, h: int) -> None:
+    """Add one (batch, head) slice's table gradients g into grads: per-head tables at their
+    head, shared tables summed over heads."""
+    for name, val in g.items():
+        if has_head_axis(name, tables[name]):
+            grads[name][h] += val
+        else:
+            grads[name] += val
 
 
 def backward(p: Params, q, k, v, tables: dict, dO):
@@ -388,15 +421,9 @@ def backward(p: Params, q, k, v, tables: dict, dO):
     dq = np.zeros((B, H, L, d))
     dk = np.zeros((B, H, L, d))
     dv = np.zeros((B, H, L, d))
-    shapes = table_shapes(p, H, L, d)
-    grads = {name: np.zeros(shape) for name, shape in shapes.items()}
+    grads = {name: np.zeros(np.shape(t)) for name, t in tables.items()}
     for b in range(B):
         for h in range(H):
             dq[b, h], dk[b, h], dv[b, h], g = backward_head(p, q, k, v, tables, dO, b, h)
-            for name, val in g.items():
-                per_head = name in ("beta", "r", "u", "v", "slopes")
-                if len(shapes[name]) >= 1 and shapes[name][0] == H and per_head:
-                    grads[name][h] += val
-                else:
-                    grads[name] += val
+            add_table_grads(grads, g, tables, h)
     return dq, dk, dv, grads

@@ -442,3 +442,90 @@ def test_projection_gradients_match_central_differences():
             arr[idx] = old
             assert abs((lp - lm) / (2 * h_) - grad[idx]) < 1e-7
 
+
+
+# ------------------------------------------------------------------------ table sharing across heads
+
+LAYOUTS = [("shaw", "per_head"), ("deberta", "per_head"), ("txl", "shared")]
+
+
+@pytest.mark.parametrize("mech,layout", LAYOUTS)
+@pytest.mark.parametrize("mask", list(MASKS))
+def test_table_layouts_match_scalar_brute_force(mech, layout, mask):
+    """Pin: with one relation table per head (Shaw, DeBERTa) or one table for every head
+    (T-XL), the pure-Python per-pair loops at L = 8 agree with the vectorised oracle to 1e-12."""
+    c = make_case(mech, 1, 3, 8, 4, dtype="fp32", window=MASKS[mask], seed=17, rel_span=3,
+                  bidirectional=(mask != "causal"), table_std=0.7, rel_layout=layout)
+    p = orc.Params(**c["params"])
+    q, k, v, tab, _ = _f64(c)
+    O, LSE = orc.forward(p, q, k, v, tab)
+    tl = {n: t.tolist() for n, t in tab.items()}
+    for h in range(3):
+        Ob, Lb = brute.forward_head(p, q[0, h].tolist(), k[0, h].tolist(), v[0, h].tolist(), tl, h)
+        np.testing.assert_allclose(O[0, h], np.array(Ob), rtol=0, atol=1e-12)
+        np.testing.assert_allclose(LSE[0, h], np.array(Lb), rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("mech,layout", LAYOUTS)
+def test_table_layout_gradients_match_central_differences(mech, layout):
+    """Pin: every gradient element, per-head and shared relation tables included, against
+    central differences of the forward pass in float64, h = 1e-6."""
+    c = make_case(mech, 2, 2, 6, 3, dtype="fp32", window=(-1, -1), seed=19, rel_span=2,
+                  table_std=0.6, rel_layout=layout)
+    p = orc.Params(**c["params"])
+    q, k, v, tab, do = _f64(c)
+    _, _, _, g = orc.backward(p, q, k, v, tab, do)
+    h = 1e-6
+    for name in tab:
+        x = tab[name]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            old = x[idx]
+            x[idx] = old + h
+            lp = _loss(p, q, k, v, tab, do)
+            x[idx] = old - h
+            lm = _loss(p, q, k, v, tab, do)
+            x[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        scale = max(1.0, float(np.max(np.abs(fd))))
+        assert g[name].shape == x.shape
+        assert np.max(np.abs(fd - g[name])) <= 1e-6 * scale, name
+
+
+@pytest.mark.parametrize("mech", ["shaw", "deberta", "txl"])
+def test_per_head_tables_decompose_into_single_head_problems(mech):
+    """Pin: head h of a problem with one table per head is the one-head problem on that head's
+    slices with that head's table; a table shared by every head gives the same outputs as one
+    copy per head, and its gradient is the sum of the per-head copies' gradients."""
+    layout = "shared" if mech == "txl" else "per_head"
+    c = make_case(mech, 2, 3, 24, 8, dtype="fp32", window=(-1, -1), seed=23, rel_span=4,
+                  table_std=0.5, rel_layout=layout)
+    p = orc.Params(**c["params"])
+    q, k, v, tab, do = _f64(c)
+    O, LSE = orc.forward(p, q, k, v, tab)
+    dq, dk, dv, g = orc.backward(p, q, k, v, tab, do)
+    rel = orc.REL_TABLE_NDIM
+    if layout == "per_head":
+        for h in range(3):
+            sub = {n: (t[h] if n in rel else t[h:h + 1]) for n, t in tab.items()}
+            sl = slice(h, h + 1)
+            O1, L1 = orc.forward(p, q[:, sl], k[:, sl], v[:, sl], sub)
+            dq1, dk1, dv1, g1 = orc.backward(p, q[:, sl], k[:, sl], v[:, sl], sub, do[:, sl])
+            assert np.allclose(O1, O[:, sl], rtol=0, atol=1e-13)
+            assert np.allclose(L1, LSE[:, sl], rtol=0, atol=1e-13)
+            for a, b_ in ((dq1, dq[:, sl]), (dk1, dk[:, sl]), (dv1, dv[:, sl])):
+                assert np.allclose(a, b_, rtol=0, atol=1e-13)
+            for n in g1:
+                ref = g[n][h] if n in rel else g[n][h:h + 1]
+                assert np.allclose(g1[n], ref, rtol=0, atol=1e-13), n
+    else:
+        rep = dict(tab)
+        rep["r"] = np.repeat(tab["r"][None], 3, axis=0)
+        O2, L2 = orc.forward(p, q, k, v, rep)
+        dq2, dk2, dv2, g2 = orc.backward(p, q, k, v, rep, do)
+        assert np.allclose(O2, O, rtol=0, atol=1e-13) and np.allclose(L2, LSE, rtol=0, atol=1e-13)
+        for a, b_ in ((dq2, dq), (dk2, dk), (dv2, dv)):
+            assert np.allclose(a, b_, rtol=0, atol=1e-13)
+        assert np.allclose(g2["r"].sum(axis=0), g["r"], rtol=0, atol=1e-12)
+        for n in ("u", "v"):
+            assert np.allclose(g2[n], g[n], rtol=0, atol=1e-13)

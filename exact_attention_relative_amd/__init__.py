@@ -37,7 +37,8 @@ class relpos_desc(ctypes.Structure):
                 ("window_left", ctypes.c_int32), ("window_right", ctypes.c_int32),
                 ("rel_span", ctypes.c_int32), ("num_buckets", ctypes.c_int32),
                 ("max_distance", ctypes.c_int32), ("bidirectional", ctypes.c_int32),
-                ("scale", ctypes.c_float), ("max_partial_bytes", ctypes.c_int64)]
+                ("scale", ctypes.c_float), ("max_partial_bytes", ctypes.c_int64),
+                ("rel_head_stride", ctypes.c_int64)]
 
 
 class relpos_proj_desc(ctypes.Structure):
@@ -93,15 +94,28 @@ def load_library(path: str | None = None):
     return lib
 
 
+def default_rel_head_stride(mech, seqlen, head_dim=64, window=(-1, -1)):
+    """The relation-table layout of the pages' workloads: T-XL one r [Nrel, d] per head, Shaw's w
+    and DeBERTa's Kr / Qr shared by every head (stride 0)."""
+    m = MECH_IDS[mech] if isinstance(mech, str) else int(mech)
+    if m != RELPOS_TXL:
+        return 0
+    nrel = seqlen if window[1] == 0 else max(2 * seqlen - 1, 0)
+    return nrel * head_dim
+
+
 def make_desc(mech, batch, heads, seqlen, head_dim=64, dtype="bf16", window=(-1, -1),
               rel_span=0, num_buckets=32, max_distance=128, bidirectional=True, scale=0.0,
-              max_partial_bytes=0):
+              max_partial_bytes=0, rel_head_stride=None):
+    """Descriptor for the attention calls.  rel_head_stride None = default_rel_head_stride."""
+    if rel_head_stride is None:
+        rel_head_stride = default_rel_head_stride(mech, seqlen, head_dim, window)
     return relpos_desc(MECH_IDS[mech] if isinstance(mech, str) else int(mech),
                        RELPOS_FP32 if dtype in ("fp32", RELPOS_FP32) else RELPOS_BF16,
                        int(batch), int(heads), int(seqlen), int(head_dim),
                        int(window[0]), int(window[1]), int(rel_span), int(num_buckets),
                        int(max_distance), 1 if bidirectional else 0, float(scale),
-                       int(max_partial_bytes))
+                       int(max_partial_bytes), int(rel_head_stride))
 
 
 def make_proj_desc(rows, in_features, heads, head_dim, dtype="bf16"):

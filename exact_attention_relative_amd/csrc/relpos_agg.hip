@@ -6,36 +6,50 @@
 
 namespace relpos {
 
-// Sum of n strided partials with 8 loads in flight: lane j of 8 accumulates owners j, j + 8,
-// ...; the eight sums are then added in a fixed tree.  Deterministic for a given n.
-__device__ __forceinline__ float strided_sum(const float* __restrict__ p, int64_t stride, int n) {
+// Sum of the partials of owners m = 0 .. n - 1 (owner m at p + slot(m) * stride) with 8 loads in
+// flight: running sum j takes the owners m with m % 8 == j; the eight sums are then added in a
+// fixed tree.  Deterministic for a given n.
+template <typename F>
+__device__ __forceinline__ float strided_sum(const float* __restrict__ p, int64_t stride, int n,
+                                             F slot) {
   float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   int o = 0;
   for (; o + 8 <= n; o += 8) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a[j] += p[(int64_t)(o + j) * stride];
+    for (int j = 0; j < 8; ++j) a[j] += p[slot(o + j) * stride];
   }
-  for (int j = 0; o + j < n; ++j) a[j] += p[(int64_t)(o + j) * stride];
+  for (int j = 0; o + j < n; ++j) a[j] += p[slot(o + j) * stride];
   return ((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7]));
 }
 
-// out[e] = scale * sum_{o < nown} part[o * stride + e]: 64 elements per workgroup, the owners
-// split over four thread groups (group g takes owners o = g mod 4, each with eight loads in
-// flight), whose sums are added in a fixed tree: ((g0 + g1) + (g2 + g3)).
+// out[h nelem + e] = scale * sum over the owners of head h of part[slot * stride + e].  The
+// owners of one output form `runs` runs of run_len consecutive slots, run r starting at slot
+// h run_len + r run_stride (one run over every slot when the table is shared).  64 elements per
+// workgroup (blockIdx.y = head); the owners, in ascending order o = 0 .. runs run_len - 1, are
+// split over four thread groups (group g takes o = g mod 4, each with eight loads in flight),
+// whose sums are added in a fixed tree: ((g0 + g1) + (g2 + g3)).
 __global__ __launch_bounds__(256) void agg_rows_kernel(const float* __restrict__ part,
-                                                       int64_t stride, int nown, int64_t nelem,
+                                                       int64_t stride, int runs, int run_len,
+                                                       int64_t run_stride, int64_t nelem,
                                                        float scale, float* __restrict__ out) {
   __shared__ float sh[4][64];
   const int g = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int h = blockIdx.y;
   const int64_t e = (int64_t)blockIdx.x * 64 + l;
+  const int nown = runs * run_len;
   float acc = 0.f;
   if (e < nelem && g < nown) {
     const int n = (nown - g + 3) / 4;   // owners g, g + 4, ...
-    acc = strided_sum(part + (int64_t)g * stride + e, 4 * stride, n);
+    const int64_t base = (int64_t)h * run_len;
+    acc = strided_sum(part + e, stride, n, [=](int m) -> int64_t {
+      const int o = g + 4 * m, r = o / run_len;
+      return base + (int64_t)r * run_stride + (o - r * run_len);
+    });
   }
   sh[g][l] = acc;
   __syncthreads();
-  if (g == 0 && e < nelem) out[e] = ((sh[0][l] + sh[1][l]) + (sh[2][l] + sh[3][l])) * scale;
+  if (g == 0 && e < nelem)
+    out[(int64_t)h * nelem + e] = ((sh[0][l] + sh[1][l]) + (sh[2][l] + sh[3][l])) * scale;
 }
 
 __device__ __forceinline__ int floordiv32(int a) { return a >= 0 ? a / 32 : -((31 - a) / 32); }
@@ -135,12 +149,14 @@ __global__ __launch_bounds__(COMPACT ? 1024 : 256) void agg_diag_kernel(
 // are one contiguous 16 KB block, read whole and added in a fixed owner order.  The slices are
 // processed in groups [s0, s0 + ns) (slot i nb + p for slice s0 + i): the first group starts
 // from zero, later groups from the raw sums already in dr, and the last applies v . diag and s.
+// With `shared`, one table serves every head: a single "head" of workgroups sums the slices of
+// every head, and the last group's diagonal term is sum_h v_h . diag_h (heads in order).
 __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict__ prow,
                                                          const float* __restrict__ diag,
                                                          const float* __restrict__ v, int H,
                                                          int L, int nb, int nrt, int wl, int wr,
                                                          int nrel, int off, float s, int s0,
-                                                         int ns, int first, int last,
+                                                         int ns, int first, int last, int shared,
                                                          float* __restrict__ dr) {
   const int nch = (nrel + 63) / 64;
   const int h = blockIdx.x / nch, row0 = 64 * (blockIdx.x % nch);
@@ -173,9 +189,10 @@ __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict
     if (x0of(m) >= nrt) hi = m; else lo = m + 1;
   }
   const int p_hi = lo;
-  // this head's slices in the group: local i = i0, i0 + H, ...
-  const int i0 = ((h - s0) % H + H) % H;
-  const int nh = i0 < ns ? (ns - i0 + H - 1) / H : 0;
+  // this head's slices in the group: local i = i0, i0 + H, ... (every slice when shared)
+  const int hstep = shared ? 1 : H;
+  const int i0 = shared ? 0 : ((h - s0) % H + H) % H;
+  const int nh = i0 < ns ? (ns - i0 + hstep - 1) / hstep : 0;
   // (slice, owner) pairs in ascending order, four at a time: the 16 loads of a group are in
   // flight together, then added owner by owner (the order of the sum does not change)
   constexpr int G = 4;
@@ -186,7 +203,7 @@ __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict
     for (int u = 0; u < G; ++u) {
       const int q = q0 + u, j = q / no, p = p_lo + (q - j * no);
       const int x0 = x0of(p);
-      const float* base = prow + ((int64_t)(i0 + j * H) * nb + p) * (int64_t)nrt * kHeadDim;
+      const float* base = prow + ((int64_t)(i0 + j * hstep) * nb + p) * (int64_t)nrt * kHeadDim;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int e = 4 * t + 1024 * k, x = x0 + (e >> 6);
@@ -207,10 +224,19 @@ __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict
     if (last) {
       const int delta = row - off;
       o = f32x4{};
-      if (delta > -L && delta < L) {
+      if (delta > -L && delta < L && !shared) {
         const float dg = diag[(int64_t)h * (2 * L - 1) + delta + L - 1];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = fmaf(v[(int64_t)h * kHeadDim + d + i], dg, acc[k][i]) * s;
+      } else if (delta > -L && delta < L) {
+        f32x4 vd = {};
+        for (int hh = 0; hh < H; ++hh) {
+          const float dg = diag[(int64_t)hh * (2 * L - 1) + delta + L - 1];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) vd[i] = fmaf(v[(int64_t)hh * kHeadDim + d + i], dg, vd[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (acc[k][i] + vd[i]) * s;
       }
     }
     *(f32x4*)(dr + ((int64_t)h * nrel + row) * kHeadDim + d) = o;
@@ -246,8 +272,9 @@ __global__ void agg_t5_kernel(const float* __restrict__ diag, const int* __restr
 // T-XL dv[h][d] = s sum_delta diag_h[delta] r_h[row(delta)][d]
 template <typename T>
 __global__ __launch_bounds__(1024) void agg_txl_dv_kernel(const float* __restrict__ diag,
-                                                          const T* __restrict__ r, int L, int nrel,
-                                                          int off, float s, float* __restrict__ dv) {
+                                                          const T* __restrict__ r, int64_t r_hs,
+                                                          int L, int nrel, int off, float s,
+                                                          float* __restrict__ dv) {
   // one workgroup per (head, 8 columns): thread t takes the offsets t, t + 1024, ..., reading 8
   // consecutive columns of each table row; then a fixed-order tree over the 1024 threads
   __shared__ float sh[8][1024];
@@ -259,7 +286,7 @@ __global__ __launch_bounds__(1024) void agg_txl_dv_kernel(const float* __restric
     const int row = x - (L - 1) + off;
     if (row >= 0 && row < nrel) {
       float rv[8];
-      load8(r + ((int64_t)h * nrel + row) * kHeadDim + d0, rv);
+      load8(r + (int64_t)h * r_hs + (int64_t)row * kHeadDim + d0, rv);
       const float dg = diag[(int64_t)h * n + x];
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[i] = fmaf(dg, rv[i], acc[i]);
@@ -316,8 +343,16 @@ static inline int nblk(int64_t n, int t) { return (int)((n + t - 1) / t); }
 hipError_t launch_agg_rows(const float* part, int64_t stride, int nown, int64_t nelem, float scale,
                            float* out, hipStream_t st) {
   if (nelem == 0) return hipSuccess;
-  hipLaunchKernelGGL(agg_rows_kernel, dim3(nblk(nelem, 64)), dim3(256), 0, st, part, stride, nown,
-                     nelem, scale, out);
+  hipLaunchKernelGGL(agg_rows_kernel, dim3(nblk(nelem, 64)), dim3(256), 0, st, part, stride, 1,
+                     nown, (int64_t)0, nelem, scale, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_agg_rows_by_head(const float* part, int64_t stride, int B, int H, int nb,
+                                   int64_t nelem, float scale, float* out, hipStream_t st) {
+  if (nelem == 0 || H == 0) return hipSuccess;
+  hipLaunchKernelGGL(agg_rows_kernel, dim3(nblk(nelem, 64), H), dim3(256), 0, st, part, stride, B,
+                     nb, (int64_t)H * nb, nelem, scale, out);
   return hipGetLastError();
 }
 
@@ -351,22 +386,23 @@ hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int
 
 hipError_t launch_agg_txl_dr(const float* prow, const float* diag, const float* v, int H, int L,
                              int nb, int nrk, int wl, int wr, int nrel, int off, float s, int s0,
-                             int ns, bool first, bool last, float* dr, hipStream_t st) {
+                             int ns, bool first, bool last, bool shared, float* dr, hipStream_t st) {
   const int nch = (nrel + 63) / 64;
-  hipLaunchKernelGGL(agg_txl_dr_kernel, dim3(H * nch), dim3(256), 0, st, prow, diag, v, H, L, nb,
-                     nrk, wl, wr, nrel, off, s, s0, ns, first ? 1 : 0, last ? 1 : 0, dr);
+  hipLaunchKernelGGL(agg_txl_dr_kernel, dim3((shared ? 1 : H) * nch), dim3(256), 0, st, prow, diag,
+                     v, H, L, nb, nrk, wl, wr, nrel, off, s, s0, ns, first ? 1 : 0, last ? 1 : 0,
+                     shared ? 1 : 0, dr);
   return hipGetLastError();
 }
 
-hipError_t launch_agg_txl_uv(const float* pkv, const float* diag, const void* r, int B, int H,
-                             int L, int nb, int nrel, int off, float s, bool fp32, float* du,
-                             float* dv, hipStream_t st) {
+hipError_t launch_agg_txl_uv(const float* pkv, const float* diag, const void* r, int64_t r_hs,
+                             int B, int H, int L, int nb, int nrel, int off, float s, bool fp32,
+                             float* du, float* dv, hipStream_t st) {
   if (fp32)
     hipLaunchKernelGGL((agg_txl_dv_kernel<float>), dim3(H * 8), dim3(1024), 0, st, diag,
-                       (const float*)r, L, nrel, off, s, dv);
+                       (const float*)r, r_hs, L, nrel, off, s, dv);
   else
     hipLaunchKernelGGL((agg_txl_dv_kernel<uint16_t>), dim3(H * 8), dim3(1024), 0, st, diag,
-                       (const uint16_t*)r, L, nrel, off, s, dv);
+                       (const uint16_t*)r, r_hs, L, nrel, off, s, dv);
   hipLaunchKernelGGL(agg_txl_du_kernel, dim3(H), dim3(256), 0, st, pkv, B, H, nb, s, du);
   return hipGetLastError();
 }

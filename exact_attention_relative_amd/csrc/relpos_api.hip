@@ -87,6 +87,8 @@ struct Plan {
   int64_t part_q_stride, part_k_stride;
   int nb, nrt, owners;
   int txl_group;   // T-XL key-side pass: (batch, head) slices per group
+  int64_t rel_rows;   // rows of each relation table (0 for T5 / ALiBi)
+  int64_t rel_hs;     // elements between the relation tables of consecutive heads (0 = shared)
   size_t fwd_bytes, bwd_bytes;
 };
 
@@ -126,7 +128,26 @@ int make_plan(const relpos_desc* d, Plan* p) {
       break;
   }
   p->nrel = (d->window_right == 0) ? L : 2 * L - 1;
+  if (p->nrel < 0) p->nrel = 0;
   p->txl_off = (d->window_right == 0) ? 0 : L - 1;
+  // relation tables: rows per table, and one table per head or one shared by every head
+  if (d->rel_head_stride < 0) return RELPOS_E_INVALID;
+  switch (d->mech) {
+    case RELPOS_SHAW: p->rel_rows = 2 * (int64_t)d->rel_span + 1; break;
+    case RELPOS_DEBERTA: p->rel_rows = 2 * (int64_t)d->rel_span; break;
+    case RELPOS_TXL: p->rel_rows = p->nrel; break;
+    default: p->rel_rows = 0; break;
+  }
+  p->rel_hs = p->rel_rows > 0 ? d->rel_head_stride : 0;
+  if (p->rel_hs != 0 && (p->rel_hs < p->rel_rows * kHeadDim || p->rel_hs % 8 != 0))
+    return RELPOS_E_INVALID;
+  // the kernels address rows inside one (batch, head) slice and inside one head's table with
+  // 32-bit byte offsets
+  {
+    const int64_t esz = p->fp32 ? 4 : 2;
+    const int64_t rows_max = std::max<int64_t>(L, p->rel_rows);
+    if (rows_max * kHeadDim * esz >= ((int64_t)1 << 32)) return RELPOS_E_UNSUPPORTED;
+  }
   if (d->scale > 0.f) p->scale = d->scale;
   else p->scale = (float)(1.0 / sqrt((d->mech == RELPOS_DEBERTA ? 3.0 : 1.0) * (double)d->head_dim));
 
@@ -217,20 +238,24 @@ hipError_t run_prep(const relpos_desc* d, const Plan& p, const void* q, const vo
     e = launch_alibi_lut(bias_a, p.H, L, 1.0f / p.scale, (float*)(ws + p.off_lut), st);
   } else if (d->mech == RELPOS_SHAW) {
     // end A (j - i >= k) reads w[2k], end B (j - i <= -k) reads w[0]
-    RowDotArgs r{q, rows, L, p.H, rel_a, 0, 2 * d->rel_span, 0, 2, (float*)(ws + p.off_rowc)};
+    RowDotArgs r{q, rows, L, p.H, rel_a, p.rel_hs, 2 * d->rel_span, 0, 2,
+                 (float*)(ws + p.off_rowc), -1};
     e = launch_rowdot(r, p.fp32, p.fp32, st);
   } else if (d->mech == RELPOS_DEBERTA) {
-    RowDotArgs r{q, rows, L, p.H, rel_a, 0, 0, 2 * d->rel_span - 1, 2, (float*)(ws + p.off_rowc)};
+    RowDotArgs r{q, rows, L, p.H, rel_a, p.rel_hs, 0, 2 * d->rel_span - 1, 2,
+                 (float*)(ws + p.off_rowc), -1};
     e = launch_rowdot(r, p.fp32, p.fp32, st);
     if (e != hipSuccess) return e;
-    RowDotArgs r2{k, rows, L, p.H, rel_b, 0, 0, 2 * d->rel_span - 1, 2, (float*)(ws + p.off_keyc)};
+    RowDotArgs r2{k, rows, L, p.H, rel_b, p.rel_hs, 0, 2 * d->rel_span - 1, 2,
+                  (float*)(ws + p.off_keyc), -1};
     e = launch_rowdot(r2, p.fp32, p.fp32, st);
   } else if (d->mech == RELPOS_TXL) {
-    RowDotArgs r{k, rows, L, p.H, bias_a, kHeadDim, 0, 0, 1, (float*)(ws + p.off_uk)};
+    RowDotArgs r{k, rows, L, p.H, bias_a, kHeadDim, 0, 0, 1, (float*)(ws + p.off_uk), -1};
     e = launch_rowdot(r, p.fp32, true, st);
     if (e != hipSuccess) return e;
+    // v_h . r_h[row] for every head and row (r_h = r + h rel_hs; the same table when shared)
     RowDotArgs r2{rel_a, (int64_t)p.H * p.nrel, p.nrel, p.H, bias_b, kHeadDim, 0, 0, 1,
-                  (float*)(ws + p.off_vr)};
+                  (float*)(ws + p.off_vr), p.rel_hs};
     e = launch_rowdot(r2, p.fp32, true, st);
   }
   return e;
@@ -248,6 +273,7 @@ AttnShape make_shape(const relpos_desc* d, const Plan& p) {
   s.nrel = p.nrel;
   s.txl_off = p.txl_off;
   s.scale = p.scale;
+  s.rel_hs = p.rel_hs;
   return s;
 }
 
@@ -269,9 +295,10 @@ int check_tables(const relpos_desc* d, const void* rel_a, const void* rel_b, con
   return RELPOS_OK;
 }
 
-// profiling hook (see relpos_profile_events)
-hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
-int g_prof_kernel = RELPOS_PROF_OFF;
+// profiling hook (see relpos_profile_events): per host thread, so that calls made from other
+// threads never record the caller's events
+thread_local hipEvent_t g_prof_start = nullptr, g_prof_stop = nullptr;
+thread_local int g_prof_kernel = RELPOS_PROF_OFF;
 
 template <typename F>
 hipError_t timed(int which, hipStream_t st, F launch) {
@@ -330,7 +357,7 @@ int relpos_profile_events(void* start_event, void* stop_event, int kernel) {
   return RELPOS_OK;
 }
 
-int relpos_version(void) { return 101; }
+int relpos_version(void) { return 200; }
 
 const char* relpos_status_string(int status) {
   switch (status) {
@@ -418,21 +445,20 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
     return RELPOS_E_INVALID;
   for (const void* ptr : {(const void*)drel_a, (const void*)drel_b, (const void*)dbias_a, (const void*)dbias_b})
     if (ptr && !aligned16(ptr)) return RELPOS_E_INVALID;
-  if (p.fp32) return RELPOS_E_UNSUPPORTED;
   hipStream_t s = (hipStream_t)stream;
-  if (p.L == 0) return RELPOS_OK;
-  if (p.B == 0) {
-    // no pairs: every table gradient is zero
+  if (p.B == 0 || p.L == 0) {
+    // no pairs: every table gradient is zero (nrel is clamped at 0 when L = 0)
     size_t n_a = 0, n_b = 0, n_ba = 0, n_bb = 0;
-    const size_t H = (size_t)p.H, L = (size_t)p.L, k2 = 2 * (size_t)desc->rel_span;
+    const size_t H = (size_t)p.H;
+    const size_t tabs = p.rel_hs ? H : 1;   // per-head relation tables or one shared table
+    const size_t rel = tabs * (size_t)p.rel_rows * kHeadDim;
     switch (desc->mech) {
       case RELPOS_T5: n_ba = H * desc->num_buckets; break;
       case RELPOS_ALIBI: n_ba = H; break;
-      case RELPOS_SHAW: n_a = (k2 + 1) * kHeadDim; break;
-      case RELPOS_TXL: n_a = H * p.nrel * kHeadDim; n_ba = n_bb = H * kHeadDim; break;
-      case RELPOS_DEBERTA: n_a = n_b = k2 * kHeadDim; break;
+      case RELPOS_SHAW: n_a = rel; break;
+      case RELPOS_TXL: n_a = rel; n_ba = n_bb = H * kHeadDim; break;
+      case RELPOS_DEBERTA: n_a = n_b = rel; break;
     }
-    (void)L;
     hipError_t e = hipSuccess;
     if (n_a) e = launch_agg_rows(nullptr, 0, 0, (int64_t)n_a, 0.f, drel_a, s);
     if (e == hipSuccess && n_b) e = launch_agg_rows(nullptr, 0, 0, (int64_t)n_b, 0.f, drel_b, s);
@@ -495,11 +521,11 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
         e = launch_agg_txl_dr(a.part_q, diag, bias_b, p.H, p.L, p.nb,
                               (int)(p.part_q_stride / kHeadDim), desc->window_left,
                               desc->window_right, p.nrel, p.txl_off, p.scale, s0, a.nbh, s0 == 0,
-                              s0 + G >= nbh, drel_a, s);
+                              s0 + G >= nbh, p.rel_hs == 0, drel_a, s);
     }
     if (e == hipSuccess)
-      e = launch_agg_txl_uv(a.part_kv, diag, rel_a, p.B, p.H, p.L, p.nb, p.nrel, p.txl_off,
-                            p.scale, p.fp32, dbias_a, dbias_b, s);
+      e = launch_agg_txl_uv(a.part_kv, diag, rel_a, p.rel_hs, p.B, p.H, p.L, p.nb, p.nrel,
+                            p.txl_off, p.scale, p.fp32, dbias_a, dbias_b, s);
     return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
   }
   e = timed(RELPOS_PROF_BWD_DKDV, s, [&] { return launch_bwd_dkdv(a, p.fp32, s); });
@@ -514,13 +540,17 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
       e = launch_agg_alibi(a.part_qv, p.B, p.H, p.nb, dbias_a, s);
       break;
     case RELPOS_SHAW:
-      e = launch_agg_rows(a.part_q, p.part_q_stride, p.owners, p.part_q_stride, p.scale, drel_a, s);
+    case RELPOS_DEBERTA: {
+      // one shared table sums every owner; per-head tables sum the owners of their head
+      auto agg = [&](const float* part, int64_t stride, float* out) {
+        return p.rel_hs == 0
+                   ? launch_agg_rows(part, stride, p.owners, stride, p.scale, out, s)
+                   : launch_agg_rows_by_head(part, stride, p.B, p.H, p.nb, stride, p.scale, out, s);
+      };
+      e = agg(a.part_q, p.part_q_stride, drel_a);
+      if (e == hipSuccess && desc->mech == RELPOS_DEBERTA) e = agg(a.part_k, p.part_k_stride, drel_b);
       break;
-    case RELPOS_DEBERTA:
-      e = launch_agg_rows(a.part_q, p.part_q_stride, p.owners, p.part_q_stride, p.scale, drel_a, s);
-      if (e == hipSuccess)
-        e = launch_agg_rows(a.part_k, p.part_k_stride, p.owners, p.part_k_stride, p.scale, drel_b, s);
-      break;
+    }
     default:
       break;
   }

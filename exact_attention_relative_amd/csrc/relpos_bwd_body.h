@@ -32,7 +32,6 @@
 namespace relpos {
 
 constexpr int ESTRT = 200;    // bf16 E2T row stride (elements): 192 window offsets + pad
-static_assert(BOTH * ESTRT * 2 <= NWAVE * WROWS * GS2 * 4, "E2T fits the column-skew buffer");
 
 // PART 0: the whole sweep.  PART 1 (light): only the steps whose workgroup tile is clipped
 // (every offset beyond the span), without any relation-product machinery, writing fp32 partial
@@ -80,36 +79,50 @@ struct BV {
 };
 
 // Zero the slots of an op_rows_tr operand (row t; slot j < 4 is column ybase + 4 kh + j, slot
-// 4 + j column ybase + 8 + 4 kh + j) outside the band y <= t <= y + 127.
-__device__ __forceinline__ void band_mask(Op<1>& o, int t, int ybase) {
+// 4 + j column ybase + 8 + 4 kh + j) outside the band y <= t <= y + 127, in every plane.
+template <int NP>
+__device__ __forceinline__ void band_mask(Op<NP>& o, int t, int ybase) {
   // recomputed where used: hoisted out of the step loop, the masks would hold registers
   asm volatile("" : "+v"(t));
   const int kh = __lane_id() >> 5;
-  u32x4 v = __builtin_bit_cast(u32x4, o.p[0]);
+  uint32_t m[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int s0 = 2 * i, s1 = 2 * i + 1;
     const int y0 = ybase + (s0 < 4 ? 4 * kh + s0 : 8 + 4 * kh + s0 - 4);
     const int y1 = ybase + (s1 < 4 ? 4 * kh + s1 : 8 + 4 * kh + s1 - 4);
-    const uint32_t m = ((unsigned)(t - y0) <= 127u ? 0x0000FFFFu : 0u) |
-                       ((unsigned)(t - y1) <= 127u ? 0xFFFF0000u : 0u);
-    v[i] &= m;
+    m[i] = ((unsigned)(t - y0) <= 127u ? 0x0000FFFFu : 0u) |
+           ((unsigned)(t - y1) <= 127u ? 0xFFFF0000u : 0u);
   }
-  o.p[0] = u4_to_bf8(v);
+#pragma unroll
+  for (int pl = 0; pl < NP; ++pl) {
+    u32x4 v = __builtin_bit_cast(u32x4, o.p[pl]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] &= m[i];
+    o.p[pl] = u4_to_bf8(v);
+  }
 }
 
 // ----------------------------------------------------------------------------- kernel
-template <int MECH, int DIR, int PART>
+// T is the element type of the inputs (uint16_t = bf16 bits, or float); fp32 operands enter the
+// matrix cores as NP = 2 bf16 planes (hi, lo), with every LDS tile holding both planes.
+template <typename T, int MECH, int DIR, int PART>
 __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   using V = BV<MECH, DIR, PART>;
-  typedef uint16_t T;
-  constexpr int NP = 1;
-  __shared__ __attribute__((aligned(16))) uint16_t ys[BOTH * TSTR];     // K (dir 0) / Q (dir 1)
-  __shared__ __attribute__((aligned(16))) uint16_t y2s[BOTH * TSTR];    // V (dir 0) / dO (dir 1)
-  __shared__ __attribute__((aligned(16))) uint16_t win[V::WINB ? WIN * TSTR : 8];
+  constexpr int NP = Elem<T>::NP;
+  __shared__ __attribute__((aligned(16))) uint16_t ys[NP * BOTH * TSTR];    // K (dir 0) / Q (dir 1)
+  __shared__ __attribute__((aligned(16))) uint16_t y2s[NP * BOTH * TSTR];   // V (dir 0) / dO (dir 1)
+  __shared__ __attribute__((aligned(16))) uint16_t win[V::WINB ? NP * WIN * TSTR : 8];
   // the skewed reads of the dX_rel operand reach up to 32 floats beyond a wave's buffer
   constexpr int GSG = V::GSREL ? 32 : 0;
-  __shared__ __attribute__((aligned(16))) float gsb_raw[V::GSB ? NWAVE * WROWS * GS2 + 2 * GSG : 4];
+  // the buffer also holds the E2T band (NP planes of BOTH x ESTRT bf16) when there is a table
+  // GEMM, and the end-row staging (2 BLANE sums and BLANE lane rows) of the general passes
+  constexpr int GS_SKEW = V::GSB ? NWAVE * WROWS * GS2 + 2 * GSG : 4;
+  constexpr int GS_E2T = V::TG1 ? NP * BOTH * ESTRT / 2 + GSG : 0;
+  constexpr int GS_END = (V::DFAT && V::ROW) ? 2 * BLANE + NP * BLANE * TSTR / 2 + GSG : 0;
+  constexpr int GS_ALL = GS_SKEW > GS_E2T ? (GS_SKEW > GS_END ? GS_SKEW : GS_END)
+                                          : (GS_E2T > GS_END ? GS_E2T : GS_END);
+  __shared__ __attribute__((aligned(16))) float gsb_raw[GS_ALL];
   __shared__ __attribute__((aligned(16))) float vec_s[V::LUTP ? WIN : 4];  // bias LUT slice
   // T-XL u.k / clipped end-row constants / ALiBi ramps +m y / s and -m y / s
   constexpr int NOVEC = (MECH == MECH_TXL && DIR == 0)
@@ -142,12 +155,11 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const T* x2g = (const T*)(DIR == 0 ? a.dout : a.v) + bh_off;
   const T* yg = (const T*)(DIR == 0 ? a.k : a.q) + bh_off;
   const T* y2g = (const T*)(DIR == 0 ? a.v : a.dout) + bh_off;
+  // this head's tables (rel_hs = 0: one table shared by every head)
   const T* trow = (const T*)(DIR == 0 ? a.rel_a : a.rel_b);   // row-side table
   const T* tcol = (const T*)(DIR == 0 ? a.rel_b : a.rel_a);   // column-side table
-  if constexpr (MECH == MECH_TXL) {
-    if (DIR == 0) trow += (int64_t)h * nrel * kHeadDim;
-    else tcol += (int64_t)h * nrel * kHeadDim;
-  }
+  if (trow) trow += h * sh.rel_hs;
+  if (tcol) tcol += h * sh.rel_hs;
   const float* rc_g = DIR == 0 ? a.rowc : a.keyc;   // lane rows . row table ends (A, B)
   const float* oc_g = DIR == 0 ? a.keyc : a.rowc;   // other rows . column table ends (A, B)
 
@@ -774,26 +786,31 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if constexpr (V::TG1) {
       // E2T[y][t] = dS[y][x] with t = y - x + 127, in the column-skew buffer's space: for one
       // register, the 32 lanes of a half-wave write 32 consecutive t
-      uint16_t* e2t = (uint16_t*)gsb;
+      uint16_t* e2t = (uint16_t*)gsb;   // NP planes of [BOTH][ESTRT]
       if (wave_none) {   // a wave with no pairs contributes zeros (wave-uniform)
         const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) dso[cc].p[0] = u4_to_bf8(z);
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+          for (int pl = 0; pl < NP; ++pl) dso[cc].p[pl] = u4_to_bf8(z);
       }
       __syncthreads();   // every wave's column-skew reads are done
       uint16_t* eb = e2t + (127 - (WROWS * w + l32) + 4 * kh) + 4 * kh * ESTRT;
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
-        // operand slot i of dso[cc] is register 8 (cc % 2) + i of block cc / 2
-        const u32x4 wv = __builtin_bit_cast(u32x4, dso[cc].p[0]);
+      for (int pl = 0; pl < NP; ++pl)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int r = 8 * (cc & 1) + i;
-          const int yc = 32 * (cc >> 1) + 8 * (r >> 2) + (r & 3);   // y - 4 kh
-          const uint32_t word = wv[i >> 1];
-          eb[yc * (ESTRT + 1)] = (uint16_t)((i & 1) ? (word >> 16) : (word & 0xFFFFu));
+        for (int cc = 0; cc < 4; ++cc) {
+          // operand slot i of dso[cc] is register 8 (cc % 2) + i of block cc / 2
+          const u32x4 wv = __builtin_bit_cast(u32x4, dso[cc].p[pl]);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int r = 8 * (cc & 1) + i;
+            const int yc = 32 * (cc >> 1) + 8 * (r >> 2) + (r & 3);   // y - 4 kh
+            const uint32_t word = wv[i >> 1];
+            eb[pl * BOTH * ESTRT + yc * (ESTRT + 1)] =
+                (uint16_t)((i & 1) ? (word >> 16) : (word & 0xFFFFu));
+          }
         }
-      }
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < 3; ++i) {
@@ -803,8 +820,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         for (int cq = 0; cq < 4; ++cq) {
           const int ylo = 16 * cq, yhi = ylo + 15;
           if (thi < ylo || tlo > yhi + 127) continue;   // no pair of this block and chunk
-          Op<NP> eop = op_rows_tr<NP>(e2t, 0, ESTRT, ylo, tlo);
-          if (!(tlo >= yhi && thi <= ylo + 127)) band_mask(eop, tlo + l32, ylo);
+          Op<NP> eop = op_rows_tr<NP>(e2t, BOTH * ESTRT, ESTRT, ylo, tlo);
+          if (!(tlo >= yhi && thi <= ylo + 127)) band_mask<NP>(eop, tlo + l32, ylo);
           Op<NP> qop2 = op_rows_tr<NP>(ys, BOTH * TSTR, TSTR, ylo, 32 * gdb);
           mma<NP>(racc[i], eop, qop2);
         }
@@ -1015,10 +1032,11 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     // end rows of the row-side table: sum over the lane rows of (cA + lA) X, with the lane rows
     // and the sums staged in the (now free) dS buffers
     float* ends = gsb;                                   // [2][BLANE]
-    uint16_t* xst = (uint16_t*)(gsb + 2 * BLANE);        // lane rows X, [BLANE][TSTR]
+    // lane rows X: two 64-row tiles of NP planes each, [2][NP][BOTH][TSTR]
+    uint16_t* xst = (uint16_t*)(gsb + 2 * BLANE);
     __syncthreads();
     stage64<T, NP>(xst, xg, A0, L);
-    stage64<T, NP>(xst + BOTH * TSTR, xg, A0 + BOTH, L);
+    stage64<T, NP>(xst + NP * BOTH * TSTR, xg, A0 + BOTH, L);
     if (kh == 0) {
       ends[WROWS * w + l32] = (my_a < L) ? cA + lA : 0.f;
       ends[BLANE + WROWS * w + l32] = (my_a < L) ? cB + lB : 0.f;
@@ -1027,7 +1045,12 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if (tid < 2 * kHeadDim) {
       const int e = tid / kHeadDim, d = tid % kHeadDim;
       float acc = 0.f;
-      for (int x = 0; x < BLANE; ++x) acc = fmaf(ends[e * BLANE + x], bf_bits2f(xst[x * TSTR + d]), acc);
+      for (int x = 0; x < BLANE; ++x) {
+        const uint16_t* xr = xst + (x >> 6) * NP * BOTH * TSTR + (x & 63) * TSTR + d;
+        float xv = bf_bits2f(xr[0]);
+        if constexpr (NP == 2) xv += bf_bits2f(xr[BOTH * TSTR]);   // hi + lo: the fp32 value
+        acc = fmaf(ends[e * BLANE + x], xv, acc);
+      }
       const int row = e == 0 ? V::rowA(span) : V::rowB(span);
       prow[(int64_t)row * kHeadDim + d] = acc;
     }
@@ -1037,8 +1060,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int d = 32 * db + 8 * (r >> 2) + 4 * kh + (r & 3);
-        const float ta = bf_bits2f(trow[(int64_t)V::rowA(span) * kHeadDim + d]);
-        const float tb = bf_bits2f(trow[(int64_t)V::rowB(span) * kHeadDim + d]);
+        const float ta = Elem<T>::to_f(trow[(int64_t)V::rowA(span) * kHeadDim + d]);
+        const float tb = Elem<T>::to_f(trow[(int64_t)V::rowB(span) * kHeadDim + d]);
         gacc[db][r] = fmaf(lA, ta, fmaf(lB, tb, gacc[db][r]));
       }
   }
@@ -1061,7 +1084,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if (tid < kHeadDim) {
       float acc = 0.f;
       for (int x = 0; x < BLANE && A0 + x < L; ++x)
-        acc = fmaf(csum[x], bf_bits2f(xg[(int64_t)(A0 + x) * kHeadDim + tid]), acc);
+        acc = fmaf(csum[x], Elem<T>::to_f(xg[(int64_t)(A0 + x) * kHeadDim + tid]), acc);
       a.part_kv[owner * kHeadDim + tid] = acc;
     }
   }
@@ -1075,22 +1098,33 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d = 32 * db + 8 * g + 4 * kh;
-        u32x2 pk = {pack_bf16x2(gacc[db][4 * g] * s, gacc[db][4 * g + 1] * s),
-                    pack_bf16x2(gacc[db][4 * g + 2] * s, gacc[db][4 * g + 3] * s)};
-        *(u32x2*)(gx + d) = pk;
-        if constexpr (DIR == 1) {
-          u32x2 pv = {pack_bf16x2(vacc[db][4 * g], vacc[db][4 * g + 1]),
-                      pack_bf16x2(vacc[db][4 * g + 2], vacc[db][4 * g + 3])};
-          *(u32x2*)(gv + d) = pv;
+        if constexpr (NP == 1) {
+          u32x2 pk = {pack_bf16x2(gacc[db][4 * g] * s, gacc[db][4 * g + 1] * s),
+                      pack_bf16x2(gacc[db][4 * g + 2] * s, gacc[db][4 * g + 3] * s)};
+          *(u32x2*)(gx + d) = pk;
+          if constexpr (DIR == 1) {
+            u32x2 pv = {pack_bf16x2(vacc[db][4 * g], vacc[db][4 * g + 1]),
+                        pack_bf16x2(vacc[db][4 * g + 2], vacc[db][4 * g + 3])};
+            *(u32x2*)(gv + d) = pv;
+          }
+        } else {
+          f32x4 v4 = {gacc[db][4 * g] * s, gacc[db][4 * g + 1] * s, gacc[db][4 * g + 2] * s,
+                      gacc[db][4 * g + 3] * s};
+          *(f32x4*)(gx + d) = v4;
+          if constexpr (DIR == 1) {
+            f32x4 w4 = {vacc[db][4 * g], vacc[db][4 * g + 1], vacc[db][4 * g + 2], vacc[db][4 * g + 3]};
+            *(f32x4*)(gv + d) = w4;
+          }
         }
       }
   }
 }
 
-// Every variant fits two workgroups per CU (LDS at most 80 KiB) and is compiled for two waves
-// per SIMD (at most 256 registers per lane).
-template <int MECH, int DIR, int PART>
-__global__ __launch_bounds__(256, 2) void bwd_kernel(BwdArgs a) {
-  bwd_body<MECH, DIR, PART>(a);
+// Every bf16 variant fits two workgroups per CU (LDS at most 80 KiB) and is compiled for two
+// waves per SIMD (at most 256 registers per lane).  The fp32 variants hold two bf16 planes of
+// every tile (at most 144 KiB of LDS) and run one workgroup per CU.
+template <typename T, int MECH, int DIR, int PART>
+__global__ __launch_bounds__(256, Elem<T>::NP == 1 ? 2 : 1) void bwd_kernel(BwdArgs a) {
+  bwd_body<T, MECH, DIR, PART>(a);
 }
 }  // namespace relpos

@@ -8,9 +8,9 @@ namespace relpos {
 
 void launch_bwd_fat_q(int mech, const BwdArgs& a, dim3 grid, hipStream_t stream) {
   if (mech == MECH_SHAW)
-    hipLaunchKernelGGL((bwd_kernel<MECH_SHAW, 0, 2>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_kernel<uint16_t, MECH_SHAW, 0, 2>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((bwd_kernel<MECH_DEBERTA, 0, 2>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((bwd_kernel<uint16_t, MECH_DEBERTA, 0, 2>), grid, dim3(256), 0, stream, a);
 }
 
 }  // namespace relpos

@@ -8,7 +8,7 @@
 namespace relpos {
 
 void launch_bwd_txl_key(const BwdArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_kernel<MECH_TXL, 1, 0>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((bwd_kernel<uint16_t, MECH_TXL, 1, 0>), grid, dim3(256), 0, stream, a);
 }
 
 }  // namespace relpos

@@ -132,7 +132,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     if (jt0 <= j_hi) kc_load(jt0);
   }
   const T* rtab = nullptr;
-  if constexpr (MECH == MECH_TXL) rtab = (const T*)a.rel_a + (int64_t)h * sh.nrel * kHeadDim;
+  if constexpr (MECH == MECH_TXL) rtab = (const T*)a.rel_a + h * sh.rel_hs;
 
   for (int j0 = jt0; j0 <= j_hi; j0 += BOTH) {
     // circular T-XL window: row x of step s sits at physical row (x - 64 s) mod 192
@@ -182,8 +182,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
       }
     } else if (wg_general) {
       const int toff = sh.txl_off, nrel = sh.nrel;
-      const T* tab = (const T*)a.rel_a;
-      if constexpr (MECH == MECH_TXL) tab += (int64_t)h * nrel * kHeadDim;
+      const T* tab = (const T*)a.rel_a + h * sh.rel_hs;
       stage_window<T, NP>(win, tab, [&](int x) {
         return row_side_row(MECH, wg_dlo + x, span, nrel, toff);
       });
@@ -280,7 +279,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
       if (wg_general) {
         // column side (p2c): restage the window with Qr rows
         __syncthreads();
-        stage_window<T, NP>(win, (const T*)a.rel_b, [&](int x) {
+        stage_window<T, NP>(win, (const T*)a.rel_b + h * sh.rel_hs, [&](int x) {
           // column window row x <-> rho = j - i = (j0 - i0 - 127) + x
           return p2c_row(-((j0 - i0 - (BLANE - 1)) + x), span);
         });

@@ -52,6 +52,7 @@ struct AttnShape {
   int nrel;         // T-XL table rows
   int txl_off;      // T-XL row = delta + txl_off
   float scale;      // s
+  int64_t rel_hs;   // elements between the relation tables of consecutive heads (0 = shared)
 };
 
 struct FwdArgs {
@@ -113,7 +114,8 @@ hipError_t launch_bwd_dq(const BwdArgs& a, bool fp32, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdArgs& a, bool fp32, hipStream_t stream);
 
 // out[n * ne + e] = x_n . y_e(h(n)) for rows x_n of length 64.  Row n belongs to head
-// (n / rows_per_head) % H; y_e(h) = y + h * y_head_stride + y_row[e] * 64.
+// h(n) = (n / rows_per_head) % H; x_n = x + 64 n when x_head_stride < 0 (dense rows), else
+// x + h(n) x_head_stride + 64 (n % rows_per_head); y_e(h) = y + h y_head_stride + 64 y_row[e].
 struct RowDotArgs {
   const void* x;
   int64_t nrows;
@@ -124,6 +126,7 @@ struct RowDotArgs {
   int y_row0, y_row1;
   int ne;
   float* out;
+  int64_t x_head_stride;
 };
 hipError_t launch_rowdot(const RowDotArgs& a, bool x_fp32, bool y_fp32, hipStream_t stream);
 
@@ -134,9 +137,14 @@ hipError_t launch_t5_lut(const float* beta, int H, int L, int nb, float inv_scal
                          float* lut, hipStream_t stream);
 hipError_t launch_index_map(int mech, int L, int span, int nrel, int txl_off, const T5Map& m,
                             int32_t* out_a, int32_t* out_b, hipStream_t stream);
-// second-pass aggregation of the backward's offset-sharded partials
+// second-pass aggregation of the backward's offset-sharded partials: out = scale * the sum of
+// the nown partials (slots 0 .. nown - 1, each `stride` floats apart), in a fixed order
 hipError_t launch_agg_rows(const float* part, int64_t stride, int nown, int64_t nelem, float scale,
                            float* out, hipStream_t st);
+// the same per head: owners are slots (b H + h) nb + p; out[h nelem + e] sums head h's owners
+// (b, p) in ascending order
+hipError_t launch_agg_rows_by_head(const float* part, int64_t stride, int B, int H, int nb,
+                                   int64_t nelem, float scale, float* out, hipStream_t st);
 hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool rev, int wl,
                            int wr, float* diag, hipStream_t st);
 // ALiBi dm[h] = -sum over the owners (b, query block) of head h of part[owner] (fixed order)
@@ -147,13 +155,16 @@ hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int
 // s0 + i, key block p: i nb + p), summed in ascending (slice, block) order.  Groups are added in
 // order: the first overwrites dr, later ones add to it; dr holds raw sums until the last group,
 // which adds v . diag and scales by s.
+// With `shared` one table serves every head: dr [nrel, 64] sums the slices of every head and
+// the diagonal term is sum_h v_h . diag_h.
 hipError_t launch_agg_txl_dr(const float* prow, const float* diag, const float* v, int H, int L,
                              int nb, int nrk, int wl, int wr, int nrel, int off, float s, int s0,
-                             int ns, bool first, bool last, float* dr, hipStream_t st);
-// T-XL dv (v . r diagonal term) and du (from the key-side per-owner sums of dS^T k)
-hipError_t launch_agg_txl_uv(const float* pkv, const float* diag, const void* r, int B, int H,
-                             int L, int nb, int nrel, int off, float s, bool fp32, float* du,
-                             float* dv, hipStream_t st);
+                             int ns, bool first, bool last, bool shared, float* dr, hipStream_t st);
+// T-XL dv (v . r diagonal term; head h reads r + h r_hs) and du (from the key-side per-owner
+// sums of dS^T k)
+hipError_t launch_agg_txl_uv(const float* pkv, const float* diag, const void* r, int64_t r_hs,
+                             int B, int H, int L, int nb, int nrel, int off, float s, bool fp32,
+                             float* du, float* dv, hipStream_t st);
 
 // Relation-table projections: rel [H, N, d] = X [N, F] . W [F, H d] (dtype of X and W; rel
 // written in that dtype), and the backward dX = dY . W^T [N, F], dW = X^T . dY [F, H d] (fp32)

@@ -77,8 +77,11 @@ __global__ void rowdot_kernel(RowDotArgs a) {
   const bool valid = n < a.nrows;
   const int64_t nn = valid ? n : 0;
   const int h = (int)((nn / a.rows_per_head) % a.H);
+  const int64_t xoff = a.x_head_stride < 0
+                           ? nn * kHeadDim
+                           : (int64_t)h * a.x_head_stride + (nn % a.rows_per_head) * kHeadDim;
   float x[8];
-  load8((const TX*)a.x + nn * kHeadDim + part * 8, x);
+  load8((const TX*)a.x + xoff + part * 8, x);
   float acc[2] = {0.f, 0.f};
 #pragma unroll
   for (int e = 0; e < 2; ++e) {

@@ -28,13 +28,31 @@ def tensor_from_f32(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     return t.to(device)
 
 
-def desc_for(case: dict):
+# relation tables (head axis optional: a table with one more axis than these is per head)
+REL_TABLES = {"shaw": ("w",), "txl": ("r",), "deberta": ("kr", "qr")}
+REL_NDIM = {"w": 2, "r": 2, "kr": 2, "qr": 2}
+
+
+def rel_head_stride(case: dict) -> int:
+    """0 when the case's relation tables are shared by every head, else the elements between
+    consecutive heads' tables (dense [H, rows, d])."""
+    names = REL_TABLES.get(case["params"]["mech"], ())
+    for n in names:
+        t = case["tables"][n]
+        if t.ndim == REL_NDIM[n] + 1:
+            return int(t.shape[1] * t.shape[2])
+    return 0
+
+
+def desc_for(case: dict, **overrides):
     p = case["params"]
     B, H, L, d = case["shape"]
-    return make_desc(p["mech"], B, H, L, d, dtype=case["dtype"],
-                     window=(p["window_left"], p["window_right"]), rel_span=p["rel_span"],
-                     num_buckets=p["num_buckets"], max_distance=p["max_distance"],
-                     bidirectional=p["bidirectional"], scale=p.get("scale", 0.0) or 0.0)
+    kw = dict(dtype=case["dtype"], window=(p["window_left"], p["window_right"]),
+              rel_span=p["rel_span"], num_buckets=p["num_buckets"],
+              max_distance=p["max_distance"], bidirectional=p["bidirectional"],
+              scale=p.get("scale", 0.0) or 0.0, rel_head_stride=rel_head_stride(case))
+    kw.update(overrides)
+    return make_desc(p["mech"], B, H, L, d, **kw)
 
 
 def to_device(case: dict, device="cuda") -> dict:

@@ -36,12 +36,14 @@
  * Layouts (row-major, last index fastest, no padding):
  *   q, k, v, o, dout, dq, dk, dv : [batch, heads, seqlen, head_dim], element type `dtype`
  *   lse                          : [batch, heads, seqlen] float (natural log)
- *   T5 beta  [heads, num_buckets] float        Shaw w     [2k+1, head_dim] dtype (shared)
- *   T-XL r   [heads, Nrel, head_dim] dtype     T-XL u, v  [heads, head_dim] float
- *   DeBERTa Kr, Qr [2k, head_dim] dtype (shared across heads)
+ *   T5 beta  [heads, num_buckets] float        T-XL u, v  [heads, head_dim] float
  *   ALiBi m  [heads] float
- * Every table gradient is float with the table's shape and is OVERWRITTEN (not accumulated).
- * Unused table / gradient slots must be NULL.
+ *   relation tables (dtype), one per head or one shared by every head (rel_head_stride):
+ *     Shaw w [2k+1, head_dim]    T-XL r [Nrel, head_dim]    DeBERTa Kr, Qr [2k, head_dim]
+ * Every table gradient is float and is OVERWRITTEN (not accumulated): beta, u, v and m have
+ * their table's shape; a relation table's gradient is [heads, rows, head_dim] (dense) when the
+ * tables are per head and [rows, head_dim] when one table is shared, the sum over every
+ * (batch, head) that reads it.  Unused table / gradient slots must be NULL.
  *
  * Ownership: the caller owns every buffer, including the workspace (size it with
  * relpos_attn_workspace_size).  The library never allocates device memory.  All device
@@ -73,7 +75,9 @@ enum {
   RELPOS_OK = 0,
   RELPOS_E_INVALID = -1,     /* bad enum, shape, NULL / misaligned pointer, span inconsistent */
   RELPOS_E_UNSUPPORTED = -2, /* valid request outside what the kernels implement: head_dim != 64,
-                                 or a backward in fp32 (the fp32 forward is implemented) */
+                                 or a sequence or table too long for the kernels' 32-bit
+                                 in-slice offsets: max(seqlen, table rows) * 64 * element size
+                                 must stay below 2^32 bytes */
   RELPOS_E_WORKSPACE = -3,   /* workspace NULL or smaller than relpos_attn_workspace_size() */
   RELPOS_E_LAUNCH = -4       /* a kernel launch failed */
 };
@@ -97,6 +101,13 @@ typedef struct relpos_desc {
                                 processed in fixed groups that fit under it (at least one slice
                                 per group).  0 = 8 GiB.  Results depend on the group size only
                                 through the (fixed) order of the fp32 sums. */
+  int64_t rel_head_stride;   /* elements between the relation tables (rel_a, rel_b) of
+                                consecutive heads: 0 = one table shared by every head; otherwise
+                                head h reads rel_a + h * rel_head_stride (and rel_b likewise),
+                                with rel_head_stride >= rows * head_dim and a multiple of 8.  The
+                                workloads of the pages share Shaw's w and DeBERTa's Kr / Qr
+                                (stride 0) and give T-XL one r per head (stride Nrel * 64).
+                                Ignored for T5 and ALiBi, whose tables are per head. */
 } relpos_desc;
 
 /* Bytes of workspace the forward (pass 0) or backward (pass 1) call needs. */
@@ -110,11 +121,17 @@ int relpos_attn_fwd(const relpos_desc* desc, const void* q, const void* k, const
 
 /* Backward from (q, k, v, o, lse, dout): writes dq, dk, dv and the table gradients
  * (T5: dbias_a = dbeta; Shaw: drel_a = dw; T-XL: drel_a = dr, dbias_a = du, dbias_b = dv;
- * DeBERTa: drel_a = dKr, drel_b = dQr; ALiBi: dbias_a = dm, the slopes' gradient).
- * Table gradients are reduced over every (batch, head)
- * that reads the table, in a fixed order, without atomics (offset-sharded partials followed
- * by a second aggregation pass).  bf16 only: dtype RELPOS_FP32 returns RELPOS_E_UNSUPPORTED
- * before any launch. */
+ * DeBERTa: drel_a = dKr, drel_b = dQr; ALiBi: dbias_a = dm, the slopes' gradient), with
+ * dS = P (dP - D), D_i = dO_i . O_i, and every table gradient the sum of dS-weighted operands
+ * over the pairs that read each table row.  Offset-based gradient sharding (abstract of "Fast and
+ * Exact Relative-Position Attention via Structure-Aware Kernels", item 3; zicq.com explainer,
+ * section on how structure-aware tiling stays exact, part 3, offset-based gradient sharding):
+ * each workgroup reduces dS along the diagonals of its own tiles into an offset-indexed partial
+ * of its own, and a second pass sums the partials of every (batch, head) that reads a table row
+ * in a fixed order, so no atomics are used and the result is bitwise reproducible.  bf16, or
+ * fp32 (every matrix-core operand split into two bf16 parts, hi and lo, with the products
+ * hi.hi + hi.lo + lo.hi accumulated in fp32).  The workspace (relpos_attn_workspace_size, pass 1) holds the partials; its size grows with
+ * B H L (T-XL: B H L^2 / 2 bytes, capped by max_partial_bytes). */
 int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const void* v,
                     const void* o, const float* lse, const void* dout, const void* rel_a,
                     const void* rel_b, const float* bias_a, const float* bias_b, void* dq,
@@ -168,11 +185,12 @@ int relpos_project_bwd(const relpos_proj_desc* desc, const void* X, const void* 
                        size_t workspace_bytes, void* stream);
 
 /* Profiling hook for benchmarks.  When `kernel` is RELPOS_PROF_FWD, RELPOS_PROF_BWD_DQ or
- * RELPOS_PROF_BWD_DKDV, later calls record `start_event` on their stream just before enqueueing
- * that kernel and `stop_event` just after it (both hipEvent_t created by the caller).
- * RELPOS_PROF_OFF (0) clears the hook.  Process-wide setting, not thread-safe; intended for
- * single-threaded benchmark drivers only.  Returns RELPOS_E_INVALID for an unknown kernel id or
- * NULL events. */
+ * RELPOS_PROF_BWD_DKDV, later calls made BY THE SAME HOST THREAD record `start_event` on their
+ * stream just before enqueueing that kernel and `stop_event` just after it (both hipEvent_t
+ * created by the caller).  RELPOS_PROF_OFF (0) clears the hook.  The setting is thread-local:
+ * calls from other threads never see it, so the library stays safe to call from several
+ * threads on their own streams.  Returns RELPOS_E_INVALID for an unknown kernel id or NULL
+ * events. */
 enum { RELPOS_PROF_OFF = 0, RELPOS_PROF_FWD = 1, RELPOS_PROF_BWD_DQ = 2, RELPOS_PROF_BWD_DKDV = 3 };
 int relpos_profile_events(void* start_event, void* stop_event, int kernel);
 

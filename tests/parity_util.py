@@ -16,14 +16,15 @@ MASKS = {"none": (-1, -1), "causal": (-1, 0), "local": (70, 45)}
 
 
 def case(mech, B=2, H=3, L=200, dtype="bf16", mask="none", seed=7, span=None, table_std=None,
-         nb=32, md=None, bidir=None):
+         nb=32, md=None, bidir=None, layout=None):
     window = MASKS[mask] if isinstance(mask, str) else mask
     if span is None:
         span = {"shaw": 48, "deberta": 40}.get(mech, 0)
     if md is None:
         md = max(16, L // 2)
     c = make_case(mech, B, H, L, 64, dtype=dtype, window=window, seed=seed, rel_span=span,
-                  num_buckets=nb, max_distance=md, bidirectional=bidir, table_std=table_std)
+                  num_buckets=nb, max_distance=md, bidirectional=bidir, table_std=table_std,
+                  rel_layout=layout)
     return c
 
 

@@ -219,3 +219,63 @@ def test_projection_rejects_bad_pointers_without_launching():
     big = ear.make_proj_desc(16383, 512, 8, 64)
     assert lib.relpos_project_bwd(ctypes.byref(big), base, base, base, None, base, base, 16,
                                   None) == ear.RELPOS_E_WORKSPACE
+
+
+@pytest.mark.parametrize("mech,stride,expected", [
+    ("shaw", 0, ear.RELPOS_OK), ("shaw", 9 * 64, ear.RELPOS_OK), ("shaw", 9 * 64 + 8, ear.RELPOS_OK),
+    ("shaw", 9 * 64 - 8, ear.RELPOS_E_INVALID), ("shaw", 9 * 64 + 4, ear.RELPOS_E_INVALID),
+    ("shaw", -1, ear.RELPOS_E_INVALID), ("deberta", 8 * 64, ear.RELPOS_OK),
+    ("deberta", 8 * 64 - 64, ear.RELPOS_E_INVALID), ("txl", 0, ear.RELPOS_OK),
+    ("txl", 199 * 64, ear.RELPOS_OK), ("txl", 198 * 64, ear.RELPOS_E_INVALID),
+    ("t5", 12345, ear.RELPOS_OK), ("alibi", 3, ear.RELPOS_OK), ("t5", -5, ear.RELPOS_E_INVALID),
+])
+def test_rel_head_stride_rules(mech, stride, expected):
+    """0 = one table shared by every head; otherwise at least one table apart and a multiple of
+    8 elements (16-byte aligned bf16 rows).  T5 and ALiBi ignore it (their tables are per head)."""
+    desc = ear.make_desc(mech, 2, 3, 100, rel_span=4, rel_head_stride=stride)
+    assert _ws(desc)[0] == expected
+
+
+def test_default_rel_head_stride_follows_the_workloads():
+    assert ear.make_desc("shaw", 1, 2, 50, rel_span=3).rel_head_stride == 0
+    assert ear.make_desc("deberta", 1, 2, 50, rel_span=3).rel_head_stride == 0
+    assert ear.make_desc("txl", 1, 2, 50).rel_head_stride == 99 * 64
+    assert ear.make_desc("txl", 1, 2, 50, window=(-1, 0)).rel_head_stride == 50 * 64
+
+
+@pytest.mark.parametrize("mech,dtype,kw,ok", [
+    # bf16 slice rows: L * 64 * 2 bytes must stay below 2^32
+    ("t5", "bf16", dict(seqlen=(1 << 25) - 1), True),
+    ("t5", "bf16", dict(seqlen=1 << 25), False),
+    ("t5", "fp32", dict(seqlen=(1 << 24) - 1), True),
+    ("t5", "fp32", dict(seqlen=1 << 24), False),
+    # Shaw table rows 2k + 1
+    ("shaw", "bf16", dict(seqlen=64, rel_span=(1 << 24) - 1), True),
+    ("shaw", "bf16", dict(seqlen=64, rel_span=1 << 24), False),
+    # T-XL full-span table rows 2L - 1
+    ("txl", "fp32", dict(seqlen=1 << 23), True),
+    ("txl", "fp32", dict(seqlen=(1 << 23) + 1), False),
+    ("txl", "bf16", dict(seqlen=(1 << 24) + 1), False),
+    # DeBERTa table rows 2k
+    ("deberta", "fp32", dict(seqlen=64, rel_span=1 << 23), False),
+    ("deberta", "fp32", dict(seqlen=64, rel_span=(1 << 23) - 1), True),
+])
+def test_32bit_in_slice_offset_limit(mech, dtype, kw, ok):
+    """Rows inside one (batch, head) slice or one head's table are addressed with 32-bit byte
+    offsets: longer sequences or tables are refused with RELPOS_E_UNSUPPORTED."""
+    desc = ear.make_desc(mech, 1, 1, kw.pop("seqlen"), dtype=dtype, **kw)
+    st, _ = _ws(desc, 0)
+    assert st == (ear.RELPOS_OK if ok else ear.RELPOS_E_UNSUPPORTED), st
+
+
+def test_profile_hook_calls_from_another_thread():
+    """The profiling hook is per host thread: setting or clearing it from another thread is a
+    call of its own that succeeds there, and invalid ids fail on every thread."""
+    import threading
+    lib = ear.load_library()
+    assert lib.relpos_profile_events(None, None, 7) == ear.RELPOS_E_INVALID
+    res = []
+    t = threading.Thread(target=lambda: res.append(lib.relpos_profile_events(None, None, 0)))
+    t.start()
+    t.join()
+    assert res == [ear.RELPOS_OK]

@@ -97,3 +97,38 @@ def test_backward_shaw_causal_future_rows_exactly_zero():
     got = _run(c)
     assert np.all(got["table_w"][49:] == 0.0)
     assert np.max(np.abs(got["table_w"][:49])) > 0
+
+
+@pytest.mark.parametrize("mech", MECHS)
+@pytest.mark.parametrize("mask", list(MASKS))
+@pytest.mark.parametrize("L", [200, 333])
+def test_backward_fp32(mech, mask, L):
+    """fp32 mode: every gradient within rel-L2 1e-4 of the oracle, several blocks and a ragged
+    tail, every mask."""
+    c = case(mech, B=2, H=3, L=L, dtype="fp32", mask=mask, seed=L + 11 * len(mask))
+    print(f"bwd fp32 mech={mech} mask={mask} L={L}", flush=True)
+    errs = _check(c, _run(c))
+    print(f"  max rel-L2 {max(errs.values()):.2e}", flush=True)
+
+
+@pytest.mark.parametrize("mech", MECHS)
+def test_backward_fp32_amplified_tables_and_determinism(mech):
+    """fp32 mode with unit-scale tables (the relative terms dominate), run twice: within 1e-4
+    of the oracle and bitwise identical."""
+    c = case(mech, B=1, H=2, L=300, dtype="fp32", mask="none", table_std=1.0, seed=29)
+    if mech == "t5":
+        c["tables"]["beta"] = c["tables"]["beta"] * np.float32(4.0)
+    g1 = _run(c)
+    _check(c, g1)
+    g2 = _run(c)
+    for k in g1:
+        assert np.array_equal(g1[k], g2[k]), k
+
+
+def test_backward_fp32_long_txl_and_deberta_spans():
+    """fp32 at a longer sequence: T-XL full span and DeBERTa with clipped tiles on both sides
+    (light and general passes), L = 1100."""
+    for mech, span in (("txl", 0), ("deberta", 96), ("shaw", 80)):
+        c = case(mech, B=1, H=2, L=1100, dtype="fp32", mask="none", span=span or None, seed=31)
+        print(f"bwd fp32 long mech={mech}", flush=True)
+        _check(c, _run(c))

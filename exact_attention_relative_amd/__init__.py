@@ -24,7 +24,7 @@ RELPOS_E_UNSUPPORTED = -2
 RELPOS_E_WORKSPACE = -3
 RELPOS_E_LAUNCH = -4
 
-EXPORTED = ("relpos_attn_workspace_size", "relpos_attn_fwd", "relpos_attn_bwd",
+EXPORTED = ("relpos_attn_workspace_size", "relpos_attn_fwd", "relpos_attn_fwd_noalloc", "relpos_attn_bwd",
             "relpos_index_map", "relpos_profile_events", "relpos_status_string", "relpos_version",
             "relpos_project_fwd", "relpos_project_workspace_size", "relpos_project_bwd")
 RELPOS_PROF_OFF, RELPOS_PROF_FWD, RELPOS_PROF_BWD_DQ, RELPOS_PROF_BWD_DKDV = 0, 1, 2, 3
@@ -71,6 +71,8 @@ def load_library(path: str | None = None):
     lib.relpos_attn_workspace_size.restype = i32
     lib.relpos_attn_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.relpos_attn_fwd.restype = i32
+    lib.relpos_attn_fwd_noalloc.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.relpos_attn_fwd_noalloc.restype = i32
     lib.relpos_attn_bwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                     vp, vp, vp, sz, vp]
     lib.relpos_attn_bwd.restype = i32
@@ -169,6 +171,19 @@ def relpos_attn_fwd(desc, q, k, v, rel_a, rel_b, bias_a, bias_b, o, lse, workspa
                                         _ptr(workspace), wsb, _stream(stream))
     if check:
         _check(st, "relpos_attn_fwd")
+    return st
+
+
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024   # RELPOS_NOALLOC_SCRATCH_BYTES
+
+
+def relpos_attn_fwd_noalloc(desc, q, k, v, rel_a, rel_b, bias_a, bias_b, o, lse, stream=None,
+                            check=True) -> int:
+    st = load_library().relpos_attn_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v),
+                                                _ptr(rel_a), _ptr(rel_b), _ptr(bias_a),
+                                                _ptr(bias_b), _ptr(o), _ptr(lse), _stream(stream))
+    if check:
+        _check(st, "relpos_attn_fwd_noalloc")
     return st
 
 

@@ -17,7 +17,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librelpos_attn.so")
 SOURCES = ["relpos_api.hip", "relpos_prep.hip", "relpos_fwd.hip", "relpos_bwd.hip", "relpos_agg.hip",
            "relpos_proj.hip", "relpos_bwd_txl_key.hip", "relpos_bwd_fat_q.hip", "relpos_bwd_trk.hip",
-           "relpos_bwd_f32.hip"]
+           "relpos_bwd_f32.hip", "relpos_noalloc.hip"]
 # per-source options: the T-XL passes and the key-side passes of Shaw and DeBERTa schedule with
 # the register-pressure trackers (fewer spills at the 256-register budget); the query-side
 # general passes of Shaw and DeBERTa keep their MFMA accumulators in VGPRs (fewer copies between

@@ -138,6 +138,22 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
                     void* dk, void* dv, float* drel_a, float* drel_b, float* dbias_a,
                     float* dbias_b, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The forward for callers that cannot allocate device memory (code under graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same kernels and results as
+ * relpos_attn_fwd, with the workspace in a device array of RELPOS_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends.  The call allocates nothing; the
+ * caller passes inputs and outputs as for relpos_attn_fwd.  A problem whose forward workspace
+ * (relpos_attn_workspace_size, pass 0) exceeds RELPOS_NOALLOC_SCRATCH_BYTES is refused with
+ * RELPOS_E_WORKSPACE before any launch.  Every call on one GPU shares that GPU's array and
+ * leaves its contents behind (nothing in it needs to start at zero: each call rewrites what it
+ * reads), so calls that overlap on one GPU (several streams or threads at once) race: serialise
+ * them.  The first call on each device looks up the array's device address (hipGetSymbolAddress)
+ * with that device current; RELPOS_E_LAUNCH if that fails. */
+#define RELPOS_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+int relpos_attn_fwd_noalloc(const relpos_desc* desc, const void* q, const void* k, const void* v,
+                            const void* rel_a, const void* rel_b, const float* bias_a,
+                            const float* bias_b, void* o, float* lse, void* stream);
+
 /* Index maps the kernels use, computed on the device: for every offset delta = i - j in
  * [-(L-1), L-1], out_a[delta + L - 1] is the table row of that offset (T5 bucket, Shaw row,
  * T-XL row or -1 when the table has no such row, DeBERTa c2p row, ALiBi distance |delta|)

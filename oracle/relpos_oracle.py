@@ -53,6 +53,7 @@ invariants, and cross-mechanism identities.
 
 from __future__ import annotations
 
+import functools
 import math
 from dataclasses import dataclass, field
 
@@ -135,8 +136,12 @@ def t5_bucket(rel: int, num_buckets: int, max_distance: int, bidirectional: bool
 
 def t5_bucket_by_offset(L: int, p: Params) -> np.ndarray:
     """bucket(j - i) for every offset rel = j - i in [-(L-1), L-1]; entry rel + L - 1."""
-    return np.array([t5_bucket(rel, p.num_buckets, p.max_distance, p.bidirectional)
-                     for rel in range(-(L - 1), L)], dtype=np.int64)
+    return _t5_offset_map(L, p.num_buckets, p.max_distance, bool(p.bidirectional)).copy()
+
+
+@functools.lru_cache(maxsize=16)
+def _t5_offset_map(L: int, nb: int, md: int, bidir: bool) -> np.ndarray:
+    return np.array([t5_bucket(rel, nb, md, bidir) for rel in range(-(L - 1), L)], dtype=np.int64)
 
 
 def txl_rows(L: int, p: Params) -> int:
@@ -412,6 +417,116 @@ def add_table_grads(grads: dict, g: dict, tables: dict, h: int) -> None:
             grads[name][h] += val
         else:
             grads[name] += val
+
+
+def backward_chunk(p: Params, q, k, v, tables: dict, dO, b: int, h: int, rows) -> dict:
+    """The part of one (batch, head)'s backward that comes from the query rows `rows`: the same
+    formulas as backward_head on those rows of S, P, dP and dS.  Each row's softmax, dP and D
+    depend on that row only, so they are whole; returns dq at those rows and the rows'
+    contributions to every sum over query rows (dK, dV, table gradients, and DeBERTa's p2c
+    scatter grouped by key, which finish_chunks turns into dK and dQr)."""
+    L = q.shape[2]
+    s = p.s()
+    rows = np.asarray(rows, dtype=np.int64)
+    qh, kh, vh, doh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _f64(dO[b, h])
+    qc, doc = qh[rows], doh[rows]
+    S = scores_rows(p, qh, kh, tables, h, rows)
+    P, lse = _softmax_rows(S)
+    dP = doc @ vh.T
+    D = np.sum(P * dP, axis=1)
+    dS = P * (dP - D[:, None])
+    idx = index_maps(rows, L, p)
+    # the forward outputs of these rows come with them (as forward_rows forms them)
+    out = {"rows": rows, "o": P @ vh, "lse": lse, "dv": P.T @ doc}
+    dqc = s * (dS @ kh)
+    g = {}
+    if p.mech == "t5":
+        out["dk"] = s * (dS.T @ qc)
+        g["beta"] = np.bincount(idx["bucket"].ravel(), weights=dS.ravel(), minlength=p.num_buckets)
+    elif p.mech == "shaw":
+        w = head_table(tables, "w", h)
+        N = _pair_scatter(dS, idx["row"], w.shape[0])
+        dqc += s * (N @ w)
+        out["dk"] = s * (dS.T @ qc)
+        g["w"] = s * (N.T @ qc)
+    elif p.mech == "txl":
+        r = head_table(tables, "r", h)
+        u = _f64(tables["u"])[h]
+        vv = _f64(tables["v"])[h]
+        N = _pair_scatter(dS, idx["row"], r.shape[0])
+        dqc += s * (N @ r)
+        out["dk"] = s * (dS.T @ (qc + u))
+        g["r"] = s * (N.T @ (qc + vv))
+        g["u"] = s * np.sum(dS @ kh, axis=0)
+        g["v"] = s * np.sum(N @ r, axis=0)
+    elif p.mech == "deberta":
+        kr = head_table(tables, "kr", h)
+        qr = head_table(tables, "qr", h)
+        N1 = _pair_scatter(dS, idx["c2p"], kr.shape[0])
+        dqc += s * (N1 @ kr)
+        out["dk"] = s * (dS.T @ qc)
+        g["kr"] = s * (N1.T @ qc)
+        out["n2"] = _pair_scatter(dS, idx["p2c"], qr.shape[0], by_key=True)
+    elif p.mech == "alibi":
+        out["dk"] = s * (dS.T @ qc)
+        g["slopes"] = -np.sum(dS * idx["dist"])
+    else:
+        raise ValueError(p.mech)
+    out["dq"] = dqc
+    out["g"] = g
+    return out
+
+
+def sum_chunks(parts) -> dict:
+    """Merge backward_chunk parts (disjoint row sets) into one part, summing in the order given."""
+    out = None
+    for part in parts:
+        if out is None:
+            out = {"rows": part["rows"], "dq": part["dq"], "o": part["o"], "lse": part["lse"],
+                   "dk": part["dk"].copy(), "dv": part["dv"].copy(),
+                   "g": {n: np.copy(v) for n, v in part["g"].items()}}
+            if "n2" in part:
+                out["n2"] = part["n2"].copy()
+            continue
+        for n in ("rows", "dq", "o", "lse"):
+            out[n] = np.concatenate([out[n], part[n]])
+        out["dk"] += part["dk"]
+        out["dv"] += part["dv"]
+        for n, v in part["g"].items():
+            out["g"][n] = out["g"][n] + v
+        if "n2" in part:
+            out["n2"] += part["n2"]
+    return out
+
+
+def finish_chunks(p: Params, k, tables: dict, b: int, h: int, part: dict) -> tuple:
+    """dq, dk, dv [L, d] and the slice's table gradients, as backward_head returns them, from the
+    merged part of every query row (DeBERTa's p2c terms need the scatter of all rows)."""
+    L, d = k.shape[2], k.shape[3]
+    s = p.s()
+    dq = np.zeros((L, d))
+    dq[part["rows"]] = part["dq"]
+    dk = part["dk"].copy()
+    g = dict(part["g"])
+    if p.mech == "deberta":
+        qr = head_table(tables, "qr", h)
+        dk += s * (part["n2"] @ qr)
+        g["qr"] = s * (part["n2"].T @ _f64(k[b, h]))
+    return dq, dk, part["dv"], g
+
+
+def row_chunks(L: int, chunk: int):
+    """Consecutive query-row ranges of at most `chunk` rows covering 0 .. L - 1."""
+    return [np.arange(r0, min(L, r0 + chunk)) for r0 in range(0, L, chunk)]
+
+
+def backward_head_chunked(p: Params, q, k, v, tables: dict, dO, b: int, h: int,
+                          chunk: int = 512):
+    """backward_head for long sequences: the query rows `chunk` at a time (backward_chunk), so
+    that no L x L matrix is held, summed in ascending row order (sum_chunks, finish_chunks)."""
+    parts = [backward_chunk(p, q, k, v, tables, dO, b, h, rows)
+             for rows in row_chunks(q.shape[2], chunk)]
+    return finish_chunks(p, k, tables, b, h, sum_chunks(parts))
 
 
 def backward(p: Params, q, k, v, tables: dict, dO):

@@ -9,7 +9,9 @@ from oracle import relpos_oracle as orc
 
 # Tolerances stated for this path: bf16 inputs with fp32 accumulation -> O max-abs <= 1e-2 and
 # relative L2 <= 2e-2 for every gradient; fp32 mode -> 1e-4 for both.
-TOL = {"bf16": {"o": 1e-2, "grad": 2e-2, "lse": 2e-3},
+# LSE (derived, not stated): the denominator sums bf16-rounded weights, each within 2^-8 relative;
+# fully correlated rounding (equal scores) moves ln of the sum by up to ln(1 + 2^-8) = 3.9e-3.
+TOL = {"bf16": {"o": 1e-2, "grad": 2e-2, "lse": 4e-3},
        "fp32": {"o": 1e-4, "grad": 1e-4, "lse": 1e-4}}
 
 MASKS = {"none": (-1, -1), "causal": (-1, 0), "local": (70, 45)}

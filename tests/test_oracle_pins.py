@@ -529,3 +529,40 @@ def test_per_head_tables_decompose_into_single_head_problems(mech):
         assert np.allclose(g2["r"].sum(axis=0), g["r"], rtol=0, atol=1e-12)
         for n in ("u", "v"):
             assert np.allclose(g2[n], g[n], rtol=0, atol=1e-13)
+
+
+# ------------------------------------------------------------------------ long-sequence backward
+
+@pytest.mark.parametrize("mech", orc.ALL_MECHS)
+@pytest.mark.parametrize("mask", ["none", "causal", "local"])
+@pytest.mark.parametrize("chunk", [1, 7, 64])
+def test_chunked_backward_equals_full_backward(mech, mask, chunk):
+    """Pin: the query-row-chunked backward (used at 16K-32K tokens, where no L x L matrix fits)
+    equals backward_head, itself pinned by central differences, to 1e-12, for chunk sizes that
+    do and do not divide L, on every mechanism and mask (per-head tables for Shaw / DeBERTa,
+    a shared T-XL table: both layouts of each go through the same code)."""
+    for layout in (None, {"shaw": "per_head", "deberta": "per_head", "txl": "shared"}.get(mech)):
+        c = make_case(mech, 1, 2, 45, 8, dtype="fp32", window=MASKS[mask], seed=37, rel_span=5,
+                      num_buckets=10, max_distance=20, bidirectional=(mask != "causal"),
+                      table_std=0.6, rel_layout=layout)
+        p = orc.Params(**c["params"])
+        q, k, v, tab, do = _f64(c)
+        for hh in range(2):
+            ref = orc.backward_head(p, q, k, v, tab, do, 0, hh)
+            got = orc.backward_head_chunked(p, q, k, v, tab, do, 0, hh, chunk=chunk)
+            for a, b_ in zip(got[:3], ref[:3]):
+                assert np.allclose(a, b_, rtol=1e-12, atol=1e-12)
+            assert set(got[3]) == set(ref[3])
+            for n in ref[3]:
+                assert np.allclose(got[3][n], ref[3][n], rtol=1e-12, atol=1e-12), n
+
+
+@pytest.mark.parametrize("mech", orc.ALL_MECHS)
+def test_chunk_forward_outputs_equal_forward_rows(mech):
+    """Pin: the O and LSE rows that backward_chunk returns with its part equal forward_rows."""
+    c, p = _case(mech, L=33, d=8, B=1, H=2, span=4, nb=8, md=16, table_std=0.6)
+    q, k, v, tab, do = _f64(c)
+    rows = np.array([0, 5, 6, 31, 32])
+    part = orc.backward_chunk(p, q, k, v, tab, do, 0, 1, rows)
+    O, lse = orc.forward_rows(p, q, k, v, tab, 0, 1, rows)
+    assert np.array_equal(part["o"], O) and np.array_equal(part["lse"], lse)

@@ -130,7 +130,14 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
                             : ((V::CLIP && V::HAS_COL && !V::DFAT) || MECH == MECH_ALIBI ? 2 * BOTH : 4);
   __shared__ float red_s[MECH == MECH_ALIBI ? NWAVE : 1];   // ALiBi: per-wave slope-gradient sums
   __shared__ __attribute__((aligned(16))) float ovec_s[NOVEC];   // per-other-row constants
-  __shared__ __attribute__((aligned(16))) float lsd_s[DIR == 1 ? 2 * BOTH : 4];   // LSE*log2e, D per query
+  // key side: -LSE / s and -D of the streamed queries, the starts of the score and dP
+  // accumulators (y units; -inf for rows past L or with no allowed key; see lsd_vals)
+  __shared__ __attribute__((aligned(16))) float lsd_s[DIR == 1 ? 2 * BOTH : 4];
+  // Key side: the score and dP accumulators start from those values (one fma and one multiply per
+  // element instead of two of each), except in the T-XL pass, whose registers are the limit
+  constexpr bool KINIT = DIR == 1 && !V::TK;
+  // key-side ALiBi: the ramps above plus -LSE / s, per step
+  __shared__ __attribute__((aligned(16))) float ainit_s[MECH == MECH_ALIBI && DIR == 1 ? 2 * BOTH : 4];
   float* const gsb = gsb_raw + GSG;
 
   const AttnShape sh = a.sh;
@@ -331,30 +338,45 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   }
   // per-row values of the streamed rows (end-row constants of the light key-side passes, LSE
   // and D of the streamed queries), read one processed step ahead
-  float pov = 0.f, pl2 = 0.f, pdd = 0.f;
+  f32x2 pov = {0.f, 0.f};
+  float pnl = 0.f, pdd = 0.f;
+  const float inv_s = 1.f / s;
   auto colfn_at = [&](int b0x) {   // column window row x <-> mu = b - a = (b0 - A0 - 127) + x
     return [=](int x) { return V::col_of((b0x - A0 - (BLANE - 1)) + x, span, nrel, toff); };
   };
   auto rowfn_at = [&](int b0x) {   // row window row x <-> lam = A0 - b0 - 63 + x
     return [=](int x) { return V::row_of(A0 - b0x - 63 + x, span, nrel, toff); };
   };
-  auto ov_load = [&](int b0x) {   // end A, end B values of the streamed rows (column side)
-    if (tid < 2 * BOTH) {
-      const int yy = b0x + (tid >> 1);
-      pov = (yy < L) ? oc_g[((int64_t)bh * L + yy) * 2 + (tid & 1)] : 0.f;
-    }
-  };
-  auto lsd_load = [&](int b0x) {   // key side: LSE log2(e) and D of the streamed queries
+  auto ov_load = [&](int b0x) {   // end A, end B values of streamed row b0x + tid (column side)
     if (tid < BOTH) {
       const int yy = b0x + tid;
-      pl2 = __builtin_inff();
-      pdd = 0.f;
+      pov = (yy < L) ? *(const f32x2*)(oc_g + ((int64_t)bh * L + yy) * 2) : f32x2{0.f, 0.f};
+    }
+  };
+  // key side: -LSE / s and -D of streamed query b0x + tid (the accumulator starts); the T-XL
+  // pass keeps LSE log2 e (+inf for rows past L or with no allowed key) and D, applied per element
+  auto lsd_vals = [&](int b0x, float& nl, float& nd) {
+    const int yy = b0x + tid;
+    if constexpr (KINIT) {
+      nl = kNegInf;
+      nd = 0.f;
       if (yy < L) {
-        pl2 = a.lse[(int64_t)bh * L + yy] * kLog2e;
-        if (!(pl2 > kNegInf)) pl2 = __builtin_inff();
-        pdd = a.dsum[(int64_t)bh * L + yy];
+        const float lse = a.lse[(int64_t)bh * L + yy];
+        if (lse > kNegInf) nl = -lse * inv_s;
+        nd = -a.dsum[(int64_t)bh * L + yy];
+      }
+    } else {
+      nl = __builtin_inff();
+      nd = 0.f;
+      if (yy < L) {
+        nl = a.lse[(int64_t)bh * L + yy] * kLog2e;
+        if (!(nl > kNegInf)) nl = __builtin_inff();
+        nd = a.dsum[(int64_t)bh * L + yy];
       }
     }
+  };
+  auto lsd_load = [&](int b0x) {
+    if (tid < BOTH) lsd_vals(b0x, pnl, pdd);
   };
   float plut = 0.f;   // T5 / ALiBi: this thread's LUT entry of the next step's window
   auto lut_load = [&](int b0x) {
@@ -446,26 +468,26 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if constexpr (MECH == MECH_TXL && DIR == 0) {
       if (tid < BOTH) ovec_s[tid] = (b0 + tid < L) ? a.uk[(int64_t)bh * L + b0 + tid] : 0.f;
     }
-    if constexpr (V::CLIP && V::HAS_COL && !V::DFAT) {
-      // end A values of the 64 streamed rows, then end B: each a contiguous vector
-      if (tid < 2 * BOTH) ovec_s[(tid & 1) * BOTH + (tid >> 1)] = pov;
-    }
-    if constexpr (PF_LSD) {
+    if constexpr (DIR == 1) {
       if (tid < BOTH) {
-        lsd_s[tid] = pl2;
-        lsd_s[BOTH + tid] = pdd;
-      }
-    } else if constexpr (DIR == 1) {
-      if (tid < BOTH) {
-        const int yy = b0 + tid;
-        float l2 = __builtin_inff(), dd = 0.f;
-        if (yy < L) {
-          l2 = a.lse[(int64_t)bh * L + yy] * kLog2e;
-          if (!(l2 > kNegInf)) l2 = __builtin_inff();
-          dd = a.dsum[(int64_t)bh * L + yy];
+        // (read here when not prefetched: locals, so that nothing stays live across steps)
+        float nl = pnl, nd = pdd;
+        if constexpr (!PF_LSD) lsd_vals(b0, nl, nd);
+        lsd_s[tid] = nl;
+        lsd_s[BOTH + tid] = nd;
+        if constexpr (MECH == MECH_ALIBI) {
+          ainit_s[tid] = ovec_s[tid] + nl;
+          ainit_s[BOTH + tid] = ovec_s[BOTH + tid] + nl;
         }
-        lsd_s[tid] = l2;
-        lsd_s[BOTH + tid] = dd;
+      }
+    }
+    if constexpr (V::CLIP && V::HAS_COL && !V::DFAT) {
+      // end A values of the 64 streamed rows, then end B: each a contiguous vector (key side:
+      // plus -LSE / s, the score start of a column-clipped tile)
+      const float nl = DIR == 1 ? pnl : 0.f;
+      if (tid < BOTH) {
+        ovec_s[tid] = pov[0] + nl;
+        ovec_s[BOTH + tid] = pov[1] + nl;
       }
     }
     // row side staged now when there is no column side
@@ -532,7 +554,19 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     f32x16 sc[2];
     Op<NP> yop[2][4];
     if (!wave_none) {
-      if constexpr (MECH == MECH_TXL && DIR == 0) {
+      if constexpr (KINIT) {
+        // key side: the scores start from -LSE / s of each streamed query (plus the streamed
+        // row's end-row constant on a column-clipped tile, or the ALiBi ramp on a one-sided
+        // tile), so that P = exp2(c S + c lconst) takes one fma per element
+        const float* iv = lsd_s;
+        if constexpr (V::CLIP && V::HAS_COL) {
+          if (ccls != 0) iv = ovec_s + (ccls == 1 ? 0 : BOTH);
+        }
+        if constexpr (MECH == MECH_ALIBI) {
+          if (acls != 0) iv = ainit_s + (acls == 1 ? BOTH : 0);
+        }
+        other_dot_lane<NP, true>(sc, ys, xop, yop, iv);
+      } else if constexpr (MECH == MECH_TXL && DIR == 0) {
         // T-XL query side: the scores start from u.k of each streamed key
         other_dot_lane<NP, true>(sc, ys, xop, yop, ovec_s);
       } else if constexpr (V::CLIP && V::HAS_COL) {
@@ -616,18 +650,26 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       // query-side pass: dP first, its MFMAs run while the exponentials below are computed
       Op<NP> y2op[2][4];
       f32x16 dp[2];
-      if constexpr (DIR == 0) other_dot_lane<NP>(dp, y2s, x2op, y2op);
-      // ---- P ----  (key-side pass: LSE of the streamed queries, 4 rows per read)
+      // dP starts from -D (the lane's on the query side, the streamed row's on the key side)
+      if constexpr (DIR == 0) other_dot_lane_from<NP>(dp, y2s, x2op, y2op, -dsum_l);
+      // ---- P ----  (the key-side scores already hold -LSE / s, except in the T-XL pass)
+      const float pbias = DIR == 0 ? lconst * c - lse2 : lconst * c;
+      if constexpr (DIR == 1 && !KINIT) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 l4 = {lse2, lse2, lse2, lse2};
-          if constexpr (DIR == 1) l4 = *(const f32x4*)(lsd_s + 32 * b + 8 * g + 4 * kh);
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 l4 = *(const f32x4*)(lsd_s + 32 * b + 8 * g + 4 * kh);
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            sc[b][4 * g + i] = fast_exp2(fmaf(sc[b][4 * g + i], c, lconst * c - l4[i]));
-        }
+            for (int i = 0; i < 4; ++i)
+              sc[b][4 * g + i] = fast_exp2(fmaf(sc[b][4 * g + i], c, lconst * c - l4[i]));
+          }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sc[b][r] = fast_exp2(fmaf(sc[b][r], c, pbias));
+      }
       if (!wave_full) {
         const int wlx = sh.wl < 0 ? L : sh.wl, wrx = sh.wr < 0 ? L : sh.wr;
 #pragma unroll
@@ -640,17 +682,24 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             sc[b][r] = pair_ok(ii, jj, L, wlx, wrx) ? sc[b][r] : 0.f;
           }
       }
-      if constexpr (DIR == 1) other_dot_lane<NP>(dp, y2s, x2op, y2op);
-      // ---- dS ----
+      if constexpr (KINIT) other_dot_lane<NP, true>(dp, y2s, x2op, y2op, lsd_s + BOTH);
+      else if constexpr (DIR == 1) other_dot_lane<NP>(dp, y2s, x2op, y2op);
+      // ---- dS = P (dP - D) ----
+      if constexpr (DIR == 1 && !KINIT) {
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 d4 = {dsum_l, dsum_l, dsum_l, dsum_l};
-          if constexpr (DIR == 1) d4 = *(const f32x4*)(lsd_s + BOTH + 32 * b + 8 * g + 4 * kh);
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 d4 = *(const f32x4*)(lsd_s + BOTH + 32 * b + 8 * g + 4 * kh);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ds[b][4 * g + i] = sc[b][4 * g + i] * (dp[b][4 * g + i] - d4[i]);
-        }
+            for (int i = 0; i < 4; ++i) ds[b][4 * g + i] = sc[b][4 * g + i] * (dp[b][4 * g + i] - d4[i]);
+          }
+      } else {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ds[b][r] = sc[b][r] * dp[b][r];
+      }
       if constexpr (MECH == MECH_TXL && DIR == 1) {
 #pragma unroll
         for (int b = 0; b < 2; ++b)

@@ -43,6 +43,7 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   const int l32 = lane & 31, kh = lane >> 5;
   const int qw0 = i0 + WROWS * w;
   const int my_i = qw0 + l32;
+  const bool lane_valid = my_i < L;   // rows past L are padding (no allowed key)
 
   const int64_t bh_off = (int64_t)bh * L * kHeadDim;
   const T* qg = (const T*)a.q + bh_off;
@@ -306,43 +307,61 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     }
 
     // ---- online softmax ----
-    // The rescale of O and l is skipped when no row of the wave raised its running max (the
-    // factor would be exactly 1), which is the common case after the first tiles.  The
-    // running max stays exact, so the largest weight of every row is exactly 1.
-    float mx = kNegInf;
+    // The weights are formed against the row's running reference m_run (y units): a tile whose
+    // scores stay below m_run + 12 / c keeps every weight below 2^12, and the sums and the O
+    // accumulator stay exact in fp32 without a rescale, so neither the tile's row maximum nor a
+    // rescale is needed.  Only when a row of the wave has no reference yet (its first allowed
+    // keys) or a lane's weights sum past 2^12 (the scores grew; inf included) does the wave take
+    // the exact path: row maxima, the rescale of O and l by exp2((m_old - m_new) c), and the
+    // weights again.  The normalisation O = acc / l and LSE = s m_run + ln l are exact for any
+    // reference, so both paths give the same softmax up to rounding.
+    Op<NP> pop[4];
+    float psum = 0.f;
+    auto weights = [&](float m_ref) {
+      const float m_use = (m_ref == kNegInf) ? 0.f : m_ref;
+      const float bias = (rowconst - m_use) * c;
+      float ps = 0.f;
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+      for (int cc = 0; cc < 4; ++cc) {
+        float x[8];
+        const f32x16& v = sc[cc >> 1];
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) mx = max3f(mx, sc[b][r], sc[b][r + 1]);
-    mx = max3f(mx, xhalf(mx), kNegInf);
-    mx += rowconst;
-    const bool raise = mx > m_run;
-    if (__any(raise)) {
+        for (int i = 0; i < 8; ++i) {
+          x[i] = fast_exp2(fmaf(v[8 * (cc & 1) + i], c, bias));
+          if constexpr (NP == 2) ps += x[i];
+        }
+        pop[cc] = op_from_f32<NP>(x);
+      }
+      // bf16: the denominator sums exactly the rounded weights that multiply V
+      if constexpr (NP == 1) {
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) ps = sum_bf16x8(pop[cc].p[0], ps);
+      }
+      return ps;
+    };
+    // ALiBi's scores climb toward the diagonal by m per key, so most tiles before it would
+    // cross the bound: it takes the exact path on every tile.
+    bool exact = (MECH == MECH_ALIBI) || __any(lane_valid && m_run == kNegInf);
+    if (!exact) {
+      psum = weights(m_run);
+      exact = __any(!(psum <= 4096.f));
+    }
+    if (exact) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = max3f(mx, sc[b][r], sc[b][r + 1]);
+      mx = max3f(mx, xhalf(mx), kNegInf);
+      mx += rowconst;
+      const bool raise = mx > m_run;
       const float m_new = raise ? mx : m_run;
       const float alpha = raise ? fast_exp2((m_run - m_new) * c) : 1.f;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 2; ++db) oacc[db] *= alpha;
       m_run = m_new;
-    }
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    const float bias = (rowconst - m_use) * c;
-    float psum = 0.f;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(fmaf(sc[b][r], c, bias));
-        sc[b][r] = p;
-        if constexpr (NP == 2) psum += p;
-      }
-    Op<NP> pop[4];
-#pragma unroll
-    for (int cc = 0; cc < 4; ++cc) pop[cc] = op_from_acc<NP>(sc, cc);
-    // bf16: the denominator sums exactly the rounded weights that multiply V
-    if constexpr (NP == 1) {
-#pragma unroll
-      for (int cc = 0; cc < 4; ++cc) psum = sum_bf16x8(pop[cc].p[0], psum);
+      psum = weights(m_run);
     }
     l_run += psum;
 

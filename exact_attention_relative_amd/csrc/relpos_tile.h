@@ -76,8 +76,16 @@ template <typename T>
 struct TilePrefetch {
   static constexpr int NCH = sizeof(T) == 2 ? 2 : 4;   // 16-byte chunks per thread
   u32x4 v[NCH];
+  // Rows at or past nvalid (>= 1) repeat row nvalid - 1 instead of reading zeros: the attention
+  // kernels mask every pair of such a row (its scores are -inf, its weights and dS exactly 0),
+  // and a finite row times a zero weight adds nothing.  Loading unconditionally keeps the
+  // registers free of a zero-fill branch.
   __device__ __forceinline__ void load(const T* base, int row0, int nvalid) {
-    load_range(base, row0, 0, nvalid);
+    const int t = threadIdx.x;
+    const int row = min(row0 + (t >> 2), nvalid - 1), c = (t & 3) * 16;
+    const u32x4* g = (const u32x4*)stage_addr(base, (int64_t)row * kHeadDim + c);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) v[i] = g[i];
   }
   // rows row0 .. row0 + 63 of base, zero outside [lo, hi)
   __device__ __forceinline__ void load_range(const T* base, int row0, int lo, int hi) {
@@ -190,6 +198,25 @@ __device__ __forceinline__ void other_dot_lane(f32x16 acc[2], const uint16_t* yt
         for (int i = 0; i < 4; ++i) acc[b][4 * q4 + i] = v4[i];
       }
     }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      yop[b][c] = op_from_lds<NP>(ytile, BOTH * TSTR, (32 * b + l32) * TSTR + 16 * c + 8 * kh);
+      mma<NP>(acc[b], yop[b][c], xop[c]);
+    }
+  }
+}
+
+// The same product with every accumulator starting from one per-lane value (a lane-row term).
+template <int NP>
+__device__ __forceinline__ void other_dot_lane_from(f32x16 acc[2], const uint16_t* ytile,
+                                                    const Op<NP> xop[4], Op<NP> yop[2][4],
+                                                    float init) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[b][r] = init;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       yop[b][c] = op_from_lds<NP>(ytile, BOTH * TSTR, (32 * b + l32) * TSTR + 16 * c + 8 * kh);

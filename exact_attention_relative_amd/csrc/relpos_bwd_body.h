@@ -78,31 +78,6 @@ struct BV {
   __device__ static int rowB(int span) { return MECH == MECH_SHAW ? 0 : 2 * span - 1; }
 };
 
-// Zero the slots of an op_rows_tr operand (row t; slot j < 4 is column ybase + 4 kh + j, slot
-// 4 + j column ybase + 8 + 4 kh + j) outside the band y <= t <= y + 127, in every plane.
-template <int NP>
-__device__ __forceinline__ void band_mask(Op<NP>& o, int t, int ybase) {
-  // recomputed where used: hoisted out of the step loop, the masks would hold registers
-  asm volatile("" : "+v"(t));
-  const int kh = __lane_id() >> 5;
-  uint32_t m[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s0 = 2 * i, s1 = 2 * i + 1;
-    const int y0 = ybase + (s0 < 4 ? 4 * kh + s0 : 8 + 4 * kh + s0 - 4);
-    const int y1 = ybase + (s1 < 4 ? 4 * kh + s1 : 8 + 4 * kh + s1 - 4);
-    m[i] = ((unsigned)(t - y0) <= 127u ? 0x0000FFFFu : 0u) |
-           ((unsigned)(t - y1) <= 127u ? 0xFFFF0000u : 0u);
-  }
-#pragma unroll
-  for (int pl = 0; pl < NP; ++pl) {
-    u32x4 v = __builtin_bit_cast(u32x4, o.p[pl]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] &= m[i];
-    o.p[pl] = u4_to_bf8(v);
-  }
-}
-
 // ----------------------------------------------------------------------------- kernel
 // T is the element type of the inputs (uint16_t = bf16 bits, or float); fp32 operands enter the
 // matrix cores as NP = 2 bf16 planes (hi, lo), with every LDS tile holding both planes.
@@ -844,6 +819,18 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           for (int pl = 0; pl < NP; ++pl) dso[cc].p[pl] = u4_to_bf8(z);
       }
       __syncthreads();   // every wave's column-skew reads are done
+      // The band covers t in [y, y + 127] of row y; every other entry of the 192 columns the
+      // GEMM reads must be zero.  The rows are cleared whole (six 16-byte stores per thread and
+      // plane) before the band is written, so the GEMM's edge chunks need no per-element masks.
+      {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        uint16_t* zr = e2t + (tid >> 2) * ESTRT + 48 * (tid & 3);
+#pragma unroll
+        for (int pl = 0; pl < NP; ++pl)
+#pragma unroll
+          for (int q = 0; q < 6; ++q) *(u32x4*)(zr + pl * BOTH * ESTRT + 8 * q) = z;
+      }
+      __syncthreads();
       uint16_t* eb = e2t + (127 - (WROWS * w + l32) + 4 * kh) + 4 * kh * ESTRT;
 #pragma unroll
       for (int pl = 0; pl < NP; ++pl)
@@ -870,7 +857,6 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           const int ylo = 16 * cq, yhi = ylo + 15;
           if (thi < ylo || tlo > yhi + 127) continue;   // no pair of this block and chunk
           Op<NP> eop = op_rows_tr<NP>(e2t, BOTH * ESTRT, ESTRT, ylo, tlo);
-          if (!(tlo >= yhi && thi <= ylo + 127)) band_mask<NP>(eop, tlo + l32, ylo);
           Op<NP> qop2 = op_rows_tr<NP>(ys, BOTH * TSTR, TSTR, ylo, 32 * gdb);
           mma<NP>(racc[i], eop, qop2);
         }

@@ -339,6 +339,9 @@ def measured_mfma_peak(torch):
     return val.value
 
 
+PASS_REPS = 10   # repetitions behind each per-mechanism forward / backward median
+
+
 def time_kernel(torch, mechs, mech, kid, reps=50):
     evs = []
     for _ in range(reps):
@@ -614,10 +617,13 @@ def main():
         mech = m["mech"]
         for name, k in kid.items():
             kernel_ms[(mech, name)] = time_kernel(torch, mechs, mech, k)
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        ev[0].record(); run_fwd(m); ev[1].record(); run_bwd(m); ev[2].record()
+        # per-mechanism forward / backward: medians over PASS_REPS event-timed repetitions
+        evs3 = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(PASS_REPS)]
+        for ev in evs3:
+            ev[0].record(); run_fwd(m); ev[1].record(); run_bwd(m); ev[2].record()
         torch.cuda.synchronize()
-        tf, tb = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+        tf = float(np.median([ev[0].elapsed_time(ev[1]) for ev in evs3]))
+        tb = float(np.median([ev[1].elapsed_time(ev[2]) for ev in evs3]))
         fl = m["flops"]
         per_mech[mech].update({
             "fwd_ms": tf, "bwd_ms": tb,

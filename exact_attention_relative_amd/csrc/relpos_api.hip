@@ -14,6 +14,7 @@ using namespace relpos;
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int64_t kGroupWorkgroups = 512;   // one wave of workgroups: 2 per CU x 256 CUs
 size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -186,11 +187,16 @@ int make_plan(const relpos_desc* d, Plan* p) {
       rows_k = std::min<int64_t>(rows_k, wrows);
     }
     p->part_q_stride = rows_k * kHeadDim;
-    // the r partials of one group of slices must fit under the cap
-    const int64_t cap = d->max_partial_bytes > 0 ? d->max_partial_bytes : (int64_t)8 << 30;
+    // Slices per group of the key-side pass.  By default, as many as give one full wave of
+    // workgroups (two per compute unit on the 256 compute units of an MI355X): the launch keeps
+    // the chip busy while the partials hold the fewest slices.  A caller's max_partial_bytes
+    // instead sizes the group by bytes.  At least one slice either way.
     const int64_t per_slice = (int64_t)p->nb * p->part_q_stride * (int64_t)sizeof(float);
     const int64_t nbh = (int64_t)p->B * p->H;
-    p->txl_group = (int)std::max<int64_t>(1, std::min<int64_t>(nbh, cap / std::max<int64_t>(per_slice, 1)));
+    const int64_t group = d->max_partial_bytes > 0
+                              ? d->max_partial_bytes / std::max<int64_t>(per_slice, 1)
+                              : kGroupWorkgroups / std::max<int64_t>(p->nb, 1);
+    p->txl_group = (int)std::max<int64_t>(1, std::min<int64_t>(nbh, group));
   }
   if (d->mech == RELPOS_TXL) {
     p->off_part_q = take(sizeof(float) * (size_t)p->txl_group * p->nb * p->part_q_stride);

@@ -96,11 +96,14 @@ typedef struct relpos_desc {
   int32_t max_distance;   /* T5: > num_buckets / 4 (bidirectional) or num_buckets / 2 */
   int32_t bidirectional;  /* T5: 1 = separate buckets for keys after the query */
   float scale;            /* 0 = default */
-  int64_t max_partial_bytes; /* T-XL backward: cap on the key-side r-partial workspace, which
-                                grows as L^2 / 2 bytes per (batch, head); the slices are then
-                                processed in fixed groups that fit under it (at least one slice
-                                per group).  0 = 8 GiB.  Results depend on the group size only
-                                through the (fixed) order of the fp32 sums. */
+  int64_t max_partial_bytes; /* T-XL backward: the key-side r partials take L^2 / 2 bytes per
+                                (batch, head) slice, so the key-side pass runs over fixed groups
+                                of slices, each group's partials summed into dr before the next
+                                reuses them.  0 = groups of as many slices as give 512 workgroups
+                                (one full wave on an MI355X; L = 8192: 8 slices, 1.1 GB);
+                                > 0 = as many slices as fit in this many bytes.  At least one
+                                slice per group.  Results depend on the group size only through
+                                the (fixed) order of the fp32 sums. */
   int64_t rel_head_stride;   /* elements between the relation tables (rel_a, rel_b) of
                                 consecutive heads: 0 = one table shared by every head; otherwise
                                 head h reads rel_a + h * rel_head_stride (and rel_b likewise),

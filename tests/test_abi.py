@@ -279,3 +279,19 @@ def test_profile_hook_calls_from_another_thread():
     t.start()
     t.join()
     assert res == [ear.RELPOS_OK]
+
+
+def test_txl_default_groups_fill_one_wave_of_workgroups():
+    """With no byte cap, the key-side pass groups as many slices as give 512 workgroups (two per
+    compute unit on 256 compute units), at least one slice, at most every slice."""
+    def group(B, H, L):
+        st, n = _ws(ear.make_desc("txl", B, H, L), 1)
+        st1, n1 = _ws(ear.make_desc("txl", B, H, L, max_partial_bytes=1), 1)   # one slice
+        nb = (L + 127) // 128
+        per_slice = nb * (L + 256) * 64 * 4
+        assert st == st1 == 0
+        return (n - n1) // per_slice + 1
+    assert group(4, 8, 8192) == 8          # 64 key blocks per slice -> 8 slices
+    assert group(1, 4, 32768) == 2         # 256 key blocks -> 2 slices
+    assert group(2, 3, 1000) == 6          # 8 key blocks -> 64 wanted, 6 exist
+    assert group(1, 2, 70000) == 1         # 547 key blocks, more than 512 -> one slice

@@ -93,10 +93,10 @@ def test_long_sequence(mech, L, H):
 
 
 def test_txl_32k_partials_processed_in_groups():
-    """Four heads at L = 32768 need 8.6 GB of key-side r partials, over the default 8 GiB cap:
-    the backward runs in two slice groups, its workspace and peak memory stay under the cap, and
-    heads 0 and 3 (one in each group) match the oracle in every output, their r, u and v
-    gradients included."""
+    """Four heads at L = 32768 would need 8.6 GB of key-side r partials at once: with 256 key
+    blocks per slice the default groups hold two slices (512 workgroups), so the backward runs
+    in two slice groups with about 4.3 GB of partials, and heads 0 and 3 (one in each group)
+    match the oracle in every output, their r, u and v gradients included."""
     import torch
     from exact_attention_relative_amd import runner, relpos_attn_workspace_size
     from exact_attention_relative_amd.inputs import make_case
@@ -108,9 +108,9 @@ def test_txl_32k_partials_processed_in_groups():
     per_slice = (L // 128) * (L + 256) * 64 * 4
     assert H * per_slice > 8 << 30
     ws = relpos_attn_workspace_size(desc, 1)
-    assert ws < 8 << 30 and ws >= 3 * per_slice
+    assert 2 * per_slice <= ws < 3 * per_slice
     o, lse, g, peak = _gpu(c)
-    assert peak < (8 << 30) + (1 << 30)
+    assert peak < 3 * per_slice + (1 << 30)
     _compare(c, o, lse, g, [(0, 0), (0, H - 1)])
     tg = {n: to_np(t) for n, t in runner.named_table_grads("txl", g).items()}
     check_row_sum_invariant("txl", c, o, tg)

@@ -111,11 +111,14 @@ def pass_of_kernel(name):
     m = _KNAME.search(name)
     if not m:
         return None
-    args = [a.strip() for a in m.group(2).split(",")]
+    # template arguments: element type, then the integers (mechanism[, direction, part])
+    args = [int(a) for a in (x.strip() for x in m.group(2).split(",")) if a.lstrip("-").isdigit()]
     inv = {v: k for k, v in MECH_ID.items()}
+    if args[0] not in inv:
+        return None
     if m.group(1) == "fwd":
-        return inv[int(args[-1])], "fwd"
-    return inv[int(args[0])], ("bwd_dq" if int(args[1]) == 0 else "bwd_dkdv")
+        return inv[args[0]], "fwd"
+    return inv[args[0]], ("bwd_dq" if args[1] == 0 else "bwd_dkdv")
 
 
 def _pmc_rows(path):

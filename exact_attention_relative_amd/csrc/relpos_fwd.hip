@@ -230,7 +230,12 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
       } else if constexpr (MECH == MECH_ALIBI) {
         // i >= j: -m (i - j0) / s + m (j - j0) / s; i < j: m (i - j0) / s - m (j - j0) / s
         if (cls != 0) other_dot_lane<NP, true>(sc, ks, qop, kop, kvec_s + (cls == 1 ? 0 : BOTH));
-        else other_dot_lane<NP>(sc, ks, qop, kop);
+        else other_dot_lane_offset<NP>(sc, ks, qop, kop, vec_s, WROWS * w);
+      } else if constexpr (MECH == MECH_T5) {
+        // a one-bucket wave tile adds its bias as a row constant; others start the
+        // accumulators from the per-offset bias
+        if (cls == 1) other_dot_lane<NP>(sc, ks, qop, kop);
+        else other_dot_lane_offset<NP>(sc, ks, qop, kop, vec_s, WROWS * w);
       } else {
         other_dot_lane<NP>(sc, ks, qop, kop);
       }
@@ -238,18 +243,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
     float rowconst = 0.f;
     // ---- relative terms (row side) ----
     if constexpr (MECH == MECH_T5) {
-      if (!wave_none) {
-        if (cls == 1) {
-          rowconst = vec_s[dlo_c - wg_dlo];
-        } else {
-          add_offset_vec(sc, vec_s, WROWS * w);
-        }
-      }
+      if (!wave_none && cls == 1) rowconst = vec_s[dlo_c - wg_dlo];
     } else if constexpr (MECH == MECH_ALIBI) {
       if (!wave_none) {
         if (cls == 1) rowconst = -am * (float)(my_i - j0);
         else if (cls == 2) rowconst = am * (float)(my_i - j0);
-        else add_offset_vec(sc, vec_s, WROWS * w);
       }
     } else if constexpr (MECH == MECH_SHAW) {
       if (!wave_none) {

@@ -206,6 +206,29 @@ __device__ __forceinline__ void other_dot_lane(f32x16 acc[2], const uint16_t* yt
   }
 }
 
+// The same product with the accumulators starting from an LDS vector indexed by the lane-side
+// window t = n - y + 63 + w0 (a per-offset additive term, added before the products).
+template <int NP>
+__device__ __forceinline__ void other_dot_lane_offset(f32x16 acc[2], const uint16_t* ytile,
+                                                      const Op<NP> xop[4], Op<NP> yop[2][4],
+                                                      const float* vec, int w0) {
+  const int lane = __lane_id();
+  const int l32 = lane & 31, kh = lane >> 5;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int y = 32 * b + 8 * (r >> 2) + 4 * kh + (r & 3);
+      acc[b][r] = vec[w0 + l32 - y + 63];
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      yop[b][c] = op_from_lds<NP>(ytile, BOTH * TSTR, (32 * b + l32) * TSTR + 16 * c + 8 * kh);
+      mma<NP>(acc[b], yop[b][c], xop[c]);
+    }
+  }
+}
+
 // The same product with every accumulator starting from one per-lane value (a lane-row term).
 template <int NP>
 __device__ __forceinline__ void other_dot_lane_from(f32x16 acc[2], const uint16_t* ytile,

@@ -243,32 +243,6 @@ __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict
   }
 }
 
-// Fixed-order block reduction helper (256 threads).
-__device__ __forceinline__ float block_sum(float v, float* sh) {
-  sh[threadIdx.x] = v;
-  __syncthreads();
-  for (int st = 128; st > 0; st >>= 1) {
-    if ((int)threadIdx.x < st) sh[threadIdx.x] += sh[threadIdx.x + st];
-    __syncthreads();
-  }
-  float r = sh[0];
-  __syncthreads();
-  return r;
-}
-
-// T5 dbeta[h][c] = sum over offsets with bucket c of diag_h[delta]
-__global__ void agg_t5_kernel(const float* __restrict__ diag, const int* __restrict__ bucket, int L,
-                              int nbk, float* __restrict__ dbeta) {
-  __shared__ float sh[256];
-  const int h = blockIdx.x / nbk, cb = blockIdx.x % nbk;
-  const int n = 2 * L - 1;
-  float acc = 0.f;
-  for (int x = threadIdx.x; x < n; x += 256)
-    if (bucket[x] == cb) acc += diag[(int64_t)h * n + x];
-  const float tot = block_sum(acc, sh);
-  if (threadIdx.x == 0) dbeta[blockIdx.x] = tot;
-}
-
 // T-XL dv[h][d] = s sum_delta diag_h[delta] r_h[row(delta)][d]
 template <typename T>
 __global__ __launch_bounds__(1024) void agg_txl_dv_kernel(const float* __restrict__ diag,
@@ -375,12 +349,6 @@ hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool
 
 hipError_t launch_agg_alibi(const float* part, int B, int H, int nb, float* dm, hipStream_t st) {
   hipLaunchKernelGGL(agg_alibi_kernel, dim3(nblk(H, 64)), dim3(64), 0, st, part, B, H, nb, dm);
-  return hipGetLastError();
-}
-
-hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int nbk, float* dbeta,
-                         hipStream_t st) {
-  hipLaunchKernelGGL(agg_t5_kernel, dim3(H * nbk), dim3(256), 0, st, diag, bucket, L, nbk, dbeta);
   return hipGetLastError();
 }
 

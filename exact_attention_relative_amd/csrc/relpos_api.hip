@@ -113,7 +113,7 @@ int make_plan(const relpos_desc* d, Plan* p) {
   const int L = p->L;
   switch (d->mech) {
     case RELPOS_T5: {
-      if (d->num_buckets < 2 || d->num_buckets > 256) return RELPOS_E_INVALID;
+      if (d->num_buckets < 2 || d->num_buckets > kMaxBuckets) return RELPOS_E_INVALID;
       if (d->bidirectional && (d->num_buckets % 2 != 0 || d->num_buckets < 4)) return RELPOS_E_INVALID;
       const int half = d->bidirectional ? d->num_buckets / 2 : d->num_buckets;
       if (half / 2 < 1 || d->max_distance <= half / 2) return RELPOS_E_INVALID;
@@ -204,11 +204,14 @@ int make_plan(const relpos_desc* d, Plan* p) {
     p->off_part_q = take(sizeof(float) * own * p->part_q_stride);
   }
   if (p->part_k_stride) p->off_part_k = take(sizeof(float) * own * p->part_k_stride);
-  if (lut_path || d->mech == RELPOS_TXL) {
-    // T5 / T-XL: per-offset sums, one partial row per wave of each query-side owner
+  if (d->mech == RELPOS_TXL) {
+    // T-XL: per-offset sums, one partial row per wave of each query-side owner
     p->off_part_qv = take(sizeof(float) * own * diag_width(L, d->window_left, d->window_right) * 4);
     p->off_diag = take(sizeof(float) * (size_t)p->H * (L > 0 ? 2 * L - 1 : 1));
   }
+  // T5: the bucket sums of each query-side owner; ALiBi: one slope sum per owner
+  if (d->mech == RELPOS_T5) p->off_part_qv = take(sizeof(float) * own * d->num_buckets);
+  if (d->mech == RELPOS_ALIBI) p->off_part_qv = take(sizeof(float) * own);
   if (d->mech == RELPOS_TXL) p->off_part_kv = take(sizeof(float) * own * kHeadDim);
   if (d->mech == RELPOS_SHAW || d->mech == RELPOS_DEBERTA) {
     // split passes: clipped-step partials handed from the light kernel to the general one
@@ -280,6 +283,7 @@ AttnShape make_shape(const relpos_desc* d, const Plan& p) {
   s.txl_off = p.txl_off;
   s.scale = p.scale;
   s.rel_hs = p.rel_hs;
+  s.nbk = d->mech == RELPOS_T5 ? d->num_buckets : 0;
   return s;
 }
 
@@ -539,8 +543,9 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
 
   switch (desc->mech) {
     case RELPOS_T5:
-      e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, desc->window_left, desc->window_right, diag, s);
-      if (e == hipSuccess) e = launch_agg_t5(diag, a.bucket, p.H, p.L, desc->num_buckets, dbias_a, s);
+      // dbeta[h][k]: the bucket sums of head h's owners, in ascending (batch, block) order
+      e = launch_agg_rows_by_head(a.part_qv, desc->num_buckets, p.B, p.H, p.nb, desc->num_buckets,
+                                  1.0f, dbias_a, s);
       break;
     case RELPOS_ALIBI:
       e = launch_agg_alibi(a.part_qv, p.B, p.H, p.nb, dbias_a, s);

@@ -49,6 +49,8 @@ struct BV {
   static constexpr bool TXL = MECH == MECH_TXL;
   static constexpr bool CLIP = MECH == MECH_SHAW || MECH == MECH_DEBERTA;
   static constexpr bool DIAG = DIR == 0 && (MECH == MECH_T5 || MECH == MECH_TXL);
+  // T5: the per-offset sums go straight into per-bucket sums of the workgroup
+  static constexpr bool T5BIN = DIAG && MECH == MECH_T5;
   // General pass of Shaw / DeBERTa: the row-side dX_rel from the wave's dS buffer and the
   // column-side table gradient over the streamed rows (no workgroup band buffer, so two
   // workgroups fit per CU); a table's interior rows come from the pass where it is the column
@@ -104,6 +106,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
                             ? BOTH
                             : ((V::CLIP && V::HAS_COL && !V::DFAT) || MECH == MECH_ALIBI ? 2 * BOTH : 4);
   __shared__ float red_s[MECH == MECH_ALIBI ? NWAVE : 1];   // ALiBi: per-wave slope-gradient sums
+  __shared__ float bins_s[V::T5BIN ? NWAVE * kMaxBuckets : 1];   // T5: per-wave bucket sums of dS
   __shared__ __attribute__((aligned(16))) float ovec_s[NOVEC];   // per-other-row constants
   // key side: -LSE / s and -D of the streamed queries, the starts of the score and dP
   // accumulators (y units; -inf for rows past L or with no allowed key; see lsd_vals)
@@ -230,11 +233,17 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int rb = (sh.wl >= 0 && sh.wr >= 0) ? bt0 + 65 : 0;
   // (slots of the r partial count from the launch's first slice)
   if constexpr (V::TK) ptg = a.part_q + (int64_t)bid * a.part_q_stride - (int64_t)rb * kHeadDim;
-  // per-offset dS sums: one partial row of ndg floats per wave (lane offset lam at index
+  // T-XL per-offset dS sums: one partial row of ndg floats per wave (lane offset lam at index
   // lam - (lam_base + 32 w) - dxo), in the owner's slot of NWAVE rows
   const int ndg = diag_width(L, sh.wl, sh.wr), dxo = diag_xoff(L, sh.wl, sh.wr, A0);
   float* pdiag = nullptr;
-  if constexpr (V::DIAG) pdiag = a.part_qv + owner * (int64_t)(NWAVE * ndg);
+  if constexpr (V::DIAG && !V::T5BIN) pdiag = a.part_qv + owner * (int64_t)(NWAVE * ndg);
+  // T5: each wave sums dS per bucket in its own LDS row; the workgroup's sums (nbk floats)
+  // go to the owner's slot at the end
+  float* const binw = bins_s + (V::T5BIN ? w * kMaxBuckets : 0);
+  if constexpr (V::T5BIN) {
+    for (int e = tid; e < NWAVE * kMaxBuckets; e += 256) bins_s[e] = 0.f;   // (first barrier below)
+  }
 
   // ---- zero what the sweep will not write ----
   if constexpr (V::DFAT && V::HAS_COL) {
@@ -254,7 +263,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       if (!(nsteps > 0 && row >= bt0 + 65 && row <= bt_last + 256)) ptg[(int64_t)rb * kHeadDim + e] = 0.f;
     }
   }
-  if constexpr (V::DIAG) {
+  if constexpr (V::DIAG && !V::T5BIN) {
     // wave ww writes the offsets [A0 + 32 ww - bt_last - 63, A0 + 32 ww - bt0 + 32]
     for (int e = tid; e < NWAVE * ndg; e += 256) {
       const int ww = e / ndg, lam = lam_base + 32 * ww + dxo + (e - ww * ndg);
@@ -422,10 +431,11 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       const int wlo = DIR == 0 ? cwin - 63 : -(cwin + 127), whi = DIR == 0 ? cwin + 127 : -(cwin - 63);
       lut_needed = wlo < 0 && whi >= 0;
     }
-    int t5cls = 0;
+    int t5cls = 0, t5b = 0;   // T5: one bucket for the whole wave tile, and which
     if constexpr (MECH == MECH_T5) {
       const int lo = clampi(dlo, 1 - L, L - 1), hi = clampi(dhi, 1 - L, L - 1);
-      if ((lo >= 0 || hi < 0) && a.bucket[lo + L - 1] == a.bucket[hi + L - 1]) t5cls = 1;
+      t5b = a.bucket[lo + L - 1];
+      if ((lo >= 0 || hi < 0) && t5b == a.bucket[hi + L - 1]) t5cls = 1;
     }
 
     // ---- stage ----
@@ -961,18 +971,55 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           for (int m = 1; m < 32; m <<= 1) tot += __shfl_xor(tot, m);
         }
         sums[0] = (lane == 63) ? tot : 0.f;
+        if constexpr (V::T5BIN) {
+          if (!wave_none && lane == 0) binw[t5b] += tot;
+        }
       }
-      // Diagonal t of this step is diagonal t + 64 of the next for t < 32: lanes 0..31 carry
-      // sums[0] into their next sums[1]; the wave's 64 offsets t = 32 .. 95 are final (lane
-      // 32 + i: t = 32 + i from sums[0]; lane i: t = 64 + i from sums[1] and the carry), and
-      // after the last step also t = 0 .. 31.  No workgroup barrier: each wave writes its own
-      // partial.
-      const float fin = (lane >= 32) ? sums[0] : sums[1] + dcarry;
-      dcarry = (lane < 32) ? sums[0] : 0.f;
-      float* pw = pdiag + w * ndg + (aw0 - b0 - 63) - (lam_base + 32 * w) - dxo;
-      pw[(lane >= 32) ? lane : 64 + lane] = fin;
-      if (step == nsteps - 1 && lane < 32) pw[lane] = dcarry;
+      if constexpr (V::T5BIN) {
+        // Multi-bucket tile: the diagonal sums join their buckets' sums.  Diagonal t holds
+        // offset i - j = aw0 - b0 - 63 + t, and every bucket is one run of consecutive offsets
+        // (the bucket grows with |i - j| on each side of the diagonal), so a segmented scan
+        // over the lanes in a fixed order sums each run and the run's last lane adds it.
+        if (!wave_none && !single) {
+          const int dbase = aw0 - b0 - 63;
+#pragma unroll
+          for (int half = 0; half < 2; ++half) {
+            const int t = lane + 64 * half;
+            const bool valid = t < 96;   // (offsets past the sequence hold dS = 0)
+            const int bk = valid ? a.bucket[clampi(dbase + t, 1 - L, L - 1) + L - 1] : -1;
+            float x = valid ? sums[half] : 0.f;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+              const float xu = __shfl_up(x, o);
+              const int bu = __shfl_up(bk, o);
+              if (lane >= o && bu == bk) x += xu;
+            }
+            const int bn = __shfl_down(bk, 1);
+            if (valid && (lane == 63 || bn != bk)) binw[bk] += x;
+          }
+        }
+      } else {
+        // Diagonal t of this step is diagonal t + 64 of the next for t < 32: lanes 0..31 carry
+        // sums[0] into their next sums[1]; the wave's 64 offsets t = 32 .. 95 are final (lane
+        // 32 + i: t = 32 + i from sums[0]; lane i: t = 64 + i from sums[1] and the carry), and
+        // after the last step also t = 0 .. 31.  No workgroup barrier: each wave writes its own
+        // partial.
+        const float fin = (lane >= 32) ? sums[0] : sums[1] + dcarry;
+        dcarry = (lane < 32) ? sums[0] : 0.f;
+        float* pw = pdiag + w * ndg + (aw0 - b0 - 63) - (lam_base + 32 * w) - dxo;
+        pw[(lane >= 32) ? lane : 64 + lane] = fin;
+        if (step == nsteps - 1 && lane < 32) pw[lane] = dcarry;
+      }
     }
+  }
+
+  // ---- T5: this workgroup's bucket sums of dS, the waves in a fixed order ----
+  if constexpr (V::T5BIN) {
+    __syncthreads();
+    const int nbk = sh.nbk;
+    for (int k = tid; k < nbk; k += 256)
+      a.part_qv[owner * nbk + k] = (bins_s[k] + bins_s[kMaxBuckets + k]) +
+                                   (bins_s[2 * kMaxBuckets + k] + bins_s[3 * kMaxBuckets + k]);
   }
 
   // ---- ALiBi: this workgroup's share of sum dS |i - j|, in a fixed order ----

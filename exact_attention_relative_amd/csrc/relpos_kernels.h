@@ -9,12 +9,13 @@
 namespace relpos {
 
 enum { MECH_T5 = 0, MECH_SHAW = 1, MECH_TXL = 2, MECH_DEBERTA = 3 };
-// ALiBi runs the attention kernels' T5 path (a per-offset LUT); only the preparation and
-// aggregation kernels see this value.
+// ALiBi: a per-offset LUT like T5, with kernels of its own (its ramps replace the LUT on the
+// tiles that lie on one side of the diagonal).
 constexpr int MECH_ALIBI = 4;
 
 constexpr int kHeadDim = 64;
 constexpr int kMaxThresholds = 64;
+constexpr int kMaxBuckets = 256;   // T5 buckets per head
 
 // Per-offset dS partials of the query-side pass (T5, T-XL): one row of diag_width floats per
 // wave of each 128-row block.  A full sweep keeps every offset: wave w of the block at A0 stores
@@ -53,6 +54,7 @@ struct AttnShape {
   int txl_off;      // T-XL row = delta + txl_off
   float scale;      // s
   int64_t rel_hs;   // elements between the relation tables of consecutive heads (0 = shared)
+  int nbk;          // T5 buckets per head (else 0)
 };
 
 struct FwdArgs {
@@ -98,7 +100,8 @@ struct BwdArgs {
   void* dv;
   float* part_q;       // query-side partials (dQ pass)
   float* part_k;       // key-side partials (dK/dV pass)
-  float* part_qv;      // query-side per-owner small vectors (T-XL dv, clipped sums)
+  float* part_qv;      // query-side per-owner small vectors (T5 bucket sums, T-XL diagonal
+                       // sums, ALiBi slope sums)
   float* part_kv;      // key-side per-owner small vectors (T-XL du)
   int64_t part_q_stride;  // floats per owner
   int64_t part_k_stride;
@@ -149,8 +152,6 @@ hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool
                            int wr, float* diag, hipStream_t st);
 // ALiBi dm[h] = -sum over the owners (b, query block) of head h of part[owner] (fixed order)
 hipError_t launch_agg_alibi(const float* part, int B, int H, int nb, float* dm, hipStream_t st);
-hipError_t launch_agg_t5(const float* diag, const int* bucket, int H, int L, int nbk, float* dbeta,
-                         hipStream_t st);
 // T-XL dr from the key-side r partials of the slice group [s0, s0 + ns) (partial slot of slice
 // s0 + i, key block p: i nb + p), summed in ascending (slice, block) order.  Groups are added in
 // order: the first overwrites dr, later ones add to it; dr holds raw sums until the last group,

@@ -117,22 +117,35 @@ def test_txl_partial_cap_groups_slices():
         assert st == 0 and n == full - (6 - group) * per_slice, (cap, group)
 
 
-def test_t5_offset_partials_shrink_under_two_sided_window():
-    """The query-side pass keeps one row of per-offset dS sums per wave (four per 128-row block):
-    L + 256 offsets for a full sweep, or, under a two-sided window, only the wave's own sweep
-    (wl + wr + 286 offsets, in whole 64-float steps) when that is fewer."""
+def _al(n):
+    return (n + 255) // 256 * 256
+
+
+def test_t5_bias_gradient_partials_are_bucket_sums():
+    """The T5 backward keeps, beyond the forward's tables, D (one float per row) and one row of
+    num_buckets sums per 128-row query block: linear in L, the same under any window."""
     B, H, L = 2, 3, 1000
     owners = B * H * ((L + 127) // 128)
-    st, full = _ws(ear.make_desc("t5", B, H, L), 1)
+    for nbk in (8, 32, 256):
+        st, f = _ws(ear.make_desc("t5", B, H, L, num_buckets=nbk), 0)
+        assert st == 0
+        for window in ((-1, -1), (100, 37), (0, 0), (-1, 0)):
+            st, n = _ws(ear.make_desc("t5", B, H, L, num_buckets=nbk, window=window), 1)
+            assert st == 0 and n - f == _al(B * H * L * 4) + _al(owners * nbk * 4), (nbk, window)
+
+
+def test_txl_offset_partials_shrink_under_two_sided_window():
+    """The T-XL query-side pass keeps one row of per-offset dS sums per wave (four per 128-row
+    block): L + 256 offsets for a full sweep, or, under a two-sided window, only the wave's own
+    sweep (wl + wr + 286 offsets, in whole 64-float steps) when that is fewer.  Checked through
+    a window that leaves the key-side r partial at full height (wl + wr + 382 >= L + 256)."""
+    B, H, L = 2, 3, 1000
+    owners = B * H * ((L + 127) // 128)
+    st, full = _ws(ear.make_desc("txl", B, H, L), 1)
     assert st == 0
-    for (wl, wr), rows in (((100, 37), 448), ((0, 0), 320), ((600, 600), L + 256),
-                           ((2000, 2000), L + 256)):
-        st, n = _ws(ear.make_desc("t5", B, H, L, window=(wl, wr)), 1)
-        assert st == 0 and full - n == owners * 4 * (L + 256 - rows) * 4, (wl, wr)
-    # one-sided windows sweep to the sequence end: no compaction
-    for w in ((-1, 0), (50, -1)):
-        st, n = _ws(ear.make_desc("t5", B, H, L, window=w, bidirectional=True), 1)
-        assert st == 0 and n == full, w
+    for (wl, wr), rows in (((450, 450), 1216), ((600, 600), L + 256), ((2000, 2000), L + 256)):
+        st, n = _ws(ear.make_desc("txl", B, H, L, window=(wl, wr)), 1)
+        assert st == 0 and full - n == _al(owners * 4 * (L + 256) * 4) - _al(owners * 4 * rows * 4), (wl, wr)
 
 
 def test_fwd_rejects_bad_pointers_without_launching():

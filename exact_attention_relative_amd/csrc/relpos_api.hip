@@ -88,6 +88,8 @@ struct Plan {
   int64_t part_q_stride, part_k_stride;
   int nb, nrt, owners;
   int txl_group;   // T-XL key-side pass: (batch, head) slices per group
+  int fold;        // Shaw / DeBERTa general passes: batch entries per workgroup
+  int fold_owners; // their partial slots: ceil(B / fold) H nb
   int64_t rel_rows;   // rows of each relation table (0 for T5 / ALiBi)
   int64_t rel_hs;     // elements between the relation tables of consecutive heads (0 = shared)
   size_t fwd_bytes, bwd_bytes;
@@ -175,6 +177,19 @@ int make_plan(const relpos_desc* d, Plan* p) {
   p->nrt = L + 256;
   p->owners = p->B * p->H * p->nb;
   const size_t own = (size_t)p->owners;
+  // Shaw / DeBERTa general passes: a workgroup runs `fold` batch entries of one head in turn
+  // into one partial slot.  The fewest groups of batch entries that still give one full wave
+  // of workgroups (two per compute unit on 256 compute units); no folding below that.
+  p->fold = 1;
+  if (d->mech == RELPOS_SHAW || d->mech == RELPOS_DEBERTA) {
+    for (int ng = 1; ng <= p->B; ++ng) {
+      if ((int64_t)ng * p->H * p->nb >= kGroupWorkgroups) {
+        p->fold = (p->B + ng - 1) / ng;
+        break;
+      }
+    }
+  }
+  p->fold_owners = (p->B + p->fold - 1) / p->fold * p->H * p->nb;
   const int k = d->rel_span;
   if (d->mech == RELPOS_SHAW) p->part_q_stride = (int64_t)(2 * k + 1) * kHeadDim;
   if (d->mech == RELPOS_DEBERTA) p->part_q_stride = p->part_k_stride = (int64_t)(2 * k) * kHeadDim;
@@ -201,9 +216,9 @@ int make_plan(const relpos_desc* d, Plan* p) {
   if (d->mech == RELPOS_TXL) {
     p->off_part_q = take(sizeof(float) * (size_t)p->txl_group * p->nb * p->part_q_stride);
   } else if (p->part_q_stride) {
-    p->off_part_q = take(sizeof(float) * own * p->part_q_stride);
+    p->off_part_q = take(sizeof(float) * (size_t)p->fold_owners * p->part_q_stride);
   }
-  if (p->part_k_stride) p->off_part_k = take(sizeof(float) * own * p->part_k_stride);
+  if (p->part_k_stride) p->off_part_k = take(sizeof(float) * (size_t)p->fold_owners * p->part_k_stride);
   if (d->mech == RELPOS_TXL) {
     // T-XL: per-offset sums, one partial row per wave of each query-side owner
     p->off_part_qv = take(sizeof(float) * own * diag_width(L, d->window_left, d->window_right) * 4);
@@ -493,6 +508,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
   a.dsum = (const float*)(ws + p.off_dsum);
   a.rel_a = rel_a; a.rel_b = rel_b;
   a.bias_a = bias_a; a.bias_b = bias_b;
+  a.fold = p.fold;
   if (desc->mech == RELPOS_T5 || desc->mech == RELPOS_ALIBI) {
     a.lut = (const float*)(ws + p.off_lut);
     a.bucket = (const int*)(ws + p.off_bucket);
@@ -552,11 +568,13 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
       break;
     case RELPOS_SHAW:
     case RELPOS_DEBERTA: {
-      // one shared table sums every owner; per-head tables sum the owners of their head
+      // one shared table sums every slot; per-head tables sum the slots of their head (slot
+      // (g H + h) nb + p for batch group g)
       auto agg = [&](const float* part, int64_t stride, float* out) {
+        const int ng = (p.B + p.fold - 1) / p.fold;
         return p.rel_hs == 0
-                   ? launch_agg_rows(part, stride, p.owners, stride, p.scale, out, s)
-                   : launch_agg_rows_by_head(part, stride, p.B, p.H, p.nb, stride, p.scale, out, s);
+                   ? launch_agg_rows(part, stride, p.fold_owners, stride, p.scale, out, s)
+                   : launch_agg_rows_by_head(part, stride, ng, p.H, p.nb, stride, p.scale, out, s);
       };
       e = agg(a.part_q, p.part_q_stride, drel_a);
       if (e == hipSuccess && desc->mech == RELPOS_DEBERTA) e = agg(a.part_k, p.part_k_stride, drel_b);

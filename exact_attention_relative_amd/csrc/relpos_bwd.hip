@@ -40,7 +40,14 @@ template <int MECH, int DIR>
 static void launch_one(const BwdArgs& a, bool fp32, dim3 grid, hipStream_t stream) {
   if constexpr (split_pass<MECH>()) {
     launch_part<MECH, DIR, 1>(a, fp32, grid, stream);
-    launch_part<MECH, DIR, 2>(a, fp32, grid, stream);
+    // general pass: a.fold launches, each with one workgroup per (group of a.fold batch entries,
+    // head, block) taking the group's next entry (same-stream order: each launch adds to the
+    // partial slots the previous one wrote)
+    const int nb = (a.sh.L + BLANE - 1) / BLANE;
+    const int ng = (a.sh.B + a.fold - 1) / a.fold * a.sh.H;
+    BwdArgs g = a;
+    for (g.sub = 0; g.sub < a.fold; ++g.sub)
+      launch_part<MECH, DIR, 2>(g, fp32, dim3((unsigned)(nb * ng)), stream);
   } else {
     launch_part<MECH, DIR, 0>(a, fp32, grid, stream);
   }

@@ -1,7 +1,7 @@
 #pragma once
 // Backward kernels.  One template, instantiated twice per mechanism:
 //   DIR 0: lane side = queries (128 per workgroup), keys streamed: dQ and the query-side table
-//          gradients (Shaw w, T-XL r and its diagonal sums, DeBERTa Kr, T5 diagonal sums).
+//          gradients (Shaw w, T-XL r and its diagonal sums, DeBERTa Kr, T5 bucket sums).
 //   DIR 1: lane side = keys, queries streamed: dK, dV and the key-side table gradient
 //          (DeBERTa Qr), plus the T-XL u gradient.
 // Both recompute S and P = exp(S - LSE) per tile exactly as the forward does and form
@@ -9,8 +9,11 @@
 // item 2).  Table gradients follow offset-based gradient sharding (abstract, item 3; zicq.com
 // explainer, section on offset-based gradient sharding): each workgroup accumulates, per
 // offset, the sum over its own rows in registers and writes every offset of its partial
-// exactly once; a second pass (relpos_agg.hip) merges the partials in a fixed order.  No
-// atomics anywhere, so results are bitwise reproducible.
+// exactly once; a second pass (relpos_agg.hip) merges the partials in a fixed order, so results
+// are bitwise reproducible.  The general passes of Shaw and DeBERTa may run the batch entries of
+// a head as consecutive launches into one partial: the first stores it, each later launch adds
+// to every element once (an atomic add; one per element and launch, launches in stream order,
+// so each element's sum keeps one order).  T5 sums dS per bucket in LDS instead.
 //
 // Relation gradients of a table applied on one side (the row side: lane rows X times the table
 // row of offset lam = a - b) are split over the two passes so that each fits two workgroups per
@@ -123,7 +126,18 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int nb = (L + BLANE - 1) / BLANE;
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   int blk = bid % nb;
-  const int bh = a.bh0 + bid / nb;
+  int bh = a.bh0 + bid / nb;
+  // folded general pass: launch `sub` of `fold` runs batch entry bg fold + sub of head h in
+  // workgroup group g = bg H + h; the first launch stores the group's partial slot, the later
+  // ones add to it
+  const bool first = !V::DFAT || a.sub == 0;
+  if constexpr (V::DFAT) {
+    if (a.fold > 1) {
+      const int g = bid / nb, bb = (g / sh.H) * a.fold + a.sub;
+      if (bb >= sh.B) return;
+      bh = bb * sh.H + g % sh.H;
+    }
+  }
   if (sh.wr == 0) blk = (DIR == 0) ? nb - 1 - blk : blk;   // causal: longest first
   const int h = bh % sh.H;
   const int A0 = blk * BLANE;
@@ -246,7 +260,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   }
 
   // ---- zero what the sweep will not write ----
-  if constexpr (V::DFAT && V::HAS_COL) {
+  if (V::DFAT && V::HAS_COL && first) {
     // column offsets mu = b - a of every window row of every step are flushed (interior ones)
     const int mlo = bt0 - A0 - (BLANE - 1), mhi = bt_last - A0 + BOTH;
     for (int64_t e = tid; e < (int64_t)prow_rows * kHeadDim; e += 256) {
@@ -286,19 +300,27 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   // stored (clipped ones belong to the end rows); when the whole block is interior its 16 rows
   // are consecutive table rows (ascending for DeBERTa, row mu + k; descending for Shaw, k - mu),
   // stored from one base without per-element tests.
+  // (a folded pass's later batch entries add to what the first stored)
   auto flush_col = [&](const f32x16& acc, int mu0) {
     const int d = 32 * gdb + l32;
     constexpr int rstep = (MECH == MECH_SHAW) ? -1 : 1;
     if (mu0 > V::TA(span) && mu0 + 27 < V::TB(span)) {
       float* fb = pcol + (uint32_t)(V::col_of(mu0, span, nrel, toff) * kHeadDim + d);
+      if (first) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) fb[rstep * (8 * (r >> 2) + (r & 3)) * kHeadDim] = acc[r];
+        for (int r = 0; r < 16; ++r) fb[rstep * (8 * (r >> 2) + (r & 3)) * kHeadDim] = acc[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) unsafeAtomicAdd(fb + rstep * (8 * (r >> 2) + (r & 3)) * kHeadDim, acc[r]);
+      }
     } else {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int mu = mu0 + 8 * (r >> 2) + (r & 3);
-        if (mu > V::TA(span) && mu < V::TB(span))
-          pcol[(uint32_t)(V::col_of(mu, span, nrel, toff) * kHeadDim + d)] = acc[r];
+        if (mu > V::TA(span) && mu < V::TB(span)) {
+          float* f = pcol + (uint32_t)(V::col_of(mu, span, nrel, toff) * kHeadDim + d);
+          if (first) *f = acc[r]; else unsafeAtomicAdd(f, acc[r]);
+        }
       }
     }
   };
@@ -1134,7 +1156,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         acc = fmaf(ends[e * BLANE + x], xv, acc);
       }
       const int row = e == 0 ? V::rowA(span) : V::rowB(span);
-      prow[(int64_t)row * kHeadDim + d] = acc;
+      float* f = prow + (int64_t)row * kHeadDim + d;
+      *f = first ? acc : *f + acc;
     }
     // dX += lA T[rowA] + lB T[rowB]
 #pragma unroll

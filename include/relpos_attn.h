@@ -49,7 +49,9 @@
  * relpos_attn_workspace_size).  The library never allocates device memory.  All device
  * pointers must be 16-byte aligned, the workspace 256-byte aligned.  Work is enqueued on
  * `stream` (a hipStream_t; NULL = the default stream) and the call returns without
- * synchronising.  Results are bitwise deterministic: no atomics are used anywhere.
+ * synchronising.  Results are bitwise deterministic: every sum is taken in a fixed order (the
+ * few atomic adds, see relpos_attn_bwd, reach each address once per launch, launches in stream
+ * order).
  *
  * Errors: every entry point returns RELPOS_OK (0) or a negative status; on error nothing has
  * been launched.  RELPOS_E_LAUNCH reports a failed kernel launch (work already enqueued by the
@@ -131,10 +133,14 @@ int relpos_attn_fwd(const relpos_desc* desc, const void* q, const void* k, const
  * section on how structure-aware tiling stays exact, part 3, offset-based gradient sharding):
  * each workgroup reduces dS along the diagonals of its own tiles into an offset-indexed partial
  * of its own, and a second pass sums the partials of every (batch, head) that reads a table row
- * in a fixed order, so no atomics are used and the result is bitwise reproducible.  bf16, or
+ * in a fixed order, so the result is bitwise reproducible.  (Shaw and DeBERTa at large B H L:
+ * the batch entries of a head run in turn, one launch each, into one partial; the first launch
+ * stores it and each later one adds to it with one atomic add per element, so every element's
+ * sum still has one fixed order.)  T5 sums dS per bucket inside the workgroup.  bf16, or
  * fp32 (every matrix-core operand split into two bf16 parts, hi and lo, with the products
- * hi.hi + hi.lo + lo.hi accumulated in fp32).  The workspace (relpos_attn_workspace_size, pass 1) holds the partials; its size grows with
- * B H L (T-XL: B H L^2 / 2 bytes, capped by max_partial_bytes). */
+ * hi.hi + hi.lo + lo.hi accumulated in fp32).  The workspace (relpos_attn_workspace_size,
+ * pass 1) holds the partials; its size grows with B H L (T-XL: L^2 / 2 bytes for each
+ * (batch, head) slice of one group, see max_partial_bytes). */
 int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const void* v,
                     const void* o, const float* lse, const void* dout, const void* rel_a,
                     const void* rel_b, const float* bias_a, const float* bias_b, void* dq,

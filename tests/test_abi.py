@@ -148,6 +148,23 @@ def test_txl_offset_partials_shrink_under_two_sided_window():
         assert st == 0 and full - n == _al(owners * 4 * (L + 256) * 4) - _al(owners * 4 * rows * 4), (wl, wr)
 
 
+def test_general_pass_partials_fold_over_the_batch():
+    """Shaw and DeBERTa: once one batch entry already gives a full wave of workgroups (H L / 128
+    >= 512), the batch entries of a head share one set of table partials, so the backward
+    workspace grows with B only by the per-row buffers (row constants, D, the light pass's fp32
+    dX and dV, its end-row sums)."""
+    H, L = 8, 8192
+    rows = H * L
+    for mech, k, per_row in (("shaw", 256, 8 + 4 + 256 + 8 + 256),
+                             ("deberta", 512, 8 + 8 + 4 + 256 + 8 + 256)):
+        sizes = {}
+        for B in (1, 2, 4, 8):
+            st, sizes[B] = _ws(ear.make_desc(mech, B, H, L, rel_span=k), 1)
+            assert st == 0
+        for B in (2, 4, 8):
+            assert sizes[B] - sizes[1] == (B - 1) * rows * per_row, (mech, B)
+
+
 def test_fwd_rejects_bad_pointers_without_launching():
     lib = ear.load_library()
     desc = ear.make_desc("shaw", 1, 1, 64, rel_span=4)

@@ -87,7 +87,7 @@ struct Plan {
   size_t off_part_q, off_part_k, off_part_qv, off_part_kv, off_diag, off_xpart, off_vpart, off_cab;
   int64_t part_q_stride, part_k_stride;
   int nb, nrt, owners;
-  int txl_group;   // T-XL key-side pass: (batch, head) slices per group
+  int txl_group;   // T-XL key-side pass under max_partial_bytes: (batch, head) slices per group
   int fold;        // Shaw / DeBERTa general passes: batch entries per workgroup
   int fold_owners; // their partial slots: ceil(B / fold) H nb
   int64_t rel_rows;   // rows of each relation table (0 for T5 / ALiBi)
@@ -177,11 +177,15 @@ int make_plan(const relpos_desc* d, Plan* p) {
   p->nrt = L + 256;
   p->owners = p->B * p->H * p->nb;
   const size_t own = (size_t)p->owners;
-  // Shaw / DeBERTa general passes: a workgroup runs `fold` batch entries of one head in turn
-  // into one partial slot.  The fewest groups of batch entries that still give one full wave
-  // of workgroups (two per compute unit on 256 compute units); no folding below that.
+  // Shaw / DeBERTa general passes and the T-XL key-side pass: the batch entries of a head run
+  // as `fold` consecutive launches into one partial slot.  The fewest groups of batch entries
+  // that still give one full wave of workgroups (two per compute unit on 256 compute units); no
+  // folding below that.  T-XL folds only when one batch entry gives at most one wave and no
+  // max_partial_bytes is set; otherwise it runs slice groups (below).
+  const bool txl_fold = d->mech == RELPOS_TXL && d->max_partial_bytes == 0 &&
+                        (int64_t)p->H * p->nb <= kGroupWorkgroups;
   p->fold = 1;
-  if (d->mech == RELPOS_SHAW || d->mech == RELPOS_DEBERTA) {
+  if (d->mech == RELPOS_SHAW || d->mech == RELPOS_DEBERTA || txl_fold) {
     for (int ng = 1; ng <= p->B; ++ng) {
       if ((int64_t)ng * p->H * p->nb >= kGroupWorkgroups) {
         p->fold = (p->B + ng - 1) / ng;
@@ -202,19 +206,20 @@ int make_plan(const relpos_desc* d, Plan* p) {
       rows_k = std::min<int64_t>(rows_k, wrows);
     }
     p->part_q_stride = rows_k * kHeadDim;
-    // Slices per group of the key-side pass.  By default, as many as give one full wave of
-    // workgroups (two per compute unit on the 256 compute units of an MI355X): the launch keeps
-    // the chip busy while the partials hold the fewest slices.  A caller's max_partial_bytes
-    // instead sizes the group by bytes.  At least one slice either way.
+    // Folded (above), the partials hold ceil(B / fold) H slices.  Otherwise the (batch, head)
+    // slices run in groups, each group's partials aggregated before the next reuses them: as
+    // many slices as give one wave of workgroups, or, under max_partial_bytes, as fit in it (at
+    // least one slice either way).
     const int64_t per_slice = (int64_t)p->nb * p->part_q_stride * (int64_t)sizeof(float);
     const int64_t nbh = (int64_t)p->B * p->H;
     const int64_t group = d->max_partial_bytes > 0
                               ? d->max_partial_bytes / std::max<int64_t>(per_slice, 1)
                               : kGroupWorkgroups / std::max<int64_t>(p->nb, 1);
-    p->txl_group = (int)std::max<int64_t>(1, std::min<int64_t>(nbh, group));
+    p->txl_group = txl_fold ? 0 : (int)std::max<int64_t>(1, std::min<int64_t>(nbh, group));
   }
   if (d->mech == RELPOS_TXL) {
-    p->off_part_q = take(sizeof(float) * (size_t)p->txl_group * p->nb * p->part_q_stride);
+    const size_t slots = p->txl_group > 0 ? (size_t)p->txl_group * p->nb : (size_t)p->fold_owners;
+    p->off_part_q = take(sizeof(float) * slots * p->part_q_stride);
   } else if (p->part_q_stride) {
     p->off_part_q = take(sizeof(float) * (size_t)p->fold_owners * p->part_q_stride);
   }
@@ -535,19 +540,42 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
   const bool rev = desc->window_right == 0;
   float* diag = p.off_diag ? (float*)(ws + p.off_diag) : nullptr;
   if (desc->mech == RELPOS_TXL) {
-    // the per-offset sums of the query-side pass, then the key-side pass group by group, each
-    // group's r partials folded into dr before the next group reuses them
+    // the per-offset sums of the query-side pass, then the key-side pass and its r partials
     e = launch_agg_diag(a.part_qv, p.B, p.H, p.L, p.nb, rev, desc->window_left, desc->window_right, diag, s);
-    const int nbh = p.B * p.H, G = p.txl_group;
-    for (int s0 = 0; s0 < nbh && e == hipSuccess; s0 += G) {
-      a.bh0 = s0;
-      a.nbh = std::min(G, nbh - s0);
-      e = timed(RELPOS_PROF_BWD_DKDV, s, [&] { return launch_bwd_dkdv(a, p.fp32, s); });
+    if (p.txl_group == 0) {
+      // batch entries folded: `fold` launches over ceil(B / fold) H slices' workgroups, each
+      // adding to the partials of the one before, then one aggregation
+      const int ng = (p.B + p.fold - 1) / p.fold;
+      a.bh0 = 0;
+      a.nbh = ng * p.H;
+      e = timed(RELPOS_PROF_BWD_DKDV, s, [&] {
+        hipError_t r = hipSuccess;
+        for (a.sub = 0; a.sub < p.fold && r == hipSuccess; ++a.sub) r = launch_bwd_dkdv(a, p.fp32, s);
+        return r;
+      });
       if (e == hipSuccess)
         e = launch_agg_txl_dr(a.part_q, diag, bias_b, p.H, p.L, p.nb,
                               (int)(p.part_q_stride / kHeadDim), desc->window_left,
-                              desc->window_right, p.nrel, p.txl_off, p.scale, s0, a.nbh, s0 == 0,
-                              s0 + G >= nbh, p.rel_hs == 0, drel_a, s);
+                              desc->window_right, p.nrel, p.txl_off, p.scale, 0, ng * p.H, true,
+                              true, p.rel_hs == 0, drel_a, s);
+    }
+    const int nbh = p.B * p.H, G = p.txl_group;
+    if (G > 0 && e == hipSuccess) {
+      // slice groups, each group's r partials folded into dr before the next reuses them
+      e = timed(RELPOS_PROF_BWD_DKDV, s, [&] {
+        hipError_t r = hipSuccess;
+        for (int s0 = 0; s0 < nbh && r == hipSuccess; s0 += G) {
+          a.bh0 = s0;
+          a.nbh = std::min(G, nbh - s0);
+          r = launch_bwd_dkdv(a, p.fp32, s);
+          if (r == hipSuccess)
+            r = launch_agg_txl_dr(a.part_q, diag, bias_b, p.H, p.L, p.nb,
+                                  (int)(p.part_q_stride / kHeadDim), desc->window_left,
+                                  desc->window_right, p.nrel, p.txl_off, p.scale, s0, a.nbh,
+                                  s0 == 0, s0 + G >= nbh, p.rel_hs == 0, drel_a, s);
+        }
+        return r;
+      });
     }
     if (e == hipSuccess)
       e = launch_agg_txl_uv(a.part_kv, diag, rel_a, p.rel_hs, p.B, p.H, p.L, p.nb, p.nrel,

@@ -127,11 +127,12 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   const int bid = xcd_remap(blockIdx.x, gridDim.x);
   int blk = bid % nb;
   int bh = a.bh0 + bid / nb;
-  // folded general pass: launch `sub` of `fold` runs batch entry bg fold + sub of head h in
-  // workgroup group g = bg H + h; the first launch stores the group's partial slot, the later
-  // ones add to it
-  const bool first = !V::DFAT || a.sub == 0;
-  if constexpr (V::DFAT) {
+  // folded pass (general passes of Shaw and DeBERTa, T-XL key side): launch `sub` of `fold`
+  // runs batch entry bg fold + sub of head h in workgroup group g = bg H + h; the first launch
+  // stores the group's partial slot, the later ones add to it
+  constexpr bool FOLDS = V::DFAT || V::TK;
+  const bool first = !FOLDS || a.sub == 0;
+  if constexpr (FOLDS) {
     if (a.fold > 1) {
       const int g = bid / nb, bb = (g / sh.H) * a.fold + a.sub;
       if (bb >= sh.B) return;
@@ -270,7 +271,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       if (!end && !(nsteps > 0 && mu >= mlo && mu <= mhi)) pcol[e] = 0.f;
     }
   }
-  if constexpr (V::TK) {
+  if (V::TK && first) {
     // rows written by the sweep: [bt0 + 65, bt_last + 256] (ptg is offset by rb rows)
     for (int64_t e = tid; e < (int64_t)nrk * kHeadDim; e += 256) {
       const int row = (int)(e / kHeadDim) + rb;
@@ -896,8 +897,13 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       // block gp leaves the window with this step (the next window starts 64 offsets higher)
       if constexpr (V::TK) {
         float* fb = ptg + (int64_t)(b0 + 65 + 32 * gp + 4 * kh) * kHeadDim + 32 * gdb + l32;
+        if (first) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = racc[0][r];
+          for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = racc[0][r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) unsafeAtomicAdd(fb + (8 * (r >> 2) + (r & 3)) * kHeadDim, racc[0][r]);
+        }
       } else {
         flush_col(racc[0], b0 - A0 - (BLANE - 1) + 32 * gp + 4 * kh);
       }
@@ -1068,8 +1074,13 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       for (int i = 0; i < 2; ++i) {
         float* fb = ptg + (int64_t)(bt_last + 65 + 32 * (gp + 2 + 2 * i) + 4 * kh) * kHeadDim +
                     32 * gdb + l32;
+        if (first) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = racc[i][r];
+          for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = racc[i][r];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) unsafeAtomicAdd(fb + (8 * (r >> 2) + (r & 3)) * kHeadDim, racc[i][r]);
+        }
       }
     }
   }
@@ -1190,7 +1201,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       float acc = 0.f;
       for (int x = 0; x < BLANE && A0 + x < L; ++x)
         acc = fmaf(csum[x], Elem<T>::to_f(xg[(int64_t)(A0 + x) * kHeadDim + tid]), acc);
-      a.part_kv[owner * kHeadDim + tid] = acc;
+      a.part_kv[((int64_t)bh * nb + bid % nb) * kHeadDim + tid] = acc;   // per slice
     }
   }
 

@@ -211,8 +211,10 @@ int relpos_project_bwd(const relpos_proj_desc* desc, const void* X, const void* 
 
 /* Profiling hook for benchmarks.  When `kernel` is RELPOS_PROF_FWD, RELPOS_PROF_BWD_DQ or
  * RELPOS_PROF_BWD_DKDV, later calls made BY THE SAME HOST THREAD record `start_event` on their
- * stream just before enqueueing that kernel and `stop_event` just after it (both hipEvent_t
- * created by the caller).  RELPOS_PROF_OFF (0) clears the hook.  The setting is thread-local:
+ * stream just before enqueueing that pass and `stop_event` just after its last launch (both
+ * hipEvent_t created by the caller).  A pass may be several launches (the light and general
+ * parts of Shaw and DeBERTa, folded batch entries); the T-XL key-side pass under
+ * max_partial_bytes also spans the aggregations between its slice groups.  RELPOS_PROF_OFF (0) clears the hook.  The setting is thread-local:
  * calls from other threads never see it, so the library stays safe to call from several
  * threads on their own streams.  Returns RELPOS_E_INVALID for an unknown kernel id or NULL
  * events. */

@@ -311,17 +311,23 @@ def test_profile_hook_calls_from_another_thread():
     assert res == [ear.RELPOS_OK]
 
 
-def test_txl_default_groups_fill_one_wave_of_workgroups():
-    """With no byte cap, the key-side pass groups as many slices as give 512 workgroups (two per
-    compute unit on 256 compute units), at least one slice, at most every slice."""
-    def group(B, H, L):
+def test_txl_default_partials_fold_the_batch():
+    """With no byte cap and at most one wave of workgroups per batch entry (H L / 128 <= 512),
+    the key-side pass folds the batch: the batch entries run as consecutive launches into one
+    set of r partials, held for the H slices of each of the fewest groups of batch entries that
+    still give 512 workgroups (two per compute unit on 256 compute units), or for every slice when
+    even all of them give fewer.  Past one wave per batch entry it runs groups of as many slices
+    as give 512 workgroups (at least one)."""
+    def held(B, H, L):
         st, n = _ws(ear.make_desc("txl", B, H, L), 1)
         st1, n1 = _ws(ear.make_desc("txl", B, H, L, max_partial_bytes=1), 1)   # one slice
         nb = (L + 127) // 128
         per_slice = nb * (L + 256) * 64 * 4
         assert st == st1 == 0
         return (n - n1) // per_slice + 1
-    assert group(4, 8, 8192) == 8          # 64 key blocks per slice -> 8 slices
-    assert group(1, 4, 32768) == 2         # 256 key blocks -> 2 slices
-    assert group(2, 3, 1000) == 6          # 8 key blocks -> 64 wanted, 6 exist
-    assert group(1, 2, 70000) == 1         # 547 key blocks, more than 512 -> one slice
+    assert held(4, 8, 8192) == 8           # 64 key blocks x 8 heads = 512: one group of 4 entries
+    assert held(8, 8, 8192) == 8           # the same set for twice the batch
+    assert held(4, 2, 8192) == 8           # 128 workgroups per entry: 4 groups of one entry
+    assert held(2, 3, 1000) == 6           # 8 key blocks: every slice, no folding
+    assert held(1, 4, 32768) == 2          # 256 key blocks x 4 heads: groups of 2 slices
+    assert held(1, 2, 70000) == 1          # 547 key blocks, more than 512 -> one slice

@@ -313,6 +313,27 @@ def run_bwd(m):
     runner.backward(m["desc"], m["dev"], m["o"], m["lse"], ws=m["ws_b"], grads=m["grads"])
 
 
+GROUP_WORKGROUPS = 512   # the library's wave of workgroups (two per CU on 256 CUs)
+
+
+def pass_launches(case, mech, kernel):
+    """Launches of one pass kernel per call, by the library's launch rule: the T-XL key-side pass
+    runs its batch entries as `fold` consecutive launches (the fewest groups of batch entries that
+    give one wave of workgroups) when one batch entry gives at most one wave, else slice groups.
+    Shaw and DeBERTa passes are two kernels (light, general) and are not counted here."""
+    B, H, L, _ = case["shape"]
+    nb = (L + 127) // 128
+    if mech in ("shaw", "deberta"):
+        return None
+    if mech == "txl" and kernel == "bwd_dkdv":
+        if H * nb <= GROUP_WORKGROUPS:
+            ng = next((g for g in range(1, B + 1) if g * H * nb >= GROUP_WORKGROUPS), B)
+            return -(-B // ng)
+        group = max(1, min(B * H, GROUP_WORKGROUPS // nb))
+        return -(-(B * H) // group)
+    return 1
+
+
 def step(mechs, hook=None):
     """One pass of the hot path.  hook = (mech, kernel_id, start, stop) records one kernel."""
     from exact_attention_relative_amd import relpos_profile_events, RELPOS_PROF_OFF
@@ -660,9 +681,16 @@ def main():
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     traffic, traffic_src = recorded_traffic(dom_mech, dom_kernel)
     peak_meas = measured_mfma_peak(torch)
+    # the pass may be several launches of one kernel: flops, time and traffic are per pass
+    nl = pass_launches(dm["case"], dom_mech, dom_kernel)
+    traffic_launch = traffic
+    if traffic is not None:
+        traffic = traffic * nl if nl else None
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
+                "traffic_per_launch": traffic_launch,
                 "kernel": f"{dom_kernel} pass kernel, {dom_mech}", "avg_ms": dom_ms,
+                "launches": nl, "avg_launch_ms": dom_ms / nl if nl else None,
                 "flops_per_launch": dom_flops, "traffic_source": traffic_src,
                 "peak_measured": peak_meas, "frac_of_measured": achieved / peak_meas,
                 "kernel_source_sha": kernel_source_sha()}

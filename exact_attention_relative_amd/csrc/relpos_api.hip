@@ -304,6 +304,16 @@ AttnShape make_shape(const relpos_desc* d, const Plan& p) {
   s.scale = p.scale;
   s.rel_hs = p.rel_hs;
   s.nbk = d->mech == RELPOS_T5 ? d->num_buckets : 0;
+  s.t5sat = 1 << 30;
+  s.t5b_pos = s.t5b_neg = 0;
+  if (d->mech == RELPOS_T5) {
+    // magnitudes at or past the last threshold share a side's last bucket (the unidirectional
+    // map sends every delta <= 0 to bucket 0)
+    const T5Map& m = p.t5;
+    s.t5sat = m.nthr > 0 ? m.thr[m.nthr - 1] : m.max_exact;
+    s.t5b_pos = m.max_exact + m.nthr;
+    s.t5b_neg = m.bidirectional ? m.half + m.max_exact + m.nthr : 0;
+  }
   return s;
 }
 

@@ -457,8 +457,16 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     int t5cls = 0, t5b = 0;   // T5: one bucket for the whole wave tile, and which
     if constexpr (MECH == MECH_T5) {
       const int lo = clampi(dlo, 1 - L, L - 1), hi = clampi(dhi, 1 - L, L - 1);
-      t5b = a.bucket[lo + L - 1];
-      if ((lo >= 0 || hi < 0) && t5b == a.bucket[hi + L - 1]) t5cls = 1;
+      if (lo >= sh.t5sat) {            // past the last threshold: no map read
+        t5cls = 1;
+        t5b = sh.t5b_pos;
+      } else if (hi <= -sh.t5sat) {
+        t5cls = 1;
+        t5b = sh.t5b_neg;
+      } else {
+        t5b = a.bucket[lo + L - 1];
+        if ((lo >= 0 || hi < 0) && t5b == a.bucket[hi + L - 1]) t5cls = 1;
+      }
     }
 
     // ---- stage ----

@@ -162,8 +162,11 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
       if (dlo >= 0) cls = 1; else if (dhi < 0) cls = 2;
     } else if constexpr (MECH == MECH_T5) {
       // one bucket for the whole wave tile: the offsets lie on one side of 0 (where the
-      // bucket map is monotone) and both ends share a bucket
-      if ((dlo_c >= 0 || dhi_c < 0) && a.bucket[dlo_c + L - 1] == a.bucket[dhi_c + L - 1])
+      // bucket map is monotone) and both ends share a bucket; past the last threshold on
+      // either side without reading the map
+      if (dlo_c >= sh.t5sat || dhi_c <= -sh.t5sat)
+        cls = 1;
+      else if ((dlo_c >= 0 || dhi_c < 0) && a.bucket[dlo_c + L - 1] == a.bucket[dhi_c + L - 1])
         cls = 1;
     }
 

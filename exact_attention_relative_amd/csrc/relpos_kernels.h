@@ -55,6 +55,9 @@ struct AttnShape {
   float scale;      // s
   int64_t rel_hs;   // elements between the relation tables of consecutive heads (0 = shared)
   int nbk;          // T5 buckets per head (else 0)
+  // T5: every offset delta >= t5sat lands in bucket t5b_pos and every delta <= -t5sat in bucket
+  // t5b_neg (the last bucket of each side); a huge t5sat for the other mechanisms
+  int t5sat, t5b_pos, t5b_neg;
 };
 
 struct FwdArgs {

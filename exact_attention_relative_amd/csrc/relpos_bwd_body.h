@@ -663,11 +663,14 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     f32x16 ds[2];
     Op<NP> dso[4];   // dS as bf16 MFMA operands (16 other-side rows each)
     if (!wave_none) {
-      // query-side pass: dP first, its MFMAs run while the exponentials below are computed
+      // dP first, its MFMAs run while the exponentials below are computed
       Op<NP> y2op[2][4];
       f32x16 dp[2];
       // dP starts from -D (the lane's on the query side, the streamed row's on the key side)
       if constexpr (DIR == 0) other_dot_lane_from<NP>(dp, y2s, x2op, y2op, -dsum_l);
+      // the key side too, except where registers are the limit (general passes, T-XL)
+      constexpr bool DP_FIRST = KINIT && !V::DFAT;
+      if constexpr (DP_FIRST) other_dot_lane<NP, true>(dp, y2s, x2op, y2op, lsd_s + BOTH);
       // ---- P ----  (the key-side scores already hold -LSE / s, except in the T-XL pass)
       const float pbias = DIR == 0 ? lconst * c - lse2 : lconst * c;
       if constexpr (DIR == 1 && !KINIT) {
@@ -698,8 +701,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             sc[b][r] = pair_ok(ii, jj, L, wlx, wrx) ? sc[b][r] : 0.f;
           }
       }
-      if constexpr (KINIT) other_dot_lane<NP, true>(dp, y2s, x2op, y2op, lsd_s + BOTH);
-      else if constexpr (DIR == 1) other_dot_lane<NP>(dp, y2s, x2op, y2op);
+      if constexpr (KINIT && !DP_FIRST) other_dot_lane<NP, true>(dp, y2s, x2op, y2op, lsd_s + BOTH);
+      else if constexpr (DIR == 1 && !KINIT) other_dot_lane<NP>(dp, y2s, x2op, y2op);
       // ---- dS = P (dP - D) ----
       if constexpr (DIR == 1 && !KINIT) {
 #pragma unroll

@@ -88,7 +88,8 @@ struct Plan {
   int64_t part_q_stride, part_k_stride;
   int nb, nrt, owners;
   int txl_group;   // T-XL key-side pass under max_partial_bytes: (batch, head) slices per group
-  int fold;        // Shaw / DeBERTa general passes: batch entries per workgroup
+  int fold;        // folded passes: batch entries (or slices, fold_slices) per partial slot
+  bool fold_slices;  // Shaw / DeBERTa with one table for every head: fold (batch, head) slices
   int fold_owners; // their partial slots: ceil(B / fold) H nb
   int64_t rel_rows;   // rows of each relation table (0 for T5 / ALiBi)
   int64_t rel_hs;     // elements between the relation tables of consecutive heads (0 = shared)
@@ -184,16 +185,22 @@ int make_plan(const relpos_desc* d, Plan* p) {
   // max_partial_bytes is set; otherwise it runs slice groups (below).
   const bool txl_fold = d->mech == RELPOS_TXL && d->max_partial_bytes == 0 &&
                         (int64_t)p->H * p->nb <= kGroupWorkgroups;
+  // A table that every head shares (Shaw / DeBERTa with rel_head_stride 0) folds whole
+  // (batch, head) slices the same way, so that even one long batch entry shares its slots.
   p->fold = 1;
+  p->fold_slices = (d->mech == RELPOS_SHAW || d->mech == RELPOS_DEBERTA) && p->rel_hs == 0;
   if (d->mech == RELPOS_SHAW || d->mech == RELPOS_DEBERTA || txl_fold) {
-    for (int ng = 1; ng <= p->B; ++ng) {
-      if ((int64_t)ng * p->H * p->nb >= kGroupWorkgroups) {
-        p->fold = (p->B + ng - 1) / ng;
+    const int units = p->fold_slices ? p->B * p->H : p->B;                        // what folds
+    const int64_t per_unit = p->fold_slices ? p->nb : (int64_t)p->H * p->nb;      // its workgroups
+    for (int ng = 1; ng <= units; ++ng) {
+      if (ng * per_unit >= kGroupWorkgroups) {
+        p->fold = (units + ng - 1) / ng;
         break;
       }
     }
   }
-  p->fold_owners = (p->B + p->fold - 1) / p->fold * p->H * p->nb;
+  p->fold_owners = p->fold_slices ? (p->B * p->H + p->fold - 1) / p->fold * p->nb
+                                  : (p->B + p->fold - 1) / p->fold * p->H * p->nb;
   const int k = d->rel_span;
   if (d->mech == RELPOS_SHAW) p->part_q_stride = (int64_t)(2 * k + 1) * kHeadDim;
   if (d->mech == RELPOS_DEBERTA) p->part_q_stride = p->part_k_stride = (int64_t)(2 * k) * kHeadDim;
@@ -524,6 +531,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
   a.rel_a = rel_a; a.rel_b = rel_b;
   a.bias_a = bias_a; a.bias_b = bias_b;
   a.fold = p.fold;
+  a.fold_slices = p.fold_slices ? 1 : 0;
   if (desc->mech == RELPOS_T5 || desc->mech == RELPOS_ALIBI) {
     a.lut = (const float*)(ws + p.off_lut);
     a.bucket = (const int*)(ws + p.off_bucket);
@@ -606,8 +614,8 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
       break;
     case RELPOS_SHAW:
     case RELPOS_DEBERTA: {
-      // one shared table sums every slot; per-head tables sum the slots of their head (slot
-      // (g H + h) nb + p for batch group g)
+      // one shared table sums every slot (slot g nb + p for slice group g); per-head tables
+      // sum the slots of their head (slot (g H + h) nb + p for batch group g)
       auto agg = [&](const float* part, int64_t stride, float* out) {
         const int ng = (p.B + p.fold - 1) / p.fold;
         return p.rel_hs == 0

@@ -44,7 +44,8 @@ static void launch_one(const BwdArgs& a, bool fp32, dim3 grid, hipStream_t strea
     // head, block) taking the group's next entry (same-stream order: each launch adds to the
     // partial slots the previous one wrote)
     const int nb = (a.sh.L + BLANE - 1) / BLANE;
-    const int ng = (a.sh.B + a.fold - 1) / a.fold * a.sh.H;
+    const int ng = a.fold_slices ? (a.sh.B * a.sh.H + a.fold - 1) / a.fold
+                                 : (a.sh.B + a.fold - 1) / a.fold * a.sh.H;
     BwdArgs g = a;
     for (g.sub = 0; g.sub < a.fold; ++g.sub)
       launch_part<MECH, DIR, 2>(g, fp32, dim3((unsigned)(nb * ng)), stream);

@@ -128,15 +128,22 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   int blk = bid % nb;
   int bh = a.bh0 + bid / nb;
   // folded pass (general passes of Shaw and DeBERTa, T-XL key side): launch `sub` of `fold`
-  // runs batch entry bg fold + sub of head h in workgroup group g = bg H + h; the first launch
-  // stores the group's partial slot, the later ones add to it
+  // runs batch entry bg fold + sub of head h in workgroup group g = bg H + h, or, for a table
+  // every head shares (fold_slices), slice g fold + sub; the first launch stores the group's
+  // partial slot, the later ones add to it
   constexpr bool FOLDS = V::DFAT || V::TK;
   const bool first = !FOLDS || a.sub == 0;
   if constexpr (FOLDS) {
     if (a.fold > 1) {
-      const int g = bid / nb, bb = (g / sh.H) * a.fold + a.sub;
-      if (bb >= sh.B) return;
-      bh = bb * sh.H + g % sh.H;
+      const int g = bid / nb;
+      if (a.fold_slices) {
+        bh = g * a.fold + a.sub;
+        if (bh >= sh.B * sh.H) return;
+      } else {
+        const int bb = (g / sh.H) * a.fold + a.sub;
+        if (bb >= sh.B) return;
+        bh = bb * sh.H + g % sh.H;
+      }
     }
   }
   if (sh.wr == 0) blk = (DIR == 0) ? nb - 1 - blk : blk;   // causal: longest first

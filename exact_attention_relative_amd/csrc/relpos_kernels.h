@@ -83,6 +83,7 @@ struct BwdArgs {
   int bh0;             // first (batch, head) slice of this launch (b-major: b H + h)
   int nbh;             // slices in this launch (0 = all B H)
   int fold;            // general passes of Shaw / DeBERTa: batch entries per partial slot (>= 1),
+  int fold_slices;     // ... or, with a table shared by every head, (batch, head) slices per slot
   int sub;             // run as `fold` launches, this one taking entry `sub` of each group
   const void* q;
   const void* k;

@@ -165,6 +165,19 @@ def test_general_pass_partials_fold_over_the_batch():
             assert sizes[B] - sizes[1] == (B - 1) * rows * per_row, (mech, B)
 
 
+def test_shared_tables_fold_whole_slices():
+    """A Shaw / DeBERTa table shared by every head folds whole (batch, head) slices into the
+    general passes' partial slots: one 32K batch entry of 8 heads (256 blocks each) keeps two
+    groups of four slices (512 slots), where per-head tables keep one slot per (head, block)."""
+    B, H, L, k = 1, 8, 32768, 512
+    slot = 2 * k * 64 * 4                      # DeBERTa: 2k rows of 64 floats per side
+    st, shared = _ws(ear.make_desc("deberta", B, H, L, rel_span=k), 1)
+    st2, per_head = _ws(ear.make_desc("deberta", B, H, L, rel_span=k,
+                                      rel_head_stride=2 * k * 64), 1)
+    assert st == st2 == 0
+    assert per_head - shared == 2 * (H * 256 - 512) * slot
+
+
 def test_fwd_rejects_bad_pointers_without_launching():
     lib = ear.load_library()
     desc = ear.make_desc("shaw", 1, 1, 64, rel_span=4)

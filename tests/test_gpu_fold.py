@@ -2,9 +2,10 @@
 
 Once the batch entries of a head fill a wave of workgroups, the general passes of Shaw and DeBERTa
 and the T-XL key-side pass run the batch entries as consecutive launches into one set of
-partials: the first launch stores each partial element, every later one adds to it.  At B = 3, H = 16,
-L = 2048 (256 workgroups per batch entry) the entries form two groups, {0, 1} and {2}, so the
-second launch skips the workgroups of the short group.  Checked on every output against the fp64
+partials: the first launch stores each partial element, every later one adds to it.  At B = 3,
+H = 16, L = 2048 (256 workgroups per batch entry) per-head tables fold the batch entries in two
+groups, {0, 1} and {2}, so the second launch skips the workgroups of the short group; tables
+shared by every head fold whole (batch, head) slices, here in pairs.  Checked on every output against the fp64
 oracle (all slices, all rows, every table gradient), for shared and per-head tables, in bf16 and
 fp32, and run twice for bitwise determinism."""
 

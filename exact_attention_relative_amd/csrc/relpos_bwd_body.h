@@ -478,7 +478,46 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 
     // ---- stage ----
     __syncthreads();
-    if constexpr (V::TG1) {   // registers are the limit here: stage directly
+    float tkl = 0.f, tkd = 0.f;   // (T-XL key side: LSE and D read with the tiles)
+    if (V::TK && NP == 1 && step > 0) {
+      // bf16 T-XL key side after the first step: the tiles, the 64 new column-window rows and
+      // their v.r values in one branch-free block of reads (rows past L and window rows of no
+      // table row read a valid row and store zeros)
+      // (lane-derived values recomputed from an opaque thread index, not hoisted and spilled)
+      int t = tid;
+      asm volatile("" : "+v"(t));
+      const int r = t >> 2, cc = (t & 3) * 16, ln = t & 63;
+      const int yr = min(b0 + r, L - 1);
+      const int wr = V::col_of((b0 - A0 - (BLANE - 1)) + 2 * BOTH + r, span, nrel, toff);
+      const int vrr = V::col_of((b0 - A0 - (BLANE - 1)) + 2 * BOTH + ln, span, nrel, toff);
+      // (bases rebuilt here from the kernel arguments in scalar registers, not hoisted and
+      // spilled; the key side streams Q and dO, and its column-side table is rel_a)
+      int hs = __builtin_amdgcn_readfirstlane(h), bhs = __builtin_amdgcn_readfirstlane(bh);
+      asm volatile("" : "+s"(hs), "+s"(bhs));
+      const int64_t sl = (int64_t)bhs * L * (2 * kHeadDim);
+      const uint32_t oq = (uint32_t)(yr * (2 * kHeadDim) + 2 * cc);
+      const uint32_t ow = (uint32_t)(max(wr, 0) * (2 * kHeadDim) + 2 * cc);
+      gchar* gq = scalar_ptr(a.q) + sl + oq;
+      gchar* go = scalar_ptr(a.dout) + sl + oq;
+      gchar* gw = scalar_ptr(a.rel_a) + 2 * ((int64_t)hs * sh.rel_hs) + ow;
+      typedef __attribute__((address_space(1))) const u32x4 gu4;
+      u32x4 q0 = *(gu4*)gq, q1 = *(gu4*)(gq + 16), o0 = *(gu4*)go, o1 = *(gu4*)(go + 16);
+      u32x4 w0 = *(gu4*)gw, w1 = *(gu4*)(gw + 16);
+      const uint32_t ol = 4u * (uint32_t)min(b0 + ln, L - 1);
+      float vr = load_f32(scalar_ptr(a.vr) + 4 * ((int64_t)hs * nrel), 4u * (uint32_t)max(vrr, 0));
+      tkl = load_f32(scalar_ptr(a.lse) + 4 * ((int64_t)bhs * L), ol);
+      tkd = load_f32(scalar_ptr(a.dsum) + 4 * ((int64_t)bhs * L), ol);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const bool yin = b0 + r < L, win_ok = wr >= 0;
+      const int p0 = wrow(2 * BOTH, xrot);
+      *(u32x4*)(ys + r * TSTR + cc) = yin ? q0 : z;
+      *(u32x4*)(ys + r * TSTR + cc + 8) = yin ? q1 : z;
+      *(u32x4*)(y2s + r * TSTR + cc) = yin ? o0 : z;
+      *(u32x4*)(y2s + r * TSTR + cc + 8) = yin ? o1 : z;
+      *(u32x4*)(win + (p0 + r) * TSTR + cc) = win_ok ? w0 : z;
+      *(u32x4*)(win + (p0 + r) * TSTR + cc + 8) = win_ok ? w1 : z;
+      if (tid < BOTH) *win_vec(win, p0 + tid) = vrr >= 0 ? vr : 0.f;
+    } else if constexpr (V::TG1) {   // registers are the limit here: stage directly
       stage64<T, NP>(ys, yg, b0, L);
       stage64<T, NP>(y2s, y2g, b0, L);
     } else {
@@ -495,7 +534,15 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       if (tid < BOTH) {
         // (read here when not prefetched: locals, so that nothing stays live across steps)
         float nl = pnl, nd = pdd;
-        if constexpr (!PF_LSD) lsd_vals(b0, nl, nd);
+        if (V::TK && NP == 1 && step > 0) {
+          // LSE log2 e (+inf for rows past L or with no allowed key) and D, as lsd_vals gives
+          const bool in = b0 + tid < L;
+          nl = tkl * kLog2e;
+          nl = (in && nl > kNegInf) ? nl : __builtin_inff();
+          nd = in ? tkd : 0.f;
+        } else if constexpr (!PF_LSD) {
+          lsd_vals(b0, nl, nd);
+        }
         lsd_s[tid] = nl;
         lsd_s[BOTH + tid] = nd;
         if constexpr (MECH == MECH_ALIBI) {
@@ -541,7 +588,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           const int r = colfn(x);
           *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
         }
-      } else {
+      } else if constexpr (NP == 2) {   // (bf16: staged with the tiles above)
         const int p0 = wrow(2 * BOTH, xrot);
         stage_window_rows<T, NP>(win, tcol, colfn, 2 * BOTH, p0);
         if (tid < BOTH) {

@@ -242,6 +242,20 @@ __device__ __forceinline__ int wave_index() {
   return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
+// A wave-uniform pointer rebuilt from scalar registers where it is used (an opaque pair of
+// SGPRs), so that the compiler does not keep it in, and spill it from, vector registers.
+typedef __attribute__((address_space(1))) const char gchar;   // global memory
+__device__ __forceinline__ gchar* scalar_ptr(const void* p) {
+  const uint64_t v = (uint64_t)p;
+  int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  int hi = __builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  asm volatile("" : "+s"(lo), "+s"(hi));
+  return (gchar*)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+__device__ __forceinline__ float load_f32(gchar* base, uint32_t byte_off) {
+  return *(const __attribute__((address_space(1))) float*)(base + byte_off);
+}
+
 // max(a, b, c) as one v_maximum3_f32 (NaN-propagating; no canonicalisation of the inputs)
 __device__ __forceinline__ float max3f(float a, float b, float c) {
   return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);

@@ -60,6 +60,15 @@ __device__ __forceinline__ void stage64(uint16_t* tile, const T* base, int row0,
   const int r = t >> 2;
   const int c = (t & 3) * 16;
   const int plane = BOTH * TSTR;
+  if constexpr (NP == 1) {
+    // bf16: the read without a branch (rows past nvalid read row nvalid - 1 and store zeros)
+    const u32x4* g = (const u32x4*)stage_addr(base, (int64_t)min(row0 + r, nvalid - 1) * kHeadDim + c);
+    const u32x4 v0 = g[0], v1 = g[1], z = {0u, 0u, 0u, 0u};
+    const bool ok = row0 + r < nvalid;
+    *(u32x4*)(tile + r * TSTR + c) = ok ? v0 : z;
+    *(u32x4*)(tile + r * TSTR + c + 8) = ok ? v1 : z;
+    return;
+  }
   if (row0 + r < nvalid) {
     const T* g = stage_addr(base, (int64_t)(row0 + r) * kHeadDim + c);
     lds_store8<T>(tile, plane, r * TSTR + c, g);
@@ -139,6 +148,28 @@ __device__ __forceinline__ void stage_window(uint16_t* win, const T* table, F ro
   const int t = threadIdx.x;
   const int c = (t & 3) * 16;
   const int plane = WIN * TSTR;
+  if constexpr (NP == 1) {
+    // bf16: every read first, without branches (a missing row reads row 0 and stores zeros),
+    // so that the three row groups cost one round trip
+    u32x4 v[3][2];
+    bool ok[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int row = rowfn(64 * i + (t >> 2));
+      ok[i] = row >= 0;
+      const u32x4* g = (const u32x4*)stage_addr(table, (int64_t)max(row, 0) * kHeadDim + c);
+      v[i][0] = g[0];
+      v[i][1] = g[1];
+    }
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int x = 64 * i + (t >> 2);
+      *(u32x4*)(win + x * TSTR + c) = ok[i] ? v[i][0] : z;
+      *(u32x4*)(win + x * TSTR + c + 8) = ok[i] ? v[i][1] : z;
+    }
+    return;
+  }
 #pragma unroll
   for (int x0 = 0; x0 < WIN; x0 += 64) {
     const int x = x0 + (t >> 2);

@@ -946,17 +946,36 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           }
         }
       __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 3; ++i) {
-        const int ab = gp + 2 * i;
-        const int tlo = 32 * ab, thi = tlo + 31;
+      if constexpr (V::TK) {
+        // (chunk-outer: each streamed-row operand is read once for the three blocks; every
+        // accumulator still takes its chunks in ascending order.  The general passes of Shaw
+        // and DeBERTa, tighter on registers, keep the block-outer order below.)
 #pragma unroll
         for (int cq = 0; cq < 4; ++cq) {
           const int ylo = 16 * cq, yhi = ylo + 15;
-          if (thi < ylo || tlo > yhi + 127) continue;   // no pair of this block and chunk
-          Op<NP> eop = op_rows_tr<NP>(e2t, BOTH * ESTRT, ESTRT, ylo, tlo);
           Op<NP> qop2 = op_rows_tr<NP>(ys, BOTH * TSTR, TSTR, ylo, 32 * gdb);
-          mma<NP>(racc[i], eop, qop2);
+#pragma unroll
+          for (int i = 0; i < 3; ++i) {
+            const int ab = gp + 2 * i;
+            const int tlo = 32 * ab, thi = tlo + 31;
+            if (thi < ylo || tlo > yhi + 127) continue;   // no pair of this block and chunk
+            Op<NP> eop = op_rows_tr<NP>(e2t, BOTH * ESTRT, ESTRT, ylo, tlo);
+            mma<NP>(racc[i], eop, qop2);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const int ab = gp + 2 * i;
+          const int tlo = 32 * ab, thi = tlo + 31;
+#pragma unroll
+          for (int cq = 0; cq < 4; ++cq) {
+            const int ylo = 16 * cq, yhi = ylo + 15;
+            if (thi < ylo || tlo > yhi + 127) continue;   // no pair of this block and chunk
+            Op<NP> eop = op_rows_tr<NP>(e2t, BOTH * ESTRT, ESTRT, ylo, tlo);
+            Op<NP> qop2 = op_rows_tr<NP>(ys, BOTH * TSTR, TSTR, ylo, 32 * gdb);
+            mma<NP>(racc[i], eop, qop2);
+          }
         }
       }
       // block gp leaves the window with this step (the next window starts 64 offsets higher)

@@ -370,6 +370,7 @@ __device__ __forceinline__ void col_skew_add(f32x16 s[2], const uint16_t* win, i
   const int lane = __lane_id();
   const int l32 = lane & 31, kh = lane >> 5;
   f32x16 h[2];
+  int prow[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
     const int bb = ob + i;
@@ -386,11 +387,16 @@ __device__ __forceinline__ void col_skew_add(f32x16 s[2], const uint16_t* win, i
         for (int j = 0; j < 4; ++j) h[i][4 * q4 + j] = v4[j];
       }
     }
-    const int prow = pb + l32;
+    prow[i] = pb + l32;
+  }
+  // (chunk-outer: each streamed-row operand is read once for both blocks; each block still
+  // takes its chunks in ascending order)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, prow * TSTR + 16 * c + 8 * kh);
-      Op<NP> yop = op_from_lds<NP>(ytile, BOTH * TSTR, (32 * ob + l32) * TSTR + 16 * c + 8 * kh);
+  for (int c = 0; c < 4; ++c) {
+    Op<NP> yop = op_from_lds<NP>(ytile, BOTH * TSTR, (32 * ob + l32) * TSTR + 16 * c + 8 * kh);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      Op<NP> aop = op_from_lds<NP>(win, WIN * TSTR, prow[i] * TSTR + 16 * c + 8 * kh);
       mma<NP>(h[i], aop, yop);
     }
   }

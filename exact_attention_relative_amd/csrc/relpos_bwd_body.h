@@ -86,7 +86,9 @@ struct BV {
 // ----------------------------------------------------------------------------- kernel
 // T is the element type of the inputs (uint16_t = bf16 bits, or float); fp32 operands enter the
 // matrix cores as NP = 2 bf16 planes (hi, lo), with every LDS tile holding both planes.
-template <typename T, int MECH, int DIR, int PART>
+// FIRSTK: 1 or 0 fixes at compile time whether this launch stores its partials (the first of
+// a folded pass) or adds to them; -1 reads it from the arguments.
+template <typename T, int MECH, int DIR, int PART, int FIRSTK = -1>
 __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   using V = BV<MECH, DIR, PART>;
   constexpr int NP = Elem<T>::NP;
@@ -132,7 +134,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   // every head shares (fold_slices), slice g fold + sub; the first launch stores the group's
   // partial slot, the later ones add to it
   constexpr bool FOLDS = V::DFAT || V::TK;
-  const bool first = !FOLDS || a.sub == 0;
+  const bool first = FIRSTK >= 0 ? FIRSTK == 1 : (!FOLDS || a.sub == 0);
   if constexpr (FOLDS) {
     if (a.fold > 1) {
       const int g = bid / nb;
@@ -302,6 +304,26 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   float colsum = 0.f;                        // dir 1 T-XL: sum_i dS_ij
   float dcarry = 0.f;                        // diagonal t = lane carried into the next step
   const int gdb = w & 1, gp = w >> 1;        // GEMM tiles of this wave: d-block, t-block parity
+  // T-XL key side: the window block that leaves with a step is written to the r partial in
+  // the next step, after that step's staging reads are issued: the vector-memory counter drains
+  // in issue order, so reads issued after the partial's stores and atomics would wait for them
+  // too.  (bf16; the fp32 pass writes it at once.)
+  constexpr bool TK_DEFER = V::TK && NP == 1;
+  f32x16 rflush = {};
+  // (addressed from the slot's base rebuilt in scalar registers plus a 32-bit lane offset: a
+  // per-lane 64-bit address would be spilled, and its reload waits for every read in flight)
+  auto flush_r = [&](const f32x16& acc, int b0x) {
+    typedef __attribute__((address_space(1))) float gfloat;
+    gchar* base = scalar_ptr(ptg);
+    const uint32_t off =
+        4u * (uint32_t)((b0x + 65 + 32 * gp + 4 * kh) * kHeadDim + 32 * gdb + l32);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      gfloat* f = (gfloat*)(base + off + 4u * (uint32_t)((8 * (r >> 2) + (r & 3)) * kHeadDim));
+      if (first) *f = acc[r];
+      else __builtin_amdgcn_global_atomic_fadd_f32(f, acc[r]);
+    }
+  };
 
   // Store one window accumulator block to the column-side table partial: register r holds
   // offset mu0 + 8 (r / 4) + r % 4 (mu = b - a), column 32 gdb + l32.  Only interior offsets are
@@ -507,6 +529,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       float vr = load_f32(scalar_ptr(a.vr) + 4 * ((int64_t)hs * nrel), 4u * (uint32_t)max(vrr, 0));
       tkl = load_f32(scalar_ptr(a.lse) + 4 * ((int64_t)bhs * L), ol);
       tkd = load_f32(scalar_ptr(a.dsum) + 4 * ((int64_t)bhs * L), ol);
+      // the previous step's leaving block, after this step's reads
+      if constexpr (TK_DEFER) flush_r(rflush, b0 - BOTH);
       const u32x4 z = {0u, 0u, 0u, 0u};
       const bool yin = b0 + r < L, win_ok = wr >= 0;
       const int p0 = wrow(2 * BOTH, xrot);
@@ -979,15 +1003,10 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         }
       }
       // block gp leaves the window with this step (the next window starts 64 offsets higher)
-      if constexpr (V::TK) {
-        float* fb = ptg + (int64_t)(b0 + 65 + 32 * gp + 4 * kh) * kHeadDim + 32 * gdb + l32;
-        if (first) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = racc[0][r];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) unsafeAtomicAdd(fb + (8 * (r >> 2) + (r & 3)) * kHeadDim, racc[0][r]);
-        }
+      if constexpr (TK_DEFER) {
+        rflush = racc[0];   // written early in the next step (or after the sweep)
+      } else if constexpr (V::TK) {
+        flush_r(racc[0], b0);
       } else {
         flush_col(racc[0], b0 - A0 - (BLANE - 1) + 32 * gp + 4 * kh);
       }
@@ -1152,20 +1171,13 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     }
   }
   if constexpr (V::TK) {
-    // blocks gp + 2 and gp + 4 of the last window (shifted into racc[0], racc[1])
+    // the last step's leaving block (still pending when deferred), then blocks gp + 2 and
+    // gp + 4 of the last window (shifted into racc[0], racc[1]), which would have left with
+    // the steps after it
     if (nsteps > 0) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        float* fb = ptg + (int64_t)(bt_last + 65 + 32 * (gp + 2 + 2 * i) + 4 * kh) * kHeadDim +
-                    32 * gdb + l32;
-        if (first) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) fb[(8 * (r >> 2) + (r & 3)) * kHeadDim] = racc[i][r];
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) unsafeAtomicAdd(fb + (8 * (r >> 2) + (r & 3)) * kHeadDim, racc[i][r]);
-        }
-      }
+      if constexpr (TK_DEFER) flush_r(rflush, bt_last);
+      flush_r(racc[0], bt_last + BOTH);
+      flush_r(racc[1], bt_last + 2 * BOTH);
     }
   }
 
@@ -1323,8 +1335,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 // Every bf16 variant fits two workgroups per CU (LDS at most 80 KiB) and is compiled for two
 // waves per SIMD (at most 256 registers per lane).  The fp32 variants hold two bf16 planes of
 // every tile (at most 144 KiB of LDS) and run one workgroup per CU.
-template <typename T, int MECH, int DIR, int PART>
+template <typename T, int MECH, int DIR, int PART, int FIRSTK = -1>
 __global__ __launch_bounds__(256, Elem<T>::NP == 1 ? 2 : 1) void bwd_kernel(BwdArgs a) {
-  bwd_body<T, MECH, DIR, PART>(a);
+  bwd_body<T, MECH, DIR, PART, FIRSTK>(a);
 }
 }  // namespace relpos

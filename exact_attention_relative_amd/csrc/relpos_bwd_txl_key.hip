@@ -7,8 +7,14 @@
 
 namespace relpos {
 
+// The first launch of a folded pass stores the r partials and the later ones add to them: a
+// kernel for each, so that neither carries the other's writes behind a branch (the compiler
+// would then count both among the memory operations a later read waits for).
 void launch_bwd_txl_key(const BwdArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_kernel<uint16_t, MECH_TXL, 1, 0>), grid, dim3(256), 0, stream, a);
+  if (a.sub == 0)
+    hipLaunchKernelGGL((bwd_kernel<uint16_t, MECH_TXL, 1, 0, 1>), grid, dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((bwd_kernel<uint16_t, MECH_TXL, 1, 0, 0>), grid, dim3(256), 0, stream, a);
 }
 
 }  // namespace relpos

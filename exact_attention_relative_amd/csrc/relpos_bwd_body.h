@@ -272,20 +272,30 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   // ---- zero what the sweep will not write ----
   if (V::DFAT && V::HAS_COL && first) {
     // column offsets mu = b - a of every window row of every step are flushed (interior ones)
+    // (table row of mu: Shaw k - mu, DeBERTa mu + k; the end rows, 0 and the last, come from
+    // the row-side sums, so only interior rows outside the flushed range are cleared here)
     const int mlo = bt0 - A0 - (BLANE - 1), mhi = bt_last - A0 + BOTH;
-    for (int64_t e = tid; e < (int64_t)prow_rows * kHeadDim; e += 256) {
-      // table row of mu: Shaw clamp(-mu) + k, DeBERTa clamp(mu + k)
-      const int row = (int)(e / kHeadDim), mu = (MECH == MECH_SHAW) ? span - row : row - span;
-      const bool end = row == V::rowA(span) || row == V::rowB(span);
-      if (!end && !(nsteps > 0 && mu >= mlo && mu <= mhi)) pcol[e] = 0.f;
+    const int rlast = prow_rows - 2;   // last interior row
+    int wl = rlast + 1, wh = rlast;    // flushed interior rows [wl, wh]
+    if (nsteps > 0) {
+      const int r0 = (MECH == MECH_SHAW) ? span - mhi : mlo + span;
+      const int r1 = (MECH == MECH_SHAW) ? span - mlo : mhi + span;
+      wl = clampi(r0, 1, rlast + 1);
+      wh = clampi(r1, wl - 1, rlast);
     }
+    for (int64_t e = kHeadDim + tid; e < (int64_t)wl * kHeadDim; e += 256) pcol[e] = 0.f;
+    for (int64_t e = (int64_t)(wh + 1) * kHeadDim + tid; e < (int64_t)(rlast + 1) * kHeadDim; e += 256)
+      pcol[e] = 0.f;
   }
   if (V::TK && first) {
-    // rows written by the sweep: [bt0 + 65, bt_last + 256] (ptg is offset by rb rows)
-    for (int64_t e = tid; e < (int64_t)nrk * kHeadDim; e += 256) {
-      const int row = (int)(e / kHeadDim) + rb;
-      if (!(nsteps > 0 && row >= bt0 + 65 && row <= bt_last + 256)) ptg[(int64_t)rb * kHeadDim + e] = 0.f;
-    }
+    // the slot holds rows [rb, rb + nrk); the sweep writes [bt0 + 65, bt_last + 256], so only
+    // the rows below and above that range are cleared here
+    const int r_end = rb + nrk;
+    const int w_lo = nsteps > 0 ? clampi(bt0 + 65, rb, r_end) : r_end;
+    const int w_hi = nsteps > 0 ? clampi(bt_last + 257, w_lo, r_end) : r_end;
+    float* zb = ptg + (int64_t)rb * kHeadDim;
+    for (int64_t e = tid; e < (int64_t)(w_lo - rb) * kHeadDim; e += 256) zb[e] = 0.f;
+    for (int64_t e = (int64_t)(w_hi - rb) * kHeadDim + tid; e < (int64_t)nrk * kHeadDim; e += 256) zb[e] = 0.f;
   }
   if constexpr (V::DIAG && !V::T5BIN) {
     // wave ww writes the offsets [A0 + 32 ww - bt_last - 63, A0 + 32 ww - bt0 + 32]

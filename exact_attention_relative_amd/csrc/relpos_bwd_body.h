@@ -298,11 +298,19 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     for (int64_t e = (int64_t)(w_hi - rb) * kHeadDim + tid; e < (int64_t)nrk * kHeadDim; e += 256) zb[e] = 0.f;
   }
   if constexpr (V::DIAG && !V::T5BIN) {
-    // wave ww writes the offsets [A0 + 32 ww - bt_last - 63, A0 + 32 ww - bt0 + 32]
-    for (int e = tid; e < NWAVE * ndg; e += 256) {
-      const int ww = e / ndg, lam = lam_base + 32 * ww + dxo + (e - ww * ndg);
-      const int lo = A0 + 32 * ww - bt_last - 63, hi = A0 + 32 * ww - bt0 + 32;
-      if (!(nsteps > 0 && lam >= lo && lam <= hi)) pdiag[e] = 0.f;
+    // wave ww writes the offsets [A0 + 32 ww - bt_last - 63, A0 + 32 ww - bt0 + 32], i.e.
+    // entries [klo, khi] of its row (entry k: lam = lam_base + 32 ww + dxo + k), the same range
+    // in every wave's row; the rest of each row is cleared here
+    int klo = ndg, khi = ndg - 1;
+    if (nsteps > 0) {
+      klo = clampi(A0 - bt_last - 63 - lam_base - dxo, 0, ndg);
+      khi = clampi(A0 - bt0 + 32 - lam_base - dxo, klo - 1, ndg - 1);
+    }
+#pragma unroll
+    for (int ww = 0; ww < NWAVE; ++ww) {
+      float* prw = pdiag + ww * ndg;
+      for (int k = tid; k < klo; k += 256) prw[k] = 0.f;
+      for (int k = khi + 1 + tid; k < ndg; k += 256) prw[k] = 0.f;
     }
   }
 

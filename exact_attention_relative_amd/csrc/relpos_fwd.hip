@@ -134,6 +134,22 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
   }
   const T* rtab = nullptr;
   if constexpr (MECH == MECH_TXL) rtab = (const T*)a.rel_a + h * sh.rel_hs;
+  if constexpr (MECH == MECH_TXL) {
+    // The first key tile's window (192 table rows and their v.r values) and u.k, staged before
+    // the sweep (the first barrier inside the loop orders these writes before any read).  Taken
+    // inside the loop on the first step only, these reads would sit in branches the compiler
+    // cannot rule out on later steps, and it would wait for every read in flight (the next
+    // tile's prefetch included) before reusing their registers.
+    if (jt0 <= j_hi) {
+      const int dlo0 = i0 - (jt0 + BOTH - 1), nrel = sh.nrel, toff = sh.txl_off;
+      stage_window<T, NP>(win, rtab, [&](int x) { return row_side_row(MECH, dlo0 + x, span, nrel, toff); });
+      for (int x = tid; x < WIN; x += 256) {
+        const int r = row_side_row(MECH, dlo0 + x, span, nrel, toff);
+        *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+      }
+      if (tid < BOTH) kvec_s[tid] = (jt0 + tid < L) ? a.uk[(int64_t)bh * L + jt0 + tid] : 0.f;
+    }
+  }
 
   for (int j0 = jt0; j0 <= j_hi; j0 += BOTH) {
     // circular T-XL window: row x of step s sits at physical row (x - 64 s) mod 192
@@ -177,12 +193,14 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
       // (ALiBi reads the slice only on workgroup tiles that straddle the diagonal)
       if ((MECH != MECH_ALIBI || (wg_dlo < 0 && wg_dhi >= 0)) && tid < WIN) vec_s[tid] = plut;
       if (j0 + BOTH <= j_hi) lut_load(j0 + BOTH);
-    } else if (MECH == MECH_TXL && j0 != jt0) {
-      // window rows 0..63 are new: physical rows xrot .. xrot + 63 (the rows that left)
-      pw.store_at(win, WIN * TSTR, xrot);
-      if (tid < BOTH) {
-        *win_vec(win, xrot + tid) = pvr;
-        kvec_s[tid] = puk;
+    } else if constexpr (MECH == MECH_TXL) {
+      if (j0 != jt0) {
+        // window rows 0..63 are new: physical rows xrot .. xrot + 63 (the rows that left)
+        pw.store_at(win, WIN * TSTR, xrot);
+        if (tid < BOTH) {
+          *win_vec(win, xrot + tid) = pvr;
+          kvec_s[tid] = puk;
+        }
       }
     } else if (wg_general) {
       const int toff = sh.txl_off, nrel = sh.nrel;
@@ -190,13 +208,6 @@ __device__ __forceinline__ void fwd_body(const FwdArgs& a) {
       stage_window<T, NP>(win, tab, [&](int x) {
         return row_side_row(MECH, wg_dlo + x, span, nrel, toff);
       });
-      if constexpr (MECH == MECH_TXL) {
-        for (int x = tid; x < WIN; x += 256) {
-          const int r = row_side_row(MECH, wg_dlo + x, span, nrel, toff);
-          *win_vec(win, x) = (r >= 0) ? a.vr[(int64_t)h * nrel + r] : 0.f;
-        }
-        if (tid < BOTH) kvec_s[tid] = (j0 + tid < L) ? a.uk[(int64_t)bh * L + j0 + tid] : 0.f;
-      }
     }
     if constexpr (MECH == MECH_DEBERTA) {
       // end A values of the 64 keys, then end B: each a contiguous vector

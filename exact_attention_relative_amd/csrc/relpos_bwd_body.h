@@ -458,6 +458,10 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   TilePrefetch<T> py, py2;
   TilePrefetch<T> pwn;   // query-side T-XL: the next step's 64 new window rows
   float pvr = 0.f;       // and their v.r values (threads 0..63)
+  float puk = 0.f;       // query-side T-XL: u.k of the next step's keys (threads 0..63)
+  if constexpr (V::TQ) {
+    if (tid < BOTH && nsteps > 0) puk = (bt0 + tid < L) ? a.uk[(int64_t)bh * L + bt0 + tid] : 0.f;
+  }
   if (!V::TG1 && next < nsteps) {
     py.load(yg, step_base(next), L);
     py2.load(y2g, step_base(next), L);
@@ -570,7 +574,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
       if (lut_needed && tid < WIN) vec_s[tid] = plut;
     }
     if constexpr (MECH == MECH_TXL && DIR == 0) {
-      if (tid < BOTH) ovec_s[tid] = (b0 + tid < L) ? a.uk[(int64_t)bh * L + b0 + tid] : 0.f;
+      if (tid < BOTH) ovec_s[tid] = puk;   // (read one step ahead)
     }
     if constexpr (DIR == 1) {
       if (tid < BOTH) {
@@ -658,6 +662,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
         if (tid < BOTH) {
           const int r = row0 + tid;
           pvr = (r >= 0 && r < nrel) ? a.vr[(int64_t)h * nrel + r] : 0.f;
+          const int yy = b0 + BOTH + tid;
+          puk = (yy < L) ? a.uk[(int64_t)bh * L + yy] : 0.f;
         }
       }
     }

@@ -418,6 +418,9 @@ STRESS_SETTINGS = {"t5": dict(num_buckets=32, max_distance=1024), "shaw": dict(r
 STRESS_MECHS = MECH_ORDER + ("alibi",)
 
 
+STRESS_WARMUP = 4   # untimed forward + backward calls per case before the timed ones
+
+
 def run_stress(torch, lengths, reps=10, windows=None):
     """Fixed token budget B * L = 32768 (H = 8, d = 64, bf16) at several lengths, or at
     L = 8192 with several symmetric local windows: forward and backward time, algorithmic
@@ -447,6 +450,9 @@ def run_stress(torch, lengths, reps=10, windows=None):
             fwd(); bwd()
             torch.cuda.synchronize()
             peak = torch.cuda.max_memory_allocated() - base
+            for _ in range(STRESS_WARMUP - 1):   # (the first call above is one warm-up)
+                fwd(); bwd()
+            torch.cuda.synchronize()
             tf, tb = [], []
             for _ in range(reps):
                 e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]

@@ -441,7 +441,8 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     }
   };
   // the next processed step's per-row values are read while the current step computes (not in
-  // the T-XL key-side pass, whose registers are the limit)
+  // the T-XL key-side pass, whose registers are the limit: it reads them with the step's own
+  // batch of reads)
   constexpr bool PF_LSD = DIR == 1 && !V::TK;
   constexpr bool PF_OV = V::CLIP && V::HAS_COL && !V::DFAT;
   auto scalars_load = [&](int b0x) {

@@ -1319,9 +1319,17 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
     if (kh == 0) csum[WROWS * w + l32] = (my_a < L) ? colsum : 0.f;
     __syncthreads();
     if (tid < kHeadDim) {
+      // (rows past L read row L - 1 and meet a zero column sum: no early exit, so the reads
+      // of each group of 16 rows are issued together instead of one round trip per row)
       float acc = 0.f;
-      for (int x = 0; x < BLANE && A0 + x < L; ++x)
-        acc = fmaf(csum[x], Elem<T>::to_f(xg[(int64_t)(A0 + x) * kHeadDim + tid]), acc);
+      for (int x0 = 0; x0 < BLANE; x0 += 16) {
+        float kv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          kv[j] = Elem<T>::to_f(xg[(int64_t)min(A0 + x0 + j, L - 1) * kHeadDim + tid]);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc = fmaf(csum[x0 + j], kv[j], acc);
+      }
       a.part_kv[((int64_t)bh * nb + bid % nb) * kHeadDim + tid] = acc;   // per slice
     }
   }

@@ -321,6 +321,19 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
   float cA = 0.f, cB = 0.f;                  // clipped-end sums of dS (lane row)
   float colsum = 0.f;                        // dir 1 T-XL: sum_i dS_ij
   float dcarry = 0.f;                        // diagonal t = lane carried into the next step
+  // T5: single-bucket wave tiles add to this lane's running sum while the bucket stays the
+  // same (it changes a few times along a row of tiles); the lanes are summed and the bucket
+  // updated only when it changes and after the last step, not once per step
+  float t5acc = 0.f;
+  int t5cur = -1;
+  auto t5_flush = [&]() {
+    if (t5cur >= 0) {
+      float tot = t5acc + xhalf(t5acc);
+      for (int m = 1; m < 32; m <<= 1) tot += __shfl_xor(tot, m);
+      if (lane == 0) binw[t5cur] += tot;
+    }
+    t5acc = 0.f;
+  };
   const int gdb = w & 1, gp = w >> 1;        // GEMM tiles of this wave: d-block, t-block parity
   // T-XL key side: the window block that leaves with a step is written to the r partial in
   // the next step, after that step's staging reads are issued: the vector-memory counter drains
@@ -1115,20 +1128,18 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
             }
           }
         }
-      } else {
-        // single bucket: the wave total goes to one offset of the tile (diagonal 63)
-        float tot = 0.f;
+      } else if constexpr (V::T5BIN) {
+        // single bucket (T5 only): the tile's dS joins this lane's running sum of its bucket
         if (!wave_none) {
+          const int bk = __builtin_amdgcn_readfirstlane(t5b);   // (wave-uniform)
+          if (bk != t5cur) {
+            t5_flush();
+            t5cur = bk;
+          }
 #pragma unroll
           for (int b = 0; b < 2; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) tot += ds[b][r];
-          tot += xhalf(tot);
-          for (int m = 1; m < 32; m <<= 1) tot += __shfl_xor(tot, m);
-        }
-        sums[0] = (lane == 63) ? tot : 0.f;
-        if constexpr (V::T5BIN) {
-          if (!wave_none && lane == 0) binw[t5b] += tot;
+            for (int r = 0; r < 16; ++r) t5acc += ds[b][r];
         }
       }
       if constexpr (V::T5BIN) {
@@ -1171,6 +1182,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
 
   // ---- T5: this workgroup's bucket sums of dS, the waves in a fixed order ----
   if constexpr (V::T5BIN) {
+    t5_flush();
     __syncthreads();
     const int nbk = sh.nbk;
     for (int k = tid; k < nbk; k += 256)

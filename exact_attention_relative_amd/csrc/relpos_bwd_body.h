@@ -883,6 +883,7 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
               cA += __uint_as_float(bits & ~(uint32_t)((sa + yc) >> 31));
               cB += __uint_as_float(bits & ~(uint32_t)((sb - yc) >> 31));
             }
+          asm volatile("" : "+v"(cA), "+v"(cB));
         }
         // dS into the wave's buffer now (its skew reads are done), so that the fp32 copy dies
         // before the content gradients; the row-side dX_rel reads it back after them

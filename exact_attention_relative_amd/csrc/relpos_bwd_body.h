@@ -1105,16 +1105,20 @@ __device__ __forceinline__ void bwd_body(const BwdArgs& a) {
           // Lane l sums diagonal t = l (rows 0 .. min(l, 31)) and, for l < 32, diagonal
           // t = l + 64 (rows l + 1 .. 31): one element of every row, rows in ascending order,
           // so the 32 reads are independent and issue back to back (every T-XL tile runs this)
+          // One running sum over the rows; its value after row min(l, 31) is diagonal l's sum
+          // and the rest of it diagonal l + 64's.
           const float* gd = gs + (63 - lane);   // row n of diagonal l: gd[n * GS2 + n]
           int ln = lane;   // opaque: the tests n <= lane are redone each step, not hoisted
           asm volatile("" : "+v"(ln));
+          float run = 0.f, pre = 0.f;
 #pragma unroll
           for (int n = 0; n < WROWS; ++n) {
             const bool first = n <= ln;
-            const float v = gd[n * GS2 + n - (first ? 0 : 64)];
-            sums[0] += first ? v : 0.f;
-            sums[1] += first ? 0.f : v;
+            run += gd[n * GS2 + n - (first ? 0 : 64)];
+            pre = first ? run : pre;
           }
+          sums[0] = pre;
+          sums[1] = run - pre;
         } else {
           // T5 reaches this only on its multi-bucket tiles: the compact loop, same order
 #pragma unroll

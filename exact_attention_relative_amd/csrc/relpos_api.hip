@@ -390,7 +390,7 @@ int make_proj_plan(const relpos_proj_desc* d, ProjPlan* p) {
 
 extern "C" {
 
-int relpos_profile_events(void* start_event, void* stop_event, int kernel) {
+int relpos_profile_events(hipEvent_t start_event, hipEvent_t stop_event, int kernel) {
   if (kernel == RELPOS_PROF_OFF) {
     g_prof_kernel = RELPOS_PROF_OFF;
     g_prof_start = g_prof_stop = nullptr;
@@ -398,8 +398,8 @@ int relpos_profile_events(void* start_event, void* stop_event, int kernel) {
   }
   if (kernel < RELPOS_PROF_FWD || kernel > RELPOS_PROF_BWD_DKDV || !start_event || !stop_event)
     return RELPOS_E_INVALID;
-  g_prof_start = (hipEvent_t)start_event;
-  g_prof_stop = (hipEvent_t)stop_event;
+  g_prof_start = start_event;
+  g_prof_stop = stop_event;
   g_prof_kernel = kernel;
   return RELPOS_OK;
 }
@@ -426,7 +426,7 @@ int relpos_attn_workspace_size(const relpos_desc* desc, int pass, size_t* bytes)
   return RELPOS_OK;
 }
 
-int relpos_index_map(const relpos_desc* desc, int32_t* out_a, int32_t* out_b, void* stream) {
+int relpos_index_map(const relpos_desc* desc, int32_t* out_a, int32_t* out_b, hipStream_t stream) {
   Plan p;
   int st = make_plan(desc, &p);
   if (st != RELPOS_OK) return st;
@@ -435,13 +435,13 @@ int relpos_index_map(const relpos_desc* desc, int32_t* out_a, int32_t* out_b, vo
   if ((desc->mech == RELPOS_DEBERTA) != (out_b != nullptr)) return RELPOS_E_INVALID;
   if (out_b && !aligned16(out_b)) return RELPOS_E_INVALID;
   hipError_t e = launch_index_map(desc->mech == RELPOS_ALIBI ? MECH_ALIBI : desc->mech, p.L, desc->rel_span, p.nrel, p.txl_off, p.t5, out_a,
-                                  out_b, (hipStream_t)stream);
+                                  out_b, stream);
   return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
 }
 
 int relpos_attn_fwd(const relpos_desc* desc, const void* q, const void* k, const void* v,
                     const void* rel_a, const void* rel_b, const float* bias_a, const float* bias_b,
-                    void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+                    void* o, float* lse, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Plan p;
   int st = make_plan(desc, &p);
   if (st != RELPOS_OK) return st;
@@ -451,7 +451,7 @@ int relpos_attn_fwd(const relpos_desc* desc, const void* q, const void* k, const
   for (const void* ptr : {q, k, v, (const void*)o, (const void*)lse})
     if (!ptr || !aligned16(ptr)) return RELPOS_E_INVALID;
   if (!ws_ok(workspace, workspace_bytes, p.fwd_bytes)) return RELPOS_E_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = stream;
   char* ws = (char*)workspace;
   hipError_t e = run_prep(desc, p, q, k, rel_a, rel_b, bias_a, bias_b, ws, s);
   if (e != hipSuccess) return RELPOS_E_LAUNCH;
@@ -480,7 +480,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
                     const void* o, const float* lse, const void* dout, const void* rel_a,
                     const void* rel_b, const float* bias_a, const float* bias_b, void* dq, void* dk,
                     void* dv, float* drel_a, float* drel_b, float* dbias_a, float* dbias_b,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
   Plan p;
   int st = make_plan(desc, &p);
   if (st != RELPOS_OK) return st;
@@ -492,7 +492,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
     return RELPOS_E_INVALID;
   for (const void* ptr : {(const void*)drel_a, (const void*)drel_b, (const void*)dbias_a, (const void*)dbias_b})
     if (ptr && !aligned16(ptr)) return RELPOS_E_INVALID;
-  hipStream_t s = (hipStream_t)stream;
+  hipStream_t s = stream;
   if (p.B == 0 || p.L == 0) {
     // no pairs: every table gradient is zero (nrel is clamped at 0 when L = 0)
     size_t n_a = 0, n_b = 0, n_ba = 0, n_bb = 0;
@@ -633,14 +633,14 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
 }
 
 int relpos_project_fwd(const relpos_proj_desc* desc, const void* X, const void* W, void* rel,
-                       void* stream) {
+                       hipStream_t stream) {
   ProjPlan p;
   int st = make_proj_plan(desc, &p);
   if (st != RELPOS_OK) return st;
   if (p.N == 0) return RELPOS_OK;
   for (const void* ptr : {X, W, (const void*)rel})
     if (!ptr || !aligned16(ptr)) return RELPOS_E_INVALID;
-  hipError_t e = launch_project_fwd(X, W, rel, p.N, p.F, p.H, p.d, p.fp32, (hipStream_t)stream);
+  hipError_t e = launch_project_fwd(X, W, rel, p.N, p.F, p.H, p.d, p.fp32, stream);
   return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
 }
 
@@ -655,7 +655,7 @@ int relpos_project_workspace_size(const relpos_proj_desc* desc, size_t* bytes) {
 
 int relpos_project_bwd(const relpos_proj_desc* desc, const void* X, const void* W,
                        const float* drel, float* dX, float* dW, void* workspace,
-                       size_t workspace_bytes, void* stream) {
+                       size_t workspace_bytes, hipStream_t stream) {
   ProjPlan p;
   int st = make_proj_plan(desc, &p);
   if (st != RELPOS_OK) return st;
@@ -668,7 +668,7 @@ int relpos_project_bwd(const relpos_proj_desc* desc, const void* X, const void* 
   if (dW && p.ws_bytes && !ws_ok(workspace, workspace_bytes, p.ws_bytes))
     return RELPOS_E_WORKSPACE;
   hipError_t e = launch_project_bwd(X, W, drel, dX, dW, (float*)workspace, p.kslices, p.N, p.F,
-                                    p.H, p.d, p.fp32, (hipStream_t)stream);
+                                    p.H, p.d, p.fp32, stream);
   return e == hipSuccess ? RELPOS_OK : RELPOS_E_LAUNCH;
 }
 

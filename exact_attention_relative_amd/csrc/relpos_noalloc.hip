@@ -38,7 +38,7 @@ void* scratch_ptr() {
 extern "C" int relpos_attn_fwd_noalloc(const relpos_desc* desc, const void* q, const void* k,
                                        const void* v, const void* rel_a, const void* rel_b,
                                        const float* bias_a, const float* bias_b, void* o,
-                                       float* lse, void* stream) {
+                                       float* lse, hipStream_t stream) {
   // size check first, on the host only: nothing is launched for a refused call
   size_t need = 0;
   int st = relpos_attn_workspace_size(desc, 0, &need);

@@ -48,7 +48,7 @@
  * Ownership: the caller owns every buffer, including the workspace (size it with
  * relpos_attn_workspace_size).  The library never allocates device memory.  All device
  * pointers must be 16-byte aligned, the workspace 256-byte aligned.  Work is enqueued on
- * `stream` (a hipStream_t; NULL = the default stream) and the call returns without
+ * `stream` (NULL = the default stream) and the call returns without
  * synchronising.  Results are bitwise deterministic: every sum is taken in a fixed order (the
  * few atomic adds, see relpos_attn_bwd, reach each address once per launch, launches in stream
  * order).
@@ -62,6 +62,12 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+/* HIP's stream and event handles, declared as HIP's runtime header declares them (opaque
+ * pointers), so that this header also compiles without the HIP headers; a repeated identical
+ * typedef is valid C11 and C++. */
+typedef struct ihipStream_t* hipStream_t;
+typedef struct ihipEvent_t* hipEvent_t;
 
 #ifdef __cplusplus
 extern "C" {
@@ -122,7 +128,7 @@ int relpos_attn_workspace_size(const relpos_desc* desc, int pass, size_t* bytes)
 int relpos_attn_fwd(const relpos_desc* desc, const void* q, const void* k, const void* v,
                     const void* rel_a, const void* rel_b, const float* bias_a,
                     const float* bias_b, void* o, float* lse, void* workspace,
-                    size_t workspace_bytes, void* stream);
+                    size_t workspace_bytes, hipStream_t stream);
 
 /* Backward from (q, k, v, o, lse, dout): writes dq, dk, dv and the table gradients
  * (T5: dbias_a = dbeta; Shaw: drel_a = dw; T-XL: drel_a = dr, dbias_a = du, dbias_b = dv;
@@ -145,7 +151,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
                     const void* o, const float* lse, const void* dout, const void* rel_a,
                     const void* rel_b, const float* bias_a, const float* bias_b, void* dq,
                     void* dk, void* dv, float* drel_a, float* drel_b, float* dbias_a,
-                    float* dbias_b, void* workspace, size_t workspace_bytes, void* stream);
+                    float* dbias_b, void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* The forward for callers that cannot allocate device memory (code under graph capture, tight
  * serving loops, harnesses that forbid allocation): the same kernels and results as
@@ -161,7 +167,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
 #define RELPOS_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
 int relpos_attn_fwd_noalloc(const relpos_desc* desc, const void* q, const void* k, const void* v,
                             const void* rel_a, const void* rel_b, const float* bias_a,
-                            const float* bias_b, void* o, float* lse, void* stream);
+                            const float* bias_b, void* o, float* lse, hipStream_t stream);
 
 /* Index maps the kernels use, computed on the device: for every offset delta = i - j in
  * [-(L-1), L-1], out_a[delta + L - 1] is the table row of that offset (T5 bucket, Shaw row,
@@ -169,7 +175,8 @@ int relpos_attn_fwd_noalloc(const relpos_desc* desc, const void* q, const void* 
  * and, for DeBERTa only,
  * out_b[delta + L - 1] is the p2c row (out_b must be NULL otherwise).  Both int32 device
  * buffers of 2L - 1 entries. */
-int relpos_index_map(const relpos_desc* desc, int32_t* out_a, int32_t* out_b, void* stream);
+int relpos_index_map(const relpos_desc* desc, int32_t* out_a, int32_t* out_b,
+                     hipStream_t stream);
 
 /* Relation-table projections.  The T-XL table r and the DeBERTa tables Kr, Qr are projections
  * of a position basis in the original mechanisms (T-XL: r = R W_r, R the sinusoid features of
@@ -203,23 +210,23 @@ typedef struct relpos_proj_desc {
 } relpos_proj_desc;
 
 int relpos_project_fwd(const relpos_proj_desc* desc, const void* X, const void* W, void* rel,
-                       void* stream);
+                       hipStream_t stream);
 int relpos_project_workspace_size(const relpos_proj_desc* desc, size_t* bytes);
 int relpos_project_bwd(const relpos_proj_desc* desc, const void* X, const void* W,
                        const float* drel, float* dX, float* dW, void* workspace,
-                       size_t workspace_bytes, void* stream);
+                       size_t workspace_bytes, hipStream_t stream);
 
 /* Profiling hook for benchmarks.  When `kernel` is RELPOS_PROF_FWD, RELPOS_PROF_BWD_DQ or
  * RELPOS_PROF_BWD_DKDV, later calls made BY THE SAME HOST THREAD record `start_event` on their
  * stream just before enqueueing that pass and `stop_event` just after its last launch (both
- * hipEvent_t created by the caller).  A pass may be several launches (the light and general
+ * created by the caller).  A pass may be several launches (the light and general
  * parts of Shaw and DeBERTa, folded batch entries); the T-XL key-side pass under
  * max_partial_bytes also spans the aggregations between its slice groups.  RELPOS_PROF_OFF (0) clears the hook.  The setting is thread-local:
  * calls from other threads never see it, so the library stays safe to call from several
  * threads on their own streams.  Returns RELPOS_E_INVALID for an unknown kernel id or NULL
  * events. */
 enum { RELPOS_PROF_OFF = 0, RELPOS_PROF_FWD = 1, RELPOS_PROF_BWD_DQ = 2, RELPOS_PROF_BWD_DKDV = 3 };
-int relpos_profile_events(void* start_event, void* stop_event, int kernel);
+int relpos_profile_events(hipEvent_t start_event, hipEvent_t stop_event, int kernel);
 
 /* Static string naming a status code. */
 const char* relpos_status_string(int status);

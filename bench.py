@@ -243,10 +243,11 @@ def summarize_sq(csv1, csv2, out, cmd, steps_per_wave=128):
              "sweep only part of the steps, so theirs read low). `MFMA busy` = "
              "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs). `VALU active` = "
              "SQ_ACTIVE_INST_VALU x 4 on the same base. `wait` = SQ_WAIT_ANY / SQ_WAVE_CYCLES. "
-             "`bank conflicts` = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
+             "`bank conflicts` = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE. `LDS active` = "
+             "SQ_LDS_IDX_ACTIVE / (GRBM_GUI_ACTIVE / 8 x 256 CUs).", "",
              "| pass | kernel | VALU / step | SALU / step | LDS / step | exp / step | MFMA ops / step | "
-             "MFMA busy | VALU active | wait | bank conflicts |",
-             "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+             "MFMA busy | VALU active | LDS active | wait | bank conflicts |",
+             "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for (key, name), d in sorted(data.items()):
         g = lambda c: d.get(c, 0.0) / max(cnt.get((key, name, c), 0), 1)
         waves = g("SQ_WAVES")
@@ -260,6 +261,7 @@ def summarize_sq(csv1, csv2, out, cmd, steps_per_wave=128):
             f"{g('SQ_INSTS_VALU_TRANS_F32') / ws:.1f} | {g('SQ_INSTS_VALU_MFMA_MOPS_BF16') / ws / 64:.1f} | "
             f"{g('SQ_VALU_MFMA_BUSY_CYCLES') / max(simd, 1):.3f} | "
             f"{4 * g('SQ_ACTIVE_INST_VALU') / max(simd, 1):.3f} | "
+            f"{g('SQ_LDS_IDX_ACTIVE') / max(simd / 4, 1):.3f} | "
             f"{g('SQ_WAIT_ANY') / max(g('SQ_WAVE_CYCLES'), 1):.3f} | "
             f"{g('SQ_LDS_BANK_CONFLICT') / max(g('SQ_LDS_IDX_ACTIVE'), 1):.3f} |")
     lines += ["", "`MFMA ops / step` counts 32x32x16 bf16 MFMAs (MOPS_BF16 / 64).", "",
@@ -361,6 +363,58 @@ def measured_mfma_peak(torch):
     if rc != 0:
         raise RuntimeError(f"MFMA probe failed ({rc})")
     return val.value
+
+
+def measured_valu_rates(torch):
+    """Sustained vector-ALU rates of this device in giga lane-operations per second: the base-2
+    exponential (v_exp_f32) and the fp32 fused multiply-add (measurement-only probe library)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_relative_amd", "librelpos_probe.so"))
+    lib.relpos_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                      ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    blocks = 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    rates = {}
+    for kind, name in ((0, "exp2_Glane_ops_per_s"), (1, "fma_f32_Glane_ops_per_s")):
+        val = ctypes.c_double(0.0)
+        rc = lib.relpos_probe_valu(kind, 2000, blocks, ctypes.c_void_p(out.data_ptr()),
+                                   ctypes.byref(val),
+                                   ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"vector-ALU probe {kind} failed ({rc})")
+        rates[name] = val.value
+    return rates
+
+
+def probe_overlap(torch, iters=4000):
+    """How much vector work hides under matrix work on one SIMD (measurement-only probe
+    library).  For each workgroup count: matrix units alone, vector units alone, both in every
+    wave, and both split over the two halves of 512-thread workgroups (the same number of them:
+    one wave of each kind per SIMD, the same work as the first two together).  `hidden` is the
+    share of the shorter alone-time that disappears: 1 = full overlap (the time is the longer
+    alone-time), 0 = none (their sum)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_attention_relative_amd", "librelpos_probe.so"))
+    lib.relpos_probe_overlap.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                         ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    res = []
+    for blocks in (256, 512):   # one or two workgroups per CU, all resident
+        out = torch.empty(2 * blocks * 256, dtype=torch.float32, device="cuda")
+        t = {}
+        for mode, nb in ((0, blocks), (1, blocks), (2, blocks), (3, blocks)):
+            val = ctypes.c_double(0.0)
+            rc = lib.relpos_probe_overlap(mode, iters, nb, ctypes.c_void_p(out.data_ptr()),
+                                          ctypes.byref(val),
+                                          ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"overlap probe mode {mode} failed ({rc})")
+            t[mode] = val.value
+        lo, hi = min(t[0], t[1]), max(t[0], t[1])
+        res.append({"workgroups_per_cu": blocks / 256, "matrix_ms": t[0], "vector_ms": t[1],
+                    "in_wave_ms": t[2], "across_waves_ms": t[3],
+                    "hidden_in_wave": (t[0] + t[1] - t[2]) / lo,
+                    "hidden_across_waves": (t[0] + t[1] - t[3]) / lo})
+    return res
 
 
 PASS_REPS = 10   # repetitions behind each per-mechanism forward / backward median
@@ -548,6 +602,8 @@ def main():
                     help="length stress at a fixed token budget (prints its own JSON line)")
     ap.add_argument("--windows", default=None, metavar="W1,W2,...",
                     help="symmetric local windows at L=8192 (prints its own JSON line)")
+    ap.add_argument("--probe-overlap", action="store_true",
+                    help="time matrix / vector work alone, in one wave and across waves")
     ap.add_argument("--projections", action="store_true",
                     help="time the relation-table projections (prints its own JSON line)")
     ap.add_argument("--only", default=None,
@@ -599,6 +655,9 @@ def main():
         return
     if args.projections:
         print(json.dumps({"projections": run_projections(torch), "data": "synthetic"}))
+        return
+    if args.probe_overlap:
+        print(json.dumps({"overlap": probe_overlap(torch)}))
         return
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * 2**20 // 4
@@ -687,6 +746,7 @@ def main():
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     traffic, traffic_src = recorded_traffic(dom_mech, dom_kernel)
     peak_meas = measured_mfma_peak(torch)
+    valu_meas = measured_valu_rates(torch)
     # the pass may be several launches of one kernel: flops, time and traffic are per pass
     nl = pass_launches(dm["case"], dom_mech, dom_kernel)
     traffic_launch = traffic
@@ -699,6 +759,7 @@ def main():
                 "launches": nl, "avg_launch_ms": dom_ms / nl if nl else None,
                 "flops_per_launch": dom_flops, "traffic_source": traffic_src,
                 "peak_measured": peak_meas, "frac_of_measured": achieved / peak_meas,
+                "valu_measured": valu_meas,
                 "kernel_source_sha": kernel_source_sha()}
 
     cpu = None

@@ -26,11 +26,12 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), n
 
 
-def test_probe_library_exports_its_declared_symbol():
-    """include/relpos_probe.h declares the measurement-only MFMA probe of librelpos_probe.so."""
+def test_probe_library_exports_its_declared_symbols():
+    """include/relpos_probe.h declares the measurement-only MFMA and vector-ALU probes of
+    librelpos_probe.so."""
     src = open(os.path.join(ROOT, "include", "relpos_probe.h")).read()
     names = set(re.findall(r"^\s*\w+\s+(relpos_\w+)\s*\(", src, re.M))
-    assert names == {"relpos_probe_mfma_bf16"}
+    assert names == {"relpos_probe_mfma_bf16", "relpos_probe_valu", "relpos_probe_overlap"}
     path = os.path.join(ROOT, "exact_attention_relative_amd", "librelpos_probe.so")
     assert os.path.exists(path), "build the package first"
     lib = ctypes.CDLL(path)

@@ -127,8 +127,9 @@ def _pmc_rows(path):
 
 
 def summarize_pmc(fetch_csv, write_csv, copy_mib, out, cmd):
-    """HBM bytes per pass launch from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each divided
-    by the factor the same counter reads for a plain copy of copy_mib MiB."""
+    """HBM bytes per pass from FETCH_SIZE / WRITE_SIZE (KiB per dispatch), each divided by the
+    factor the same counter reads for a plain copy of copy_mib MiB; a pass's kernels are weighted
+    by their dispatches per pass."""
     known_kib = copy_mib * 1024.0
     res = {}
     for ctr, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -156,16 +157,19 @@ def summarize_pmc(fetch_csv, write_csv, copy_mib, out, cmd):
              "calibrated MB/dispatch |", "|---|---|---:|---:|---:|---:|"]
     records = []
     for key in sorted(per_fetch):
+        # a pass may be several kernels, some dispatched more than once per pass (the folded
+        # launches): the kernel dispatched least often runs once per pass
+        passes = min(len(vals) for vals in per_fetch[key].values())
         total = 0.0
         for name, vals in sorted(per_fetch[key].items()):
             fv = float(np.mean(vals))
             wv = float(np.mean(per_write.get(key, {}).get(name, [0.0])))
             b = (fv / f_fetch + wv / f_write) * 1024.0
-            total += b
+            total += b * len(vals) / passes
             lines.append(f"| {key[0]} {key[1]} | `{name[:70]}` | {len(vals)} | {fv:.1f} | {wv:.1f} | "
                          f"{b / 1e6:.1f} |")
         records.append({"mech": key[0], "pass": key[1], "source_sha": sha,
-                        "bytes_per_launch": total})
+                        "bytes_per_pass": total})
     lines += ["", f"Kernel sources hash: `{sha}`.", ""]
     for r in records:
         lines.append("traffic-record: " + json.dumps(r))
@@ -271,7 +275,7 @@ def summarize_sq(csv1, csv2, out, cmd, steps_per_wave=128):
 
 
 def recorded_traffic(mech, pass_name):
-    """Calibrated HBM bytes per launch of (mech, pass), if counters exist for these sources."""
+    """Calibrated HBM bytes of one (mech, pass) pass, if counters exist for these sources."""
     sha = kernel_source_sha()
     for path in sorted(glob.glob(os.path.join(PROFILES, "hbm_traffic_*.md"))):
         with open(path) as f:
@@ -279,7 +283,7 @@ def recorded_traffic(mech, pass_name):
                 if line.startswith("traffic-record: "):
                     r = json.loads(line[len("traffic-record: "):])
                     if r["mech"] == mech and r["pass"] == pass_name and r["source_sha"] == sha:
-                        return r["bytes_per_launch"], os.path.relpath(path, ROOT)
+                        return r["bytes_per_pass"], os.path.relpath(path, ROOT)
     return None, None
 
 
@@ -749,9 +753,7 @@ def main():
     valu_meas = measured_valu_rates(torch)
     # the pass may be several launches of one kernel: flops, time and traffic are per pass
     nl = pass_launches(dm["case"], dom_mech, dom_kernel)
-    traffic_launch = traffic
-    if traffic is not None:
-        traffic = traffic * nl if nl else None
+    traffic_launch = traffic / nl if (traffic is not None and nl) else None
     roofline = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": achieved / PEAK_BF16_TFLOPS, "traffic": traffic,
                 "traffic_per_launch": traffic_launch,

@@ -71,7 +71,9 @@ __global__ __launch_bounds__(COMPACT ? 1024 : 256) void agg_diag_kernel(
   __shared__ float sh[NG][64];
   const int t = threadIdx.x, j = t & 63, g = t >> 6;
   const int n = 2 * L - 1, nch = (n + 63) / 64;
-  const int h = blockIdx.x / nch, c0 = 64 * (blockIdx.x - h * nch);
+  // heads vary fastest along the grid: the workgroups that land on one CU then hold chunks
+  // spread over the offset range (the owner count of a chunk falls off away from offset 0)
+  const int h = blockIdx.x % H, c0 = 64 * (blockIdx.x / H);
   const bool valid = c0 + j < n;
   const int ndg = diag_width(L, wl, wr);
   // lane offset delta = c0 + j - (L - 1) sits at x = lim - xs(u) of wave row u, with
@@ -159,7 +161,9 @@ __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict
                                                          int ns, int first, int last, int shared,
                                                          float* __restrict__ dr) {
   const int nch = (nrel + 63) / 64;
-  const int h = blockIdx.x / nch, row0 = 64 * (blockIdx.x % nch);
+  // heads vary fastest along the grid (as in agg_diag_kernel): balanced work per CU
+  const int HG = gridDim.x / nch;
+  const int h = blockIdx.x % HG, row0 = 64 * (blockIdx.x / HG);
   const int t = threadIdx.x;
   const int delta0 = row0 - off;
   f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};

@@ -72,7 +72,8 @@ __global__ __launch_bounds__(COMPACT ? 1024 : 256) void agg_diag_kernel(
   const int t = threadIdx.x, j = t & 63, g = t >> 6;
   const int n = 2 * L - 1, nch = (n + 63) / 64;
   // heads vary fastest along the grid: the workgroups that land on one CU then hold chunks
-  // spread over the offset range (the owner count of a chunk falls off away from offset 0)
+  // spread over the offset range (the owner count of a chunk falls off away from offset 0), and
+  // each XCD (workgroups go to the XCDs in turn) reads the partials of fewer heads
   const int h = blockIdx.x % H, c0 = 64 * (blockIdx.x / H);
   const bool valid = c0 + j < n;
   const int ndg = diag_width(L, wl, wr);
@@ -149,25 +150,38 @@ __global__ __launch_bounds__(COMPACT ? 1024 : 256) void agg_diag_kernel(
 // window, the first row of the owner's sweep (its first 64-row step + 65).  One workgroup
 // per (head, 64 consecutive offsets): for every owner the 64 rows it holds for those offsets
 // are one contiguous 16 KB block, read whole and added in a fixed owner order.  The slices are
-// processed in groups [s0, s0 + ns) (slot i nb + p for slice s0 + i): the first group starts
-// from zero, later groups from the raw sums already in dr, and the last applies v . diag and s.
-// With `shared`, one table serves every head: a single "head" of workgroups sums the slices of
-// every head, and the last group's diagonal term is sum_h v_h . diag_h (heads in order).
+// processed in groups [s0, s0 + ns) of the nslices slices (slot i nb + p for slice s0 + i),
+// launched for the heads with a slice in the group only: a head's first group (the one holding
+// its slice h) starts from zero, later ones from the raw sums already in dr, and its last group
+// applies v . diag and s.  With `shared`, one table serves every head: a single "head" of
+// workgroups sums the slices of every head, the call flags `first` / `last` mark its first and
+// last group, and the last group's diagonal term is sum_h v_h . diag_h (heads in order).
 __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict__ prow,
                                                          const float* __restrict__ diag,
                                                          const float* __restrict__ v, int H,
                                                          int L, int nb, int nrt, int wl, int wr,
                                                          int nrel, int off, float s, int s0,
-                                                         int ns, int first, int last, int shared,
-                                                         float* __restrict__ dr) {
+                                                         int ns, int nslices, int first, int last,
+                                                         int shared, float* __restrict__ dr) {
   const int nch = (nrel + 63) / 64;
-  // heads vary fastest along the grid (as in agg_diag_kernel): balanced work per CU
+  // heads vary fastest along the grid, as in agg_diag_kernel.  The grid holds only the heads
+  // with a slice in this group, hb = 0 .. HG - 1 for head (s0 + hb) mod H (one when shared), so
+  // a group of a few heads still spreads its work over every XCD.
   const int HG = gridDim.x / nch;
-  const int h = blockIdx.x % HG, row0 = 64 * (blockIdx.x / HG);
+  const int hb = blockIdx.x % HG, row0 = 64 * (blockIdx.x / HG);
+  const int h = shared ? 0 : (s0 + hb) % H;
   const int t = threadIdx.x;
   const int delta0 = row0 - off;
+  // this head's slices in the group: local i = i0, i0 + H, ... (every slice when shared)
+  const int hstep = shared ? 1 : H;
+  const int i0 = shared ? 0 : ((h - s0) % H + H) % H;
+  const int nh = i0 < ns ? (ns - i0 + hstep - 1) / hstep : 0;
+  // head h's slices are h, h + H, ...: this group holds its first one when s0 <= h, and its last
+  // one when the next slice of h after the group's lies past the end
+  const bool head_first = shared ? first != 0 : h >= s0;
+  const bool head_last = shared ? last != 0 : s0 + i0 + nh * H >= nslices;
   f32x4 acc[4] = {f32x4{}, f32x4{}, f32x4{}, f32x4{}};
-  if (!first) {
+  if (!head_first) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const int e = 4 * t + 1024 * k, row = row0 + (e >> 6);
@@ -193,10 +207,6 @@ __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict
     if (x0of(m) >= nrt) hi = m; else lo = m + 1;
   }
   const int p_hi = lo;
-  // this head's slices in the group: local i = i0, i0 + H, ... (every slice when shared)
-  const int hstep = shared ? 1 : H;
-  const int i0 = shared ? 0 : ((h - s0) % H + H) % H;
-  const int nh = i0 < ns ? (ns - i0 + hstep - 1) / hstep : 0;
   // (slice, owner) pairs in ascending order, four at a time: the 16 loads of a group are in
   // flight together, then added owner by owner (the order of the sum does not change)
   constexpr int G = 4;
@@ -225,7 +235,7 @@ __global__ __launch_bounds__(256) void agg_txl_dr_kernel(const float* __restrict
     const int e = 4 * t + 1024 * k, row = row0 + (e >> 6), d = e & 63;
     if (row >= nrel) continue;
     f32x4 o = acc[k];
-    if (last) {
+    if (head_last) {
       const int delta = row - off;
       o = f32x4{};
       if (delta > -L && delta < L && !shared) {
@@ -358,10 +368,15 @@ hipError_t launch_agg_alibi(const float* part, int B, int H, int nb, float* dm, 
 
 hipError_t launch_agg_txl_dr(const float* prow, const float* diag, const float* v, int H, int L,
                              int nb, int nrk, int wl, int wr, int nrel, int off, float s, int s0,
-                             int ns, bool first, bool last, bool shared, float* dr, hipStream_t st) {
+                             int ns, int nslices, bool first, bool last, bool shared, float* dr,
+                             hipStream_t st) {
   const int nch = (nrel + 63) / 64;
-  hipLaunchKernelGGL(agg_txl_dr_kernel, dim3((shared ? 1 : H) * nch), dim3(256), 0, st, prow, diag,
-                     v, H, L, nb, nrk, wl, wr, nrel, off, s, s0, ns, first ? 1 : 0, last ? 1 : 0,
+  // the heads with a slice in the group [s0, s0 + ns): ns consecutive slices cover min(ns, H)
+  // consecutive heads (mod H) from s0 mod H
+  const int heads = shared ? 1 : std::min(ns, H);
+  if (heads <= 0 || nch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(agg_txl_dr_kernel, dim3(heads * nch), dim3(256), 0, st, prow, diag,
+                     v, H, L, nb, nrk, wl, wr, nrel, off, s, s0, ns, nslices, first ? 1 : 0, last ? 1 : 0,
                      shared ? 1 : 0, dr);
   return hipGetLastError();
 }

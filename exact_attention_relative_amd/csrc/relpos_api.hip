@@ -574,8 +574,8 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
       if (e == hipSuccess)
         e = launch_agg_txl_dr(a.part_q, diag, bias_b, p.H, p.L, p.nb,
                               (int)(p.part_q_stride / kHeadDim), desc->window_left,
-                              desc->window_right, p.nrel, p.txl_off, p.scale, 0, ng * p.H, true,
-                              true, p.rel_hs == 0, drel_a, s);
+                              desc->window_right, p.nrel, p.txl_off, p.scale, 0, ng * p.H,
+                              ng * p.H, true, true, p.rel_hs == 0, drel_a, s);
     }
     const int nbh = p.B * p.H, G = p.txl_group;
     if (G > 0 && e == hipSuccess) {
@@ -590,7 +590,7 @@ int relpos_attn_bwd(const relpos_desc* desc, const void* q, const void* k, const
             r = launch_agg_txl_dr(a.part_q, diag, bias_b, p.H, p.L, p.nb,
                                   (int)(p.part_q_stride / kHeadDim), desc->window_left,
                                   desc->window_right, p.nrel, p.txl_off, p.scale, s0, a.nbh,
-                                  s0 == 0, s0 + G >= nbh, p.rel_hs == 0, drel_a, s);
+                                  nbh, s0 == 0, s0 + G >= nbh, p.rel_hs == 0, drel_a, s);
         }
         return r;
       });

@@ -158,15 +158,17 @@ hipError_t launch_agg_diag(const float* pdiag, int B, int H, int L, int nb, bool
                            int wr, float* diag, hipStream_t st);
 // ALiBi dm[h] = -sum over the owners (b, query block) of head h of part[owner] (fixed order)
 hipError_t launch_agg_alibi(const float* part, int B, int H, int nb, float* dm, hipStream_t st);
-// T-XL dr from the key-side r partials of the slice group [s0, s0 + ns) (partial slot of slice
-// s0 + i, key block p: i nb + p), summed in ascending (slice, block) order.  Groups are added in
-// order: the first overwrites dr, later ones add to it; dr holds raw sums until the last group,
-// which adds v . diag and scales by s.
-// With `shared` one table serves every head: dr [nrel, 64] sums the slices of every head and
-// the diagonal term is sum_h v_h . diag_h.
+// T-XL dr from the key-side r partials of the slice group [s0, s0 + ns) of nslices slices
+// (partial slot of slice s0 + i, key block p: i nb + p), summed in ascending (slice, block)
+// order.  Groups are added in order, each launched for the heads with a slice in it: a head's
+// first group overwrites its dr, later ones add to it; its dr holds raw sums until its last
+// group, which adds v . diag and scales by s.  With `shared` one table serves every head:
+// dr [nrel, 64] sums the slices of every head, `first` / `last` mark the first and last group,
+// and the diagonal term is sum_h v_h . diag_h.
 hipError_t launch_agg_txl_dr(const float* prow, const float* diag, const float* v, int H, int L,
                              int nb, int nrk, int wl, int wr, int nrel, int off, float s, int s0,
-                             int ns, bool first, bool last, bool shared, float* dr, hipStream_t st);
+                             int ns, int nslices, bool first, bool last, bool shared, float* dr,
+                             hipStream_t st);
 // T-XL dv (v . r diagonal term; head h reads r + h r_hs) and du (from the key-side per-owner
 // sums of dS^T k)
 hipError_t launch_agg_txl_uv(const float* pkv, const float* diag, const void* r, int64_t r_hs,
